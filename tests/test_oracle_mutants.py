@@ -1,0 +1,150 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that at least
+one pin catches each: the pins must be able to fail."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.taylor_oracle as orc
+import pins
+
+_orig_taylor = orc.taylor_kernel
+_orig_feat = orc.feature_map
+_orig_weights = orc.multinomial_weights
+_orig_readout = orc._readout
+
+
+def _taylor_dropped_term(x, n):
+    return _orig_taylor(x, max(n - 1, 1)) if n > 1 else _orig_taylor(x, n)
+
+
+def _taylor_wrong_factorial(x, n):
+    x = np.asarray(x, dtype=np.float64)
+    return sum(x ** m / max(m, 1) for m in range(n))
+
+
+def _taylor_wrong_sign(x, n):
+    x = np.asarray(x, dtype=np.float64)
+    return sum((-x) ** m / math.factorial(m) if m == 1 else x ** m / math.factorial(m) for m in range(n))
+
+
+def _weights_none(d, n):
+    return np.ones_like(_orig_weights(d, n))
+
+
+def _weights_mfact(d, n):
+    # m!/alpha! instead of 1/alpha!: the multinomial count without the Taylor 1/m!
+    w, r = _orig_weights(d, n).copy(), 0
+    for m, width in enumerate(orc.block_widths(d, n)):
+        w[r:r + width] *= math.factorial(m)
+        r += width
+    return w
+
+
+def _feat_index_flip(X, n, weighted):
+    X = np.asarray(X, dtype=np.float64)
+    return _orig_feat(X[..., ::-1], n, weighted) if X.shape[-1] > 1 else _orig_feat(X, n, weighted)
+
+
+def _feat_key_side_weighted(X, n, weighted):
+    return _orig_feat(X, n, True)
+
+
+def _readout_den_dropped_row0(phi, S):
+    num = phi @ S[..., :-1]
+    den = phi @ S[..., -1] - phi[..., 0] * S[..., 0, -1] + 1.0
+    return num / den[..., None]
+
+
+def _quadratic_exclusive(Q, K, V, n):
+    Qh, lead = orc._heads(Q)
+    Kh, _ = orc._heads(K)
+    Vh, _ = orc._heads(V)
+    N = Qh.shape[1]
+    mask = np.tril(np.ones((N, N), dtype=bool), k=-1)
+    mask[0, 0] = True
+    out = np.empty(Vh.shape)
+    for h in range(Qh.shape[0]):
+        P = np.where(mask, orc.taylor_kernel(Qh[h] @ Kh[h].T, n), 0.0)
+        out[h] = (P @ Vh[h]) / P.sum(axis=1, keepdims=True)
+    return out.reshape(lead + Vh.shape[1:])
+
+
+def _quadratic_transposed(Q, K, V, n):
+    Qh, lead = orc._heads(Q)
+    Kh, _ = orc._heads(K)
+    Vh, _ = orc._heads(V)
+    N = Qh.shape[1]
+    mask = np.tril(np.ones((N, N), dtype=bool))
+    out = np.empty(Vh.shape)
+    for h in range(Qh.shape[0]):
+        P = np.where(mask, orc.taylor_kernel(Kh[h] @ Qh[h].T, n), 0.0)
+        out[h] = (P @ Vh[h]) / P.sum(axis=1, keepdims=True)
+    return out.reshape(lead + Vh.shape[1:])
+
+
+_orig_decode = orc.decode_step
+
+
+def _decode_readout_first(q, k, v, S, n):
+    o_old, _ = _orig_decode(q, np.zeros_like(np.asarray(k, dtype=np.float64)),
+                            np.zeros_like(np.asarray(v, dtype=np.float64)), S, 1)
+    _, S_new = _orig_decode(q, k, v, S, n)
+    phi = orc.feature_map(q, n, True)
+    num = np.einsum("...t,...tc->...c", phi, np.asarray(S)[..., :-1])
+    den = np.einsum("...t,...t->...", phi, np.asarray(S)[..., -1])
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return num / den[..., None], S_new
+
+
+_orig_merge = orc.merge_states
+
+
+def _merge_wrong(a, b):
+    return np.asarray(a) + 0.5 * np.asarray(b)
+
+
+_orig_planes = orc.states_to_planes
+
+
+def _planes_interleaved(S):
+    return np.asarray(S).reshape(-1)
+
+
+MUTANTS = {
+    "taylor_dropped_term": ("taylor_kernel", _taylor_dropped_term),
+    "taylor_wrong_factorial": ("taylor_kernel", _taylor_wrong_factorial),
+    "taylor_wrong_sign": ("taylor_kernel", _taylor_wrong_sign),
+    "weights_missing": ("multinomial_weights", _weights_none),
+    "weights_times_mfact": ("multinomial_weights", _weights_mfact),
+    "feature_index_flip": ("feature_map", _feat_index_flip),
+    "key_side_weighted": ("feature_map", _feat_key_side_weighted),
+    "readout_den_row0": ("_readout", _readout_den_dropped_row0),
+    "mask_exclusive": ("quadratic_attention", _quadratic_exclusive),
+    "qk_transposed": ("quadratic_attention", _quadratic_transposed),
+    "decode_readout_before_update": ("decode_step", _decode_readout_first),
+    "merge_wrong": ("merge_states", _merge_wrong),
+    "planes_interleaved": ("states_to_planes", _planes_interleaved),
+}
+
+# cheap pins first; each mutant must make at least one of them fail
+_PINS = [pins.pin_hand_example, pins.pin_kron_features, pins.pin_unit_identity,
+         pins.pin_special_cases, pins.pin_decode_equals_recurrence,
+         pins.pin_planes_layout, pins.pin_exact_rational, pins.pin_chunk_additivity,
+         pins.pin_recurrent_vs_quadratic, pins.pin_softmax_library,
+         pins.pin_softmax_convergence]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(orc, attr, fn)
+    caught = []
+    for pin in _PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, ZeroDivisionError, IndexError, KeyError):
+            caught.append(pin.__name__)
+            break
+    assert caught, f"mutant {name} passed every pin"

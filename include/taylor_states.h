@@ -1,0 +1,130 @@
+/*
+ * taylor_states.h -- C ABI of libtaylor_states.so
+ *
+ * Causal attention under the truncated Taylor kernel
+ *     K_n(x) = sum_{m=0}^{n-1} x^m / m!,   x = q.k,
+ * on L2-normalised q and k, computed through n additive recurrent states
+ * ("Expanding Attention: A Taylor-Series Route to Linear-Time Transformers
+ * with a Fixed Number of Recurrent States", abstract): each Taylor term is a
+ * tensor-power inner product, so the history of a head collapses into the
+ * state
+ *     S[t, c] = sum_j mu_t(k_j) * v_j[c]   (c < dv),   S[t, dv] = sum_j mu_t(k_j),
+ * over W = C(dk+n-1, n-1) feature rows t.  mu_t is a packed symmetric
+ * monomial (product of the coordinates named by the non-decreasing index
+ * tuple t); the readout uses phi_t(q) = mu_t(q) / alpha(t)!, so that
+ * phi(q).mu(k) = K_n(q.k), and
+ *     o = phi(q).S[:, :dv] / phi(q).S[:, dv]
+ * (the extra column carries the normaliser; comment thread on the paper,
+ * item 46888355, reply on the "+1").
+ *
+ * Feature rows: blocks m = 0 .. n-1 in ascending order; inside block m the
+ * non-decreasing index tuples of length m in lexicographic order.
+ *
+ * State buffer of B*H heads (floats, contiguous): first the value plane
+ * [B][H][W][dv], then the normaliser plane [B][H][W].  Rows in feature
+ * order.  tt_state_floats() gives W*(dv+1) per head.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major and contiguous,
+ *     allocated and owned by the caller.  The library allocates nothing and
+ *     keeps no state between calls.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *     the default stream).  Kernel faults surface at the caller's next
+ *     synchronisation, not in the return code.
+ *   - Arguments are validated before anything is launched.  On error the
+ *     return value is negative, nothing is launched, and tt_last_error()
+ *     describes the problem (thread-local, valid until the next call on the
+ *     same thread).
+ *   - Inputs are used as given: q and k are NOT re-normalised (unit norm is
+ *     the caller's precondition).  NaN/Inf inputs propagate; a zero
+ *     normaliser (possible for n = 2, where K_2(-1) = 0) gives IEEE Inf/NaN.
+ *   - Outputs must not alias inputs unless stated.
+ *   - Supported shapes: dv = 64; (dk, n) with dk in {16, 32, 64} and
+ *     W <= 4845, i.e. dk=16: n in 1..5, dk=32: n in 1..3, dk=64: n in 1..3.
+ *     Other shapes return TT_ERR_UNSUPPORTED.
+ */
+#ifndef TAYLOR_STATES_H
+#define TAYLOR_STATES_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TT_F32 = 0, TT_BF16 = 1 } tt_dtype;
+
+enum {
+  TT_OK = 0,
+  TT_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad enum      */
+  TT_ERR_UNSUPPORTED = -2, /* valid but outside the compiled shapes          */
+  TT_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required     */
+  TT_ERR_HIP = -4          /* a HIP call or kernel launch reported an error  */
+};
+
+/* Number of feature rows W = sum_{m<n} C(dk+m-1, m) = C(dk+n-1, n-1): the
+ * widths of the n states ("Expanding Attention", abstract).  Pure host
+ * function; 0 if dk < 1, n < 1 or on overflow. */
+size_t tt_state_rows(int dk, int n);
+
+/* Floats of one head's state, W * (dv + 1) (9945 for dk=16, dv=64, n=3,
+ * "Expanding Attention", abstract).  0 on invalid input or overflow. */
+size_t tt_state_floats(int dk, int dv, int n);
+
+/* Bytes of device workspace tt_prefill needs for this shape (written to
+ * *bytes).  Returns TT_OK or an error code as tt_prefill would. */
+int tt_prefill_workspace_bytes(int B, int H, int N, int dk, int dv, int n,
+                               int chunk, size_t *bytes);
+
+/* Chunked causal prefill ("Expanding Attention", abstract: the states add
+ * across chunks, so prefill is a parallel scan; comment thread item
+ * 46888355, reply on (Q'K)V = Q'(KV)).
+ *   Q, K : [B][H][N][dk]   in_dtype (TT_F32 or TT_BF16), read-only
+ *   V    : [B][H][N][dv]   in_dtype, read-only
+ *   O    : [B][H][N][dv]   fp32, written: o_i = sum_{j<=i} K_n(q_i.k_j) v_j
+ *                          / sum_{j<=i} K_n(q_i.k_j)  (causal, inclusive)
+ *   states : B*H*W*(dv+1) fp32 in the plane layout above, written with the
+ *            states of all N tokens (prefill starts from zero states)
+ *   workspace : device scratch of at least tt_prefill_workspace_bytes();
+ *            contents undefined on return
+ *   chunk : tokens per chunk of the intra-chunk quadratic block; 64.
+ * Any N >= 1 is accepted (the tail chunk is masked).  Results do not
+ * depend on how the work is split beyond fp32 rounding. */
+int tt_prefill(const void *Q, const void *K, const void *V, tt_dtype in_dtype,
+               int B, int H, int N, int dk, int dv, int n, int chunk,
+               float *O, float *states, void *workspace, size_t workspace_bytes,
+               void *stream);
+
+/* One generated token per head ("Expanding Attention", abstract: one
+ * rank-one update per state per token, independent of context length):
+ *   S += mu(k) (x) [v, 1];  o = phi(q).S[:, :dv] / phi(q).S[:, dv]
+ * (update first, then read out: the token attends to itself).
+ *   q, k   : [B][H][dk] in_dtype;  v : [B][H][dv] in_dtype
+ *   states : B*H*W*(dv+1) fp32, plane layout, updated in place
+ *   o      : [B][H][dv] fp32, written */
+int tt_decode_step(const void *q, const void *k, const void *v, tt_dtype in_dtype,
+                   int B, int H, int dk, int dv, int n,
+                   float *states, float *o, void *stream);
+
+/* dst[i] = a[i] + b[i] for i < nfloats: the states of two disjoint token
+ * sets add ("Expanding Attention", abstract: additivity across chunks).
+ * dst may alias a or b.  nfloats == 0 is a no-op. */
+int tt_state_merge(float *dst, const float *a, const float *b, size_t nfloats,
+                   void *stream);
+
+/* Feature map of `rows` vectors x[rows][dk] (in_dtype) into out[rows][W]
+ * fp32: mu_t(x) (weighted = 0) or phi_t(x) = mu_t(x)/alpha(t)! (weighted =
+ * 1), rows in feature order ("Expanding Attention", abstract: tensor-power
+ * factorisation of each Taylor term).  A test hook for the device function
+ * the prefill and decode kernels use. */
+int tt_feature_map(const void *x, tt_dtype in_dtype, size_t rows, int dk, int n,
+                   int weighted, float *out, void *stream);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char *tt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TAYLOR_STATES_H */

@@ -129,14 +129,14 @@ def feature_map(X: np.ndarray, n: int, weighted: bool) -> np.ndarray:
     """
     X = np.asarray(X, dtype=np.float64)
     d = X.shape[-1]
-    cols = []
+    blocks = []
     for m in range(n):
-        for t in multi_indices(d, m):
-            v = np.ones(X.shape[:-1], dtype=np.float64)
-            for i in t:
-                v = v * X[..., i]
-            cols.append(v)
-    F = np.stack(cols, axis=-1)
+        T = np.array(multi_indices(d, m), dtype=np.intp).reshape(len(multi_indices(d, m)), m)
+        v = np.ones(X.shape[:-1] + (T.shape[0],), dtype=np.float64)
+        for l in range(m):  # coordinates multiplied left to right along each tuple
+            v = v * X[..., T[:, l]]
+        blocks.append(v)
+    F = np.concatenate(blocks, axis=-1)
     if weighted:
         F = F * multinomial_weights(d, n)
     return F

@@ -1,0 +1,148 @@
+// C entry points of libtaylor_states.so: argument validation, planning and
+// launch on the caller's stream.  No allocation, no global state (apart from
+// the thread-local error message).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "tt_device.hpp"
+#include "tt_internal.hpp"
+
+namespace tt {
+
+static thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+static int ok() {
+  g_err[0] = '\0';
+  return TT_OK;
+}
+
+static int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(TT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static bool shape_supported(int dk, int dv, int n) {
+  if (dv != 64 || n < 1) return false;
+  if (dk == 16) return n <= 5;
+  if (dk == 32 || dk == 64) return n <= 3;
+  return false;
+}
+
+static int check_shape(int dk, int dv, int n) {
+  if (dk < 1 || dv < 1 || n < 1) return fail(TT_ERR_INVALID_ARG, "dk=%d dv=%d n=%d must be >= 1", dk, dv, n);
+  if (!shape_supported(dk, dv, n))
+    return fail(TT_ERR_UNSUPPORTED,
+                "(dk=%d, dv=%d, n=%d) not compiled: dv must be 64; dk=16 with n<=5, dk=32/64 with n<=3", dk,
+                dv, n);
+  return TT_OK;
+}
+
+static int check_dtype(tt_dtype dt) {
+  if (dt != TT_F32 && dt != TT_BF16) return fail(TT_ERR_INVALID_ARG, "in_dtype %d is not TT_F32/TT_BF16", (int)dt);
+  return TT_OK;
+}
+
+}  // namespace tt
+
+using namespace tt;
+
+extern "C" {
+
+size_t tt_state_rows(int dk, int n) {
+  if (dk < 1 || n < 1) return 0;
+  // C(dk+n-1, n-1) computed incrementally; exact at each step
+  unsigned __int128 r = 1;
+  for (int i = 1; i <= n - 1; ++i) {
+    r = r * (unsigned __int128)(dk + i) / (unsigned __int128)i;
+    if (r > (unsigned __int128)SIZE_MAX) return 0;
+  }
+  return (size_t)r;
+}
+
+size_t tt_state_floats(int dk, int dv, int n) {
+  if (dv < 1) return 0;
+  const size_t w = tt_state_rows(dk, n);
+  if (w == 0) return 0;
+  unsigned __int128 f = (unsigned __int128)w * (unsigned __int128)(dv + 1);
+  if (f > (unsigned __int128)SIZE_MAX) return 0;
+  return (size_t)f;
+}
+
+int tt_prefill_workspace_bytes(int B, int H, int N, int dk, int dv, int n, int chunk, size_t* bytes) {
+  if (!bytes) return fail(TT_ERR_INVALID_ARG, "bytes is NULL");
+  if (B < 1 || H < 1 || N < 1) return fail(TT_ERR_INVALID_ARG, "B=%d H=%d N=%d must be >= 1", B, H, N);
+  int rc = check_shape(dk, dv, n);
+  if (rc) return rc;
+  PrefillPlan p;
+  rc = plan_prefill(B, H, N, dk, dv, n, chunk, TT_F32, &p);
+  if (rc) return rc;
+  *bytes = p.ws_floats * sizeof(float);
+  return ok();
+}
+
+int tt_prefill(const void* Q, const void* K, const void* V, tt_dtype in_dtype, int B, int H, int N, int dk,
+               int dv, int n, int chunk, float* O, float* states, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  if (!Q || !K || !V || !O || !states) return fail(TT_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (B < 1 || H < 1 || N < 1) return fail(TT_ERR_INVALID_ARG, "B=%d H=%d N=%d must be >= 1", B, H, N);
+  int rc = check_dtype(in_dtype);
+  if (rc) return rc;
+  rc = check_shape(dk, dv, n);
+  if (rc) return rc;
+  if ((long long)B * H > (1LL << 24)) return fail(TT_ERR_UNSUPPORTED, "B*H=%lld too large", (long long)B * H);
+  PrefillPlan p;
+  rc = plan_prefill(B, H, N, dk, dv, n, chunk, in_dtype, &p);
+  if (rc) return rc;
+  const size_t need = p.ws_floats * sizeof(float);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(TT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (((uintptr_t)workspace & 15u) != 0) return fail(TT_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return hip_status(launch_prefill(Q, K, V, in_dtype, B * H, N, dk, n, p, O, states, (float*)workspace,
+                                   (hipStream_t)stream),
+                    "tt_prefill launch");
+}
+
+int tt_decode_step(const void* q, const void* k, const void* v, tt_dtype in_dtype, int B, int H, int dk, int dv,
+                   int n, float* states, float* o, void* stream) {
+  if (!q || !k || !v || !states || !o) return fail(TT_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (B < 1 || H < 1) return fail(TT_ERR_INVALID_ARG, "B=%d H=%d must be >= 1", B, H);
+  int rc = check_dtype(in_dtype);
+  if (rc) return rc;
+  rc = check_shape(dk, dv, n);
+  if (rc) return rc;
+  if ((long long)B * H > 0x7fffffffLL) return fail(TT_ERR_UNSUPPORTED, "B*H too large");
+  return hip_status(launch_decode(q, k, v, in_dtype, B * H, dk, n, states, o, (hipStream_t)stream),
+                    "tt_decode_step launch");
+}
+
+int tt_state_merge(float* dst, const float* a, const float* b, size_t nfloats, void* stream) {
+  if (nfloats == 0) return ok();
+  if (!dst || !a || !b) return fail(TT_ERR_INVALID_ARG, "a pointer is NULL");
+  return hip_status(launch_merge(dst, a, b, nfloats, (hipStream_t)stream), "tt_state_merge launch");
+}
+
+int tt_feature_map(const void* x, tt_dtype in_dtype, size_t rows, int dk, int n, int weighted, float* out,
+                   void* stream) {
+  if (rows == 0) return ok();
+  if (!x || !out) return fail(TT_ERR_INVALID_ARG, "a pointer is NULL");
+  if (weighted != 0 && weighted != 1) return fail(TT_ERR_INVALID_ARG, "weighted must be 0 or 1");
+  int rc = check_dtype(in_dtype);
+  if (rc) return rc;
+  if (dk < 1 || n < 1) return fail(TT_ERR_INVALID_ARG, "dk=%d n=%d must be >= 1", dk, n);
+  if (!shape_supported(dk, 64, n)) return fail(TT_ERR_UNSUPPORTED, "(dk=%d, n=%d) not compiled", dk, n);
+  return hip_status(launch_feature_map(x, in_dtype, rows, dk, n, weighted, out, (hipStream_t)stream),
+                    "tt_feature_map launch");
+}
+
+const char* tt_last_error(void) { return g_err; }
+
+}  // extern "C"

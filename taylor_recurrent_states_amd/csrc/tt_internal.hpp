@@ -1,0 +1,37 @@
+// Host-side declarations shared by the translation units of libtaylor_states.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/taylor_states.h"
+
+namespace tt {
+
+// Records a message for tt_last_error() and returns `code`.
+int fail(int code, const char* fmt, ...);
+
+// Launchers (argument checking is done by the C entry points).
+hipError_t launch_feature_map(const void* x, tt_dtype dt, size_t rows, int dk, int n, int weighted,
+                              float* out, hipStream_t s);
+hipError_t launch_merge(float* dst, const float* a, const float* b, size_t n, hipStream_t s);
+hipError_t launch_decode(const void* q, const void* k, const void* v, tt_dtype dt, int BH, int dk, int n,
+                         float* states, float* o, hipStream_t s);
+
+// Prefill plan: how the sequence and the columns are split over workgroups.
+struct PrefillPlan {
+  int W;          // feature rows
+  int Wpad;       // rows rounded up to the row-tile multiple
+  int chunk;      // tokens per chunk
+  int span;       // tokens per span (multiple of chunk)
+  int nspan;      // spans per head
+  int ngroups;    // column groups (workgroups per head-span)
+  size_t ws_floats;  // span-state workspace, floats
+};
+
+int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype dt, PrefillPlan* p);
+hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype dt, int BH, int N, int dk,
+                          int n, const PrefillPlan& p, float* O, float* states, float* ws, hipStream_t s);
+
+}  // namespace tt

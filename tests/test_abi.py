@@ -1,0 +1,88 @@
+"""The C-ABI library loads, exports every declared symbol, and validates
+arguments on the host (no kernel is launched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from taylor_recurrent_states_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "taylor_states.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tt_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = ops.lib()
+    declared = _declared()
+    assert set(declared) == set(ops.EXPORTED), declared
+    for name in declared:
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_state_sizes():
+    assert ops.tt_state_rows(16, 3) == 153
+    assert ops.tt_state_floats(16, 64, 3) == 9945
+    assert ops.tt_state_floats(16, 64, 5) == 314925
+    assert ops.tt_state_floats(64, 64, 3) == 139425
+    assert ops.tt_state_rows(16, 1) == 1
+    assert ops.tt_state_rows(0, 3) == 0
+    assert ops.tt_state_rows(16, 0) == 0
+    assert ops.tt_state_floats(16, 0, 3) == 0
+    assert ops.tt_state_rows(1 << 30, 40) == 0  # overflow -> 0
+
+
+def test_workspace_query_and_errors():
+    assert ops.tt_prefill_workspace_bytes(4, 8, 8192, 16, 64, 3, 64) >= 0
+    with pytest.raises(ops.TTError) as e:
+        ops.tt_prefill_workspace_bytes(1, 1, 0, 16, 64, 3, 64)
+    assert e.value.code == ops.TT_ERR_INVALID_ARG
+    with pytest.raises(ops.TTError) as e:
+        ops.tt_prefill_workspace_bytes(1, 1, 16, 16, 48, 3, 64)
+    assert e.value.code == ops.TT_ERR_UNSUPPORTED
+    with pytest.raises(ops.TTError) as e:
+        ops.tt_prefill_workspace_bytes(1, 1, 16, 64, 64, 4, 64)
+    assert e.value.code == ops.TT_ERR_UNSUPPORTED
+
+
+def test_entry_points_reject_bad_arguments_without_launching():
+    L = ops.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    rc = L.tt_decode_step(None, fake, fake, 0, 1, 1, 16, 64, 3, fake, fake, None)
+    assert rc == ops.TT_ERR_INVALID_ARG and "NULL" in ops.tt_last_error()
+    rc = L.tt_decode_step(fake, fake, fake, 7, 1, 1, 16, 64, 3, fake, fake, None)
+    assert rc == ops.TT_ERR_INVALID_ARG
+    rc = L.tt_decode_step(fake, fake, fake, 0, 1, 1, 16, 64, 9, fake, fake, None)
+    assert rc == ops.TT_ERR_UNSUPPORTED
+    rc = L.tt_decode_step(fake, fake, fake, 0, 0, 1, 16, 64, 3, fake, fake, None)
+    assert rc == ops.TT_ERR_INVALID_ARG
+    rc = L.tt_prefill(fake, fake, fake, 1, 1, 1, 100, 16, 64, 3, 64, fake, fake, None, 0, None)
+    need = ops.tt_prefill_workspace_bytes(1, 1, 100, 16, 64, 3, 64)
+    if need > 0:
+        assert rc == ops.TT_ERR_WORKSPACE
+    rc = L.tt_prefill(fake, fake, fake, 1, 1, 1, 100, 16, 64, 3, 48, fake, fake, fake, 1 << 30, None)
+    assert rc == ops.TT_ERR_UNSUPPORTED
+    rc = L.tt_state_merge(None, fake, fake, 4, None)
+    assert rc == ops.TT_ERR_INVALID_ARG
+    assert L.tt_state_merge(None, None, None, 0, None) == ops.TT_OK
+    rc = L.tt_feature_map(fake, 0, 4, 16, 3, 2, fake, None)
+    assert rc == ops.TT_ERR_INVALID_ARG
+    assert L.tt_feature_map(None, 0, 0, 16, 3, 0, None, None) == ops.TT_OK
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    """The package never imports the oracle and has no host compute path."""
+    pkg = os.path.join(ROOT, "taylor_recurrent_states_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
+                assert "taylor_oracle" not in text, f

@@ -71,8 +71,9 @@ size_t tt_state_rows(int dk, int n);
  * "Expanding Attention", abstract).  0 on invalid input or overflow. */
 size_t tt_state_floats(int dk, int dv, int n);
 
-/* Bytes of device workspace tt_prefill needs for this shape (written to
- * *bytes).  Returns TT_OK or an error code as tt_prefill would. */
+/* Bytes of device workspace tt_prefill needs for this shape with either
+ * input dtype (written to *bytes).  Returns TT_OK or an error code as
+ * tt_prefill would. */
 int tt_prefill_workspace_bytes(int B, int H, int N, int dk, int dv, int n,
                                int chunk, size_t *bytes);
 

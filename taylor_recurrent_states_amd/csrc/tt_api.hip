@@ -81,10 +81,13 @@ int tt_prefill_workspace_bytes(int B, int H, int N, int dk, int dv, int n, int c
   if (B < 1 || H < 1 || N < 1) return fail(TT_ERR_INVALID_ARG, "B=%d H=%d N=%d must be >= 1", B, H, N);
   int rc = check_shape(dk, dv, n);
   if (rc) return rc;
-  PrefillPlan p;
-  rc = plan_prefill(B, H, N, dk, dv, n, chunk, TT_F32, &p);
+  // the query takes no dtype: report the larger of the fp32 and bf16 plans
+  PrefillPlan pf, pb;
+  rc = plan_prefill(B, H, N, dk, dv, n, chunk, TT_F32, &pf);
   if (rc) return rc;
-  *bytes = p.ws_floats * sizeof(float);
+  rc = plan_prefill(B, H, N, dk, dv, n, chunk, TT_BF16, &pb);
+  if (rc) return rc;
+  *bytes = (pf.ws_floats > pb.ws_floats ? pf.ws_floats : pb.ws_floats) * sizeof(float);
   return ok();
 }
 

@@ -1,26 +1,712 @@
-// Chunked causal prefill (placeholder until the kernels land).
+// Chunked causal prefill on MFMA.
+//
+// "Expanding Attention: A Taylor-Series Route to Linear-Time Transformers
+// with a Fixed Number of Recurrent States" (abstract): the causal history of
+// a head is the state S[t, :] = sum_j mu_t(k_j) [v_j, 1]; states of disjoint
+// token sets add, so prefill is a scan over spans of the sequence.  Inside a
+// chunk of 64 tokens the output is the readout of the state before the chunk
+// plus the chunk's own causal block of the quadratic form, (Q'K)V = Q'(KV)
+// applied to everything but the diagonal block (comment thread on the paper,
+// item 46888355, reply on the associativity):
+//
+//   num/den(i) = phi(q_i).S_prev + sum_{j in chunk, j <= i} K_n(q_i.k_j) [v_j, 1]
+//   S_prev    += mu(K_chunk)^T [V_chunk, 1]
+//
+// Three launches per call:
+//   1. totals : one workgroup per (head, span, column group) folds its span
+//               into a state from zero and writes it to the workspace.  bf16
+//               inputs use a hi+lo bf16 split of mu, which is exact for a
+//               product of two bf16 values, so span totals carry fp32
+//               accumulation error only.
+//   2. scan   : exclusive prefix over spans, in place; the sum over all spans
+//               is the final state (written in the library's plane layout).
+//   3. sweep  : one workgroup per (head, span, column group) starts from its
+//               prefix, keeps the state in MFMA accumulators, and per chunk
+//               does the readout, the intra-chunk block and the update.
+//
+// The state never leaves registers inside a span.  It is held as 16x16 MFMA
+// accumulator tiles (rows = feature rows, columns = value columns).  The
+// normaliser column ("+1", comment thread reply on the extra column) lives in
+// LDS as one fp32 per feature row and is contracted by MFMA against a ones
+// column, so it stays in fp32.
+//
+// Lane layouts (probed on gfx950): lane l = 16g + i.
+//   bf16 16x16x32: A[i][8g..8g+7], B[8g..8g+7][i];   f32 16x16x4: A[i][g], B[g][i];
+//   D: lane holds D[4g + s][i], s = 0..3.
+// For bf16 a 32-row K-block is two accumulator tiles tau = 0, 1 whose M index
+// 4g'+s holds row 8g' + 4tau + s.  Read back as an MFMA B operand, lane g's
+// k-slots 8g..8g+7 are then rows 8g..8g+7 in natural order, so every LDS
+// tile (features, P, V^T) is stored in natural order.
 #include "tt_device.hpp"
 #include "tt_internal.hpp"
 
 namespace tt {
+namespace {
+
+enum { MODE_TOTALS = 0, MODE_OUTPUT = 1 };
+
+constexpr int kCH = 64;  // tokens per chunk
+constexpr int kDV = 64;  // value columns
+
+// Pick J (K-blocks per wave per slab) <= jmax minimising the padded count.
+constexpr int pick_j(int maxkb, int jmax) {
+  int best = 1, best_pad = 1 << 30;
+  for (int j = (jmax < 1 ? 1 : jmax); j >= 1; --j) {
+    int ns = (maxkb + j - 1) / j;
+    int pad = ns * j;
+    if (pad < best_pad) { best = j; best_pad = pad; }
+  }
+  return best;
+}
+
+template <typename TIn_, int DK_, int NT_, int NVT_, int NRP_, int MODE_>
+struct Cfg {
+  using TIn = TIn_;
+  static constexpr bool BF = std::is_same<TIn_, uint16_t>::value;
+  static constexpr bool OUT = (MODE_ == MODE_OUTPUT);
+  static constexpr int DK = DK_, NT = NT_, NVT = NVT_, NRP = NRP_;
+  static constexpr int NW = NVT * NRP;
+  static constexpr int NTHR = NW * 64;
+  static constexpr int W = rows_for(DK, NT);
+  static constexpr int KB = BF ? 32 : 16;  // feature rows (and tokens) per K-block
+  static constexpr int TPK = BF ? 2 : 1;   // accumulator tiles per K-block
+  static constexpr int NKB = (W + KB - 1) / KB;
+  static constexpr int MAXKB = (NKB + NRP - 1) / NRP;
+  static constexpr int SRMAX = BF ? 256 : 128;
+  static constexpr int J = pick_j(MAXKB, SRMAX / (NRP * KB));
+  static constexpr int NSLAB = (MAXKB + J - 1) / J;
+  static constexpr int MKB = NSLAB * J;    // K-blocks per wave (padded)
+  static constexpr int SR = NRP * J * KB;  // feature rows per slab
+  static constexpr int WP = NSLAB * SR;    // padded feature rows
+  static constexpr int TB = kCH / KB;      // token K-blocks per chunk
+  static constexpr int GC = 16 * NVT;      // value columns per workgroup
+  using Elem = typename std::conditional<BF, uint16_t, float>::type;
+  static constexpr int ES = sizeof(Elem);
+  static constexpr int PADE = 16 / ES;     // 16-byte row padding
+  static constexpr int XS = DK + 1;        // fp32 stride of the Q/K staging rows
+  static constexpr int PHS = SR + PADE;    // phi row stride (elements)
+  static constexpr int MUS = kCH + PADE;   // mu^T row stride
+  static constexpr int VS = kCH + PADE;    // V^T row stride
+  static constexpr int PS = kCH + PADE;    // P row stride
+  static constexpr int NMU = (BF && !OUT) ? 2 : 1;  // mu planes (hi, lo) in the totals pass
+  static constexpr int NPP = BF ? 2 : 1;            // P planes (hi, lo)
+  static constexpr int PPL = kCH * PS;              // elements per P plane
+  static constexpr int MUPL = SR * MUS;             // elements per mu plane
+  // LDS carve-up (bytes, 16-aligned); Q, P and phi exist in the output pass only
+  static constexpr int al(int b) { return (b + 15) / 16 * 16; }
+  static constexpr int O_TAB = 0;
+  static constexpr int O_K = O_TAB + al(WP * 4);
+  static constexpr int O_Q = O_K + al(kCH * XS * 4);
+  static constexpr int O_V = O_Q + (OUT ? al(kCH * XS * 4) : 0);
+  static constexpr int O_P = O_V + al(GC * VS * ES);
+  static constexpr int O_DEN = O_P + (OUT ? al(NPP * PPL * ES) : 0);
+  static constexpr int O_DENQ = O_DEN + al(WP * 4);
+  static constexpr int O_PHI = O_DENQ + al(kCH * 4);
+  static constexpr int O_MU = O_PHI + (OUT ? al(kCH * PHS * ES) : 0);
+  static constexpr int O_END = O_MU + al(NMU * MUPL * ES);
+  static constexpr int RED_BYTES = OUT ? NW * 4 * 64 * 16 : 0;  // partial num tiles
+  static constexpr int LDS = (O_END > O_PHI + RED_BYTES ? O_END : O_PHI + RED_BYTES);
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// 1 / alpha(t)! from a row code (runs of equal indices in the sorted tuple)
+__device__ inline float inv_alpha_fact(uint32_t code) {
+  const int m = row_order(code);
+  int denom = 1, run = 1;
+  for (int l = 1; l < m; ++l) {
+    if (row_index(code, l) == row_index(code, l - 1)) {
+      ++run;
+      denom *= run;
+    } else {
+      run = 1;
+    }
+  }
+  return 1.0f / (float)denom;
+}
+
+template <int NT>
+__device__ inline float taylor_poly(float x) {
+  // K_n(x) = sum_{m<n} x^m/m!  by Horner, coefficients 1/m! in fp32
+  constexpr float c[5] = {1.0f, 1.0f, 0.5f, 1.0f / 6.0f, 1.0f / 24.0f};
+  float p = c[NT - 1];
+#pragma unroll
+  for (int m = NT - 2; m >= 0; --m) p = fmaf(p, x, c[m]);
+  return p;
+}
+
+// bf16 accumulator-tile row for M index i of tile tau: 8*(i/4) + 4*tau + i%4
+__device__ inline int rho(int tau, int i) { return 8 * (i >> 2) + 4 * tau + (i & 3); }
+
+__device__ inline u32x4 lds_u32x4(const unsigned char* base, int byte_off) {
+  return *reinterpret_cast<const u32x4*>(base + byte_off);
+}
+__device__ inline f32x4 lds_f32x4(const unsigned char* base, int byte_off) {
+  return *reinterpret_cast<const f32x4*>(base + byte_off);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* __restrict__ Qg,
+                                                        const typename C::TIn* __restrict__ Kg,
+                                                        const typename C::TIn* __restrict__ Vg, int N,
+                                                        int span, int nspan, float* __restrict__ ws,
+                                                        float* __restrict__ Og) {
+  using TIn = typename C::TIn;
+  using Elem = typename C::Elem;
+  constexpr bool BF = C::BF;
+  constexpr bool OUT = C::OUT;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS];
+
+  uint32_t* sTab = reinterpret_cast<uint32_t*>(lds + C::O_TAB);
+  float* sQ = reinterpret_cast<float*>(lds + C::O_Q);
+  float* sK = reinterpret_cast<float*>(lds + C::O_K);
+  Elem* sV = reinterpret_cast<Elem*>(lds + C::O_V);
+  Elem* sP = reinterpret_cast<Elem*>(lds + C::O_P);
+  float* sDen = reinterpret_cast<float*>(lds + C::O_DEN);
+  float* sDenQ = reinterpret_cast<float*>(lds + C::O_DENQ);
+  Elem* sPhi = reinterpret_cast<Elem*>(lds + C::O_PHI);
+  Elem* sMu = reinterpret_cast<Elem*>(lds + C::O_MU);
+  float* sRed = reinterpret_cast<float*>(lds + C::O_PHI);  // reused after the slabs
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int li = lane & 15;  // i
+  const int lg = lane >> 4;  // g
+  const int ct = w % C::NVT;  // value column tile of this wave
+  const int rp = w / C::NVT;  // row part of this wave
+  const int ngroups = kDV / C::GC;
+  const int grp = blockIdx.x % ngroups;
+  const int s_idx = (blockIdx.x / ngroups) % nspan;
+  const int bh = blockIdx.x / (ngroups * nspan);
+  const int gcol0 = grp * C::GC;  // first value column of the group
+  const int t_begin = s_idx * span;
+  const int t_end = min(N, t_begin + span);
+
+  const TIn* Qh = Qg + (size_t)bh * N * C::DK;
+  const TIn* Kh = Kg + (size_t)bh * N * C::DK;
+  const TIn* Vh = Vg + (size_t)bh * N * kDV;
+  const size_t ws_span = (size_t)C::WP * (kDV + 1);
+  float* wsS = ws + ((size_t)bh * nspan + s_idx) * ws_span;
+
+  // feature-row codes; padded rows get order 15 (feature 0)
+  const auto& tab = RowsOf<C::DK>::get();
+  for (int r = tid; r < C::WP; r += C::NTHR) sTab[r] = (r < C::W) ? tab.code[r] : (15u << 24);
+
+  // state registers: st[j][tau], K-block kb = (slab*NRP + rp)*J + j%J
+  f32x4 st[C::MKB][C::TPK];
+#pragma unroll
+  for (int j = 0; j < C::MKB; ++j)
+#pragma unroll
+    for (int t = 0; t < C::TPK; ++t) st[j][t] = zero4();
+
+  auto kb_of = [&](int j) { return ((j / C::J) * C::NRP + rp) * C::J + (j % C::J); };
+  // feature row held by lane (col, g) at register s of tile tau of K-block kb
+  auto acc_row = [&](int kb, int tau, int s) {
+    return BF ? kb * C::KB + 8 * lg + 4 * tau + s : kb * C::KB + 4 * lg + s;
+  };
+
+  if constexpr (OUT) {
+    // start from the exclusive prefix of this span
+#pragma unroll
+    for (int j = 0; j < C::MKB; ++j) {
+      const int kb = kb_of(j);
+#pragma unroll
+      for (int t = 0; t < C::TPK; ++t) {
+        f32x4 v;
+        v.x = wsS[(size_t)acc_row(kb, t, 0) * kDV + gcol0 + ct * 16 + li];
+        v.y = wsS[(size_t)acc_row(kb, t, 1) * kDV + gcol0 + ct * 16 + li];
+        v.z = wsS[(size_t)acc_row(kb, t, 2) * kDV + gcol0 + ct * 16 + li];
+        v.w = wsS[(size_t)acc_row(kb, t, 3) * kDV + gcol0 + ct * 16 + li];
+        st[j][t] = v;
+      }
+    }
+    for (int r = tid; r < C::WP; r += C::NTHR) sDen[r] = wsS[(size_t)C::WP * kDV + r];
+  } else {
+    for (int r = tid; r < C::WP; r += C::NTHR) sDen[r] = 0.f;
+  }
+  __syncthreads();
+
+  const u32x4 ones_bf = (li == 0) ? u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}
+                                  : u32x4{0u, 0u, 0u, 0u};
+  const float ones_f = (li == 0) ? 1.0f : 0.0f;
+
+  for (int c0 = t_begin; c0 < t_end; c0 += kCH) {
+    const int nvalid = min(kCH, t_end - c0);
+
+    // ---- 1. stage Q, K (fp32) and V^T (value columns of the group) ----
+    for (int e = tid; e < kCH * C::DK; e += C::NTHR) {
+      const int tok = e / C::DK, d = e - (e / C::DK) * C::DK;
+      const bool ok = tok < nvalid;
+      sK[tok * C::XS + d] = ok ? load_f32(Kh, (size_t)(c0 + tok) * C::DK + d) : 0.f;
+      if constexpr (OUT) sQ[tok * C::XS + d] = ok ? load_f32(Qh, (size_t)(c0 + tok) * C::DK + d) : 0.f;
+    }
+    for (int e = tid; e < kCH * C::GC; e += C::NTHR) {
+      const int tok = e / C::GC, col = e - (e / C::GC) * C::GC;
+      Elem v = 0;
+      if (tok < nvalid) v = Vh[(size_t)(c0 + tok) * kDV + gcol0 + col];
+      sV[col * C::VS + tok] = v;
+    }
+    __syncthreads();
+
+    // ---- 2. intra-chunk block P = tril(K_n(Q K^T)) (output pass) ----
+    f32x4 num[4];
+    f32x4 den[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { num[q] = zero4(); den[q] = zero4(); }
+    float m0 = 0.f, den0 = 0.f;
+    if constexpr (OUT) {
+      constexpr int NKT = BF ? 6 : 10;  // (key block, query tile) pairs on or below the diagonal
+      constexpr int NTILE = NKT * C::TPK;
+      for (int ti = w; ti < NTILE; ti += C::NW) {
+        const int pair = ti / C::TPK, tau = ti % C::TPK;
+        int kb, qt;
+        if constexpr (BF) {  // key blocks of 32: (0, qt 0..3), (1, qt 2..3)
+          kb = pair < 4 ? 0 : 1;
+          qt = pair < 4 ? pair : pair - 2;
+        } else {             // key blocks of 16: kb <= qt
+          qt = pair >= 6 ? 3 : (pair >= 3 ? 2 : (pair >= 1 ? 1 : 0));
+          kb = pair - qt * (qt + 1) / 2;
+        }
+        const int key_row = BF ? kb * 32 + rho(tau, li) : kb * 16 + li;  // A operand row (key)
+        const int qry_row = qt * 16 + li;                                // B operand column (query)
+        f32x4 x = zero4();
+        if constexpr (BF) {
+          if constexpr (C::DK == 16) {
+            typedef short s16x4 __attribute__((ext_vector_type(4)));
+            const float* kr = sK + key_row * C::XS + 4 * lg;
+            const float* qr = sQ + qry_row * C::XS + 4 * lg;
+            uint2 a, b;
+            a.x = pack_bf16x2(kr[0], kr[1]); a.y = pack_bf16x2(kr[2], kr[3]);
+            b.x = pack_bf16x2(qr[0], qr[1]); b.y = pack_bf16x2(qr[2], qr[3]);
+            x = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                          __builtin_bit_cast(s16x4, b), x, 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int h = 0; h < C::DK / 32; ++h) {
+              const float* kr = sK + key_row * C::XS + 32 * h + 8 * lg;
+              const float* qr = sQ + qry_row * C::XS + 32 * h + 8 * lg;
+              u32x4 a, b;
+              a.x = pack_bf16x2(kr[0], kr[1]); a.y = pack_bf16x2(kr[2], kr[3]);
+              a.z = pack_bf16x2(kr[4], kr[5]); a.w = pack_bf16x2(kr[6], kr[7]);
+              b.x = pack_bf16x2(qr[0], qr[1]); b.y = pack_bf16x2(qr[2], qr[3]);
+              b.z = pack_bf16x2(qr[4], qr[5]); b.w = pack_bf16x2(qr[6], qr[7]);
+              x = mfma_bf16(a, b, x);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int jd = 0; jd < C::DK / 4; ++jd)
+            x = mfma_f32(sK[key_row * C::XS + 4 * jd + lg], sQ[qry_row * C::XS + 4 * jd + lg], x);
+        }
+        // lane (query = qt*16 + li, g) holds keys key_of(s)
+        const int query = qt * 16 + li;
+        float p[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int key = BF ? kb * 32 + 8 * lg + 4 * tau + s : kb * 16 + 4 * lg + s;
+          p[s] = (key <= query && key < nvalid) ? taylor_poly<C::NT>(x[s]) : 0.f;
+        }
+        const int kbase = BF ? kb * 32 + 8 * lg + 4 * tau : kb * 16 + 4 * lg;
+        if constexpr (BF) {
+          uint16_t h0, l0, h1, l1, h2, l2, h3, l3;
+          split_bf16(p[0], h0, l0); split_bf16(p[1], h1, l1);
+          split_bf16(p[2], h2, l2); split_bf16(p[3], h3, l3);
+          uint2 hi = {(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)};
+          uint2 lo = {(uint32_t)l0 | ((uint32_t)l1 << 16), (uint32_t)l2 | ((uint32_t)l3 << 16)};
+          *reinterpret_cast<uint2*>(&sP[query * C::PS + kbase]) = hi;
+          *reinterpret_cast<uint2*>(&sP[C::PPL + query * C::PS + kbase]) = lo;
+        } else {
+          *reinterpret_cast<f32x4*>(&sP[query * C::PS + kbase]) = f32x4{p[0], p[1], p[2], p[3]};
+        }
+      }
+      // m = 0 row (exact in fp32): S[0][cols] and the token count S[0][dv]
+      m0 = __shfl(st[0][0].x, li);  // lane (col, g = 0) holds row 0 of K-block 0 (rp = 0 only)
+      den0 = sDen[0];
+    }
+
+    // ---- 3. feature slabs: readout (output pass) then update ----
+#pragma unroll
+    for (int sl = 0; sl < C::NSLAB; ++sl) {
+      const int row0 = sl * C::SR;
+      // phi (query side, row 0 excluded: the m = 0 term is added in fp32)
+      if constexpr (OUT) {
+        for (int e = tid; e < kCH * C::SR; e += C::NTHR) {
+          const int rl = e >> 6, q = e & 63;
+          const int r = row0 + rl;
+          const uint32_t te = sTab[r];
+          const int m = (int)(te >> 24);
+          float val = 0.f;
+          if (r > 0 && m < 15 && q < nvalid) {
+            val = inv_alpha_fact(te);
+            for (int l = 0; l < m; ++l) val *= sQ[q * C::XS + row_index(te, l)];
+          }
+          if constexpr (BF) sPhi[q * C::PHS + rl] = (Elem)f32_to_bf16(val);
+          else sPhi[q * C::PHS + rl] = val;
+        }
+      }
+      // mu^T (key side)
+      for (int e = tid; e < kCH * C::SR; e += C::NTHR) {
+        const int rl = e >> 6, tok = e & 63;
+        const int r = row0 + rl;
+        const uint32_t te = sTab[r];
+        const int m = (int)(te >> 24);
+        float val = 0.f;
+        if (m < 15 && tok < nvalid) {
+          val = 1.f;
+          for (int l = 0; l < m; ++l) val *= sK[tok * C::XS + row_index(te, l)];
+        }
+        if constexpr (BF) {
+          uint16_t hi, lo;
+          split_bf16(val, hi, lo);
+          sMu[rl * C::MUS + tok] = hi;
+          if constexpr (!OUT) sMu[C::MUPL + rl * C::MUS + tok] = lo;
+        } else {
+          sMu[rl * C::MUS + tok] = val;
+        }
+      }
+      __syncthreads();
+
+      if constexpr (OUT) {
+        // value readout over this wave's K-blocks of the slab
+#pragma unroll
+        for (int jl = 0; jl < C::J; ++jl) {
+          const int j = sl * C::J + jl;
+          const int kbl = rp * C::J + jl;  // K-block within the slab
+          if constexpr (BF) {
+            u32x4 b;
+            b.x = pack_bf16x2(st[j][0].x, st[j][0].y);
+            b.y = pack_bf16x2(st[j][0].z, st[j][0].w);
+            b.z = pack_bf16x2(st[j][C::TPK - 1].x, st[j][C::TPK - 1].y);
+            b.w = pack_bf16x2(st[j][C::TPK - 1].z, st[j][C::TPK - 1].w);
+#pragma unroll
+            for (int qt = 0; qt < 4; ++qt) {
+              const u32x4 a = lds_u32x4((const unsigned char*)sPhi,
+                                        ((qt * 16 + li) * C::PHS + kbl * 32 + 8 * lg) * 2);
+              num[qt] = mfma_bf16(a, b, num[qt]);
+            }
+          } else {
+#pragma unroll
+            for (int qt = 0; qt < 4; ++qt) {
+              const f32x4 a = lds_f32x4((const unsigned char*)sPhi,
+                                        ((qt * 16 + li) * C::PHS + kbl * 16 + 4 * lg) * 4);
+              num[qt] = mfma_f32(a.x, st[j][0].x, num[qt]);
+              num[qt] = mfma_f32(a.y, st[j][0].y, num[qt]);
+              num[qt] = mfma_f32(a.z, st[j][0].z, num[qt]);
+              num[qt] = mfma_f32(a.w, st[j][0].w, num[qt]);
+            }
+          }
+        }
+        // normaliser readout for the query tiles this wave owns
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+          if (qt % C::NW != w) continue;
+          for (int kbl = 0; kbl < C::NRP * C::J; ++kbl) {
+            if constexpr (BF) {
+              const float* dr = sDen + row0 + kbl * 32 + 8 * lg;
+              u32x4 b = {0u, 0u, 0u, 0u};
+              if (li == 0) {
+                b.x = pack_bf16x2(dr[0], dr[1]); b.y = pack_bf16x2(dr[2], dr[3]);
+                b.z = pack_bf16x2(dr[4], dr[5]); b.w = pack_bf16x2(dr[6], dr[7]);
+              }
+              const u32x4 a = lds_u32x4((const unsigned char*)sPhi,
+                                        ((qt * 16 + li) * C::PHS + kbl * 32 + 8 * lg) * 2);
+              den[qt] = mfma_bf16(a, b, den[qt]);
+            } else {
+              const f32x4 a = lds_f32x4((const unsigned char*)sPhi,
+                                        ((qt * 16 + li) * C::PHS + kbl * 16 + 4 * lg) * 4);
+              const f32x4 d = *reinterpret_cast<const f32x4*>(sDen + row0 + kbl * 16 + 4 * lg);
+              den[qt] = mfma_f32(a.x, ones_f * d.x, den[qt]);
+              den[qt] = mfma_f32(a.y, ones_f * d.y, den[qt]);
+              den[qt] = mfma_f32(a.z, ones_f * d.z, den[qt]);
+              den[qt] = mfma_f32(a.w, ones_f * d.w, den[qt]);
+            }
+          }
+        }
+        __syncthreads();  // normaliser reads of this slab finish before its update
+      }
+
+      // value update: S[kb] += mu^T V
+#pragma unroll
+      for (int jl = 0; jl < C::J; ++jl) {
+        const int j = sl * C::J + jl;
+        const int kbl = rp * C::J + jl;
+#pragma unroll
+        for (int tb = 0; tb < C::TB; ++tb) {
+          if constexpr (BF) {
+            const u32x4 b = lds_u32x4((const unsigned char*)sV, ((ct * 16 + li) * C::VS + tb * 32 + 8 * lg) * 2);
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+              const int rowl = kbl * 32 + rho(tau, li);
+              const u32x4 ah = lds_u32x4((const unsigned char*)sMu, (rowl * C::MUS + tb * 32 + 8 * lg) * 2);
+              st[j][tau % C::TPK] = mfma_bf16(ah, b, st[j][tau % C::TPK]);
+              if constexpr (!OUT) {
+                const u32x4 al = lds_u32x4((const unsigned char*)sMu,
+                                           (C::MUPL + rowl * C::MUS + tb * 32 + 8 * lg) * 2);
+                st[j][tau % C::TPK] = mfma_bf16(al, b, st[j][tau % C::TPK]);
+              }
+            }
+          } else {
+            const f32x4 b = lds_f32x4((const unsigned char*)sV, ((ct * 16 + li) * C::VS + tb * 16 + 4 * lg) * 4);
+            const f32x4 a = lds_f32x4((const unsigned char*)sMu, ((kbl * 16 + li) * C::MUS + tb * 16 + 4 * lg) * 4);
+            st[j][0] = mfma_f32(a.x, b.x, st[j][0]);
+            st[j][0] = mfma_f32(a.y, b.y, st[j][0]);
+            st[j][0] = mfma_f32(a.z, b.z, st[j][0]);
+            st[j][0] = mfma_f32(a.w, b.w, st[j][0]);
+          }
+        }
+      }
+      // normaliser update: sDen[rows] += mu^T 1, K-blocks of the slab spread over waves
+      for (int kbl = w; kbl < C::NRP * C::J; kbl += C::NW) {
+#pragma unroll
+        for (int tau = 0; tau < C::TPK; ++tau) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int tb = 0; tb < C::TB; ++tb) {
+            if constexpr (BF) {
+              const int rowl = kbl * 32 + rho(tau, li);
+              const u32x4 ah = lds_u32x4((const unsigned char*)sMu, (rowl * C::MUS + tb * 32 + 8 * lg) * 2);
+              acc = mfma_bf16(ah, ones_bf, acc);
+              if constexpr (!OUT) {
+                const u32x4 al = lds_u32x4((const unsigned char*)sMu,
+                                           (C::MUPL + rowl * C::MUS + tb * 32 + 8 * lg) * 2);
+                acc = mfma_bf16(al, ones_bf, acc);
+              }
+            } else {
+              const f32x4 a = lds_f32x4((const unsigned char*)sMu, ((kbl * 16 + li) * C::MUS + tb * 16 + 4 * lg) * 4);
+              acc = mfma_f32(a.x, ones_f, acc);
+              acc = mfma_f32(a.y, ones_f, acc);
+              acc = mfma_f32(a.z, ones_f, acc);
+              acc = mfma_f32(a.w, ones_f, acc);
+            }
+          }
+          if (li == 0) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              const int r = row0 + (BF ? kbl * 32 + 8 * lg + 4 * tau + s : kbl * 16 + 4 * lg + s);
+              sDen[r] += acc[s];
+            }
+          }
+        }
+      }
+      __syncthreads();  // slab buffers are rewritten by the next slab
+    }
+
+    if constexpr (OUT) {
+      // ---- 4. intra-chunk contribution, m = 0 row, reduction, normalise ----
+      if (rp == 0) {
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+          constexpr int KBW = BF ? 32 : 16;
+#pragma unroll
+          for (int kb = 0; kb < kCH / KBW; ++kb) {
+            if (kb * KBW > qt * 16 + 15) continue;
+            if constexpr (BF) {
+              const u32x4 b = lds_u32x4((const unsigned char*)sV, ((ct * 16 + li) * C::VS + kb * 32 + 8 * lg) * 2);
+              const u32x4 ah = lds_u32x4((const unsigned char*)sP, ((qt * 16 + li) * C::PS + kb * 32 + 8 * lg) * 2);
+              const u32x4 al = lds_u32x4((const unsigned char*)sP,
+                                         (C::PPL + (qt * 16 + li) * C::PS + kb * 32 + 8 * lg) * 2);
+              num[qt] = mfma_bf16(ah, b, num[qt]);
+              num[qt] = mfma_bf16(al, b, num[qt]);
+            } else {
+              const f32x4 b = lds_f32x4((const unsigned char*)sV, ((ct * 16 + li) * C::VS + kb * 16 + 4 * lg) * 4);
+              const f32x4 a = lds_f32x4((const unsigned char*)sP, ((qt * 16 + li) * C::PS + kb * 16 + 4 * lg) * 4);
+              num[qt] = mfma_f32(a.x, b.x, num[qt]);
+              num[qt] = mfma_f32(a.y, b.y, num[qt]);
+              num[qt] = mfma_f32(a.z, b.z, num[qt]);
+              num[qt] = mfma_f32(a.w, b.w, num[qt]);
+            }
+          }
+          num[qt] += f32x4{m0, m0, m0, m0};
+        }
+      }
+      // intra-chunk normaliser for owned query tiles, then publish den per query
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        if (qt % C::NW != w) continue;
+        constexpr int KBW = BF ? 32 : 16;
+#pragma unroll
+        for (int kb = 0; kb < kCH / KBW; ++kb) {
+          if (kb * KBW > qt * 16 + 15) continue;
+          if constexpr (BF) {
+            const u32x4 ah = lds_u32x4((const unsigned char*)sP, ((qt * 16 + li) * C::PS + kb * 32 + 8 * lg) * 2);
+            const u32x4 al = lds_u32x4((const unsigned char*)sP,
+                                       (C::PPL + (qt * 16 + li) * C::PS + kb * 32 + 8 * lg) * 2);
+            den[qt] = mfma_bf16(ah, ones_bf, den[qt]);
+            den[qt] = mfma_bf16(al, ones_bf, den[qt]);
+          } else {
+            const f32x4 a = lds_f32x4((const unsigned char*)sP, ((qt * 16 + li) * C::PS + kb * 16 + 4 * lg) * 4);
+            den[qt] = mfma_f32(a.x, ones_f, den[qt]);
+            den[qt] = mfma_f32(a.y, ones_f, den[qt]);
+            den[qt] = mfma_f32(a.z, ones_f, den[qt]);
+            den[qt] = mfma_f32(a.w, ones_f, den[qt]);
+          }
+        }
+        if (li == 0) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) sDenQ[qt * 16 + 4 * lg + s] = den[qt][s] + den0;
+        }
+      }
+      if constexpr (C::NRP > 1) {
+        if (rp != 0) {
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt)
+            *reinterpret_cast<f32x4*>(sRed + (((w * 4 + qt) * 64) + lane) * 4) = num[qt];
+        }
+      }
+      __syncthreads();
+      if (rp == 0) {
+        if constexpr (C::NRP > 1) {
+          for (int r2 = 1; r2 < C::NRP; ++r2) {
+            const int w2 = r2 * C::NVT + ct;
+#pragma unroll
+            for (int qt = 0; qt < 4; ++qt)
+              num[qt] += *reinterpret_cast<const f32x4*>(sRed + (((w2 * 4 + qt) * 64) + lane) * 4);
+          }
+        }
+        const int col = gcol0 + ct * 16 + li;
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int q = qt * 16 + 4 * lg + s;
+            if (q < nvalid) Og[((size_t)bh * N + c0 + q) * kDV + col] = num[qt][s] / sDenQ[q];
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  if constexpr (!OUT) {
+    // span total -> workspace
+#pragma unroll
+    for (int j = 0; j < C::MKB; ++j) {
+      const int kb = kb_of(j);
+#pragma unroll
+      for (int t = 0; t < C::TPK; ++t) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          wsS[(size_t)acc_row(kb, t, s) * kDV + gcol0 + ct * 16 + li] = st[j][t][s];
+      }
+    }
+    if (grp == 0)
+      for (int r = tid; r < C::WP; r += C::NTHR) wsS[(size_t)C::WP * kDV + r] = sDen[r];
+  }
+}
+
+// Exclusive scan of span totals over spans (in place) and the final states.
+__global__ void scan_kernel(float* __restrict__ ws, int nspan, int WP, int W, int BH,
+                            float* __restrict__ states) {
+  const size_t per = (size_t)WP * (kDV + 1);
+  const size_t total = (size_t)BH * per;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (size_t)gridDim.x * blockDim.x) {
+    const size_t bh = e / per;
+    const size_t off = e - bh * per;
+    float* p = ws + bh * nspan * per + off;
+    float run = 0.f;
+    for (int s = 0; s < nspan; ++s) {
+      const float t = p[(size_t)s * per];
+      p[(size_t)s * per] = run;
+      run += t;
+    }
+    if (off < (size_t)WP * kDV) {
+      const size_t r = off / kDV, c = off - (off / kDV) * kDV;
+      if (r < (size_t)W) states[(bh * W + r) * kDV + c] = run;
+    } else {
+      const size_t r = off - (size_t)WP * kDV;
+      if (r < (size_t)W) states[(size_t)BH * W * kDV + bh * W + r] = run;
+    }
+  }
+}
+
+// Per-shape launch configuration: the smallest row split NRP (waves sharing a
+// value-column tile) that keeps the state at <= 160 accumulator floats per
+// lane; 4 waves for NRP = 1, else 8 waves with 8/NRP value tiles per group.
+constexpr int pick_nrp(int nkb, int fpk) {
+  const int opts[4] = {1, 2, 4, 8};
+  for (int i = 0; i < 4; ++i)
+    if ((nkb + opts[i] - 1) / opts[i] * fpk <= 160) return opts[i];
+  return 8;
+}
+
+template <typename TIn, int DK, int NT>
+struct Shape {
+  static constexpr bool BF = std::is_same<TIn, uint16_t>::value;
+  static constexpr int W = rows_for(DK, NT);
+  static constexpr int KB = BF ? 32 : 16;
+  static constexpr int NKB = (W + KB - 1) / KB;
+  static constexpr int NRP = pick_nrp(NKB, BF ? 8 : 4);
+  static constexpr int NVT = NRP == 1 ? 4 : 8 / NRP;
+  using Tot = Cfg<TIn, DK, NT, NVT, NRP, MODE_TOTALS>;
+  using Out = Cfg<TIn, DK, NT, NVT, NRP, MODE_OUTPUT>;
+  static_assert(Tot::WP == Out::WP, "modes share the workspace layout");
+};
+
+}  // namespace
 
 int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype dt, PrefillPlan* p) {
-  (void)dt;
-  if (chunk != 64) return fail(TT_ERR_UNSUPPORTED, "chunk=%d not compiled (64 only)", chunk);
+  (void)dv;
+  if (chunk != kCH) return fail(TT_ERR_UNSUPPORTED, "chunk=%d not compiled (64 only)", chunk);
+  int wp = 0, ngroups = 0;
+  hipError_t e = with_dkn(dk, n, [&](auto DKc, auto Nc) {
+    constexpr int DK = decltype(DKc)::value, NT = decltype(Nc)::value;
+    if (dt == TT_BF16) {
+      using S = Shape<uint16_t, DK, NT>;
+      wp = S::Out::WP;
+      ngroups = kDV / S::Out::GC;
+    } else {
+      using S = Shape<float, DK, NT>;
+      wp = S::Out::WP;
+      ngroups = kDV / S::Out::GC;
+    }
+    return hipSuccess;
+  });
+  if (e != hipSuccess) return fail(TT_ERR_UNSUPPORTED, "(dk=%d, n=%d) not compiled", dk, n);
+  const long long BH = (long long)B * H;
+  const int nchunk = (N + kCH - 1) / kCH;
+  // about two workgroups per CU over 256 CUs
+  long long want = (512 + BH * ngroups - 1) / (BH * ngroups);
+  if (want < 1) want = 1;
+  if (want > nchunk) want = nchunk;
+  const int span = (int)(((nchunk + want - 1) / want) * kCH);
+  const int nspan = (N + span - 1) / span;
   p->W = rows_for(dk, n);
-  p->Wpad = (p->W + 31) / 32 * 32;
-  p->chunk = chunk;
-  p->span = N;
-  p->nspan = 1;
-  p->ngroups = 1;
-  p->ws_floats = 0;
-  (void)B; (void)H; (void)dv;
+  p->Wpad = wp;
+  p->chunk = kCH;
+  p->span = span;
+  p->nspan = nspan;
+  p->ngroups = ngroups;
+  p->ws_floats = (size_t)BH * nspan * (size_t)wp * (kDV + 1);
   return TT_OK;
 }
 
-hipError_t launch_prefill(const void*, const void*, const void*, tt_dtype, int, int, int, int, const PrefillPlan&,
-                          float*, float*, float*, hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype dt, int BH, int N, int dk, int n,
+                          const PrefillPlan& p, float* O, float* states, float* ws, hipStream_t s) {
+  return with_dkn(dk, n, [&](auto DKc, auto Nc) {
+    constexpr int DK = decltype(DKc)::value, NT = decltype(Nc)::value;
+    auto go = [&](auto tag) {
+      using TIn = decltype(tag);
+      using S = Shape<TIn, DK, NT>;
+      const unsigned nblk = (unsigned)((size_t)BH * p.nspan * p.ngroups);
+      hipLaunchKernelGGL((sweep_kernel<typename S::Tot>), dim3(nblk), dim3(S::Tot::NTHR), 0, s, (const TIn*)Q,
+                         (const TIn*)K, (const TIn*)V, N, p.span, p.nspan, ws, O);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const size_t total = (size_t)BH * S::Out::WP * (kDV + 1);
+      unsigned g = (unsigned)((total + 255) / 256);
+      if (g > 16384) g = 16384;
+      hipLaunchKernelGGL(scan_kernel, dim3(g), dim3(256), 0, s, ws, p.nspan, (int)S::Out::WP, (int)S::Out::W, BH,
+                         states);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((sweep_kernel<typename S::Out>), dim3(nblk), dim3(S::Out::NTHR), 0, s, (const TIn*)Q,
+                         (const TIn*)K, (const TIn*)V, N, p.span, p.nspan, ws, O);
+      return hipGetLastError();
+    };
+    if (dt == TT_BF16) return go(uint16_t{});
+    return go(float{});
+  });
 }
 
 }  // namespace tt

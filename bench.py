@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of the truncated-Taylor recurrent-state attention hot path on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+Prints ONE JSON line.  A step is one tt_prefill call over the prefill
+workload (B=4, H=8, N=8192, dk=16, dv=64, n=3, bf16 inputs, fp32 states
+and outputs): totals, span scan and the state sweep.  `value` is prefill
+tokens/s = B*N / (time per step).  The decode workload (B=64 x H=32 states
+of a 65536-token prefix, 256 successive single-token steps) is timed in the
+same run and reported under "decode" as us per step.  Inputs are resident
+in HBM before the timed regions; timing uses HIP events on the stream the
+kernels are launched on.  "roofline" relates algorithmic bytes per launch
+to the measured time; "cpu_baseline" times the fp64 oracle on the host on a
+bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "prefill tokens/s @N=8192 + decode µs/token (B·H states); % of roofline"
+
+
+def _source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "taylor_recurrent_states_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, src_hash):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    e = t.get(kernel_key)
+    if not e or e.get("source_hash") != src_hash:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def _time_events(fn, steps, torch):
+    s = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(s)
+    for _ in range(steps):
+        fn()
+    stop.record(s)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / 1e3  # seconds
+
+
+def bench_prefill(args, torch, ops, wl):
+    w = wl.WORKLOADS["prefill"]
+    q, k, v = wl.draw_qkv(w.seed, w.B, w.H, w.N, w.dk, w.dv, w.dtype)
+    dev = torch.device("cuda:0")
+
+    def to_dev(r):
+        import numpy as np
+        return torch.from_numpy(np.ascontiguousarray(r.device).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    Q, K, V = to_dev(q), to_dev(k), to_dev(v)
+    O = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.float32, device=dev)
+    S = torch.empty(w.B * w.H * ops.tt_state_floats(w.dk, w.dv, w.n), dtype=torch.float32, device=dev)
+    ws = torch.empty(ops.tt_prefill_workspace_bytes(w.B, w.H, w.N, w.dk, w.dv, w.n, w.chunk), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        ops.tt_prefill(Q, K, V, w.n, w.chunk, O=O, states=S, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    t = _time_events(step, args.steps, torch)
+    t_step = t / args.steps
+    tokens = w.B * w.N
+    head_tokens = w.B * w.H * w.N
+    # algorithmic bytes per call: q, k (bf16) + v (bf16) read, O (fp32) written, final states written
+    alg_bytes = head_tokens * (2 * w.dk * 2 + w.dv * 2 + w.dv * 4) + w.B * w.H * ops.tt_state_floats(w.dk, w.dv, w.n) * 4
+    achieved = alg_bytes / t_step / 1e9
+    src = _source_hash("tt_prefill.hip", "tt_device.hpp")
+    return {
+        "value": tokens / t_step, "t_step": t_step, "workload": w, "alg_bytes": alg_bytes,
+        "roofline": {"bound": "hbm", "kernel": "tt_prefill (span totals + span scan + state sweep)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic("prefill", src), "alg_bytes_per_launch": alg_bytes,
+                     "source_hash": src},
+        "inputs": (q, k, v),
+    }
+
+
+def bench_decode(args, torch, ops, wl):
+    """States of a 65536-token prefix per (b, h), then 256 single-token steps."""
+    w = wl.WORKLOADS["decode"]
+    dev = torch.device("cuda:0")
+    BH = w.B * w.H
+    nf = ops.tt_state_floats(w.dk, w.dv, w.n)
+    # prefix: k, v ~ N(0,1) from the seeded device generator, k L2-normalised,
+    # states built with tt_prefill (fp32) in batches of heads
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    per = 256
+    num = torch.empty(BH * ops.tt_state_rows(w.dk, w.n) * w.dv, dtype=torch.float32, device=dev)
+    den = torch.empty(BH * ops.tt_state_rows(w.dk, w.n), dtype=torch.float32, device=dev)
+    W = ops.tt_state_rows(w.dk, w.n)
+    for h0 in range(0, BH, per):
+        nh = min(per, BH - h0)
+        kp = torch.randn((1, nh, w.N, w.dk), generator=g, device=dev)
+        kp = kp / kp.norm(dim=-1, keepdim=True)
+        vp = torch.randn((1, nh, w.N, w.dv), generator=g, device=dev)
+        _, Sb = ops.tt_prefill(kp, kp, vp, w.n, 64)
+        num[h0 * W * w.dv:(h0 + nh) * W * w.dv] = Sb[:nh * W * w.dv]
+        den[h0 * W:(h0 + nh) * W] = Sb[nh * W * w.dv:]
+        del kp, vp, Sb
+    states = torch.cat([num, den])
+    del num, den
+    assert states.numel() == BH * nf
+    # per-step inputs, resident before timing
+    T = w.steps
+    qs = torch.randn((T, w.B, w.H, w.dk), generator=g, device=dev)
+    qs = qs / qs.norm(dim=-1, keepdim=True)
+    ks = torch.randn((T, w.B, w.H, w.dk), generator=g, device=dev)
+    ks = ks / ks.norm(dim=-1, keepdim=True)
+    vs = torch.randn((T, w.B, w.H, w.dv), generator=g, device=dev)
+    o = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def run(steps):
+        for t in range(steps):
+            ops.tt_decode_step(qs[t % T], ks[t % T], vs[t % T], states, w.n, o=o)
+
+    run(min(args.warmup * 4, T))
+    t = _time_events(lambda: run(T), 1, torch)
+    t_step = t / T
+    state_bytes = BH * nf * 4
+    alg_bytes = 2 * state_bytes + BH * (2 * w.dk + w.dv) * 4 + BH * w.dv * 4
+    achieved = alg_bytes / t_step / 1e9
+    # MALL-cold variant: a 512 MB write between steps evicts the 256 MB infinity cache
+    flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream()
+    cold = []
+    for t2 in range(8):
+        flush.fill_(float(t2))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        ops.tt_decode_step(qs[t2], ks[t2], vs[t2], states, w.n, o=o)
+        e1.record(s)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1) / 1e3)
+    del flush
+    t_cold = sorted(cold)[len(cold) // 2]
+    src = _source_hash("tt_decode.hip", "tt_device.hpp")
+    return {
+        "us_per_step": t_step * 1e6, "us_per_step_mall_cold": t_cold * 1e6, "steps": T,
+        "workload": w.name,
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel<16,3,float>", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "achieved_mall_cold": round(alg_bytes / t_cold / 1e9, 1),
+                     "frac_mall_cold": round(alg_bytes / t_cold / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic("decode", src), "alg_bytes_per_launch": alg_bytes,
+                     "source_hash": src},
+    }
+
+
+def cpu_baselines(pre, wl):
+    """The fp64 oracle as it stands, on the host cores, on bounded samples."""
+    import numpy as np
+    import oracle.taylor_oracle as orc
+    cores = len(os.sched_getaffinity(0))
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        blas_threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        blas_threads = cores
+    w = wl.WORKLOADS["prefill"]
+    q, k, v = pre["inputs"]
+    # prefill: the quadratic-form definition plus the states, on 1 of the 32 heads
+    t0 = time.perf_counter()
+    orc.quadratic_attention(q.exact[0, :1], k.exact[0, :1], v.exact[0, :1], w.n)
+    orc.states_definition(k.exact[0, :1], v.exact[0, :1], w.n)
+    t_head = time.perf_counter() - t0
+    # tokens/s of the whole workload: one head-sequence is 1/(B*H) of the work
+    pre_cpu = {"value": round(w.B * w.N / (t_head * w.B * w.H), 2), "unit": "tokens/s",
+               "cores": blas_threads, "kind": "oracle",
+               "sample": f"1 of {w.B * w.H} heads (N={w.N}): quadratic form + state definition, fp64, "
+                         f"{t_head:.1f} s; scaled to B*H heads"}
+    # decode: the oracle's decode step vectorised over all 2048 states, 2 steps
+    d = wl.WORKLOADS["decode"]
+    W = orc.state_rows(d.dk, d.n)
+    rng = np.random.Generator(np.random.PCG64(5))
+    S = rng.standard_normal((d.B, d.H, W, d.dv + 1))
+    qq, kk, vv = wl.draw_decode_token(0, d.B, d.H, d.dk, d.dv)
+    t0 = time.perf_counter()
+    for _ in range(2):
+        _, S = orc.decode_step(qq.exact, kk.exact, vv.exact, S, d.n)
+    t_dec = (time.perf_counter() - t0) / 2
+    dec_cpu = {"value": round(t_dec * 1e6, 1), "unit": "us/step", "cores": blas_threads, "kind": "oracle",
+               "sample": f"2 full decode steps over all {d.B * d.H} states, fp64"}
+    return pre_cpu, dec_cpu, cores
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline (profiling runs)")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="run only tt_state_merge over 2 x 256 MiB -> 256 MiB (known HBM bytes), "
+                         "to scale the FETCH_SIZE / WRITE_SIZE counters")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the hot path has no multi-GPU code (see DESIGN.md, "
+              "'How the path would shard'); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from taylor_recurrent_states_amd import ops
+    from taylor_recurrent_states_amd import workloads as wl
+    ops.lib()  # fails loudly if the library is not built
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    if args.calibrate:
+        n = 64 * 1024 * 1024
+        a = torch.ones(n, device="cuda")
+        b = torch.ones(n, device="cuda")
+        d = torch.empty(n, device="cuda")
+        for _ in range(3):
+            ops.tt_state_merge(a, b, dst=d)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate": "tt_state_merge", "read_bytes_per_launch": 2 * n * 4,
+                          "write_bytes_per_launch": n * 4, "launches": 3}), flush=True)
+        return
+
+    pre = dec = None
+    if args.only in (None, "prefill"):
+        pre = bench_prefill(args, torch, ops, wl)
+        print(f"# prefill: {pre['t_step'] * 1e6:.1f} us/step, {pre['value']:.4g} tokens/s", file=sys.stderr,
+              flush=True)
+    if args.only in (None, "decode"):
+        dec = bench_decode(args, torch, ops, wl)
+        print(f"# decode: {dec['us_per_step']:.2f} us/step", file=sys.stderr, flush=True)
+
+    out = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic"}
+    w = wl.WORKLOADS["prefill"]
+    if pre is not None:
+        out.update({"value": round(pre["value"], 1), "ms_per_step": round(pre["t_step"] * 1e3, 5),
+                    "roofline": pre["roofline"]})
+    else:
+        out.update({"value": None, "ms_per_step": None, "roofline": None})
+    out["config"] = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "dk": w.dk, "dv": w.dv, "n": w.n,
+                     "chunk": w.chunk, "states": "fp32", "outputs": "fp32",
+                     "decode_workload": wl.WORKLOADS["decode"].name}
+    if dec is not None:
+        out["decode"] = dec
+    if not args.no_cpu and pre is not None:
+        pre_cpu, dec_cpu, cores = cpu_baselines(pre, wl)
+        out["cpu_baseline"] = pre_cpu
+        if dec is not None:
+            out["decode"]["cpu_baseline"] = dec_cpu
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -20,8 +20,9 @@ namespace tt {
 // ---------------------------------------------------------------------------
 // Compile-time row tables.  One table per supported key width holds the rows
 // of the largest supported order; smaller orders use a prefix (blocks are in
-// ascending m).  Entry: code = idx0 | idx1<<6 | idx2<<12 | idx3<<18 | m<<24,
-// weight = 1/alpha(t)! rounded to fp32.
+// ascending m).  Entry: code = idx0 | idx1<<6 | idx2<<12 | idx3<<18 | m<<24
+// | w<<27, where w indexes 1/alpha(t)! in {1, 1/2, 1/4, 1/6, 1/24}; weight =
+// 1/alpha(t)! rounded to fp32.
 // ---------------------------------------------------------------------------
 
 constexpr int binom(int a, int b) {
@@ -56,7 +57,8 @@ struct RowTable {
             run = 1;
           }
         }
-        code[r] = c;
+        const uint32_t widx = denom == 1 ? 0u : denom == 2 ? 1u : denom == 4 ? 2u : denom == 6 ? 3u : 4u;
+        code[r] = c | (widx << 27);
         weight[r] = 1.0f / (float)denom;
         ++r;
         // next non-decreasing tuple in lexicographic order
@@ -87,7 +89,15 @@ template <> struct RowsOf<16> { static __device__ const RowTable<16, 5>& get() {
 template <> struct RowsOf<32> { static __device__ const RowTable<32, 3>& get() { return kRows32; } };
 template <> struct RowsOf<64> { static __device__ const RowTable<64, 3>& get() { return kRows64; } };
 
-__device__ inline int row_order(uint32_t code) { return (int)(code >> 24); }
+__host__ __device__ constexpr int row_order(uint32_t code) { return (int)((code >> 24) & 7u); }
+__host__ __device__ constexpr int row_index_c(uint32_t code, int l) { return (int)((code >> (6 * l)) & 63u); }
+// 1/alpha(t)! from the weight index of a row code
+__host__ __device__ constexpr float row_weight(uint32_t code) {
+  const uint32_t w = (code >> 27) & 7u;
+  return w == 0 ? 1.0f : w == 1 ? 0.5f : w == 2 ? 0.25f : w == 3 ? 1.0f / 6.0f : 1.0f / 24.0f;
+}
+// code of a padding row (order 7: contributes nothing)
+constexpr uint32_t kPadRow = 7u << 24;
 __device__ inline int row_index(uint32_t code, int l) { return (int)((code >> (6 * l)) & 63u); }
 
 // mu_t(x) for a row code, reading coordinates through `get(i)`.
@@ -151,6 +161,15 @@ __device__ inline f32x4 mfma_f32(float a, float b, f32x4 c) {
 }
 
 __device__ inline f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+// static_for<B, E>(f): f(integral_constant<int, i>) for i in [B, E)
+template <int B, int E, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // Calls fn(integral_constant<DK>, integral_constant<N>) for a supported
 // (dk, n); hipErrorInvalidValue otherwise.

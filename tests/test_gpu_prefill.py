@@ -66,25 +66,39 @@ def _sample_rows(N, rng, extra=24):
     return sorted(r for r in base if 0 <= r < N)
 
 
-def _full_workload(name, heads_checked=None):
+def _full_workload(name, heads_checked=None, state_heads=None):
+    """Run the named workload at full size; compare sampled output rows of
+    ``heads_checked`` (default: all heads) and every state element of
+    ``state_heads`` (default: the same heads) against the oracle."""
     w = wl.WORKLOADS[name]
+    print(f"\n[{name}] drawing inputs", flush=True)
     q, k, v = wl.draw_qkv(w.seed, w.B, w.H, w.N, w.dk, w.dv, w.dtype)
     O, S = _prefill(q, k, v, w.n)
+    print(f"[{name}] GPU prefill done", flush=True)
     rng = np.random.Generator(np.random.PCG64([w.seed, 99]))
     BH = w.B * w.H
     Qx = q.exact.reshape(BH, w.N, w.dk)
     Kx = k.exact.reshape(BH, w.N, w.dk)
     Vx = v.exact.reshape(BH, w.N, w.dv)
     Og = O.reshape(BH, w.N, w.dv)
-    heads = range(BH) if heads_checked is None else heads_checked
+    heads = list(range(BH)) if heads_checked is None else list(heads_checked)
     worst = 0.0
     for h in heads:
         rows = _sample_rows(w.N, rng)
         ref = orc.quadratic_rows(Qx[h, rows], Kx[h], Vx[h], rows, w.n)
         worst = max(worst, assert_out(Og[h, rows], ref, w.tol, f"{name} head {h}"))
-    S_ref = orc.states_definition(k.exact, v.exact, w.n)
-    errs = assert_states(S, S_ref, w.dk, w.n, w.tol, name)
-    return O, S, worst, errs
+    print(f"[{name}] sampled rows of {len(heads)} heads ok (worst {worst:.2e})", flush=True)
+    W = orc.state_rows(w.dk, w.n)
+    heads = heads if state_heads is None else list(state_heads)
+    S_got = orc.planes_to_states(S, 1, BH, W, w.dv)[0][heads]
+    refs = []
+    for h in heads:
+        refs.append(orc.states_definition(Kx[h], Vx[h], w.n))
+        print(f"[{name}] oracle states of head {h}", flush=True)
+    S_ref = np.stack(refs)
+    errs = assert_states(orc.states_to_planes(S_got[None]), S_ref[None], w.dk, w.n, w.tol, name)
+    print(f"[{name}] states of {len(heads)} heads ok", flush=True)
+    return q, k, v, S, S_ref, heads, errs
 
 
 def test_prefill_workload_full_size():
@@ -93,17 +107,19 @@ def test_prefill_workload_full_size():
 
 
 def test_order5_workload_full_size():
-    """B=1, H=16, N=16384, dk=16, n=5, fp32."""
-    _full_workload("order5")
+    """B=1, H=16, N=16384, dk=16, n=5, fp32: sampled rows of every head,
+    every state element of 6 heads."""
+    _full_workload("order5", state_heads=(0, 3, 6, 9, 12, 15))
 
 
 def test_wide_workload_full_size_and_split_merge():
-    """B=1, H=16, N=65536, dk=64, n=3, bf16; then the states of 8 random
-    chunk splits merged with tt_state_merge equal the single pass."""
+    """B=1, H=16, N=65536, dk=64, n=3, bf16 (states and rows checked on 4 of
+    the 16 heads); then the states of 8 random chunk splits merged with
+    tt_state_merge equal the single pass on every head (GPU vs GPU) and the
+    oracle on the checked heads."""
     import torch
     w = wl.WORKLOADS["wide"]
-    _, S_single, _, _ = _full_workload("wide", heads_checked=range(0, 16, 3))
-    q, k, v = wl.draw_qkv(w.seed, w.B, w.H, w.N, w.dk, w.dv, w.dtype)
+    q, k, v, S_single, S_ref, heads, _ = _full_workload("wide", heads_checked=(0, 5, 10, 15))
     Qd, Kd, Vd = to_device(q), to_device(k), to_device(v)
     cuts = [0] + wl.draw_split_points(w.N, w.extra["splits"] - 1) + [w.N]
     merged = None
@@ -113,10 +129,11 @@ def test_wide_workload_full_size_and_split_merge():
         merged = S if merged is None else ops.tt_state_merge(merged, S)
     torch.cuda.synchronize()
     m = merged.cpu().numpy()
-    # merged splits against the single pass (GPU vs GPU) and against the oracle
-    S_ref = orc.states_definition(k.exact, v.exact, w.n)
-    assert_states(m, S_ref, w.dk, w.n, w.tol, "merged splits")
+    print(f"[wide] merged {len(cuts) - 1} splits at {cuts[1:-1]}", flush=True)
     assert np.max(np.abs(m - S_single)) <= 5e-3
+    W = orc.state_rows(w.dk, w.n)
+    m_heads = orc.planes_to_states(m, 1, w.B * w.H, W, w.dv)[0][list(heads)]
+    assert_states(orc.states_to_planes(m_heads[None]), S_ref[None], w.dk, w.n, w.tol, "merged splits")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -104,6 +104,41 @@ def bench_prefill(args, torch, ops, wl):
     }
 
 
+def bench_prefill_other(name, args, torch, ops, wl):
+    """Secondary prefill workloads (order 5 fp32, wide head bf16): time per
+    call and the MFMA roofline on algorithmic flops (4 W (dv+1) per head-token:
+    readout plus state update), against the peak of the input dtype's MFMA."""
+    w = wl.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    tg = torch.Generator(device=dev)
+    tg.manual_seed(w.seed)
+    Q = torch.randn((w.B, w.H, w.N, w.dk), generator=tg, device=dev)
+    K = torch.randn((w.B, w.H, w.N, w.dk), generator=tg, device=dev)
+    Q = (Q / Q.norm(dim=-1, keepdim=True)).to(dt)
+    K = (K / K.norm(dim=-1, keepdim=True)).to(dt)
+    V = torch.randn((w.B, w.H, w.N, w.dv), generator=tg, device=dev).to(dt)
+    O = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.float32, device=dev)
+    S = torch.empty(w.B * w.H * ops.tt_state_floats(w.dk, w.dv, w.n), dtype=torch.float32, device=dev)
+    ws = torch.empty(ops.tt_prefill_workspace_bytes(w.B, w.H, w.N, w.dk, w.dv, w.n, w.chunk), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        ops.tt_prefill(Q, K, V, w.n, w.chunk, O=O, states=S, workspace=ws)
+
+    step()
+    steps = max(2, min(args.steps, 10))
+    t = _time_events(step, steps, torch) / steps
+    W = ops.tt_state_rows(w.dk, w.n)
+    flops = 4.0 * W * (w.dv + 1) * w.B * w.H * w.N
+    peak = 157.3 if w.dtype == "f32" else 2516.6
+    achieved = flops / t / 1e12
+    return {"workload": w.name, "ms_per_call": round(t * 1e3, 4), "tokens_per_s": round(w.B * w.N / t, 1),
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                         "frac": round(achieved / peak, 4), "alg_flops_per_launch": flops,
+                         "traffic": None}}
+
+
 def bench_decode(args, torch, ops, wl):
     """States of a 65536-token prefix per (b, h), then 256 single-token steps."""
     w = wl.WORKLOADS["decode"]
@@ -221,7 +256,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline (profiling runs)")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "others"], default=None)
     ap.add_argument("--calibrate", action="store_true",
                     help="run only tt_state_merge over 2 x 256 MiB -> 256 MiB (known HBM bytes), "
                          "to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -258,6 +293,11 @@ def main():
     if args.only in (None, "decode"):
         dec = bench_decode(args, torch, ops, wl)
         print(f"# decode: {dec['us_per_step']:.2f} us/step", file=sys.stderr, flush=True)
+    others = {}
+    if args.only in (None, "others"):
+        for name in ("order5", "wide"):
+            others[name] = bench_prefill_other(name, args, torch, ops, wl)
+            print(f"# {name}: {others[name]['ms_per_call']:.3f} ms/call", file=sys.stderr, flush=True)
 
     out = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -273,6 +313,8 @@ def main():
                      "decode_workload": wl.WORKLOADS["decode"].name}
     if dec is not None:
         out["decode"] = dec
+    if others:
+        out["other_prefill_workloads"] = others
     if not args.no_cpu and pre is not None:
         pre_cpu, dec_cpu, cores = cpu_baselines(pre, wl)
         out["cpu_baseline"] = pre_cpu

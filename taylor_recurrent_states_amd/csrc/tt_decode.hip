@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const TIn* __res
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const auto& tab = RowsOf<DK>::get();
 
   if (tid < DK) {

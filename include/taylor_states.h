@@ -89,7 +89,7 @@ int tt_prefill_workspace_bytes(int B, int H, int N, int dk, int dv, int n,
  *   workspace : device scratch of at least tt_prefill_workspace_bytes();
  *            contents undefined on return
  *   chunk : tokens per chunk of the intra-chunk quadratic block; 64.
- * Q, K, V and workspace must be 16-byte aligned (TT_ERR_INVALID_ARG).
+ * Q, K, V, O and workspace must be 16-byte aligned (TT_ERR_INVALID_ARG).
  * Any N >= 1 is accepted (the tail chunk is masked).  Results do not
  * depend on how the work is split beyond fp32 rounding. */
 int tt_prefill(const void *Q, const void *K, const void *V, tt_dtype in_dtype,

@@ -108,8 +108,8 @@ int tt_prefill(const void* Q, const void* K, const void* V, tt_dtype in_dtype, i
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(TT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
-  if ((((uintptr_t)Q) | ((uintptr_t)K) | ((uintptr_t)V) | ((uintptr_t)workspace)) & 15u)
-    return fail(TT_ERR_INVALID_ARG, "Q, K, V and workspace must be 16-byte aligned");
+  if ((((uintptr_t)Q) | ((uintptr_t)K) | ((uintptr_t)V) | ((uintptr_t)O) | ((uintptr_t)workspace)) & 15u)
+    return fail(TT_ERR_INVALID_ARG, "Q, K, V, O and workspace must be 16-byte aligned");
   return hip_status(launch_prefill(Q, K, V, in_dtype, B * H, N, dk, n, p, O, states, (float*)workspace,
                                    (hipStream_t)stream),
                     "tt_prefill launch");

@@ -162,6 +162,30 @@ __device__ inline f32x4 mfma_f32(float a, float b, f32x4 c) {
 
 __device__ inline f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
+// Workgroup barrier ordering LDS only: each wave waits for its own LDS
+// operations, not for its global loads and stores in flight (a plain
+// __syncthreads() also drains outstanding global stores).  For kernels whose
+// waves never read global memory written by another wave of the workgroup.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Transposing LDS read of 16-bit data (gfx950 ds_read_b64_tr_b16).  Within
+// each group of 16 lanes, lane l receives element l%4 of the 8-byte pieces
+// addressed by lanes 4s + l/4, s = 0..3 (probed on gfx950).  Consequence used
+// by the kernels: if lane j of group g addresses row 8g + 4h + j/4 and column
+// c(j%4) of a row-major bf16 tile X[k][col], lane (i, g) receives
+// X[8g + 4h + s][c(i/4) + i%4] for s = 0..3; two reads (h = 0, 1) give the
+// bf16 16x16x32 MFMA fragment whose K index runs over the tile's rows.
+__device__ inline uint2 lds_tr16(const void* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 // static_for<B, E>(f): f(integral_constant<int, i>) for i in [B, E)
 template <int B, int E, typename F>
 __device__ inline void static_for(F&& f) {

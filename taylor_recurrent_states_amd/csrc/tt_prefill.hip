@@ -59,6 +59,51 @@ constexpr int pick_j(int maxkb, int jmax) {
   return best;
 }
 
+// Octet-aligned internal row order for bf16 inputs with n = 3 and dk >= 32.
+// Rows come in groups of 8 ("octets") x_a * x[b0 .. b0+7] with b0 a multiple
+// of 8: octet 0 holds the order-0 row (then 7 zero rows), then dk/8 octets of
+// order 1 (x[b0..b0+7]), then for every a the octets b0 = 8*floor(a/8), ...,
+// dk-8 of order 2, whose rows with b < a are zero.  A lane (= token) builds an
+// octet from one 16-byte read of its coordinates and one scalar read.  The
+// span workspace uses this order; the final states are written in feature
+// order through abi_row().
+constexpr bool use_oct(bool bf, int dk, int nt) { return bf && nt == 3 && dk >= 32; }
+constexpr int oct_rows(int dk) { return 8 + dk + dk * (dk + 8) / 2; }
+constexpr int internal_rows(bool bf, int dk, int nt) { return use_oct(bf, dk, nt) ? oct_rows(dk) : rows_for(dk, nt); }
+
+// octet descriptors: m | a << 8 | b0 << 16
+template <int DK>
+struct OctTable {
+  static constexpr int NO = oct_rows(DK) / 8;
+  uint32_t d[NO];
+  constexpr OctTable() : d() {
+    int o = 0;
+    d[o++] = 0u;
+    for (int b0 = 0; b0 < DK; b0 += 8) d[o++] = 1u | ((uint32_t)b0 << 16);
+    for (int a = 0; a < DK; ++a)
+      for (int b0 = a / 8 * 8; b0 < DK; b0 += 8) d[o++] = 2u | ((uint32_t)a << 8) | ((uint32_t)b0 << 16);
+  }
+};
+static __device__ const OctTable<32> kOct32 = OctTable<32>();
+static __device__ const OctTable<64> kOct64 = OctTable<64>();
+template <int DK> struct OctOf;
+template <> struct OctOf<32> { static __device__ const OctTable<32>& get() { return kOct32; } };
+template <> struct OctOf<64> { static __device__ const OctTable<64>& get() { return kOct64; } };
+
+// feature-order row of internal octet row r, or -1 for a zero (padding) row
+template <int DK>
+__device__ inline int abi_row(int r) {
+  constexpr int NO = OctTable<DK>::NO;
+  const int o = r >> 3, u = r & 7;
+  if (o >= NO) return -1;
+  const uint32_t d = OctOf<DK>::get().d[o];
+  const int m = d & 0xFF, a = (d >> 8) & 0xFF, b = (int)(d >> 16) + u;
+  if (m == 0) return u == 0 ? 0 : -1;
+  if (m == 1) return 1 + b;
+  if (b < a) return -1;
+  return 1 + DK + a * DK - a * (a - 1) / 2 + (b - a);
+}
+
 template <typename TIn_, int DK_, int NT_, int NVT_, int NRP_, int MODE_>
 struct Cfg {
   using TIn = TIn_;
@@ -67,10 +112,12 @@ struct Cfg {
   static constexpr int DK = DK_, NT = NT_, NVT = NVT_, NRP = NRP_;
   static constexpr int NW = NVT * NRP;
   static constexpr int NTHR = NW * 64;
-  static constexpr int W = rows_for(DK, NT);
+  static constexpr int W = rows_for(DK, NT);             // feature rows
+  static constexpr bool OCT = use_oct(BF, DK, NT);       // octet-aligned internal row order
+  static constexpr int WI = internal_rows(BF, DK, NT);   // internal rows
   static constexpr int KB = BF ? 32 : 16;  // feature rows (and tokens) per K-block
   static constexpr int TPK = BF ? 2 : 1;   // accumulator tiles per K-block
-  static constexpr int NKB = (W + KB - 1) / KB;
+  static constexpr int NKB = (WI + KB - 1) / KB;
   static constexpr int MAXKB = (NKB + NRP - 1) / NRP;
   static constexpr int SRMAX = BF ? 256 : 128;
   static constexpr int J = pick_j(MAXKB, SRMAX / (NRP * KB));
@@ -89,17 +136,19 @@ struct Cfg {
   // small feature sets are generated by fully unrolled code (lane = token)
   static constexpr bool UNR = WP <= 256;
   static constexpr int PHS = SR + PADE;    // phi row stride (elements)
-  static constexpr int MUS = kCH + PADE;   // mu^T row stride
+  // mu: [row][token] (mu^T, read with plain vector loads), or token-major
+  // [token][row] for the octet generator (read with transposing loads)
+  static constexpr int MUS = OCT ? SR + PADE : kCH + PADE;
   static constexpr int VS = kCH + PADE;    // V^T row stride
   static constexpr int PS = kCH + PADE;    // P row stride
   static constexpr int NMU = (BF && !OUT) ? 2 : 1;  // mu planes (hi, lo) in the totals pass
   static constexpr int NPP = BF ? 2 : 1;            // P planes (hi, lo)
   static constexpr int PPL = kCH * PS;              // elements per P plane
-  static constexpr int MUPL = SR * MUS;             // elements per mu plane
+  static constexpr int MUPL = OCT ? kCH * MUS : SR * MUS;  // elements per mu plane
   // LDS carve-up (bytes, 16-aligned); Q, P and phi exist in the output pass only
   static constexpr int al(int b) { return (b + 15) / 16 * 16; }
   static constexpr int O_TAB = 0;
-  static constexpr int O_K = O_TAB + (UNR ? 0 : al(WP * 4));
+  static constexpr int O_K = O_TAB + (UNR || OCT ? 0 : al(WP * 4));
   static constexpr int O_Q = O_K + al(kCH * XS * ES);
   static constexpr int O_V = O_Q + (OUT ? al(kCH * XS * ES) : 0);
   static constexpr int O_P = O_V + al(GC * VS * ES);
@@ -241,6 +290,72 @@ __device__ inline void gen_unrolled(int sl, int w, int lane, int nvalid, const t
 }
 
 
+// Octet generator (bf16, octet row order): wave w builds the octets of slab sl
+// with index == w (mod NW), lane = token.  phi (row 0 excluded: the order-0
+// term is added in fp32; weight 1/2 on b == a) to sPhi[token][row]; mu to the
+// token-major sMu[token][row], hi and (totals pass) lo planes split exactly.
+template <class C>
+__device__ inline void gen_octets(int sl, int w, int lane, int nvalid, const uint16_t* sQ, const uint16_t* sK,
+                                  uint16_t* sPhi, uint16_t* sMu) {
+  constexpr int NOS = C::SR / 8;
+  constexpr int NO = OctTable<C::DK>::NO;
+  const float kmask = lane < nvalid ? 1.f : 0.f;
+  auto unpack8 = [](const u32x4 v, float* x) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(v[e] << 16);
+      x[2 * e + 1] = __uint_as_float(v[e] & 0xFFFF0000u);
+    }
+  };
+  for (int oi = w; oi < NOS; oi += C::NW) {
+    const int o = sl * NOS + oi;
+    const uint32_t d = o < NO ? OctOf<C::DK>::get().d[o] : 0xFFu;
+    const int m = d & 0xFF, a = (d >> 8) & 0xFF, b0 = (int)(d >> 16);
+    float mu[8], ph[8];
+    if (m == 1 || m == 2) {
+      float kx[8];
+      unpack8(*reinterpret_cast<const u32x4*>(sK + lane * C::XS + b0), kx);
+      const float ka = m == 2 ? bf16_to_f32(sK[lane * C::XS + a]) : 1.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) mu[u] = (b0 + u >= a || m == 1) ? ka * kx[u] : 0.f;
+      if constexpr (C::OUT) {
+        float qx[8];
+        unpack8(*reinterpret_cast<const u32x4*>(sQ + lane * C::XS + b0), qx);
+        const float qa = m == 2 ? bf16_to_f32(sQ[lane * C::XS + a]) : 1.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float wgt = (m == 1 || b0 + u > a) ? 1.f : (b0 + u == a ? 0.5f : 0.f);
+          ph[u] = wgt * qa * qx[u];
+        }
+      }
+    } else {  // order 0 (row 0 only) or past the last octet
+#pragma unroll
+      for (int u = 0; u < 8; ++u) { mu[u] = (m == 0 && u == 0) ? kmask : 0.f; ph[u] = 0.f; }
+    }
+    const int rl = oi * 8;
+    if constexpr (C::OUT) {
+      *reinterpret_cast<u32x4*>(sPhi + lane * C::PHS + rl) =
+          u32x4{pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]), pack_bf16x2(ph[4], ph[5]), pack_bf16x2(ph[6], ph[7])};
+      *reinterpret_cast<u32x4*>(sMu + lane * C::MUS + rl) =
+          u32x4{pack_bf16x2(mu[0], mu[1]), pack_bf16x2(mu[2], mu[3]), pack_bf16x2(mu[4], mu[5]), pack_bf16x2(mu[6], mu[7])};
+    } else {
+      // rows are products of at most two bf16 values: hi = truncation, lo = rest, both exact
+      uint32_t hb[8], lb[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        hb[u] = __float_as_uint(mu[u]) & 0xFFFF0000u;
+        lb[u] = __float_as_uint(mu[u] - __uint_as_float(hb[u]));
+      }
+      auto pk = [](const uint32_t* x) {
+        return u32x4{__builtin_amdgcn_perm(x[1], x[0], 0x07060302u), __builtin_amdgcn_perm(x[3], x[2], 0x07060302u),
+                     __builtin_amdgcn_perm(x[5], x[4], 0x07060302u), __builtin_amdgcn_perm(x[7], x[6], 0x07060302u)};
+      };
+      *reinterpret_cast<u32x4*>(sMu + lane * C::MUS + rl) = pk(hb);
+      *reinterpret_cast<u32x4*>(sMu + C::MUPL + lane * C::MUS + rl) = pk(lb);
+    }
+  }
+}
+
 // Feature generation for the row groups g == part (mod nparts) of all WP rows,
 // lane = token; xq/xk hold the token's query and key coordinates.  Both sides
 // go to token-major tiles with one 16-byte store per group of 8 rows: phi to
@@ -358,7 +473,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
   float* wsS = ws + ((size_t)bh * nspan + s_idx) * ws_span;
 
   // feature-row codes for the table-driven generator; padded rows contribute nothing
-  if constexpr (!C::UNR) {
+  if constexpr (!C::UNR && !C::OCT) {
     const auto& tab = RowsOf<C::DK>::get();
     for (int r = tid; r < C::WP; r += C::NTHR) sTab[r] = (r < C::W) ? tab.code[r] : kPadRow;
   }
@@ -542,11 +657,14 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
     }
 
     // ---- 3. feature slabs: readout (output pass) then update ----
-#pragma unroll
-    for (int sl = 0; sl < C::NSLAB; ++sl) {
+    // slabs unrolled at compile time so that every state register index is static
+    static_for<0, C::NSLAB>([&](auto slc) {
+      constexpr int sl = decltype(slc)::value;
       const int row0 = sl * C::SR;
       if constexpr (C::UNR) {
         gen_unrolled<C>(sl, w, lane, nvalid, sQ, sK, sPhi, sMu);
+      } else if constexpr (C::OCT) {
+        gen_octets<C>(sl, w, lane, nvalid, sQ, sK, sPhi, sMu);
       } else {
         // table-driven generator. phi (query side; row 0 excluded: the m = 0
         // term is added in fp32): lanes = queries, one row per wave step
@@ -645,6 +763,18 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
         __syncthreads();  // normaliser reads of this slab finish before its update
       }
 
+      // bf16 mu^T fragment (A operand, rows rho(tau, i)) of slab K-block kbl, token block tb, plane pl
+      auto mu_frag = [&](int pl, int kbl, int tau, int tb) -> u32x4 {
+        if constexpr (C::OCT) {  // token-major tile: two transposing reads
+          const unsigned char* p = (const unsigned char*)sMu +
+              (pl * C::MUPL + (tb * 32 + 8 * lg + (li >> 2)) * C::MUS + kbl * 32 + 8 * (li & 3) + 4 * tau) * 2;
+          const uint2 x = lds_tr16(p), y = lds_tr16(p + 4 * C::MUS * 2);
+          return u32x4{x.x, x.y, y.x, y.y};
+        } else {
+          return lds_u32x4((const unsigned char*)sMu,
+                           (pl * C::MUPL + (kbl * 32 + rho(tau, li)) * C::MUS + tb * 32 + 8 * lg) * 2);
+        }
+      };
       // value update: S[kb] += mu^T V
 #pragma unroll
       for (int jl = 0; jl < C::J; ++jl) {
@@ -656,12 +786,10 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
             const u32x4 b = lds_u32x4((const unsigned char*)sV, ((ct * 16 + li) * C::VS + tb * 32 + 8 * lg) * 2);
 #pragma unroll
             for (int tau = 0; tau < 2; ++tau) {
-              const int rowl = kbl * 32 + rho(tau, li);
-              const u32x4 ah = lds_u32x4((const unsigned char*)sMu, (rowl * C::MUS + tb * 32 + 8 * lg) * 2);
+              const u32x4 ah = mu_frag(0, kbl, tau, tb);
               st[j][tau % C::TPK] = mfma_bf16(ah, b, st[j][tau % C::TPK]);
               if constexpr (!OUT) {
-                const u32x4 al = lds_u32x4((const unsigned char*)sMu,
-                                           (C::MUPL + rowl * C::MUS + tb * 32 + 8 * lg) * 2);
+                const u32x4 al = mu_frag(1, kbl, tau, tb);
                 st[j][tau % C::TPK] = mfma_bf16(al, b, st[j][tau % C::TPK]);
               }
             }
@@ -683,14 +811,8 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
 #pragma unroll
           for (int tb = 0; tb < C::TB; ++tb) {
             if constexpr (BF) {
-              const int rowl = kbl * 32 + rho(tau, li);
-              const u32x4 ah = lds_u32x4((const unsigned char*)sMu, (rowl * C::MUS + tb * 32 + 8 * lg) * 2);
-              acc = mfma_bf16(ah, ones_bf, acc);
-              if constexpr (!OUT) {
-                const u32x4 al = lds_u32x4((const unsigned char*)sMu,
-                                           (C::MUPL + rowl * C::MUS + tb * 32 + 8 * lg) * 2);
-                acc = mfma_bf16(al, ones_bf, acc);
-              }
+              acc = mfma_bf16(mu_frag(0, kbl, tau, tb), ones_bf, acc);
+              if constexpr (!OUT) acc = mfma_bf16(mu_frag(1, kbl, tau, tb), ones_bf, acc);
             } else {
               const f32x4 a = lds_f32x4((const unsigned char*)sMu, ((kbl * 16 + li) * C::MUS + tb * 16 + 4 * lg) * 4);
               acc = mfma_f32(a.x, ones_f, acc);
@@ -709,7 +831,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
         }
       }
       __syncthreads();  // slab buffers are rewritten by the next slab
-    }
+    });
 
     if constexpr (OUT) {
       // ---- 4. intra-chunk contribution, m = 0 row, reduction, normalise ----
@@ -1310,7 +1432,9 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
 }
 
 // Exclusive scan of span totals over spans (in place) and the final states.
-__global__ void scan_kernel(float* __restrict__ ws, int nspan, int WP, int W, int BH,
+// The workspace rows are internal rows: feature order, or the octet order
+// when octdk is 32 or 64 (mapped back with abi_row; padding rows dropped).
+__global__ void scan_kernel(float* __restrict__ ws, int nspan, int WP, int W, int BH, int octdk,
                             float* __restrict__ states) {
   const size_t per = (size_t)WP * (kDV + 1);
   const size_t total = (size_t)BH * per;
@@ -1336,12 +1460,15 @@ __global__ void scan_kernel(float* __restrict__ ws, int nspan, int WP, int W, in
       p[(size_t)s * per] = run;
       run += t;
     }
-    if (off < (size_t)WP * kDV) {
-      const size_t r = off / kDV, c = off - (off / kDV) * kDV;
-      if (r < (size_t)W) states[(bh * W + r) * kDV + c] = run;
+    const bool val = off < (size_t)WP * kDV;
+    const int r = (int)(val ? off / kDV : off - (size_t)WP * kDV);
+    const int ra = octdk == 64 ? abi_row<64>(r) : octdk == 32 ? abi_row<32>(r) : (r < W ? r : -1);
+    if (ra < 0) continue;
+    if (val) {
+      const size_t c = off - (size_t)r * kDV;
+      states[(bh * W + ra) * kDV + c] = run;
     } else {
-      const size_t r = off - (size_t)WP * kDV;
-      if (r < (size_t)W) states[(size_t)BH * W * kDV + bh * W + r] = run;
+      states[(size_t)BH * W * kDV + bh * W + ra] = run;
     }
   }
 }
@@ -1359,7 +1486,7 @@ constexpr int pick_nrp(int nkb, int fpk) {
 template <typename TIn, int DK, int NT>
 struct Shape {
   static constexpr bool BF = std::is_same<TIn, uint16_t>::value;
-  static constexpr int W = rows_for(DK, NT);
+  static constexpr int W = internal_rows(BF, DK, NT);
   static constexpr int KB = BF ? 32 : 16;
   static constexpr int NKB = (W + KB - 1) / KB;
   static constexpr int NRP = pick_nrp(NKB, BF ? 8 : 4);
@@ -1422,11 +1549,11 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype 
                           const PrefillPlan& p, float* O, float* states, float* ws, hipStream_t s) {
   return with_dkn(dk, n, [&](auto DKc, auto Nc) {
     constexpr int DK = decltype(DKc)::value, NT = decltype(Nc)::value;
-    auto scan = [&](int WP, int W) {
+    auto scan = [&](int WP, int octdk) {
       const size_t total = (size_t)BH * WP * (kDV + 1);
       unsigned g = (unsigned)((total + 255) / 256);
       if (g > 16384) g = 16384;
-      hipLaunchKernelGGL(scan_kernel, dim3(g), dim3(256), 0, s, ws, p.nspan, WP, W, BH, states);
+      hipLaunchKernelGGL(scan_kernel, dim3(g), dim3(256), 0, s, ws, p.nspan, WP, p.W, BH, octdk, states);
       return hipGetLastError();
     };
     auto go = [&](auto tag) {
@@ -1437,7 +1564,7 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype 
                          (const TIn*)K, (const TIn*)V, N, p.span, p.nspan, ws, O);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      e = scan((int)S::Out::WP, (int)S::Out::W);
+      e = scan((int)S::Out::WP, S::Out::OCT ? DK : 0);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((sweep_kernel<typename S::Out>), dim3(nblk), dim3(S::Out::NTHR), 0, s, (const TIn*)Q,
                          (const TIn*)K, (const TIn*)V, N, p.span, p.nspan, ws, O);
@@ -1452,7 +1579,7 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype 
                            (const uint16_t*)K, (const uint16_t*)V, N, p.span, p.nspan, ws, O);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        e = scan((int)PO::WP, (int)PO::W);
+        e = scan((int)PO::WP, 0);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((pipe_kernel<PO>), dim3(nblk), dim3(PO::NTHR), 0, s, (const uint16_t*)Q,
                            (const uint16_t*)K, (const uint16_t*)V, N, p.span, p.nspan, ws, O);

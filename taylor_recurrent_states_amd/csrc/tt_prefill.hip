@@ -145,20 +145,35 @@ struct Cfg {
   static constexpr int NPP = BF ? 2 : 1;            // P planes (hi, lo)
   static constexpr int PPL = kCH * PS;              // elements per P plane
   static constexpr int MUPL = OCT ? kCH * MUS : SR * MUS;  // elements per mu plane
-  // LDS carve-up (bytes, 16-aligned); Q, P and phi exist in the output pass only
+  // LDS carve-up (bytes, 16-aligned); Q, P and phi exist in the output pass
+  // only.  The normaliser is double-buffered across chunks (read the state
+  // before the chunk, write the state after it); the phi/mu slab tiles are
+  // double-buffered across slabs when the budget allows, so that the next
+  // slab is generated while this one is contracted.
   static constexpr int al(int b) { return (b + 15) / 16 * 16; }
+  static constexpr int TABB = UNR ? 0 : al((OCT ? WI / 8 : WP) * 4);  // row codes / octet descriptors
+  static constexpr int B_PHI = OUT ? al(kCH * PHS * ES) : 0;
+  static constexpr int B_MU = al(NMU * MUPL * ES);
+  static constexpr int RED_BYTES = OUT ? NW * 4 * 64 * 16 : 0;  // partial num tiles
+  static constexpr int lds_for(int nbuf) {
+    const int fixed = TABB + al(kCH * XS * ES) * (OUT ? 2 : 1) + al(GC * VS * ES) + (OUT ? al(NPP * PPL * ES) : 0) +
+                      al(2 * WP * 4) + al(kCH * 4);
+    const int slabs = nbuf * (B_PHI + B_MU);
+    return fixed + (slabs > RED_BYTES ? slabs : RED_BYTES);
+  }
+  static constexpr int NBUF = lds_for(2) <= 160 * 1024 ? 2 : 1;
   static constexpr int O_TAB = 0;
-  static constexpr int O_K = O_TAB + (UNR || OCT ? 0 : al(WP * 4));
+  static constexpr int O_K = O_TAB + TABB;
   static constexpr int O_Q = O_K + al(kCH * XS * ES);
   static constexpr int O_V = O_Q + (OUT ? al(kCH * XS * ES) : 0);
   static constexpr int O_P = O_V + al(GC * VS * ES);
   static constexpr int O_DEN = O_P + (OUT ? al(NPP * PPL * ES) : 0);
-  static constexpr int O_DENQ = O_DEN + al(WP * 4);
+  static constexpr int O_DENQ = O_DEN + al(2 * WP * 4);
   static constexpr int O_PHI = O_DENQ + al(kCH * 4);
-  static constexpr int O_MU = O_PHI + (OUT ? al(kCH * PHS * ES) : 0);
-  static constexpr int O_END = O_MU + al(NMU * MUPL * ES);
-  static constexpr int RED_BYTES = OUT ? NW * 4 * 64 * 16 : 0;  // partial num tiles
+  static constexpr int O_MU = O_PHI + NBUF * B_PHI;
+  static constexpr int O_END = O_MU + NBUF * B_MU;
   static constexpr int LDS = (O_END > O_PHI + RED_BYTES ? O_END : O_PHI + RED_BYTES);
+  static_assert(LDS == lds_for(NBUF), "LDS carve-up");
   static_assert(LDS <= 160 * 1024, "LDS budget");
   // global -> register staging in 16-byte segments
   static constexpr int EPS = 16 / ES;                // elements per segment
@@ -295,8 +310,8 @@ __device__ inline void gen_unrolled(int sl, int w, int lane, int nvalid, const t
 // term is added in fp32; weight 1/2 on b == a) to sPhi[token][row]; mu to the
 // token-major sMu[token][row], hi and (totals pass) lo planes split exactly.
 template <class C>
-__device__ inline void gen_octets(int sl, int w, int lane, int nvalid, const uint16_t* sQ, const uint16_t* sK,
-                                  uint16_t* sPhi, uint16_t* sMu) {
+__device__ inline void gen_octets(int sl, int w, int lane, int nvalid, const uint32_t* tab, const uint16_t* sQ,
+                                  const uint16_t* sK, uint16_t* sPhi, uint16_t* sMu) {
   constexpr int NOS = C::SR / 8;
   constexpr int NO = OctTable<C::DK>::NO;
   const float kmask = lane < nvalid ? 1.f : 0.f;
@@ -309,7 +324,7 @@ __device__ inline void gen_octets(int sl, int w, int lane, int nvalid, const uin
   };
   for (int oi = w; oi < NOS; oi += C::NW) {
     const int o = sl * NOS + oi;
-    const uint32_t d = o < NO ? OctOf<C::DK>::get().d[o] : 0xFFu;
+    const uint32_t d = o < NO ? tab[o] : 0xFFu;
     const int m = d & 0xFF, a = (d >> 8) & 0xFF, b0 = (int)(d >> 16);
     float mu[8], ph[8];
     if (m == 1 || m == 2) {
@@ -352,6 +367,82 @@ __device__ inline void gen_octets(int sl, int w, int lane, int nvalid, const uin
       };
       *reinterpret_cast<u32x4*>(sMu + lane * C::MUS + rl) = pk(hb);
       *reinterpret_cast<u32x4*>(sMu + C::MUPL + lane * C::MUS + rl) = pk(lb);
+    }
+  }
+}
+
+// Run generator (table-driven rows, any order): wave w builds the rows
+// [w*RPW, (w+1)*RPW) of slab sl, lane = token.  Consecutive rows of one order
+// that share all but their last index form a run; the product over the shared
+// indices is kept for the run, so a row costs one coordinate read and one
+// multiply per side.  phi rows (query side, weight folded in, row 0 left out)
+// go to sPhi[token][row] in 16-byte stores; mu rows to sMu[row][token].
+template <class C>
+__device__ inline void gen_runs(int sl, int w, int lane, int nvalid, const uint32_t* tab,
+                                const typename C::Elem* sQ, const typename C::Elem* sK, typename C::Elem* sPhi,
+                                typename C::Elem* sMu) {
+  using Elem = typename C::Elem;
+  constexpr int RPW = C::SR / C::NW;  // rows per wave
+  constexpr int G = C::BF ? 8 : 4;    // rows per 16-byte phi store
+  static_assert(RPW % G == 0, "rows per wave must fill whole phi stores");
+  const int rb = w * RPW;
+  const uint32_t* trow = tab + sl * C::SR + rb;
+  const float kmask = lane < nvalid ? 1.f : 0.f;
+  const Elem* xq = sQ + lane * C::XS;
+  const Elem* xk = sK + lane * C::XS;
+  uint32_t pkey = 0xFFFFFFFFu;  // order and leading indices of the run in progress
+  float pq = 1.f, pk = 1.f;
+  for (int g0 = 0; g0 < RPW; g0 += G) {
+    uint32_t codes[G];
+#pragma unroll
+    for (int c4 = 0; c4 < G / 4; ++c4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(trow + g0 + 4 * c4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) codes[4 * c4 + e] = __builtin_amdgcn_readfirstlane(v[e]);
+    }
+    float ph[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const uint32_t code = codes[u];
+      const int m = row_order(code);
+      float mu = 0.f, phv = 0.f;
+      if (m == 0) {
+        mu = kmask;
+      } else if (m < 7) {
+        const uint32_t key = (code & ((1u << (6 * (m - 1))) - 1u)) | ((uint32_t)m << 24);
+        if (key != pkey) {
+          pkey = key;
+          pq = 1.f;
+          pk = 1.f;
+          for (int l = 0; l < m - 1; ++l) {
+            const int ix = row_index(code, l);
+            pk *= to_f32(xk[ix]);
+            if constexpr (C::OUT) pq *= to_f32(xq[ix]);
+          }
+        }
+        const int il = row_index(code, m - 1);
+        mu = pk * to_f32(xk[il]);
+        if constexpr (C::OUT) phv = row_weight(code) * pq * to_f32(xq[il]);
+      }
+      ph[u] = phv;
+      const int rl = rb + g0 + u;
+      if constexpr (C::BF) {
+        uint16_t hi, lo;
+        split_bf16(mu, hi, lo);
+        sMu[rl * C::MUS + lane] = hi;
+        if constexpr (!C::OUT) sMu[C::MUPL + rl * C::MUS + lane] = lo;
+      } else {
+        sMu[rl * C::MUS + lane] = mu;
+      }
+    }
+    if constexpr (C::OUT) {
+      Elem* dst = sPhi + lane * C::PHS + rb + g0;
+      if constexpr (C::BF) {
+        *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]),
+                                               pack_bf16x2(ph[4], ph[5]), pack_bf16x2(ph[6], ph[7])};
+      } else {
+        *reinterpret_cast<f32x4*>(dst) = f32x4{ph[0], ph[1], ph[2], ph[3]};
+      }
     }
   }
 }
@@ -445,10 +536,10 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
   Elem* sK = reinterpret_cast<Elem*>(lds + C::O_K);
   Elem* sV = reinterpret_cast<Elem*>(lds + C::O_V);
   Elem* sP = reinterpret_cast<Elem*>(lds + C::O_P);
-  float* sDen = reinterpret_cast<float*>(lds + C::O_DEN);
+  float* sDen = reinterpret_cast<float*>(lds + C::O_DEN);  // [2][WP]: state before / after the chunk
   float* sDenQ = reinterpret_cast<float*>(lds + C::O_DENQ);
-  Elem* sPhi = reinterpret_cast<Elem*>(lds + C::O_PHI);
-  Elem* sMu = reinterpret_cast<Elem*>(lds + C::O_MU);
+  auto phi_buf = [&](int b) { return reinterpret_cast<Elem*>(lds + C::O_PHI + b * C::B_PHI); };
+  auto mu_buf = [&](int b) { return reinterpret_cast<Elem*>(lds + C::O_MU + b * C::B_MU); };
   float* sRed = reinterpret_cast<float*>(lds + C::O_PHI);  // reused after the slabs
 
   const int tid = threadIdx.x;
@@ -473,7 +564,10 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
   float* wsS = ws + ((size_t)bh * nspan + s_idx) * ws_span;
 
   // feature-row codes for the table-driven generator; padded rows contribute nothing
-  if constexpr (!C::UNR && !C::OCT) {
+  if constexpr (C::OCT) {
+    const auto& tab = OctOf<C::DK>::get();
+    for (int r = tid; r < C::WI / 8; r += C::NTHR) sTab[r] = tab.d[r];
+  } else if constexpr (!C::UNR) {
     const auto& tab = RowsOf<C::DK>::get();
     for (int r = tid; r < C::WP; r += C::NTHR) sTab[r] = (r < C::W) ? tab.code[r] : kPadRow;
   }
@@ -580,8 +674,11 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
   };
 
   issue(t_begin);
+  int db = 0;  // normaliser buffer holding the state before the current chunk
   for (int c0 = t_begin; c0 < t_end; c0 += kCH) {
     const int nvalid = min(kCH, t_end - c0);
+    const float* Den = sDen + db * C::WP;
+    float* DenN = sDen + (db ^ 1) * C::WP;
 
     // ---- 1. stage this chunk, start loading the next ----
     commit();
@@ -653,57 +750,32 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
       }
       // m = 0 row (exact in fp32): S[0][cols] and the token count S[0][dv]
       m0 = __shfl(st[0][0].x, li);  // lane (col, g = 0) holds row 0 of K-block 0 (rp = 0 only)
-      den0 = sDen[0];
+      den0 = Den[0];
     }
 
     // ---- 3. feature slabs: readout (output pass) then update ----
+    // phi / mu tiles of slab sl (compile-time) into the given buffers
+    auto gen_slab = [&](auto slc, Elem* sPhi, Elem* sMu) {
+      constexpr int sl = decltype(slc)::value;
+      const int row0 = sl * C::SR;
+      (void)row0;
+      if constexpr (C::UNR) {
+        gen_unrolled<C>(sl, w, lane, nvalid, sQ, sK, sPhi, sMu);
+      } else if constexpr (C::OCT) {
+        gen_octets<C>(sl, w, lane, nvalid, sTab, sQ, sK, sPhi, sMu);
+      } else {
+        gen_runs<C>(sl, w, lane, nvalid, sTab, sQ, sK, sPhi, sMu);
+      }
+    };
+    gen_slab(std::integral_constant<int, 0>{}, phi_buf(0), mu_buf(0));
+    __syncthreads();
     // slabs unrolled at compile time so that every state register index is static
     static_for<0, C::NSLAB>([&](auto slc) {
       constexpr int sl = decltype(slc)::value;
       const int row0 = sl * C::SR;
-      if constexpr (C::UNR) {
-        gen_unrolled<C>(sl, w, lane, nvalid, sQ, sK, sPhi, sMu);
-      } else if constexpr (C::OCT) {
-        gen_octets<C>(sl, w, lane, nvalid, sQ, sK, sPhi, sMu);
-      } else {
-        // table-driven generator. phi (query side; row 0 excluded: the m = 0
-        // term is added in fp32): lanes = queries, one row per wave step
-        if constexpr (OUT) {
-          for (int e = tid; e < kCH * C::SR; e += C::NTHR) {
-            const int rl = e >> 6, q = e & 63;
-            const uint32_t te = sTab[row0 + rl];
-            const int m = row_order(te);
-            float val = 0.f;
-            if (row0 + rl > 0 && m < 7) {
-              val = row_weight(te);
-              for (int l = 0; l < m; ++l) val *= to_f32(sQ[q * C::XS + row_index(te, l)]);
-            }
-            if constexpr (BF) sPhi[q * C::PHS + rl] = (Elem)f32_to_bf16(val);
-            else sPhi[q * C::PHS + rl] = val;
-          }
-        }
-        // mu^T (key side): lanes = tokens
-        for (int e = tid; e < kCH * C::SR; e += C::NTHR) {
-          const int rl = e >> 6, tok = e & 63;
-          const uint32_t te = sTab[row0 + rl];
-          const int m = row_order(te);
-          float val = 0.f;
-          if (m < 7 && tok < nvalid) {
-            val = 1.f;
-            for (int l = 0; l < m; ++l) val *= to_f32(sK[tok * C::XS + row_index(te, l)]);
-          }
-          if constexpr (BF) {
-            uint16_t hi, lo;
-            split_bf16(val, hi, lo);
-            sMu[rl * C::MUS + tok] = hi;
-            if constexpr (!OUT) sMu[C::MUPL + rl * C::MUS + tok] = lo;
-          } else {
-            sMu[rl * C::MUS + tok] = val;
-          }
-        }
-      }
-      __syncthreads();
-
+      Elem* const sPhi = phi_buf(sl % C::NBUF);
+      Elem* const sMu = mu_buf(sl % C::NBUF);
+      (void)sPhi;
       if constexpr (OUT) {
         // value readout over this wave's K-blocks of the slab
 #pragma unroll
@@ -740,7 +812,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
           if (qt % C::NW != w) continue;
           for (int kbl = 0; kbl < C::NRP * C::J; ++kbl) {
             if constexpr (BF) {
-              const float* dr = sDen + row0 + kbl * 32 + 8 * lg;
+              const float* dr = Den + row0 + kbl * 32 + 8 * lg;
               u32x4 b = {0u, 0u, 0u, 0u};
               if (li == 0) {
                 b.x = pack_bf16x2(dr[0], dr[1]); b.y = pack_bf16x2(dr[2], dr[3]);
@@ -752,7 +824,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
             } else {
               const f32x4 a = lds_f32x4((const unsigned char*)sPhi,
                                         ((qt * 16 + li) * C::PHS + kbl * 16 + 4 * lg) * 4);
-              const f32x4 d = *reinterpret_cast<const f32x4*>(sDen + row0 + kbl * 16 + 4 * lg);
+              const f32x4 d = *reinterpret_cast<const f32x4*>(Den + row0 + kbl * 16 + 4 * lg);
               den[qt] = mfma_f32(a.x, ones_f * d.x, den[qt]);
               den[qt] = mfma_f32(a.y, ones_f * d.y, den[qt]);
               den[qt] = mfma_f32(a.z, ones_f * d.z, den[qt]);
@@ -760,7 +832,6 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
             }
           }
         }
-        __syncthreads();  // normaliser reads of this slab finish before its update
       }
 
       // bf16 mu^T fragment (A operand, rows rho(tau, i)) of slab K-block kbl, token block tb, plane pl
@@ -803,7 +874,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
           }
         }
       }
-      // normaliser update: sDen[rows] += mu^T 1, K-blocks of the slab spread over waves
+      // normaliser update: DenN = Den + mu^T 1 on the slab rows, K-blocks spread over waves
       for (int kbl = w; kbl < C::NRP * C::J; kbl += C::NW) {
 #pragma unroll
         for (int tau = 0; tau < C::TPK; ++tau) {
@@ -825,14 +896,19 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
               const int r = row0 + (BF ? kbl * 32 + 8 * lg + 4 * tau + s : kbl * 16 + 4 * lg + s);
-              sDen[r] += acc[s];
+              DenN[r] = Den[r] + acc[s];
             }
           }
         }
       }
-      __syncthreads();  // slab buffers are rewritten by the next slab
+      // next slab: into the other buffer while this one may still be read,
+      // or (single buffer) after every wave is done with this one
+      if constexpr (sl + 1 < C::NSLAB) {
+        if constexpr (C::NBUF == 1) __syncthreads();
+        gen_slab(std::integral_constant<int, sl + 1>{}, phi_buf((sl + 1) % C::NBUF), mu_buf((sl + 1) % C::NBUF));
+      }
+      __syncthreads();
     });
-
     if constexpr (OUT) {
       // ---- 4. intra-chunk contribution, m = 0 row, reduction, normalise ----
       if (rp == 0) {
@@ -926,6 +1002,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
       }
       __syncthreads();
     }
+    db ^= 1;
   }
 
   if constexpr (!OUT) {
@@ -941,7 +1018,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
       }
     }
     if (grp == 0)
-      for (int r = tid; r < C::WP; r += C::NTHR) wsS[(size_t)C::WP * kDV + r] = sDen[r];
+      for (int r = tid; r < C::WP; r += C::NTHR) wsS[(size_t)C::WP * kDV + r] = sDen[db * C::WP + r];
   }
 }
 

@@ -27,7 +27,9 @@ struct PrefillPlan {
   int span;       // tokens per span (multiple of chunk)
   int nspan;      // spans per head
   int ngroups;    // column groups (workgroups per head-span)
-  size_t ws_floats;  // span-state workspace, floats
+  int nrg;        // row groups (workgroups per head-span and column group)
+  size_t part_floats;  // row-group partial outputs, floats (0 with one row group)
+  size_t ws_floats;    // workspace: span states, then the partial outputs, floats
 };
 
 int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype dt, PrefillPlan* p);

@@ -104,12 +104,13 @@ __device__ inline int abi_row(int r) {
   return 1 + DK + a * DK - a * (a - 1) / 2 + (b - a);
 }
 
-template <typename TIn_, int DK_, int NT_, int NVT_, int NRP_, int MODE_>
+template <typename TIn_, int DK_, int NT_, int NVT_, int NRP_, int NRG_, int MODE_>
 struct Cfg {
   using TIn = TIn_;
   static constexpr bool BF = std::is_same<TIn_, uint16_t>::value;
   static constexpr bool OUT = (MODE_ == MODE_OUTPUT);
   static constexpr int DK = DK_, NT = NT_, NVT = NVT_, NRP = NRP_;
+  static constexpr int NRG = NRG_;  // row groups: workgroups that split the feature rows of one span
   static constexpr int NW = NVT * NRP;
   static constexpr int NTHR = NW * 64;
   static constexpr int W = rows_for(DK, NT);             // feature rows
@@ -121,10 +122,12 @@ struct Cfg {
   static constexpr int MAXKB = (NKB + NRP - 1) / NRP;
   static constexpr int SRMAX = BF ? 256 : 128;
   static constexpr int J = pick_j(MAXKB, SRMAX / (NRP * KB));
-  static constexpr int NSLAB = (MAXKB + J - 1) / J;
+  static constexpr int NSLAB_ALL = (MAXKB + J - 1) / J;  // slabs over all feature rows
+  static constexpr int NSLAB = (NSLAB_ALL + NRG - 1) / NRG;  // slabs per row group
   static constexpr int MKB = NSLAB * J;    // K-blocks per wave (padded)
   static constexpr int SR = NRP * J * KB;  // feature rows per slab
-  static constexpr int WP = NSLAB * SR;    // padded feature rows
+  static constexpr int WP = NSLAB_ALL * SR;  // padded feature rows
+  static constexpr int RWG = NSLAB * SR;     // feature rows of one row group
   static constexpr int TB = kCH / KB;      // token K-blocks per chunk
   static constexpr int GC = 16 * NVT;      // value columns per workgroup
   using Elem = typename std::conditional<BF, uint16_t, float>::type;
@@ -157,7 +160,7 @@ struct Cfg {
   static constexpr int RED_BYTES = OUT ? NW * 4 * 64 * 16 : 0;  // partial num tiles
   static constexpr int lds_for(int nbuf) {
     const int fixed = TABB + al(kCH * XS * ES) * (OUT ? 2 : 1) + al(GC * VS * ES) + (OUT ? al(NPP * PPL * ES) : 0) +
-                      al(2 * WP * 4) + al(kCH * 4);
+                      al(2 * RWG * 4) + al(kCH * 4);
     const int slabs = nbuf * (B_PHI + B_MU);
     return fixed + (slabs > RED_BYTES ? slabs : RED_BYTES);
   }
@@ -168,7 +171,7 @@ struct Cfg {
   static constexpr int O_V = O_Q + (OUT ? al(kCH * XS * ES) : 0);
   static constexpr int O_P = O_V + al(GC * VS * ES);
   static constexpr int O_DEN = O_P + (OUT ? al(NPP * PPL * ES) : 0);
-  static constexpr int O_DENQ = O_DEN + al(2 * WP * 4);
+  static constexpr int O_DENQ = O_DEN + al(2 * RWG * 4);
   static constexpr int O_PHI = O_DENQ + al(kCH * 4);
   static constexpr int O_MU = O_PHI + NBUF * B_PHI;
   static constexpr int O_END = O_MU + NBUF * B_MU;
@@ -212,7 +215,7 @@ __device__ inline float to_f32(uint16_t b) { return bf16_to_f32(b); }
 // row-contiguous tile sPhi[token][row] as one 16-byte store per group; mu rows
 // (key side) go to sMu[row][token] (hi and, in the totals pass, lo planes).
 template <class C>
-__device__ inline void gen_unrolled(int sl, int w, int lane, int nvalid, const typename C::Elem* sQ,
+__device__ __attribute__((always_inline)) inline void gen_unrolled(int sl, int w, int lane, int nvalid, const typename C::Elem* sQ,
                                     const typename C::Elem* sK, typename C::Elem* sPhi, typename C::Elem* sMu) {
   using Elem = typename C::Elem;
   constexpr bool BF = C::BF;
@@ -310,7 +313,7 @@ __device__ inline void gen_unrolled(int sl, int w, int lane, int nvalid, const t
 // term is added in fp32; weight 1/2 on b == a) to sPhi[token][row]; mu to the
 // token-major sMu[token][row], hi and (totals pass) lo planes split exactly.
 template <class C>
-__device__ inline void gen_octets(int sl, int w, int lane, int nvalid, const uint32_t* tab, const uint16_t* sQ,
+__device__ __attribute__((always_inline)) inline void gen_octets(int sl, int w, int lane, int nvalid, const uint32_t* tab, const uint16_t* sQ,
                                   const uint16_t* sK, uint16_t* sPhi, uint16_t* sMu) {
   constexpr int NOS = C::SR / 8;
   constexpr int NO = OctTable<C::DK>::NO;
@@ -378,7 +381,7 @@ __device__ inline void gen_octets(int sl, int w, int lane, int nvalid, const uin
 // multiply per side.  phi rows (query side, weight folded in, row 0 left out)
 // go to sPhi[token][row] in 16-byte stores; mu rows to sMu[row][token].
 template <class C>
-__device__ inline void gen_runs(int sl, int w, int lane, int nvalid, const uint32_t* tab,
+__device__ __attribute__((always_inline)) inline void gen_runs(int sl, int w, int lane, int nvalid, const uint32_t* tab,
                                 const typename C::Elem* sQ, const typename C::Elem* sK, typename C::Elem* sPhi,
                                 typename C::Elem* sMu) {
   using Elem = typename C::Elem;
@@ -453,7 +456,7 @@ __device__ inline void gen_runs(int sl, int w, int lane, int nvalid, const uint3
 // sPhi[token][row], mu to sMu[token][row] (hi, and lo in the totals pass),
 // which the update reads back through transposing LDS reads.
 template <class C>
-__device__ inline void gen_groups(int part, int nparts, int lane, int nvalid, const float* xq, const float* xk,
+__device__ __attribute__((always_inline)) inline void gen_groups(int part, int nparts, int lane, int nvalid, const float* xq, const float* xk,
                                   typename C::Elem* sPhi, typename C::Elem* sMu) {
   constexpr int G = 8;
   constexpr int NG = C::WP / G;
@@ -524,7 +527,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
                                                         const typename C::TIn* __restrict__ Kg,
                                                         const typename C::TIn* __restrict__ Vg, int N,
                                                         int span, int nspan, float* __restrict__ ws,
-                                                        float* __restrict__ Og) {
+                                                        float* __restrict__ part, float* __restrict__ Og) {
   using TIn = typename C::TIn;
   using Elem = typename C::Elem;
   constexpr bool BF = C::BF;
@@ -536,7 +539,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
   Elem* sK = reinterpret_cast<Elem*>(lds + C::O_K);
   Elem* sV = reinterpret_cast<Elem*>(lds + C::O_V);
   Elem* sP = reinterpret_cast<Elem*>(lds + C::O_P);
-  float* sDen = reinterpret_cast<float*>(lds + C::O_DEN);  // [2][WP]: state before / after the chunk
+  float* sDen = reinterpret_cast<float*>(lds + C::O_DEN);  // [2][RWG]: state before / after the chunk
   float* sDenQ = reinterpret_cast<float*>(lds + C::O_DENQ);
   auto phi_buf = [&](int b) { return reinterpret_cast<Elem*>(lds + C::O_PHI + b * C::B_PHI); };
   auto mu_buf = [&](int b) { return reinterpret_cast<Elem*>(lds + C::O_MU + b * C::B_MU); };
@@ -550,9 +553,12 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
   const int ct = w % C::NVT;  // value column tile of this wave
   const int rp = w / C::NVT;  // row part of this wave
   const int ngroups = kDV / C::GC;
-  const int grp = blockIdx.x % ngroups;
-  const int s_idx = (blockIdx.x / ngroups) % nspan;
-  const int bh = blockIdx.x / (ngroups * nspan);
+  const int rg = blockIdx.x % C::NRG;                      // row group
+  const int grp = (blockIdx.x / C::NRG) % ngroups;         // column group
+  const int s_idx = (blockIdx.x / (C::NRG * ngroups)) % nspan;
+  const int bh = blockIdx.x / (C::NRG * ngroups * nspan);
+  const int slab0 = rg * C::NSLAB;                         // first slab of the row group
+  const int nsl = min(C::NSLAB, C::NSLAB_ALL - slab0);     // its slabs (>= 1)
   const int gcol0 = grp * C::GC;  // first value column of the group
   const int t_begin = s_idx * span;
   const int t_end = min(N, t_begin + span);
@@ -562,6 +568,12 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
   const TIn* Vh = Vg + (size_t)bh * N * kDV;
   const size_t ws_span = (size_t)C::WP * (kDV + 1);
   float* wsS = ws + ((size_t)bh * nspan + s_idx) * ws_span;
+  // partial outputs of the row groups: numerators [BH][NRG][N][dv], then normalisers [BH][NRG][N]
+  const int nbh = gridDim.x / (C::NRG * ngroups * nspan);
+  float* pnum = part + ((size_t)bh * C::NRG + rg) * N * kDV;
+  float* pden = part + (size_t)nbh * C::NRG * N * kDV + ((size_t)bh * C::NRG + rg) * N;
+  (void)pnum;
+  (void)pden;
 
   // feature-row codes for the table-driven generator; padded rows contribute nothing
   if constexpr (C::OCT) {
@@ -579,16 +591,17 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
 #pragma unroll
     for (int t = 0; t < C::TPK; ++t) st[j][t] = zero4();
 
-  auto kb_of = [&](int j) { return ((j / C::J) * C::NRP + rp) * C::J + (j % C::J); };
+  auto kb_of = [&](int j) { return ((slab0 + j / C::J) * C::NRP + rp) * C::J + (j % C::J); };
   // feature row held by lane (col, g) at register s of tile tau of K-block kb
   auto acc_row = [&](int kb, int tau, int s) {
     return BF ? kb * C::KB + 8 * lg + 4 * tau + s : kb * C::KB + 4 * lg + s;
   };
 
   if constexpr (OUT) {
-    // start from the exclusive prefix of this span
+    // start from the exclusive prefix of this span (the row group's slabs)
 #pragma unroll
     for (int j = 0; j < C::MKB; ++j) {
+      if (j / C::J >= nsl) continue;
       const int kb = kb_of(j);
 #pragma unroll
       for (int t = 0; t < C::TPK; ++t) {
@@ -600,9 +613,10 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
         st[j][t] = v;
       }
     }
-    for (int r = tid; r < C::WP; r += C::NTHR) sDen[r] = wsS[(size_t)C::WP * kDV + r];
+    for (int r = tid; r < C::RWG; r += C::NTHR)
+      sDen[r] = r < nsl * C::SR ? wsS[(size_t)C::WP * kDV + slab0 * C::SR + r] : 0.f;
   } else {
-    for (int r = tid; r < C::WP; r += C::NTHR) sDen[r] = 0.f;
+    for (int r = tid; r < C::RWG; r += C::NTHR) sDen[r] = 0.f;
   }
   __syncthreads();
 
@@ -677,8 +691,8 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
   int db = 0;  // normaliser buffer holding the state before the current chunk
   for (int c0 = t_begin; c0 < t_end; c0 += kCH) {
     const int nvalid = min(kCH, t_end - c0);
-    const float* Den = sDen + db * C::WP;
-    float* DenN = sDen + (db ^ 1) * C::WP;
+    const float* Den = sDen + db * C::RWG;  // rows of the row group
+    float* DenN = sDen + (db ^ 1) * C::RWG;
 
     // ---- 1. stage this chunk, start loading the next ----
     commit();
@@ -691,7 +705,8 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
 #pragma unroll
     for (int q = 0; q < 4; ++q) { num[q] = zero4(); den[q] = zero4(); }
     float m0 = 0.f, den0 = 0.f;
-    if constexpr (OUT) {
+    // the intra-chunk block and the m = 0 row belong to the row group holding row 0
+    if constexpr (OUT) if (rg == 0) {
       constexpr int NKT = BF ? 6 : 10;  // (key block, query tile) pairs on or below the diagonal
       constexpr int NTILE = NKT * C::TPK;
       for (int ti = w; ti < NTILE; ti += C::NW) {
@@ -762,9 +777,9 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
       if constexpr (C::UNR) {
         gen_unrolled<C>(sl, w, lane, nvalid, sQ, sK, sPhi, sMu);
       } else if constexpr (C::OCT) {
-        gen_octets<C>(sl, w, lane, nvalid, sTab, sQ, sK, sPhi, sMu);
+        gen_octets<C>(slab0 + sl, w, lane, nvalid, sTab, sQ, sK, sPhi, sMu);
       } else {
-        gen_runs<C>(sl, w, lane, nvalid, sTab, sQ, sK, sPhi, sMu);
+        gen_runs<C>(slab0 + sl, w, lane, nvalid, sTab, sQ, sK, sPhi, sMu);
       }
     };
     gen_slab(std::integral_constant<int, 0>{}, phi_buf(0), mu_buf(0));
@@ -772,7 +787,8 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
     // slabs unrolled at compile time so that every state register index is static
     static_for<0, C::NSLAB>([&](auto slc) {
       constexpr int sl = decltype(slc)::value;
-      const int row0 = sl * C::SR;
+      if (sl >= nsl) return;  // past the row group's last slab (uniform)
+      const int row0 = sl * C::SR;  // first row of the slab within the row group
       Elem* const sPhi = phi_buf(sl % C::NBUF);
       Elem* const sMu = mu_buf(sl % C::NBUF);
       (void)sPhi;
@@ -904,14 +920,18 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
       // next slab: into the other buffer while this one may still be read,
       // or (single buffer) after every wave is done with this one
       if constexpr (sl + 1 < C::NSLAB) {
-        if constexpr (C::NBUF == 1) __syncthreads();
-        gen_slab(std::integral_constant<int, sl + 1>{}, phi_buf((sl + 1) % C::NBUF), mu_buf((sl + 1) % C::NBUF));
+        if (sl + 1 < nsl) {
+          if constexpr (C::NBUF == 1) __syncthreads();
+          gen_slab(std::integral_constant<int, sl + 1>{}, phi_buf((sl + 1) % C::NBUF), mu_buf((sl + 1) % C::NBUF));
+        }
       }
       __syncthreads();
     });
     if constexpr (OUT) {
       // ---- 4. intra-chunk contribution, m = 0 row, reduction, normalise ----
-      if (rp == 0) {
+      // (with several row groups: partial num / den of this group's rows to
+      // the partial buffers, normalised by combine_kernel)
+      if (rp == 0 && rg == 0) {
 #pragma unroll
         for (int qt = 0; qt < 4; ++qt) {
           constexpr int KBW = BF ? 32 : 16;
@@ -944,7 +964,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
         constexpr int KBW = BF ? 32 : 16;
 #pragma unroll
         for (int kb = 0; kb < kCH / KBW; ++kb) {
-          if (kb * KBW > qt * 16 + 15) continue;
+          if (kb * KBW > qt * 16 + 15 || rg != 0) continue;
           if constexpr (BF) {
             const u32x4 ah = lds_u32x4((const unsigned char*)sP, ((qt * 16 + li) * C::PS + kb * 32 + 8 * lg) * 2);
             const u32x4 al = lds_u32x4((const unsigned char*)sP,
@@ -960,8 +980,14 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
           }
         }
         if (li == 0) {
+          if constexpr (C::NRG == 1) {
 #pragma unroll
-          for (int s = 0; s < 4; ++s) sDenQ[qt * 16 + 4 * lg + s] = 1.0f / (den[qt][s] + den0);
+            for (int s = 0; s < 4; ++s) sDenQ[qt * 16 + 4 * lg + s] = 1.0f / (den[qt][s] + den0);
+          } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              if (qt * 16 + 4 * lg + s < nvalid) pden[c0 + qt * 16 + 4 * lg + s] = den[qt][s] + den0;
+          }
         }
       }
       if constexpr (C::NRP > 1) {
@@ -981,6 +1007,15 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
               num[qt] += *reinterpret_cast<const f32x4*>(sRed + (((w2 * 4 + qt) * 64) + lane) * 4);
           }
         }
+        if constexpr (C::NRG > 1) {
+          // partial numerator of this row group; lane (col, g) holds queries 4g+s of each query tile
+          float* pb = pnum + (size_t)(c0 + 4 * lg) * kDV + gcol0 + ct * 16 + li;
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              if (qt * 16 + 4 * lg + s < nvalid) pb[(qt * 16 + s) * kDV] = num[qt][s];
+        } else {
         // o = num * (1/den); lane (col, g) holds queries 4g+s of each query tile
         float* ob = Og + ((size_t)bh * N + c0 + 4 * lg) * kDV + gcol0 + ct * 16 + li;
         if (nvalid == kCH) {
@@ -999,6 +1034,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
               if (qt * 16 + 4 * lg + s < nvalid) ob[(qt * 16 + s) * kDV] = num[qt][s] * rd[s];
           }
         }
+        }
       }
       __syncthreads();
     }
@@ -1006,9 +1042,10 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
   }
 
   if constexpr (!OUT) {
-    // span total -> workspace
+    // span total of the row group's rows -> workspace
 #pragma unroll
     for (int j = 0; j < C::MKB; ++j) {
+      if (j / C::J >= nsl) continue;
       const int kb = kb_of(j);
 #pragma unroll
       for (int t = 0; t < C::TPK; ++t) {
@@ -1018,7 +1055,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
       }
     }
     if (grp == 0)
-      for (int r = tid; r < C::WP; r += C::NTHR) wsS[(size_t)C::WP * kDV + r] = sDen[db * C::WP + r];
+      for (int r = tid; r < nsl * C::SR; r += C::NTHR) wsS[(size_t)C::WP * kDV + slab0 * C::SR + r] = sDen[db * C::RWG + r];
   }
 }
 
@@ -1560,18 +1597,63 @@ constexpr int pick_nrp(int nkb, int fpk) {
   return 8;
 }
 
+// Row groups for large feature sets: the fewest groups of whole slabs that
+// keep a wave's share of the state at <= 112 accumulator floats per lane,
+// with the slabs spread evenly (every group gets at least one).
+constexpr int pick_nrg(int nkb, int nrp, int kb, bool bf) {
+  const int maxkb = (nkb + nrp - 1) / nrp;
+  const int j = pick_j(maxkb, (bf ? 256 : 128) / (nrp * kb));
+  const int ns = (maxkb + j - 1) / j;
+  const int per = j * (bf ? 2 : 1) * 4;  // accumulator floats per lane per slab
+  int rgs = 112 / per;
+  if (rgs < 1) rgs = 1;
+  if (rgs > ns) rgs = ns;
+  const int nrg = (ns + rgs - 1) / rgs;
+  const int even = (ns + nrg - 1) / nrg;
+  return (ns + even - 1) / even;
+}
+
+// Small feature sets (<= 256 rows): one workgroup holds the whole state of
+// NVT column tiles.  Larger ones: 8 waves over all 64 columns (NVT = 4,
+// NRP = 2) and the rows split over NRG row groups, so every feature row is
+// generated once per chunk; the output pass then writes per-group partial
+// numerators and normalisers that combine_kernel adds and divides.
 template <typename TIn, int DK, int NT>
 struct Shape {
   static constexpr bool BF = std::is_same<TIn, uint16_t>::value;
   static constexpr int W = internal_rows(BF, DK, NT);
   static constexpr int KB = BF ? 32 : 16;
   static constexpr int NKB = (W + KB - 1) / KB;
-  static constexpr int NRP = pick_nrp(NKB, BF ? 8 : 4);
-  static constexpr int NVT = NRP == 1 ? 4 : 8 / NRP;
-  using Tot = Cfg<TIn, DK, NT, NVT, NRP, MODE_TOTALS>;
-  using Out = Cfg<TIn, DK, NT, NVT, NRP, MODE_OUTPUT>;
+  static constexpr bool LARGE = NKB * KB > 256;
+  static constexpr int NRP = LARGE ? 2 : pick_nrp(NKB, BF ? 8 : 4);
+  static constexpr int NVT = LARGE ? 4 : (NRP == 1 ? 4 : 8 / NRP);
+  static constexpr int NRG = LARGE ? pick_nrg(NKB, NRP, KB, BF) : 1;
+  using Tot = Cfg<TIn, DK, NT, NVT, NRP, NRG, MODE_TOTALS>;
+  using Out = Cfg<TIn, DK, NT, NVT, NRP, NRG, MODE_OUTPUT>;
   static_assert(Tot::WP == Out::WP, "modes share the workspace layout");
+  static_assert((NRG - 1) * Out::NSLAB < Out::NSLAB_ALL, "every row group holds a slab");
+  static_assert(NRG == 1 || !Out::UNR, "row groups only with the run or octet generators");
 };
+
+// O = (sum over row groups of the partial numerators) / (sum of the partial
+// normalisers), four columns per thread.
+__global__ void combine_kernel(const float* __restrict__ part, int BH, int N, int nrg, float* __restrict__ O) {
+  const size_t total = (size_t)BH * N * (kDV / 4);
+  const float* pden = part + (size_t)BH * nrg * N * kDV;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+    const size_t c4 = e % (kDV / 4);
+    const size_t t = (e / (kDV / 4)) % N;
+    const size_t bh = e / ((size_t)(kDV / 4) * N);
+    f32x4 acc = zero4();
+    float d = 0.f;
+    for (int r = 0; r < nrg; ++r) {
+      const size_t row = (bh * nrg + r) * N + t;
+      acc += *reinterpret_cast<const f32x4*>(part + row * kDV + 4 * c4);
+      d += pden[row];
+    }
+    *reinterpret_cast<f32x4*>(O + (bh * N + t) * kDV + 4 * c4) = acc * (1.0f / d);
+  }
+}
 
 }  // namespace
 
@@ -1582,7 +1664,7 @@ constexpr bool use_pipe() { return (rows_for(DK, NT) + 31) / 32 * 32 <= 256; }
 int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype dt, PrefillPlan* p) {
   (void)dv;
   if (chunk != kCH) return fail(TT_ERR_UNSUPPORTED, "chunk=%d not compiled (64 only)", chunk);
-  int wp = 0, ngroups = 0, wg_per_cu = 2;
+  int wp = 0, ngroups = 0, nrg = 1, wg_per_cu = 2;
   hipError_t e = with_dkn(dk, n, [&](auto DKc, auto Nc) {
     constexpr int DK = decltype(DKc)::value, NT = decltype(Nc)::value;
     if (dt == TT_BF16) {
@@ -1594,11 +1676,13 @@ int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype
         using S = Shape<uint16_t, DK, NT>;
         wp = S::Out::WP;
         ngroups = kDV / S::Out::GC;
+        nrg = S::NRG;
       }
     } else {
       using S = Shape<float, DK, NT>;
       wp = S::Out::WP;
       ngroups = kDV / S::Out::GC;
+      nrg = S::NRG;
     }
     return hipSuccess;
   });
@@ -1607,7 +1691,7 @@ int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype
   const int nchunk = (N + kCH - 1) / kCH;
   // enough workgroups to fill the 256 CUs once
   const long long slots = 256LL * wg_per_cu;
-  long long want = (slots + BH * ngroups - 1) / (BH * ngroups);
+  long long want = (slots + BH * ngroups * nrg - 1) / (BH * ngroups * nrg);
   if (want < 1) want = 1;
   if (want > nchunk) want = nchunk;
   const int span = (int)(((nchunk + want - 1) / want) * kCH);
@@ -1618,7 +1702,9 @@ int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype
   p->span = span;
   p->nspan = nspan;
   p->ngroups = ngroups;
-  p->ws_floats = (size_t)BH * nspan * (size_t)wp * (kDV + 1);
+  p->nrg = nrg;
+  p->part_floats = nrg > 1 ? (size_t)BH * nrg * (size_t)N * (kDV + 1) : 0;
+  p->ws_floats = (size_t)BH * nspan * (size_t)wp * (kDV + 1) + p->part_floats;
   return TT_OK;
 }
 
@@ -1636,15 +1722,22 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype 
     auto go = [&](auto tag) {
       using TIn = decltype(tag);
       using S = Shape<TIn, DK, NT>;
-      const unsigned nblk = (unsigned)((size_t)BH * p.nspan * p.ngroups);
+      const unsigned nblk = (unsigned)((size_t)BH * p.nspan * p.ngroups * S::NRG);
+      float* part = ws + (size_t)BH * p.nspan * S::Out::WP * (kDV + 1);  // row-group partial outputs
       hipLaunchKernelGGL((sweep_kernel<typename S::Tot>), dim3(nblk), dim3(S::Tot::NTHR), 0, s, (const TIn*)Q,
-                         (const TIn*)K, (const TIn*)V, N, p.span, p.nspan, ws, O);
+                         (const TIn*)K, (const TIn*)V, N, p.span, p.nspan, ws, part, O);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       e = scan((int)S::Out::WP, S::Out::OCT ? DK : 0);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((sweep_kernel<typename S::Out>), dim3(nblk), dim3(S::Out::NTHR), 0, s, (const TIn*)Q,
-                         (const TIn*)K, (const TIn*)V, N, p.span, p.nspan, ws, O);
+                         (const TIn*)K, (const TIn*)V, N, p.span, p.nspan, ws, part, O);
+      e = hipGetLastError();
+      if (e != hipSuccess || S::NRG == 1) return e;
+      const size_t total = (size_t)BH * N * (kDV / 4);
+      unsigned g = (unsigned)((total + 255) / 256);
+      if (g > 16384) g = 16384;
+      hipLaunchKernelGGL(combine_kernel, dim3(g), dim3(256), 0, s, (const float*)part, BH, N, S::NRG, O);
       return hipGetLastError();
     };
     if (dt == TT_BF16) {

@@ -141,7 +141,9 @@ struct Cfg {
   static constexpr int PHS = SR + PADE;    // phi row stride (elements)
   // mu: [row][token] (mu^T, read with plain vector loads), or token-major
   // [token][row] for the octet generator (read with transposing loads)
-  static constexpr int MUS = OCT ? SR + PADE : kCH + PADE;
+  // (token-major stride = 40 mod 128 elements: the fastest measured for the
+  // transposing reads, 336 bytes at 128-row slabs)
+  static constexpr int MUS = OCT ? (SR + 8 + 87) / 128 * 128 + 40 : kCH + PADE;
   static constexpr int VS = kCH + PADE;    // V^T row stride
   static constexpr int PS = kCH + PADE;    // P row stride
   static constexpr int NMU = (BF && !OUT) ? 2 : 1;  // mu planes (hi, lo) in the totals pass
@@ -862,11 +864,17 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
                            (pl * C::MUPL + (kbl * 32 + rho(tau, li)) * C::MUS + tb * 32 + 8 * lg) * 2);
         }
       };
-      // value update: S[kb] += mu^T V
+      // value update S[kb] += mu^T V; the wave whose column tile is kbl % NVT
+      // also takes the normaliser rows DenN = Den + mu^T 1 of the K-block from
+      // the same fragments
 #pragma unroll
       for (int jl = 0; jl < C::J; ++jl) {
         const int j = sl * C::J + jl;
         const int kbl = rp * C::J + jl;
+        const bool den_own = (kbl % C::NVT) == ct;  // wave-uniform
+        f32x4 dacc[C::TPK];
+#pragma unroll
+        for (int t = 0; t < C::TPK; ++t) dacc[t] = zero4();
 #pragma unroll
         for (int tb = 0; tb < C::TB; ++tb) {
           if constexpr (BF) {
@@ -875,9 +883,11 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
             for (int tau = 0; tau < 2; ++tau) {
               const u32x4 ah = mu_frag(0, kbl, tau, tb);
               st[j][tau % C::TPK] = mfma_bf16(ah, b, st[j][tau % C::TPK]);
+              if (den_own) dacc[tau] = mfma_bf16(ah, ones_bf, dacc[tau]);
               if constexpr (!OUT) {
                 const u32x4 al = mu_frag(1, kbl, tau, tb);
                 st[j][tau % C::TPK] = mfma_bf16(al, b, st[j][tau % C::TPK]);
+                if (den_own) dacc[tau] = mfma_bf16(al, ones_bf, dacc[tau]);
               }
             }
           } else {
@@ -887,34 +897,22 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
             st[j][0] = mfma_f32(a.y, b.y, st[j][0]);
             st[j][0] = mfma_f32(a.z, b.z, st[j][0]);
             st[j][0] = mfma_f32(a.w, b.w, st[j][0]);
-          }
-        }
-      }
-      // normaliser update: DenN = Den + mu^T 1 on the slab rows, K-blocks spread over waves
-      for (int kbl = w; kbl < C::NRP * C::J; kbl += C::NW) {
-#pragma unroll
-        for (int tau = 0; tau < C::TPK; ++tau) {
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int tb = 0; tb < C::TB; ++tb) {
-            if constexpr (BF) {
-              acc = mfma_bf16(mu_frag(0, kbl, tau, tb), ones_bf, acc);
-              if constexpr (!OUT) acc = mfma_bf16(mu_frag(1, kbl, tau, tb), ones_bf, acc);
-            } else {
-              const f32x4 a = lds_f32x4((const unsigned char*)sMu, ((kbl * 16 + li) * C::MUS + tb * 16 + 4 * lg) * 4);
-              acc = mfma_f32(a.x, ones_f, acc);
-              acc = mfma_f32(a.y, ones_f, acc);
-              acc = mfma_f32(a.z, ones_f, acc);
-              acc = mfma_f32(a.w, ones_f, acc);
+            if (den_own) {
+              dacc[0] = mfma_f32(a.x, ones_f, dacc[0]);
+              dacc[0] = mfma_f32(a.y, ones_f, dacc[0]);
+              dacc[0] = mfma_f32(a.z, ones_f, dacc[0]);
+              dacc[0] = mfma_f32(a.w, ones_f, dacc[0]);
             }
           }
-          if (li == 0) {
+        }
+        if (den_own && li == 0) {
+#pragma unroll
+          for (int tau = 0; tau < C::TPK; ++tau)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
               const int r = row0 + (BF ? kbl * 32 + 8 * lg + 4 * tau + s : kbl * 16 + 4 * lg + s);
-              DenN[r] = Den[r] + acc[s];
+              DenN[r] = Den[r] + dacc[tau][s];
             }
-          }
         }
       }
       // next slab: into the other buffer while this one may still be read,

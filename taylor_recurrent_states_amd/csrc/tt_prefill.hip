@@ -1354,8 +1354,8 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
     // the second read) of a 32-token block; V columns ct*16 + 4*(li%4); mu
     // columns 8*(li%4) + 4*tau of a K-block (rows rho(tau, i) of the A tile)
     const int trow = 8 * lg + (li >> 2);
-    auto load_v = [&](const unsigned char* V, int tb) {
-      const unsigned char* p = V + ((tb * 32 + trow) * C::VS + ct * 16 + 4 * (li & 3)) * 2;
+    auto load_v = [&](const unsigned char* V, int tb, int col_tile) {
+      const unsigned char* p = V + ((tb * 32 + trow) * C::VS + col_tile * 16 + 4 * (li & 3)) * 2;
       const uint2 a = lds_tr16(p), c = lds_tr16(p + 4 * C::VS * 2);
       return u32x4{a.x, a.y, c.x, c.y};
     };
@@ -1377,8 +1377,10 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
       // V^T fragments of this wave's 16 columns for both 32-token blocks:
       // the A operand of P.V (output pass) and the B operand of the update
       u32x4 bvk[2];
-      bvk[0] = load_v(V, 0);
-      bvk[1] = load_v(V, 1);
+      if constexpr (OUT) {
+        bvk[0] = load_v(V, 0, ct);
+        bvk[1] = load_v(V, 1, ct);
+      }
       // update of K-block j from mu fragments mf[tau][tb][pl]: S += mu^T V, and
       // the normaliser (mu^T 1) of the blocks this wave owns from the same fragments
       auto update_block = [&](int j, const u32x4 (*mf)[2][NPL]) {
@@ -1496,13 +1498,64 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
         for (int q = 0; q < 4; ++q) nprev[q] = num[q];
       }
       if constexpr (!OUT) {
-        // totals pass: update only (hi + lo planes), next K-block's fragments prefetched
-        u32x4 mf[2][2][2][NPL];
-        fetch_mu(0, mf[0]);
+        // totals pass (hi + lo planes), state split by rows: consumer ct owns
+        // K-blocks 4q + ct for all four column tiles (st[4q + c'], so each mu
+        // fragment is read by one wave only); the last NKB % 4 K-blocks are
+        // split by column tile (st[4*FQ + jr], column tile ct)
+        constexpr int FQ = C::NKB / 4, R = C::NKB % 4;
+        u32x4 bva[4][2];
 #pragma unroll
-        for (int j = 0; j < C::NKB; ++j) {
-          if (j + 1 < C::NKB) fetch_mu(j + 1, mf[(j + 1) & 1]);
-          update_block(j, mf[j & 1]);
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+            bva[c][tb] = load_v(V, tb, c);
+        u32x4 mf[FQ + R][2][2][NPL];
+#pragma unroll
+        for (int q = 0; q < FQ; ++q) fetch_mu(4 * q + ct, mf[q]);
+#pragma unroll
+        for (int jr = 0; jr < R; ++jr) fetch_mu(4 * FQ + jr, mf[FQ + jr]);
+#pragma unroll
+        for (int q = 0; q < FQ; ++q) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+              for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                for (int pl = 0; pl < NPL; ++pl) st[4 * q + c][tau] = mfma_bf16(mf[q][tau][tb][pl], bva[c][tb], st[4 * q + c][tau]);
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+              for (int pl = 0; pl < NPL; ++pl) dstate[q][tau] = mfma_bf16(mf[q][tau][tb][pl], ones_bf, dstate[q][tau]);
+        }
+#pragma unroll
+        for (int jr = 0; jr < R; ++jr) {
+          const int j = 4 * FQ + jr;
+          u32x4 bv0 = bva[0][0], bv1 = bva[0][1];  // this wave's column tile (ct is wave-uniform)
+#pragma unroll
+          for (int c = 1; c < 4; ++c) {
+            bv0 = c == ct ? bva[c][0] : bv0;
+            bv1 = c == ct ? bva[c][1] : bv1;
+          }
+#pragma unroll
+          for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+            for (int pl = 0; pl < NPL; ++pl) {
+              st[j][tau] = mfma_bf16(mf[FQ + jr][tau][0][pl], bv0, st[j][tau]);
+              st[j][tau] = mfma_bf16(mf[FQ + jr][tau][1][pl], bv1, st[j][tau]);
+            }
+          if (j % 4 == ct) {
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+              for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                for (int pl = 0; pl < NPL; ++pl)
+                  dstate[j / 4][tau] = mfma_bf16(mf[FQ + jr][tau][tb][pl], ones_bf, dstate[j / 4][tau]);
+          }
         }
       }
       if constexpr (OUT) publish_den(b ^ 1);
@@ -1521,8 +1574,19 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
         }
       }
     } else {
+      // span total: row-split K-blocks (all column tiles), then the column-split ones
+      constexpr int FQ = C::NKB / 4;
 #pragma unroll
-      for (int j = 0; j < C::NKB; ++j)
+      for (int q = 0; q < FQ; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              wsS[(size_t)((4 * q + ct) * 32 + 8 * lg + 4 * t + s) * kDV + c * 16 + li] = st[4 * q + c][t][s];
+#pragma unroll
+      for (int j = 4 * FQ; j < C::NKB; ++j)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll

@@ -329,25 +329,40 @@ __device__ __attribute__((always_inline)) inline void gen_octets(int sl, int w, 
   };
   for (int oi = w; oi < NOS; oi += C::NW) {
     const int o = sl * NOS + oi;
-    const uint32_t d = o < NO ? tab[o] : 0xFFu;
+    const uint32_t d = __builtin_amdgcn_readfirstlane(o < NO ? tab[o] : 0xFFu);  // wave-uniform: scalar branches
     const int m = d & 0xFF, a = (d >> 8) & 0xFF, b0 = (int)(d >> 16);
     float mu[8], ph[8];
-    if (m == 1 || m == 2) {
-      float kx[8];
-      unpack8(*reinterpret_cast<const u32x4*>(sK + lane * C::XS + b0), kx);
-      const float ka = m == 2 ? bf16_to_f32(sK[lane * C::XS + a]) : 1.f;
+    if (m == 2) {
+      // x_a * x[b0 + u] straight from packed bf16: a bf16 dot product with
+      // one zero term is the exact product (16 significant bits) in fp32
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      auto prod8 = [](uint32_t xa_bits, const u32x4 xb, float* out) {
+        const bf16x2_t lo = __builtin_bit_cast(bf16x2_t, xa_bits);        // {x_a, 0}
+        const bf16x2_t hi = __builtin_bit_cast(bf16x2_t, xa_bits << 16);  // {0, x_a}
 #pragma unroll
-      for (int u = 0; u < 8; ++u) mu[u] = (b0 + u >= a || m == 1) ? ka * kx[u] : 0.f;
-      if constexpr (C::OUT) {
-        float qx[8];
-        unpack8(*reinterpret_cast<const u32x4*>(sQ + lane * C::XS + b0), qx);
-        const float qa = m == 2 ? bf16_to_f32(sQ[lane * C::XS + a]) : 1.f;
+        for (int e = 0; e < 4; ++e) {
+          // the element goes through a scalar first: bit-casting the vector
+          // element expression directly made clang reuse element 0 for all e
+          const uint32_t w = xb[e];
+          const bf16x2_t v = __builtin_bit_cast(bf16x2_t, w);
+          out[2 * e] = __builtin_amdgcn_fdot2_f32_bf16(lo, v, 0.f, false);
+          out[2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(hi, v, 0.f, false);
+        }
+      };
+      prod8((uint32_t)sK[lane * C::XS + a], *reinterpret_cast<const u32x4*>(sK + lane * C::XS + b0), mu);
+      if constexpr (C::OUT)
+        prod8((uint32_t)sQ[lane * C::XS + a], *reinterpret_cast<const u32x4*>(sQ + lane * C::XS + b0), ph);
+      if (b0 <= a) {  // the octet holding the diagonal b == a (wave-uniform): rows b < a are zero,
+                      // and the query weight of (a, a) is 1/2
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const float wgt = (m == 1 || b0 + u > a) ? 1.f : (b0 + u == a ? 0.5f : 0.f);
-          ph[u] = wgt * qa * qx[u];
+          mu[u] = b0 + u >= a ? mu[u] : 0.f;
+          if constexpr (C::OUT) ph[u] = b0 + u > a ? ph[u] : (b0 + u == a ? 0.5f * ph[u] : 0.f);
         }
       }
+    } else if (m == 1) {
+      unpack8(*reinterpret_cast<const u32x4*>(sK + lane * C::XS + b0), mu);
+      if constexpr (C::OUT) unpack8(*reinterpret_cast<const u32x4*>(sQ + lane * C::XS + b0), ph);
     } else {  // order 0 (row 0 only) or past the last octet
 #pragma unroll
       for (int u = 0; u < 8; ++u) { mu[u] = (m == 0 && u == 0) ? kmask : 0.f; ph[u] = 0.f; }

@@ -177,3 +177,19 @@ def test_prefill_rejects_small_workspace():
     with pytest.raises(ops.TTError) as e:
         ops.tt_prefill(to_device(q), to_device(k), to_device(v), 3, workspace=ws)
     assert e.value.code == ops.TT_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("which", ["O"])
+def test_prefill_rejects_misaligned_outputs(which):
+    """O is written with 16-byte stores: a buffer that is not 16-byte aligned
+    is refused before anything is launched."""
+    import torch
+    q, k, v = wl.draw_qkv(7, 1, 2, 100, 16, 64, "bf16")
+    nf = ops.tt_state_floats(16, 64, 3)
+    buf_o = torch.empty(1 * 2 * 100 * 64 + 1, dtype=torch.float32, device="cuda")
+    buf_s = torch.empty(2 * nf + 1, dtype=torch.float32, device="cuda")
+    O = buf_o[1:].view(1, 2, 100, 64) if which == "O" else None
+    S = buf_s[1:] if which == "states" else None
+    with pytest.raises(ops.TTError) as e:
+        ops.tt_prefill(to_device(q), to_device(k), to_device(v), 3, O=O, states=S)
+    assert e.value.code == ops.TT_ERR_INVALID_ARG

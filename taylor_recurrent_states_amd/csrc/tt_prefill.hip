@@ -128,6 +128,12 @@ struct Cfg {
   static constexpr int SR = NRP * J * KB;  // feature rows per slab
   static constexpr int WP = NSLAB_ALL * SR;  // padded feature rows
   static constexpr int RWG = NSLAB * SR;     // feature rows of one row group
+  // Totals pass over large feature sets: there is no readout, so each wave
+  // takes one K-block of a slab for J column tiles (WPK waves per K-block)
+  // instead of J K-blocks for one column tile; mu fragments are then read by
+  // fewer waves.  Same accumulator count per wave.
+  static constexpr bool TR = !OUT && WP > 256 && NVT == 4 && NW % (NRP * J) == 0 && (NW / (NRP * J)) * J == 4;
+  static constexpr int WPK = TR ? NW / (NRP * J) : 1;
   static constexpr int TB = kCH / KB;      // token K-blocks per chunk
   static constexpr int GC = 16 * NVT;      // value columns per workgroup
   using Elem = typename std::conditional<BF, uint16_t, float>::type;
@@ -715,6 +721,16 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
     commit();
     __syncthreads();
     if (c0 + kCH < t_end) issue(c0 + kCH);
+    // totals remap (bf16): V^T fragments of this wave's J column tiles, once per chunk
+    u32x4 vfr[C::TR && BF ? C::J : 1][C::TB];
+    if constexpr (C::TR && BF) {
+#pragma unroll
+      for (int c = 0; c < C::J; ++c)
+#pragma unroll
+        for (int tb = 0; tb < C::TB; ++tb)
+          vfr[c][tb] = lds_u32x4((const unsigned char*)sV,
+                                 ((((w % C::WPK) * C::J + c) * 16 + li) * C::VS + tb * 32 + 8 * lg) * 2);
+    }
 
     // ---- 2. intra-chunk block P = tril(K_n(Q K^T)) (output pass) ----
     f32x4 num[4];
@@ -879,6 +895,61 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
                            (pl * C::MUPL + (kbl * 32 + rho(tau, li)) * C::MUS + tb * 32 + 8 * lg) * 2);
         }
       };
+      if constexpr (C::TR) {
+        // totals remap: K-block kbl of the slab, column tiles ct0 .. ct0+J-1 in st[sl*J + c];
+        // the first of the K-block's WPK waves also takes its normaliser rows
+        const int kbl = w / C::WPK;
+        const int ct0 = (w % C::WPK) * C::J;
+        const bool den_own = (w % C::WPK) == 0;
+        f32x4 dacc[C::TPK];
+#pragma unroll
+        for (int t = 0; t < C::TPK; ++t) dacc[t] = zero4();
+#pragma unroll
+        for (int tb = 0; tb < C::TB; ++tb) {
+          if constexpr (BF) {
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+              const u32x4 ah = mu_frag(0, kbl, tau, tb);
+              const u32x4 al = mu_frag(1, kbl, tau, tb);
+#pragma unroll
+              for (int c = 0; c < C::J; ++c) {
+                st[sl * C::J + c][tau] = mfma_bf16(ah, vfr[c][tb], st[sl * C::J + c][tau]);
+                st[sl * C::J + c][tau] = mfma_bf16(al, vfr[c][tb], st[sl * C::J + c][tau]);
+              }
+              if (den_own) {
+                dacc[tau] = mfma_bf16(ah, ones_bf, dacc[tau]);
+                dacc[tau] = mfma_bf16(al, ones_bf, dacc[tau]);
+              }
+            }
+          } else {
+            const f32x4 a = lds_f32x4((const unsigned char*)sMu, ((kbl * 16 + li) * C::MUS + tb * 16 + 4 * lg) * 4);
+#pragma unroll
+            for (int c = 0; c < C::J; ++c) {
+              const f32x4 b = lds_f32x4((const unsigned char*)sV, (((ct0 + c) * 16 + li) * C::VS + tb * 16 + 4 * lg) * 4);
+              f32x4& s4 = st[sl * C::J + c][0];
+              s4 = mfma_f32(a.x, b.x, s4);
+              s4 = mfma_f32(a.y, b.y, s4);
+              s4 = mfma_f32(a.z, b.z, s4);
+              s4 = mfma_f32(a.w, b.w, s4);
+            }
+            if (den_own) {
+              dacc[0] = mfma_f32(a.x, ones_f, dacc[0]);
+              dacc[0] = mfma_f32(a.y, ones_f, dacc[0]);
+              dacc[0] = mfma_f32(a.z, ones_f, dacc[0]);
+              dacc[0] = mfma_f32(a.w, ones_f, dacc[0]);
+            }
+          }
+        }
+        if (den_own && li == 0) {
+#pragma unroll
+          for (int tau = 0; tau < C::TPK; ++tau)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              const int r = row0 + (BF ? kbl * 32 + 8 * lg + 4 * tau + s : kbl * 16 + 4 * lg + s);
+              DenN[r] = Den[r] + dacc[tau][s];
+            }
+        }
+      } else {
       // value update S[kb] += mu^T V; the wave whose column tile is kbl % NVT
       // also takes the normaliser rows DenN = Den + mu^T 1 of the K-block from
       // the same fragments
@@ -929,6 +1000,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
               DenN[r] = Den[r] + dacc[tau][s];
             }
         }
+      }
       }
       // next slab: into the other buffer while this one may still be read,
       // or (single buffer) after every wave is done with this one
@@ -1059,12 +1131,18 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
 #pragma unroll
     for (int j = 0; j < C::MKB; ++j) {
       if (j / C::J >= nsl) continue;
-      const int kb = kb_of(j);
+      int kb, col;
+      if constexpr (C::TR) {  // (slab j/J, K-block w/WPK, column tile (w%WPK)*J + j%J)
+        kb = (slab0 + j / C::J) * C::NRP * C::J + w / C::WPK;
+        col = ((w % C::WPK) * C::J + j % C::J) * 16 + li;
+      } else {
+        kb = kb_of(j);
+        col = gcol0 + ct * 16 + li;
+      }
 #pragma unroll
       for (int t = 0; t < C::TPK; ++t) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          wsS[(size_t)acc_row(kb, t, s) * kDV + gcol0 + ct * 16 + li] = st[j][t][s];
+        for (int s = 0; s < 4; ++s) wsS[(size_t)acc_row(kb, t, s) * kDV + col] = st[j][t][s];
       }
     }
     if (grp == 0)

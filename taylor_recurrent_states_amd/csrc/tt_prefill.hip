@@ -165,7 +165,7 @@ struct Cfg {
   static constexpr int TABB = UNR ? 0 : al((OCT ? WI / 8 : WP) * 4);  // row codes / octet descriptors
   static constexpr int B_PHI = OUT ? al(kCH * PHS * ES) : 0;
   static constexpr int B_MU = al(NMU * MUPL * ES);
-  static constexpr int RED_BYTES = OUT ? NW * 4 * 64 * 16 : 0;  // partial num tiles
+  static constexpr int RED_BYTES = OUT ? NW * 4 * 64 * 16 * 2 : 0;  // partial num and normaliser tiles
   static constexpr int lds_for(int nbuf) {
     const int fixed = TABB + al(kCH * XS * ES) * (OUT ? 2 : 1) + al(GC * VS * ES) + (OUT ? al(NPP * PPL * ES) : 0) +
                       al(2 * RWG * 4) + al(kCH * 4);
@@ -721,8 +721,14 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
     commit();
     __syncthreads();
     if (c0 + kCH < t_end) issue(c0 + kCH);
-    // totals remap (bf16): V^T fragments of this wave's J column tiles, once per chunk
+    // V^T fragments, once per chunk (bf16): the totals remap's J column tiles, or
+    // this wave's column tile in the output pass
     u32x4 vfr[C::TR && BF ? C::J : 1][C::TB];
+    if constexpr (OUT && BF) {
+#pragma unroll
+      for (int tb = 0; tb < C::TB; ++tb)
+        vfr[0][tb] = lds_u32x4((const unsigned char*)sV, ((ct * 16 + li) * C::VS + tb * 32 + 8 * lg) * 2);
+    }
     if constexpr (C::TR && BF) {
 #pragma unroll
       for (int c = 0; c < C::J; ++c)
@@ -826,7 +832,9 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
       Elem* const sMu = mu_buf(sl % C::NBUF);
       (void)sPhi;
       if constexpr (OUT) {
-        // value readout over this wave's K-blocks of the slab
+        // value readout over this wave's K-blocks of the slab; with the same phi
+        // fragments, the normaliser readout of the query tiles qt == ct (mod NVT)
+        // over these K-blocks (partials over the row parts are added per chunk)
 #pragma unroll
         for (int jl = 0; jl < C::J; ++jl) {
           const int j = sl * C::J + jl;
@@ -837,13 +845,22 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
             b.y = pack_bf16x2(st[j][0].z, st[j][0].w);
             b.z = pack_bf16x2(st[j][C::TPK - 1].x, st[j][C::TPK - 1].y);
             b.w = pack_bf16x2(st[j][C::TPK - 1].z, st[j][C::TPK - 1].w);
+            u32x4 bd = {0u, 0u, 0u, 0u};  // normaliser rows of the K-block in column 0
+            if (li == 0) {
+              const f32x4 d0 = *reinterpret_cast<const f32x4*>(Den + row0 + kbl * 32 + 8 * lg);
+              const f32x4 d1 = *reinterpret_cast<const f32x4*>(Den + row0 + kbl * 32 + 8 * lg + 4);
+              bd = u32x4{pack_bf16x2(d0.x, d0.y), pack_bf16x2(d0.z, d0.w), pack_bf16x2(d1.x, d1.y),
+                         pack_bf16x2(d1.z, d1.w)};
+            }
 #pragma unroll
             for (int qt = 0; qt < 4; ++qt) {
               const u32x4 a = lds_u32x4((const unsigned char*)sPhi,
                                         ((qt * 16 + li) * C::PHS + kbl * 32 + 8 * lg) * 2);
               num[qt] = mfma_bf16(a, b, num[qt]);
+              if (qt % C::NVT == ct) den[qt] = mfma_bf16(a, bd, den[qt]);
             }
           } else {
+            const f32x4 d = *reinterpret_cast<const f32x4*>(Den + row0 + kbl * 16 + 4 * lg);
 #pragma unroll
             for (int qt = 0; qt < 4; ++qt) {
               const f32x4 a = lds_f32x4((const unsigned char*)sPhi,
@@ -852,32 +869,12 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
               num[qt] = mfma_f32(a.y, st[j][0].y, num[qt]);
               num[qt] = mfma_f32(a.z, st[j][0].z, num[qt]);
               num[qt] = mfma_f32(a.w, st[j][0].w, num[qt]);
-            }
-          }
-        }
-        // normaliser readout for the query tiles this wave owns
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
-          if (qt % C::NW != w) continue;
-          for (int kbl = 0; kbl < C::NRP * C::J; ++kbl) {
-            if constexpr (BF) {
-              const float* dr = Den + row0 + kbl * 32 + 8 * lg;
-              u32x4 b = {0u, 0u, 0u, 0u};
-              if (li == 0) {
-                b.x = pack_bf16x2(dr[0], dr[1]); b.y = pack_bf16x2(dr[2], dr[3]);
-                b.z = pack_bf16x2(dr[4], dr[5]); b.w = pack_bf16x2(dr[6], dr[7]);
+              if (qt % C::NVT == ct) {
+                den[qt] = mfma_f32(a.x, ones_f * d.x, den[qt]);
+                den[qt] = mfma_f32(a.y, ones_f * d.y, den[qt]);
+                den[qt] = mfma_f32(a.z, ones_f * d.z, den[qt]);
+                den[qt] = mfma_f32(a.w, ones_f * d.w, den[qt]);
               }
-              const u32x4 a = lds_u32x4((const unsigned char*)sPhi,
-                                        ((qt * 16 + li) * C::PHS + kbl * 32 + 8 * lg) * 2);
-              den[qt] = mfma_bf16(a, b, den[qt]);
-            } else {
-              const f32x4 a = lds_f32x4((const unsigned char*)sPhi,
-                                        ((qt * 16 + li) * C::PHS + kbl * 16 + 4 * lg) * 4);
-              const f32x4 d = *reinterpret_cast<const f32x4*>(Den + row0 + kbl * 16 + 4 * lg);
-              den[qt] = mfma_f32(a.x, ones_f * d.x, den[qt]);
-              den[qt] = mfma_f32(a.y, ones_f * d.y, den[qt]);
-              den[qt] = mfma_f32(a.z, ones_f * d.z, den[qt]);
-              den[qt] = mfma_f32(a.w, ones_f * d.w, den[qt]);
             }
           }
         }
@@ -964,7 +961,9 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
 #pragma unroll
         for (int tb = 0; tb < C::TB; ++tb) {
           if constexpr (BF) {
-            const u32x4 b = lds_u32x4((const unsigned char*)sV, ((ct * 16 + li) * C::VS + tb * 32 + 8 * lg) * 2);
+            u32x4 b;
+            if constexpr (OUT) b = vfr[0][tb];
+            else b = lds_u32x4((const unsigned char*)sV, ((ct * 16 + li) * C::VS + tb * 32 + 8 * lg) * 2);
 #pragma unroll
             for (int tau = 0; tau < 2; ++tau) {
               const u32x4 ah = mu_frag(0, kbl, tau, tb);
@@ -1042,44 +1041,16 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
           num[qt] += f32x4{m0, m0, m0, m0};
         }
       }
-      // intra-chunk normaliser for owned query tiles, then publish den per query
-#pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-        if (qt % C::NW != w) continue;
-        constexpr int KBW = BF ? 32 : 16;
-#pragma unroll
-        for (int kb = 0; kb < kCH / KBW; ++kb) {
-          if (kb * KBW > qt * 16 + 15 || rg != 0) continue;
-          if constexpr (BF) {
-            const u32x4 ah = lds_u32x4((const unsigned char*)sP, ((qt * 16 + li) * C::PS + kb * 32 + 8 * lg) * 2);
-            const u32x4 al = lds_u32x4((const unsigned char*)sP,
-                                       (C::PPL + (qt * 16 + li) * C::PS + kb * 32 + 8 * lg) * 2);
-            den[qt] = mfma_bf16(ah, ones_bf, den[qt]);
-            den[qt] = mfma_bf16(al, ones_bf, den[qt]);
-          } else {
-            const f32x4 a = lds_f32x4((const unsigned char*)sP, ((qt * 16 + li) * C::PS + kb * 16 + 4 * lg) * 4);
-            den[qt] = mfma_f32(a.x, ones_f, den[qt]);
-            den[qt] = mfma_f32(a.y, ones_f, den[qt]);
-            den[qt] = mfma_f32(a.z, ones_f, den[qt]);
-            den[qt] = mfma_f32(a.w, ones_f, den[qt]);
-          }
-        }
-        if (li == 0) {
-          if constexpr (C::NRG == 1) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) sDenQ[qt * 16 + 4 * lg + s] = 1.0f / (den[qt][s] + den0);
-          } else {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-              if (qt * 16 + 4 * lg + s < nvalid) pden[c0 + qt * 16 + 4 * lg + s] = den[qt][s] + den0;
-          }
-        }
-      }
+      // row-part partials (numerators, and the normaliser of the owned query
+      // tiles qt == ct mod NVT) of the waves with rp != 0 go through LDS
+      float* sRedD = sRed + C::NW * 4 * 64 * 4;
       if constexpr (C::NRP > 1) {
         if (rp != 0) {
 #pragma unroll
-          for (int qt = 0; qt < 4; ++qt)
+          for (int qt = 0; qt < 4; ++qt) {
             *reinterpret_cast<f32x4*>(sRed + (((w * 4 + qt) * 64) + lane) * 4) = num[qt];
+            *reinterpret_cast<f32x4*>(sRedD + (((w * 4 + qt) * 64) + lane) * 4) = den[qt];
+          }
         }
       }
       __syncthreads();
@@ -1088,10 +1059,48 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
           for (int r2 = 1; r2 < C::NRP; ++r2) {
             const int w2 = r2 * C::NVT + ct;
 #pragma unroll
-            for (int qt = 0; qt < 4; ++qt)
+            for (int qt = 0; qt < 4; ++qt) {
               num[qt] += *reinterpret_cast<const f32x4*>(sRed + (((w2 * 4 + qt) * 64) + lane) * 4);
+              den[qt] += *reinterpret_cast<const f32x4*>(sRedD + (((w2 * 4 + qt) * 64) + lane) * 4);
+            }
           }
         }
+        // intra-chunk normaliser (row group 0) of the owned query tiles, then publish per query
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+          if (qt % C::NVT != ct) continue;
+          constexpr int KBW = BF ? 32 : 16;
+#pragma unroll
+          for (int kb = 0; kb < kCH / KBW; ++kb) {
+            if (kb * KBW > qt * 16 + 15 || rg != 0) continue;
+            if constexpr (BF) {
+              const u32x4 ah = lds_u32x4((const unsigned char*)sP, ((qt * 16 + li) * C::PS + kb * 32 + 8 * lg) * 2);
+              const u32x4 al = lds_u32x4((const unsigned char*)sP,
+                                         (C::PPL + (qt * 16 + li) * C::PS + kb * 32 + 8 * lg) * 2);
+              den[qt] = mfma_bf16(ah, ones_bf, den[qt]);
+              den[qt] = mfma_bf16(al, ones_bf, den[qt]);
+            } else {
+              const f32x4 a = lds_f32x4((const unsigned char*)sP, ((qt * 16 + li) * C::PS + kb * 16 + 4 * lg) * 4);
+              den[qt] = mfma_f32(a.x, ones_f, den[qt]);
+              den[qt] = mfma_f32(a.y, ones_f, den[qt]);
+              den[qt] = mfma_f32(a.z, ones_f, den[qt]);
+              den[qt] = mfma_f32(a.w, ones_f, den[qt]);
+            }
+          }
+          if (li == 0) {
+            if constexpr (C::NRG == 1) {
+#pragma unroll
+              for (int s = 0; s < 4; ++s) sDenQ[qt * 16 + 4 * lg + s] = 1.0f / (den[qt][s] + den0);
+            } else {
+#pragma unroll
+              for (int s = 0; s < 4; ++s)
+                if (qt * 16 + 4 * lg + s < nvalid) pden[c0 + qt * 16 + 4 * lg + s] = den[qt][s] + den0;
+            }
+          }
+        }
+      }
+      if constexpr (C::NRG == 1) __syncthreads();  // every query's 1/den is published
+      if (rp == 0) {
         if constexpr (C::NRG > 1) {
           // partial numerator of this row group; lane (col, g) holds queries 4g+s of each query tile
           float* pb = pnum + (size_t)(c0 + 4 * lg) * kDV + gcol0 + ct * 16 + li;
@@ -1753,14 +1762,14 @@ constexpr int pick_nrp(int nkb, int fpk) {
 }
 
 // Row groups for large feature sets: the fewest groups of whole slabs that
-// keep a wave's share of the state at <= 112 accumulator floats per lane,
+// keep a wave's share of the state at <= 96 accumulator floats per lane,
 // with the slabs spread evenly (every group gets at least one).
 constexpr int pick_nrg(int nkb, int nrp, int kb, bool bf) {
   const int maxkb = (nkb + nrp - 1) / nrp;
   const int j = pick_j(maxkb, (bf ? 256 : 128) / (nrp * kb));
   const int ns = (maxkb + j - 1) / j;
   const int per = j * (bf ? 2 : 1) * 4;  // accumulator floats per lane per slab
-  int rgs = 112 / per;
+  int rgs = 96 / per;
   if (rgs < 1) rgs = 1;
   if (rgs > ns) rgs = ns;
   const int nrg = (ns + rgs - 1) / rgs;

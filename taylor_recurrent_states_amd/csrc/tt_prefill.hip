@@ -937,14 +937,12 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
             }
           }
         }
-        if (den_own && li == 0) {
+        if (den_own && li == 0) {  // four consecutive normaliser rows per tile: one 16-byte access each way
 #pragma unroll
-          for (int tau = 0; tau < C::TPK; ++tau)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const int r = row0 + (BF ? kbl * 32 + 8 * lg + 4 * tau + s : kbl * 16 + 4 * lg + s);
-              DenN[r] = Den[r] + dacc[tau][s];
-            }
+          for (int tau = 0; tau < C::TPK; ++tau) {
+            const int r = row0 + (BF ? kbl * 32 + 8 * lg + 4 * tau : kbl * 16 + 4 * lg);
+            *reinterpret_cast<f32x4*>(DenN + r) = *reinterpret_cast<const f32x4*>(Den + r) + dacc[tau];
+          }
         }
       } else {
       // value update S[kb] += mu^T V; the wave whose column tile is kbl % NVT
@@ -990,14 +988,12 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
             }
           }
         }
-        if (den_own && li == 0) {
+        if (den_own && li == 0) {  // four consecutive normaliser rows per tile: one 16-byte access each way
 #pragma unroll
-          for (int tau = 0; tau < C::TPK; ++tau)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const int r = row0 + (BF ? kbl * 32 + 8 * lg + 4 * tau + s : kbl * 16 + 4 * lg + s);
-              DenN[r] = Den[r] + dacc[tau][s];
-            }
+          for (int tau = 0; tau < C::TPK; ++tau) {
+            const int r = row0 + (BF ? kbl * 32 + 8 * lg + 4 * tau : kbl * 16 + 4 * lg);
+            *reinterpret_cast<f32x4*>(DenN + r) = *reinterpret_cast<const f32x4*>(Den + r) + dacc[tau];
+          }
         }
       }
       }

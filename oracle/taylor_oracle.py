@@ -53,6 +53,7 @@ __all__ = [
     "multinomial_weights", "feature_map", "taylor_kernel",
     "quadratic_attention", "quadratic_rows", "states_definition",
     "recurrent_attention", "chunked_attention", "decode_step",
+    "prefill_from_states",
     "merge_states", "softmax_attention", "states_to_planes",
     "planes_to_states", "block_row_ranges",
 ]
@@ -313,6 +314,38 @@ def decode_step(q, k, v, S, n: int) -> Tuple[np.ndarray, np.ndarray]:
     num = np.einsum("...t,...tc->...c", phi, S_new[..., :-1])
     den = np.einsum("...t,...t->...", phi, S_new[..., -1])
     return num / den[..., None], S_new
+
+
+def prefill_from_states(Q, K, V, S0, n: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Prefill of new tokens that continues from the states S0 of earlier ones.
+
+    Q, K: [..., N, d]; V: [..., N, e]; S0: [..., W, e+1].  For row i,
+    num_i = phi(q_i).S0[:, :e] + sum_{j<=i} K_n(q_i.k_j) v_j and
+    den_i = phi(q_i).S0[:, e] + sum_{j<=i} K_n(q_i.k_j); o_i = num_i / den_i.
+    The returned states are S0 plus the states of the new tokens.  The earlier
+    tokens enter only through their summed state, which is what lets a
+    prefill resume after decoding or start from another segment's total
+    [ExpAttn abstract: additive states, constant-size recurrent state;
+    HN-thread, reply on the "+1" column for the den part].
+    """
+    Qh, lead = _heads(Q)
+    Kh, _ = _heads(K)
+    Vh, _ = _heads(V)
+    H, N, d = Qh.shape
+    e = Vh.shape[2]
+    W = state_rows(d, n)
+    S0h = np.asarray(S0, dtype=np.float64).reshape(H, W, e + 1)
+    mask = np.tril(np.ones((N, N), dtype=bool))
+    O = np.empty((H, N, e))
+    S_all = np.empty((H, W, e + 1))
+    for h in range(H):
+        phi = feature_map(Qh[h], n, weighted=True)
+        vp = np.concatenate([Vh[h], np.ones((N, 1))], axis=1)
+        P = np.where(mask, taylor_kernel(Qh[h] @ Kh[h].T, n), 0.0)
+        acc = phi @ S0h[h] + P @ vp
+        O[h] = acc[:, :e] / acc[:, e:]
+        S_all[h] = S0h[h] + states_definition(Kh[h], Vh[h], n)
+    return O.reshape(lead + (N, e)), S_all.reshape(lead + (W, e + 1))
 
 
 def merge_states(a, b) -> np.ndarray:

@@ -426,10 +426,47 @@ def pin_quadratic_rows():
     assert rel_err(part, full[rows]) <= 1e-14
 
 
+def pin_prefill_from_states():
+    """Prefill resumed from the states of a prefix equals the quadratic form
+    over the whole sequence on the resumed rows, and its states equal the
+    single-pass states [ExpAttn abstract: additive states].  Checked against
+    exact rational arithmetic (d = 2, 3) and in fp64 at d = 5; zero states
+    reduce it to the plain prefill."""
+    rng = np.random.Generator(np.random.PCG64(12))
+    for d in (2, 3):
+        units = _RATIONAL_UNITS[d]
+        for n in (1, 2, 3, 4):
+            N = 6
+            q = [units[i] for i in rng.integers(0, len(units), N)]
+            k = [units[i] for i in rng.integers(0, len(units), N)]
+            v = [[Fraction(int(a), 4) for a in rng.integers(-8, 9, 2)] for _ in range(N)]
+            exact = _exact_quadratic(q, k, v, n)
+            qf = np.array([[float(a) for a in r] for r in q])
+            kf = np.array([[float(a) for a in r] for r in k])
+            vf = np.array([[float(a) for a in r] for r in v])
+            for p in (1, 3, 5):
+                S0 = orc.states_definition(kf[:p], vf[:p], n)
+                o, _ = orc.prefill_from_states(qf[p:], kf[p:], vf[p:], S0, n)
+                ref = np.array([[float(a) for a in r] for r in exact[p:]])
+                assert np.max(np.abs(o - ref)) <= 4e-15 * max(1.0, np.max(np.abs(ref)))
+    q, k, v = wl.draw_qkv(13, 1, 2, 40, 5, 3, "f32")
+    for n in (1, 2, 3):
+        o_full = orc.quadratic_attention(q.exact, k.exact, v.exact, n)
+        S_full = orc.states_definition(k.exact, v.exact, n)
+        for p in (1, 13, 39):
+            S0 = orc.states_definition(k.exact[:, :, :p], v.exact[:, :, :p], n)
+            o, S = orc.prefill_from_states(q.exact[:, :, p:], k.exact[:, :, p:], v.exact[:, :, p:], S0, n)
+            assert rel_err(o, o_full[:, :, p:]) <= 1e-13
+            assert rel_err(S, S_full) <= 1e-13
+        Z = np.zeros_like(S_full)
+        o0, S0r = orc.prefill_from_states(q.exact, k.exact, v.exact, Z, n)
+        assert rel_err(o0, o_full) <= 1e-13 and rel_err(S0r, S_full) <= 1e-13
+
+
 ALL_PINS = [
     pin_hand_example, pin_page_widths, pin_exact_rational, pin_kron_features,
     pin_unit_identity, pin_recurrent_vs_quadratic, pin_chunk_additivity,
     pin_decode_equals_recurrence, pin_softmax_library, pin_softmax_convergence,
     pin_normalisation_required, pin_svd_rank, pin_special_cases, pin_convex_hull,
-    pin_planes_layout, pin_quadratic_rows,
+    pin_planes_layout, pin_quadratic_rows, pin_prefill_from_states,
 ]

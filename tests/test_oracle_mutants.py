@@ -111,6 +111,23 @@ def _planes_interleaved(S):
     return np.asarray(S).reshape(-1)
 
 
+_orig_prefill_from = orc.prefill_from_states
+
+
+def _prefill_from_den_without_states(Q, K, V, S0, n):
+    # the carried-in states enter the numerator only
+    S0 = np.array(S0, dtype=np.float64)
+    S0[..., -1] = 0.0
+    o, _ = _orig_prefill_from(Q, K, V, S0, n)
+    return o, orc.states_definition(K, V, n) + np.asarray(S0)
+
+
+def _prefill_from_exclusive_states(Q, K, V, S0, n):
+    # returns only the new tokens' states
+    o, S = _orig_prefill_from(Q, K, V, S0, n)
+    return o, S - np.asarray(S0)
+
+
 MUTANTS = {
     "taylor_dropped_term": ("taylor_kernel", _taylor_dropped_term),
     "taylor_wrong_factorial": ("taylor_kernel", _taylor_wrong_factorial),
@@ -125,6 +142,8 @@ MUTANTS = {
     "decode_readout_before_update": ("decode_step", _decode_readout_first),
     "merge_wrong": ("merge_states", _merge_wrong),
     "planes_interleaved": ("states_to_planes", _planes_interleaved),
+    "prefill_from_den_without_states": ("prefill_from_states", _prefill_from_den_without_states),
+    "prefill_from_exclusive_states": ("prefill_from_states", _prefill_from_exclusive_states),
 }
 
 # cheap pins first; each mutant must make at least one of them fail
@@ -132,7 +151,7 @@ _PINS = [pins.pin_hand_example, pins.pin_kron_features, pins.pin_unit_identity,
          pins.pin_special_cases, pins.pin_decode_equals_recurrence,
          pins.pin_planes_layout, pins.pin_exact_rational, pins.pin_chunk_additivity,
          pins.pin_recurrent_vs_quadratic, pins.pin_softmax_library,
-         pins.pin_softmax_convergence]
+         pins.pin_softmax_convergence, pins.pin_prefill_from_states]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

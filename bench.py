@@ -93,8 +93,20 @@ def bench_prefill(args, torch, ops, wl):
     alg_bytes = head_tokens * (2 * w.dk * 2 + w.dv * 2 + w.dv * 4) + w.B * w.H * ops.tt_state_floats(w.dk, w.dv, w.n) * 4
     achieved = alg_bytes / t_step / 1e9
     src = _source_hash("tt_prefill.hip", "tt_device.hpp")
+    # the same workload continued from carried-in states (read once more)
+    S_in = S.clone()
+
+    def step_from():
+        ops.tt_prefill_from(Q, K, V, S_in, w.n, w.chunk, O=O, states=S, workspace=ws)
+
+    step_from()
+    t_from = _time_events(step_from, args.steps, torch) / args.steps
+    from_bytes = alg_bytes + S_in.numel() * 4
     return {
         "value": tokens / t_step, "t_step": t_step, "workload": w, "alg_bytes": alg_bytes,
+        "prefill_from": {"ms_per_call": round(t_from * 1e3, 5), "tokens_per_s": round(tokens / t_from, 1),
+                         "hbm_frac": round(from_bytes / t_from / 1e9 / HBM_PEAK_GBS, 4),
+                         "alg_bytes_per_launch": from_bytes},
         "roofline": {"bound": "hbm", "kernel": "tt_prefill (span totals + span scan + state sweep)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -305,7 +317,7 @@ def main():
     w = wl.WORKLOADS["prefill"]
     if pre is not None:
         out.update({"value": round(pre["value"], 1), "ms_per_step": round(pre["t_step"] * 1e3, 5),
-                    "roofline": pre["roofline"]})
+                    "roofline": pre["roofline"], "prefill_from": pre["prefill_from"]})
     else:
         out.update({"value": None, "ms_per_step": None, "roofline": None})
     out["config"] = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "dk": w.dk, "dv": w.dv, "n": w.n,

@@ -97,6 +97,25 @@ int tt_prefill(const void *Q, const void *K, const void *V, tt_dtype in_dtype,
                float *O, float *states, void *workspace, size_t workspace_bytes,
                void *stream);
 
+/* Prefill that continues from carried-in states: the same computation as
+ * tt_prefill for tokens that follow earlier ones whose summed states are
+ * states_in ("Expanding Attention", abstract: the states are sums over
+ * tokens and add across segments, so earlier tokens enter only through
+ * their state; comment thread item 46888355, reply on the "+1" column):
+ *   o_i = (phi(q_i).S_in[:, :dv] + sum_{j<=i} K_n(q_i.k_j) v_j)
+ *       / (phi(q_i).S_in[:, dv]  + sum_{j<=i} K_n(q_i.k_j))
+ *   states = S_in + the states of the N new tokens.
+ * Arguments as for tt_prefill, plus
+ *   states_in : B*H*W*(dv+1) fp32, plane layout, read-only.  It may be the
+ *               same buffer as `states` (the call then continues in place)
+ *               but must not otherwise overlap `states`, O or the
+ *               workspace (TT_ERR_INVALID_ARG); NULL is TT_ERR_INVALID_ARG.
+ * Uses the same workspace size as tt_prefill. */
+int tt_prefill_from(const void *Q, const void *K, const void *V, tt_dtype in_dtype,
+                    int B, int H, int N, int dk, int dv, int n, int chunk,
+                    const float *states_in, float *O, float *states,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* One generated token per head ("Expanding Attention", abstract: one
  * rank-one update per state per token, independent of context length):
  *   S += mu(k) (x) [v, 1];  o = phi(q).S[:, :dv] / phi(q).S[:, dv]

@@ -53,7 +53,7 @@ __all__ = [
     "multinomial_weights", "feature_map", "taylor_kernel",
     "quadratic_attention", "quadratic_rows", "states_definition",
     "recurrent_attention", "chunked_attention", "decode_step",
-    "prefill_from_states",
+    "prefill_from_states", "prefill_from_rows",
     "merge_states", "softmax_attention", "states_to_planes",
     "planes_to_states", "block_row_ranges",
 ]
@@ -346,6 +346,28 @@ def prefill_from_states(Q, K, V, S0, n: int) -> Tuple[np.ndarray, np.ndarray]:
         O[h] = acc[:, :e] / acc[:, e:]
         S_all[h] = S0h[h] + states_definition(Kh[h], Vh[h], n)
     return O.reshape(lead + (N, e)), S_all.reshape(lead + (W, e + 1))
+
+
+def prefill_from_rows(q_rows, K, V, S0, rows: Sequence[int], n: int) -> np.ndarray:
+    """``prefill_from_states`` evaluated for selected query rows of one head.
+
+    q_rows: [len(rows), d]; K: [N, d]; V: [N, e]; S0: [W, e+1].  Row i reads
+    out the carried-in states and adds the kernel sum over the new keys
+    0 .. i.  Used to check long sequences on sampled outputs.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    S0 = np.asarray(S0, dtype=np.float64)
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    e = V.shape[1]
+    base = feature_map(q_rows, n, weighted=True) @ S0
+    out = np.empty((len(rows), e), dtype=np.float64)
+    for r, i in enumerate(rows):
+        p = taylor_kernel(K[: i + 1] @ q_rows[r], n)
+        num = base[r, :e] + p @ V[: i + 1]
+        den = base[r, e] + p.sum()
+        out[r] = num / den
+    return out
 
 
 def merge_states(a, b) -> np.ndarray:

@@ -50,6 +50,46 @@ static int check_dtype(tt_dtype dt) {
   return TT_OK;
 }
 
+static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// tt_prefill and tt_prefill_from: states_in is null for zero states.
+static int prefill_impl(const void* Q, const void* K, const void* V, tt_dtype in_dtype, int B, int H, int N,
+                        int dk, int dv, int n, int chunk, const float* states_in, float* O, float* states,
+                        void* workspace, size_t workspace_bytes, void* stream, const char* name) {
+  if (!Q || !K || !V || !O || !states) return fail(TT_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (B < 1 || H < 1 || N < 1) return fail(TT_ERR_INVALID_ARG, "B=%d H=%d N=%d must be >= 1", B, H, N);
+  int rc = check_dtype(in_dtype);
+  if (rc) return rc;
+  rc = check_shape(dk, dv, n);
+  if (rc) return rc;
+  if ((long long)B * H > (1LL << 24)) return fail(TT_ERR_UNSUPPORTED, "B*H=%lld too large", (long long)B * H);
+  PrefillPlan p;
+  rc = plan_prefill(B, H, N, dk, dv, n, chunk, in_dtype, &p);
+  if (rc) return rc;
+  const size_t need = p.ws_floats * sizeof(float);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(TT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if ((((uintptr_t)Q) | ((uintptr_t)K) | ((uintptr_t)V) | ((uintptr_t)O) | ((uintptr_t)workspace)) & 15u)
+    return fail(TT_ERR_INVALID_ARG, "Q, K, V, O and workspace must be 16-byte aligned");
+  if (states_in) {
+    const size_t sb = (size_t)B * H * tt_state_floats(dk, dv, n) * sizeof(float);
+    if (states_in != states && overlap(states_in, sb, states, sb))
+      return fail(TT_ERR_INVALID_ARG, "states_in and states overlap without being the same buffer");
+    if (overlap(states_in, sb, O, (size_t)B * H * N * dv * sizeof(float)) ||
+        (workspace && overlap(states_in, sb, workspace, need)))
+      return fail(TT_ERR_INVALID_ARG, "states_in overlaps O or the workspace");
+  }
+  char what[64];
+  snprintf(what, sizeof(what), "%s launch", name);
+  return hip_status(launch_prefill(Q, K, V, in_dtype, B * H, N, dk, n, p, states_in, O, states,
+                                   (float*)workspace, (hipStream_t)stream),
+                    what);
+}
+
 }  // namespace tt
 
 using namespace tt;
@@ -94,25 +134,16 @@ int tt_prefill_workspace_bytes(int B, int H, int N, int dk, int dv, int n, int c
 int tt_prefill(const void* Q, const void* K, const void* V, tt_dtype in_dtype, int B, int H, int N, int dk,
                int dv, int n, int chunk, float* O, float* states, void* workspace, size_t workspace_bytes,
                void* stream) {
-  if (!Q || !K || !V || !O || !states) return fail(TT_ERR_INVALID_ARG, "a tensor pointer is NULL");
-  if (B < 1 || H < 1 || N < 1) return fail(TT_ERR_INVALID_ARG, "B=%d H=%d N=%d must be >= 1", B, H, N);
-  int rc = check_dtype(in_dtype);
-  if (rc) return rc;
-  rc = check_shape(dk, dv, n);
-  if (rc) return rc;
-  if ((long long)B * H > (1LL << 24)) return fail(TT_ERR_UNSUPPORTED, "B*H=%lld too large", (long long)B * H);
-  PrefillPlan p;
-  rc = plan_prefill(B, H, N, dk, dv, n, chunk, in_dtype, &p);
-  if (rc) return rc;
-  const size_t need = p.ws_floats * sizeof(float);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(TT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                workspace ? workspace_bytes : (size_t)0);
-  if ((((uintptr_t)Q) | ((uintptr_t)K) | ((uintptr_t)V) | ((uintptr_t)O) | ((uintptr_t)workspace)) & 15u)
-    return fail(TT_ERR_INVALID_ARG, "Q, K, V, O and workspace must be 16-byte aligned");
-  return hip_status(launch_prefill(Q, K, V, in_dtype, B * H, N, dk, n, p, O, states, (float*)workspace,
-                                   (hipStream_t)stream),
-                    "tt_prefill launch");
+  return prefill_impl(Q, K, V, in_dtype, B, H, N, dk, dv, n, chunk, nullptr, O, states, workspace,
+                      workspace_bytes, stream, "tt_prefill");
+}
+
+int tt_prefill_from(const void* Q, const void* K, const void* V, tt_dtype in_dtype, int B, int H, int N, int dk,
+                    int dv, int n, int chunk, const float* states_in, float* O, float* states, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!states_in) return fail(TT_ERR_INVALID_ARG, "states_in is NULL (use tt_prefill for zero states)");
+  return prefill_impl(Q, K, V, in_dtype, B, H, N, dk, dv, n, chunk, states_in, O, states, workspace,
+                      workspace_bytes, stream, "tt_prefill_from");
 }
 
 int tt_decode_step(const void* q, const void* k, const void* v, tt_dtype in_dtype, int B, int H, int dk, int dv,

@@ -33,7 +33,9 @@ struct PrefillPlan {
 };
 
 int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype dt, PrefillPlan* p);
+// states_in: carried-in states in the plane layout, or null for zero states.
 hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype dt, int BH, int N, int dk,
-                          int n, const PrefillPlan& p, float* O, float* states, float* ws, hipStream_t s);
+                          int n, const PrefillPlan& p, const float* states_in, float* O, float* states,
+                          float* ws, hipStream_t s);
 
 }  // namespace tt

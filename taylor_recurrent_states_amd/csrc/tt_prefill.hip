@@ -1708,16 +1708,26 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
 // Exclusive scan of span totals over spans (in place) and the final states.
 // The workspace rows are internal rows: feature order, or the octet order
 // when octdk is 32 or 64 (mapped back with abi_row; padding rows dropped).
-__global__ void scan_kernel(float* __restrict__ ws, int nspan, int WP, int W, int BH, int octdk,
-                            float* __restrict__ states) {
+// The scan starts from the carried-in states `init` (plane layout; null for
+// zero states).  Each state element is read from `init` and written to
+// `states` by the same thread, so the two may be the same buffer.
+__global__ void scan_kernel(float* ws, int nspan, int WP, int W, int BH, int octdk, const float* init,
+                            float* states) {
   const size_t per = (size_t)WP * (kDV + 1);
   const size_t total = (size_t)BH * per;
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
        e += (size_t)gridDim.x * blockDim.x) {
     const size_t bh = e / per;
     const size_t off = e - bh * per;
+    const bool val = off < (size_t)WP * kDV;
+    const int r = (int)(val ? off / kDV : off - (size_t)WP * kDV);
+    const int ra = octdk == 64 ? abi_row<64>(r) : octdk == 32 ? abi_row<32>(r) : (r < W ? r : -1);
+    // index of this element in the plane layout (padding rows: none)
+    const size_t si = ra < 0 ? 0
+                      : val ? (bh * W + ra) * kDV + (off - (size_t)r * kDV)
+                            : (size_t)BH * W * kDV + bh * W + ra;
     float* p = ws + bh * nspan * per + off;
-    float run = 0.f;
+    float run = (init != nullptr && ra >= 0) ? init[si] : 0.f;
     int s = 0;
     for (; s + 8 <= nspan; s += 8) {  // eight independent loads in flight
       float t[8];
@@ -1734,16 +1744,7 @@ __global__ void scan_kernel(float* __restrict__ ws, int nspan, int WP, int W, in
       p[(size_t)s * per] = run;
       run += t;
     }
-    const bool val = off < (size_t)WP * kDV;
-    const int r = (int)(val ? off / kDV : off - (size_t)WP * kDV);
-    const int ra = octdk == 64 ? abi_row<64>(r) : octdk == 32 ? abi_row<32>(r) : (r < W ? r : -1);
-    if (ra < 0) continue;
-    if (val) {
-      const size_t c = off - (size_t)r * kDV;
-      states[(bh * W + ra) * kDV + c] = run;
-    } else {
-      states[(size_t)BH * W * kDV + bh * W + ra] = run;
-    }
+    if (ra >= 0) states[si] = run;
   }
 }
 
@@ -1869,14 +1870,16 @@ int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype
 }
 
 hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype dt, int BH, int N, int dk, int n,
-                          const PrefillPlan& p, float* O, float* states, float* ws, hipStream_t s) {
+                          const PrefillPlan& p, const float* states_in, float* O, float* states, float* ws,
+                          hipStream_t s) {
   return with_dkn(dk, n, [&](auto DKc, auto Nc) {
     constexpr int DK = decltype(DKc)::value, NT = decltype(Nc)::value;
     auto scan = [&](int WP, int octdk) {
       const size_t total = (size_t)BH * WP * (kDV + 1);
       unsigned g = (unsigned)((total + 255) / 256);
       if (g > 16384) g = 16384;
-      hipLaunchKernelGGL(scan_kernel, dim3(g), dim3(256), 0, s, ws, p.nspan, WP, p.W, BH, octdk, states);
+      hipLaunchKernelGGL(scan_kernel, dim3(g), dim3(256), 0, s, ws, p.nspan, WP, p.W, BH, octdk, states_in,
+                         states);
       return hipGetLastError();
     };
     auto go = [&](auto tag) {

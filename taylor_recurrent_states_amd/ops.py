@@ -5,8 +5,8 @@ kernels of the library.  PyTorch supplies device memory and the stream.
 The calls keep the C names:
 
     tt_state_rows, tt_state_floats, tt_prefill_workspace_bytes,
-    tt_prefill, tt_decode_step, tt_state_merge, tt_feature_map,
-    tt_last_error
+    tt_prefill, tt_prefill_from, tt_decode_step, tt_state_merge,
+    tt_feature_map, tt_last_error
 
 Loading fails loudly (ImportError / OSError) when the library has not been
 built; there is no fallback implementation.
@@ -25,7 +25,7 @@ TT_F32, TT_BF16 = 0, 1
 TT_OK, TT_ERR_INVALID_ARG, TT_ERR_UNSUPPORTED, TT_ERR_WORKSPACE, TT_ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTED = ("tt_state_rows", "tt_state_floats", "tt_prefill_workspace_bytes", "tt_prefill",
-            "tt_decode_step", "tt_state_merge", "tt_feature_map", "tt_last_error")
+            "tt_prefill_from", "tt_decode_step", "tt_state_merge", "tt_feature_map", "tt_last_error")
 
 _lib = None
 
@@ -56,6 +56,9 @@ def lib() -> ctypes.CDLL:
     L.tt_prefill.argtypes = [c_void, c_void, c_void, c_int] + [c_int] * 7 + [c_float_p, c_float_p, c_void,
                                                                               c_size, c_void]
     L.tt_prefill.restype = c_int
+    L.tt_prefill_from.argtypes = [c_void, c_void, c_void, c_int] + [c_int] * 7 + [c_float_p, c_float_p, c_float_p,
+                                                                                   c_void, c_size, c_void]
+    L.tt_prefill_from.restype = c_int
     L.tt_decode_step.argtypes = [c_void, c_void, c_void, c_int] + [c_int] * 5 + [c_float_p, c_float_p, c_void]
     L.tt_decode_step.restype = c_int
     L.tt_state_merge.argtypes = [c_float_p, c_float_p, c_float_p, c_size, c_void]
@@ -127,10 +130,7 @@ def tt_prefill_workspace_bytes(B: int, H: int, N: int, dk: int, dv: int, n: int,
     return int(out.value)
 
 
-def tt_prefill(Q, K, V, n: int, chunk: int = 64, O=None, states=None, workspace=None, stream=None):
-    """Causal prefill of Q, K [B, H, N, dk] and V [B, H, N, dv] (float32 or
-    bfloat16, same dtype).  Returns (O [B, H, N, dv] float32, states flat
-    float32 in the library's plane layout)."""
+def _prefill_args(Q, K, V, n, chunk, O, states, workspace):
     torch = _torch()
     for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
         _dev(t, nm)
@@ -149,9 +149,32 @@ def tt_prefill(Q, K, V, n: int, chunk: int = 64, O=None, states=None, workspace=
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return (B, H, N, dk, dv), O, states, ws_ptr, ws_bytes
+
+
+def tt_prefill(Q, K, V, n: int, chunk: int = 64, O=None, states=None, workspace=None, stream=None):
+    """Causal prefill of Q, K [B, H, N, dk] and V [B, H, N, dv] (float32 or
+    bfloat16, same dtype).  Returns (O [B, H, N, dv] float32, states flat
+    float32 in the library's plane layout)."""
+    (B, H, N, dk, dv), O, states, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace)
     _check(lib().tt_prefill(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk, dv, n, chunk,
                             _dev(O, "O").data_ptr(), _dev(states, "states").data_ptr(), ws_ptr, ws_bytes,
                             _stream(stream)))
+    return O, states
+
+
+def tt_prefill_from(Q, K, V, states_in, n: int, chunk: int = 64, O=None, states=None, workspace=None,
+                    stream=None):
+    """Prefill continuing from carried-in states (flat float32, plane layout).
+    ``states`` may be ``states_in`` itself to continue in place.  Returns
+    (O, states)."""
+    _dev(states_in, "states_in")
+    (B, H, N, dk, dv), O, states, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace)
+    if states_in.dtype != _torch().float32 or states_in.numel() != B * H * tt_state_floats(dk, dv, n):
+        raise ValueError("states_in must hold B*H*W*(dv+1) float32 values")
+    _check(lib().tt_prefill_from(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk, dv, n,
+                                 chunk, states_in.data_ptr(), _dev(O, "O").data_ptr(),
+                                 _dev(states, "states").data_ptr(), ws_ptr, ws_bytes, _stream(stream)))
     return O, states
 
 

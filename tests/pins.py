@@ -461,6 +461,15 @@ def pin_prefill_from_states():
         Z = np.zeros_like(S_full)
         o0, S0r = orc.prefill_from_states(q.exact, k.exact, v.exact, Z, n)
         assert rel_err(o0, o_full) <= 1e-13 and rel_err(S0r, S_full) <= 1e-13
+    # sampled-row form against the quadratic form over the whole sequence
+    q, k, v = wl.draw_qkv(14, 1, 1, 90, 4, 3, "f32")
+    Qx, Kx, Vx = q.exact[0, 0], k.exact[0, 0], v.exact[0, 0]
+    p, n = 30, 3
+    S0 = orc.states_definition(Kx[:p], Vx[:p], n)
+    rows = [0, 1, 7, 31, 59]
+    got = orc.prefill_from_rows(Qx[p:][rows], Kx[p:], Vx[p:], S0, rows, n)
+    ref = orc.quadratic_rows(Qx[[p + r for r in rows]], Kx, Vx, [p + r for r in rows], n)
+    assert rel_err(got, ref) <= 1e-13
 
 
 ALL_PINS = [

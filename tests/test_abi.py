@@ -69,6 +69,20 @@ def test_entry_points_reject_bad_arguments_without_launching():
         assert rc == ops.TT_ERR_WORKSPACE
     rc = L.tt_prefill(fake, fake, fake, 1, 1, 1, 100, 16, 64, 3, 48, fake, fake, fake, 1 << 30, None)
     assert rc == ops.TT_ERR_UNSUPPORTED
+    ws = ctypes.c_void_p(0x100000)
+    rc = L.tt_prefill_from(fake, fake, fake, 1, 1, 1, 100, 16, 64, 3, 64, None, fake, fake, ws, 1 << 30, None)
+    assert rc == ops.TT_ERR_INVALID_ARG and "states_in" in ops.tt_last_error()
+    nbytes = ops.tt_state_floats(16, 64, 3) * 4
+    # states_in overlapping states without being the same buffer
+    s_out, s_in = 0x40000000, 0x40000000 + 64
+    rc = L.tt_prefill_from(fake, fake, fake, 1, 1, 1, 100, 16, 64, 3, 64, ctypes.c_void_p(s_in), fake,
+                           ctypes.c_void_p(s_out), ws, 1 << 30, None)
+    assert rc == ops.TT_ERR_INVALID_ARG and "overlap" in ops.tt_last_error()
+    # states_in overlapping the workspace
+    rc = L.tt_prefill_from(fake, fake, fake, 1, 1, 1, 100, 16, 64, 3, 64, ctypes.c_void_p(0x100000 + 4096), fake,
+                           ctypes.c_void_p(s_out), ws, 1 << 30, None)
+    assert rc == ops.TT_ERR_INVALID_ARG and "overlap" in ops.tt_last_error()
+    assert nbytes > 64
     rc = L.tt_state_merge(None, fake, fake, 4, None)
     assert rc == ops.TT_ERR_INVALID_ARG
     assert L.tt_state_merge(None, None, None, 0, None) == ops.TT_OK

@@ -1378,6 +1378,7 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
   const int ct = pw;
   const u32x4 ones_bf = (li == 0) ? u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}
                                   : u32x4{0u, 0u, 0u, 0u};
+  const u32x4 ones_all = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
   // Producer and consumer waves run separate loops with the same number of
   // workgroup barriers (one per chunk, plus one after the prologue), so their
@@ -1513,13 +1514,13 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
         f32x4 num[4], den = zero4();
 #pragma unroll
         for (int q = 0; q < 4; ++q) num[q] = zero4();
-        // normaliser fragments of every K-block (column 0 of the B tile, lanes li == 0)
+        // normaliser fragments of every K-block: the same normaliser rows in
+        // every column of the B tile, so every column of the product holds
+        // the readout (lanes li == 0 use it)
         u32x4 bdn[C::NKB];
 #pragma unroll
-        for (int j = 0; j < C::NKB; ++j) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(sDenB + b * C::WP + j * 32 + 8 * lg);
-          bdn[j] = li == 0 ? v : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int j = 0; j < C::NKB; ++j)
+          bdn[j] = *reinterpret_cast<const u32x4*>(sDenB + b * C::WP + j * 32 + 8 * lg);
         const float den0 = sDen0[b];
         // m = 0 row (fp32): S[0][col] for this lane's four columns
         f32x4 m0;
@@ -1547,11 +1548,14 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
           bs.w = pack_bf16x2(st[j][1].z, st[j][1].w);
 #pragma unroll
           for (int qt = 0; qt < 4; ++qt) num[qt] = mfma_bf16(bs, af[j % 3][qt], num[qt]);
-          // normaliser readout of this wave's query tile (ct is wave-uniform)
-          u32x4 a_ct = af[j % 3][0];
-#pragma unroll
-          for (int qt = 1; qt < 4; ++qt) a_ct = (qt == ct) ? af[j % 3][qt] : a_ct;
-          den = mfma_bf16(a_ct, bdn[j], den);
+          // normaliser readout of this wave's query tile: ct is wave-uniform,
+          // so this is a scalar branch to one of four MFMAs (no operand select)
+          switch (ct) {
+            case 0: den = mfma_bf16(af[j % 3][0], bdn[j], den); break;
+            case 1: den = mfma_bf16(af[j % 3][1], bdn[j], den); break;
+            case 2: den = mfma_bf16(af[j % 3][2], bdn[j], den); break;
+            default: den = mfma_bf16(af[j % 3][3], bdn[j], den); break;
+          }
           update_block(j, mf[j & 1]);
         }
         // intra-chunk block: O^T += V^T P^T, normaliser P.1 for query tile ct
@@ -1572,8 +1576,8 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
               num[qt] = mfma_bf16(bvk[kb], ph[qt][kb], num[qt]);
               num[qt] = mfma_bf16(bvk[kb], pl[qt][kb], num[qt]);
               if (qt == ct) {
-                den = mfma_bf16(ph[qt][kb], ones_bf, den);
-                den = mfma_bf16(pl[qt][kb], ones_bf, den);
+                den = mfma_bf16(ph[qt][kb], ones_all, den);
+                den = mfma_bf16(pl[qt][kb], ones_all, den);
               }
             }
           }
@@ -1632,12 +1636,7 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
 #pragma unroll
         for (int jr = 0; jr < R; ++jr) {
           const int j = 4 * FQ + jr;
-          u32x4 bv0 = bva[0][0], bv1 = bva[0][1];  // this wave's column tile (ct is wave-uniform)
-#pragma unroll
-          for (int c = 1; c < 4; ++c) {
-            bv0 = c == ct ? bva[c][0] : bv0;
-            bv1 = c == ct ? bva[c][1] : bv1;
-          }
+          const u32x4 bv0 = bva[ct][0], bv1 = bva[ct][1];  // this wave's column tile (ct is wave-uniform)
 #pragma unroll
           for (int tau = 0; tau < 2; ++tau)
 #pragma unroll

@@ -151,6 +151,50 @@ def bench_prefill_other(name, args, torch, ops, wl):
                          "traffic": None}}
 
 
+def bench_orders(args, torch, ops, wl):
+    """The variant axis: time per call of the prefill workload's shape
+    (B=4, H=8, N=8192, dk=16, bf16) for n = 1 .. 5 Taylor terms, and the
+    largest deviation from exact softmax attention of the GPU outputs on a
+    small seeded case (B=1, H=4, N=512).  The softmax reference is torch's
+    causal attention with scale 1 in fp64 on the CPU."""
+    import math
+    import numpy as np
+    w = wl.WORKLOADS["prefill"]
+    dev = torch.device("cuda:0")
+
+    def to_dev(r):
+        return torch.from_numpy(np.ascontiguousarray(r.device).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = wl.draw_qkv(w.seed, w.B, w.H, w.N, w.dk, w.dv, w.dtype)
+    Q, K, V = to_dev(q), to_dev(k), to_dev(v)
+    qs, ks, vs = wl.draw_qkv(4000, 1, 4, 512, w.dk, w.dv, w.dtype)
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a.exact, dtype=np.float64)) for a in (qs, ks, vs))
+    o_soft = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=1.0).numpy()
+    Qs, Ks, Vs = to_dev(qs), to_dev(ks), to_dev(vs)
+    rows = []
+    for n in range(1, 6):
+        O = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.float32, device=dev)
+        S = torch.empty(w.B * w.H * ops.tt_state_floats(w.dk, w.dv, n), dtype=torch.float32, device=dev)
+        ws = torch.empty(ops.tt_prefill_workspace_bytes(w.B, w.H, w.N, w.dk, w.dv, n, w.chunk), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            ops.tt_prefill(Q, K, V, n, w.chunk, O=O, states=S, workspace=ws)
+
+        for _ in range(3):
+            step()
+        steps = max(2, min(args.steps, 20))
+        t = _time_events(step, steps, torch) / steps
+        o_small, _ = ops.tt_prefill(Qs, Ks, Vs, n)
+        err = float(np.max(np.abs(o_small.cpu().numpy().astype(np.float64) - o_soft)))
+        rows.append({"n": n, "state_rows": ops.tt_state_rows(w.dk, n), "ms_per_call": round(t * 1e3, 4),
+                     "tokens_per_s": round(w.B * w.N / t, 1), "max_abs_err_vs_softmax": err,
+                     "taylor_eps": math.e / math.factorial(n)})
+        print(f"# n={n}: {t * 1e6:.1f} us/call, max|o - softmax| = {err:.2e}", file=sys.stderr, flush=True)
+    return {"workload": w.name.replace("n3", "n1..5"), "softmax_check": "B1 H4 N512 dk16 bf16, seed 4000",
+            "orders": rows}
+
+
 def bench_decode(args, torch, ops, wl):
     """States of a 65536-token prefix per (b, h), then 256 single-token steps."""
     w = wl.WORKLOADS["decode"]
@@ -269,6 +313,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline (profiling runs)")
     ap.add_argument("--only", choices=["prefill", "decode", "others"], default=None)
+    ap.add_argument("--orders", action="store_true",
+                    help="print the order sweep (n = 1..5: time per call and error against softmax) instead")
     ap.add_argument("--calibrate", action="store_true",
                     help="run only tt_state_merge over 2 x 256 MiB -> 256 MiB (known HBM bytes), "
                          "to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -284,6 +330,10 @@ def main():
     ops.lib()  # fails loudly if the library is not built
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+
+    if args.orders:
+        print(json.dumps(bench_orders(args, torch, ops, wl)), flush=True)
+        return
 
     if args.calibrate:
         n = 64 * 1024 * 1024

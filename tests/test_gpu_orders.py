@@ -1,0 +1,52 @@
+"""Order sweep on the GPU: the truncated kernel's outputs approach softmax
+attention as the number of Taylor terms n grows ("Expanding Attention",
+abstract: accuracy improves exponentially in the number of terms).
+
+For n = 1 .. 5 (dk = 16) the GPU outputs must (a) match the oracle's own
+n-term truncation to the parity bar and (b) lie within the Taylor-remainder
+bound of the softmax output: with unit q, k and eps = e/n!,
+|o_n - o_softmax| <= eps/(1-eps) * max_{j<=i} |v_j - o_softmax,i| per
+coordinate (plus the parity tolerance), and the error must fall from n = 3
+to n = 5.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.taylor_oracle as orc
+from gpu_util import assert_out, to_device
+from taylor_recurrent_states_amd import ops
+from taylor_recurrent_states_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_order_sweep_approaches_softmax(dtype):
+    import torch
+    B, H, N, dk, dv = 1, 4, 512, 16, 64
+    tol = ("rel", 1e-5) if dtype == "f32" else ("abs", 5e-3)
+    q, k, v = wl.draw_qkv(4000, B, H, N, dk, dv, dtype)
+    o_s = orc.softmax_attention(q.exact, k.exact, v.exact)
+    V = v.exact
+    # per query and coordinate: max_{j<=i} |v_j - o_s,i|
+    spread = np.empty_like(o_s)
+    for i in range(N):
+        spread[:, :, i] = np.max(np.abs(V[:, :, : i + 1] - o_s[:, :, i : i + 1]), axis=2)
+    Qd, Kd, Vd = to_device(q), to_device(k), to_device(v)
+    errs = {}
+    for n in range(1, 6):
+        O, _ = ops.tt_prefill(Qd, Kd, Vd, n)
+        torch.cuda.synchronize()
+        O = O.cpu().numpy().astype(np.float64)
+        ref = orc.quadratic_attention(q.exact, k.exact, v.exact, n)
+        par = assert_out(O, ref, tol, f"n{n}")
+        slack = par if tol[0] == "abs" else par * float(np.max(np.abs(ref)))
+        errs[n] = float(np.max(np.abs(O - o_s)))
+        eps = math.e / math.factorial(n)
+        if eps < 1:
+            assert np.all(np.abs(O - o_s) <= eps / (1 - eps) * spread + slack + 1e-6), f"n{n} outside the remainder bound"
+    with np.printoptions(precision=3):
+        print("\n  max |o_n - o_softmax| on the GPU: " + ", ".join(f"n={n}: {e:.2e}" for n, e in errs.items()))
+    assert errs[4] < errs[3] and errs[5] < errs[4]

@@ -23,7 +23,9 @@ Notation: d = key/query width, e = value width, n = number of Taylor terms
 Readings where the pages leave a step open (each is listed in the design doc):
 
 * no temperature inside the exponential: the kernel is K_n(q.k) on inputs
-  the caller has already L2-normalised;
+  the caller has already L2-normalised; the optional normalised path
+  (``normalized_inputs``) makes the unit rows itself, folds a temperature
+  tau into the queries, and rounds the unit rows back to the input dtype;
 * "n terms" means the orders 0 .. n-1;
 * the state stores *raw* symmetric monomials mu_t(k) = prod_l k_{t_l}; the
   multinomial weight 1/alpha(t)! lives on the query side,
@@ -56,6 +58,7 @@ __all__ = [
     "prefill_from_states", "prefill_from_rows",
     "merge_states", "softmax_attention", "states_to_planes",
     "planes_to_states", "block_row_ranges",
+    "normalize_rows", "round_to_dtype", "normalized_inputs",
 ]
 
 
@@ -391,6 +394,54 @@ def softmax_attention(Q, K, V) -> np.ndarray:
         P = np.exp(X)
         out[h] = (P @ Vh[h]) / P.sum(axis=1, keepdims=True)
     return out.reshape(lead + Vh.shape[1:])
+
+
+# ---------------------------------------------------------------------------
+# Input side: L2 normalisation of q and k, optional temperature  [ExpAttn
+# abstract: normalisation is the prerequisite that keeps q.k inside the
+# series' convergence radius; arXivNews "Engineering Trade-offs and
+# Performance": without it, more terms stop helping]
+# ---------------------------------------------------------------------------
+
+def normalize_rows(X, scale: float = 1.0) -> np.ndarray:
+    """scale * x / ||x||_2 for every row x of X (last axis), in fp64.
+
+    With unit q and k, |q.k| <= 1, the region where the truncated series
+    converges fast [ExpAttn abstract].  A temperature tau is folded into the
+    queries as scale = tau, which turns the kernel into K_n(tau q.k) on the
+    unit vectors.  A zero row has no direction and gives NaN.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return X * (float(scale) / np.sqrt(np.sum(X * X, axis=-1, keepdims=True)))
+
+
+def round_to_dtype(X, dtype: str) -> np.ndarray:
+    """fp64 values rounded to the working dtype and returned as fp64.
+
+    "f32": round to nearest even fp32.  "bf16": to fp32, then to bf16 by
+    round to nearest even (torch's CPU cast).  The normalised inputs are
+    rounded back to the dtype the caller's q and k came in, so a prefill on
+    raw inputs sees the same values as one on inputs normalised beforehand.
+    """
+    import torch
+    x32 = torch.from_numpy(np.ascontiguousarray(X, dtype=np.float64)).to(torch.float32)
+    if dtype == "f32":
+        return x32.to(torch.float64).numpy()
+    if dtype == "bf16":
+        return x32.to(torch.bfloat16).to(torch.float64).numpy()
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def normalized_inputs(Q, K, temperature: float, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
+    """(q_hat, k_hat): q_hat = round(tau q/||q||), k_hat = round(k/||k||).
+
+    The attention of the normalised path is then the definition above on
+    these rows, e.g. quadratic_attention(q_hat, k_hat, V, n), whose kernel is
+    K_n(tau q.k / (||q|| ||k||)) up to the rounding of the unit rows.
+    """
+    return (round_to_dtype(normalize_rows(Q, temperature), dtype),
+            round_to_dtype(normalize_rows(K, 1.0), dtype))
 
 
 # ---------------------------------------------------------------------------

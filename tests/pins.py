@@ -472,10 +472,58 @@ def pin_prefill_from_states():
     assert rel_err(got, ref) <= 1e-13
 
 
+# ---------------------------------------------------------------------------
+# Input side: L2 normalisation and temperature [ExpAttn abstract: unit q and
+# k keep q.k inside the convergence radius; arXivNews "Engineering
+# Trade-offs and Performance"]
+# ---------------------------------------------------------------------------
+
+def pin_normalize_rows():
+    """Hand values, unit norms, invariance to positive scale (exact for
+    powers of two), the NaN of a zero row, and a temperature worked by hand
+    in tests/golden/normalized_d1_temperature.json."""
+    got = orc.normalize_rows(np.array([[3.0, 4.0], [1.0, 2.0]]), 2.0)
+    assert np.allclose(got[0], [1.2, 1.6], rtol=0, atol=1e-15)
+    assert np.allclose(got[1], [2 / math.sqrt(5), 4 / math.sqrt(5)], rtol=0, atol=1e-15)
+    assert np.allclose(orc.normalize_rows([[1.0, 2.0, 2.0]]), [[1 / 3, 2 / 3, 2 / 3]], rtol=0, atol=1e-16)
+    X = np.random.Generator(np.random.PCG64(40)).standard_normal((50, 16)) * 7.0
+    for tau in (1.0, 0.5, 3.0):
+        U = orc.normalize_rows(X, tau)
+        assert np.max(np.abs(np.linalg.norm(U, axis=1) - tau)) <= 1e-14 * tau
+        assert np.array_equal(orc.normalize_rows(X * 8.0, tau), U)
+        assert np.array_equal(orc.normalize_rows(-X, tau), -U)
+        # same direction: x . u = tau |x|
+        assert np.allclose(np.sum(X * U, axis=1), tau * np.linalg.norm(X, axis=1), rtol=1e-14, atol=0)
+    assert np.isnan(orc.normalize_rows([[0.0, 0.0]])).all()
+    g = json.load(open(os.path.join(GOLDEN, "normalized_d1_temperature.json")))
+    tau = float(_frac(g["tau"]))
+    q = np.array([[float(_frac(x))] for x in g["q"]])
+    k = np.array([[float(_frac(x))] for x in g["k"]])
+    v = np.array([[float(_frac(x))] for x in g["v"]])
+    for n_str, o in g["o"].items():
+        qh, kh = orc.normalized_inputs(q, k, tau, "f32")
+        ref = np.array([[float(_frac(x))] for x in o])
+        assert np.allclose(orc.quadratic_attention(qh, kh, v, int(n_str)), ref, rtol=0, atol=1e-15)
+
+
+def pin_round_to_dtype():
+    """bf16 rounding is round-to-nearest-even on the fp32 value: hand ties
+    around 1 (ulp 2^-7), and agreement with an integer-bit implementation
+    of the same rule on random values; f32 rounding is numpy's cast."""
+    ulp = 2.0 ** -7
+    x = np.array([1 + ulp / 2, 1 + 1.5 * ulp, 1 + ulp / 2 + 2.0 ** -20, -(1 + 1.5 * ulp), 3.0])
+    assert np.array_equal(orc.round_to_dtype(x, "bf16"), [1.0, 1 + 2 * ulp, 1 + ulp, -(1 + 2 * ulp), 3.0])
+    r = np.random.Generator(np.random.PCG64(41)).standard_normal(4096) * 3.0
+    bits = wl.f32_to_bf16_bits(r.astype(np.float32))
+    assert np.array_equal(orc.round_to_dtype(r, "bf16"), wl.bf16_bits_to_f32(bits).astype(np.float64))
+    assert np.array_equal(orc.round_to_dtype(r, "f32"), r.astype(np.float32).astype(np.float64))
+
+
 ALL_PINS = [
     pin_hand_example, pin_page_widths, pin_exact_rational, pin_kron_features,
     pin_unit_identity, pin_recurrent_vs_quadratic, pin_chunk_additivity,
     pin_decode_equals_recurrence, pin_softmax_library, pin_softmax_convergence,
     pin_normalisation_required, pin_svd_rank, pin_special_cases, pin_convex_hull,
     pin_planes_layout, pin_quadratic_rows, pin_prefill_from_states,
+    pin_normalize_rows, pin_round_to_dtype,
 ]

@@ -128,6 +128,27 @@ def _prefill_from_exclusive_states(Q, K, V, S0, n):
     return o, S - np.asarray(S0)
 
 
+_orig_normalize = orc.normalize_rows
+_orig_round = orc.round_to_dtype
+
+
+def _normalize_no_sqrt(X, scale=1.0):
+    X = np.asarray(X, dtype=np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return X * (float(scale) / np.sum(X * X, axis=-1, keepdims=True))
+
+
+def _normalize_inverted_temperature(X, scale=1.0):
+    return _orig_normalize(X, 1.0 / float(scale))
+
+
+def _round_truncating(X, dtype):
+    if dtype != "bf16":
+        return _orig_round(X, dtype)
+    u = np.ascontiguousarray(X, dtype=np.float64).astype(np.float32).view(np.uint32) & np.uint32(0xFFFF0000)
+    return u.view(np.float32).astype(np.float64)
+
+
 MUTANTS = {
     "taylor_dropped_term": ("taylor_kernel", _taylor_dropped_term),
     "taylor_wrong_factorial": ("taylor_kernel", _taylor_wrong_factorial),
@@ -144,6 +165,9 @@ MUTANTS = {
     "planes_interleaved": ("states_to_planes", _planes_interleaved),
     "prefill_from_den_without_states": ("prefill_from_states", _prefill_from_den_without_states),
     "prefill_from_exclusive_states": ("prefill_from_states", _prefill_from_exclusive_states),
+    "normalize_no_sqrt": ("normalize_rows", _normalize_no_sqrt),
+    "normalize_inverted_temperature": ("normalize_rows", _normalize_inverted_temperature),
+    "round_bf16_truncating": ("round_to_dtype", _round_truncating),
 }
 
 # cheap pins first; each mutant must make at least one of them fail
@@ -151,7 +175,8 @@ _PINS = [pins.pin_hand_example, pins.pin_kron_features, pins.pin_unit_identity,
          pins.pin_special_cases, pins.pin_decode_equals_recurrence,
          pins.pin_planes_layout, pins.pin_exact_rational, pins.pin_chunk_additivity,
          pins.pin_recurrent_vs_quadratic, pins.pin_softmax_library,
-         pins.pin_softmax_convergence, pins.pin_prefill_from_states]
+         pins.pin_softmax_convergence, pins.pin_prefill_from_states,
+         pins.pin_normalize_rows, pins.pin_round_to_dtype]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

@@ -102,11 +102,39 @@ def bench_prefill(args, torch, ops, wl):
     step_from()
     t_from = _time_events(step_from, args.steps, torch) / args.steps
     from_bytes = alg_bytes + S_in.numel() * 4
+    # the same workload on raw (not normalised) q, k: the library normalises
+    # them (one pass over Q and K into the workspace), then runs the prefill
+    qr, kr, _ = wl.draw_qkv(w.seed, w.B, w.H, w.N, w.dk, w.dv, w.dtype, normalise=False)
+    Qr, Kr = to_dev(qr), to_dev(kr)
+    ws_n = torch.empty(ops.tt_prefill_normed_workspace_bytes(w.B, w.H, w.N, w.dk, w.dv, w.n, w.chunk),
+                       dtype=torch.uint8, device=dev)
+
+    def step_normed():
+        ops.tt_prefill_normed(Qr, Kr, V, w.n, 1.0, chunk=w.chunk, O=O, states=S, workspace=ws_n)
+
+    step_normed()
+    t_normed = _time_events(step_normed, args.steps, torch) / args.steps
+    # the normalisation pass alone: Q and K rows in one launch
+    QK = torch.cat([Qr.reshape(-1, w.dk), Kr.reshape(-1, w.dk)])
+    QKn = torch.empty_like(QK)
+
+    def step_norm():
+        ops.tt_normalize_rows(QK, 1.0, out=QKn)
+
+    step_norm()
+    t_norm = _time_events(step_norm, args.steps, torch) / args.steps
+    norm_bytes = 2 * QK.numel() * QK.element_size()
     return {
         "value": tokens / t_step, "t_step": t_step, "workload": w, "alg_bytes": alg_bytes,
         "prefill_from": {"ms_per_call": round(t_from * 1e3, 5), "tokens_per_s": round(tokens / t_from, 1),
                          "hbm_frac": round(from_bytes / t_from / 1e9 / HBM_PEAK_GBS, 4),
                          "alg_bytes_per_launch": from_bytes},
+        "prefill_normed": {"ms_per_call": round(t_normed * 1e3, 5), "tokens_per_s": round(tokens / t_normed, 1),
+                           "inputs": "raw Gaussian q, k (normalised by the library), temperature 1",
+                           "normalize_pass": {"us_per_launch": round(t_norm * 1e6, 2),
+                                              "alg_bytes_per_launch": norm_bytes,
+                                              "achieved_GBs": round(norm_bytes / t_norm / 1e9, 1),
+                                              "frac": round(norm_bytes / t_norm / 1e9 / HBM_PEAK_GBS, 4)}},
         "roofline": {"bound": "hbm", "kernel": "tt_prefill (span totals + span scan + state sweep)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -255,9 +283,20 @@ def bench_decode(args, torch, ops, wl):
         cold.append(e0.elapsed_time(e1) / 1e3)
     del flush
     t_cold = sorted(cold)[len(cold) // 2]
+    # raw q, k normalised inside the decode kernel (temperature 1)
+    qr = torch.randn((T, w.B, w.H, w.dk), generator=g, device=dev)
+    kr = torch.randn((T, w.B, w.H, w.dk), generator=g, device=dev)
+
+    def run_normed(steps):
+        for t in range(steps):
+            ops.tt_decode_step_normed(qr[t % T], kr[t % T], vs[t % T], states, w.n, 1.0, o=o)
+
+    run_normed(8)
+    t_normed = _time_events(lambda: run_normed(T), 1, torch) / T
     src = _source_hash("tt_decode.hip", "tt_device.hpp")
     return {
         "us_per_step": t_step * 1e6, "us_per_step_mall_cold": t_cold * 1e6, "steps": T,
+        "us_per_step_normed": round(t_normed * 1e6, 3),
         "workload": w.name,
         "roofline": {"bound": "hbm", "kernel": "decode_kernel<16,3,float>", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -367,7 +406,8 @@ def main():
     w = wl.WORKLOADS["prefill"]
     if pre is not None:
         out.update({"value": round(pre["value"], 1), "ms_per_step": round(pre["t_step"] * 1e3, 5),
-                    "roofline": pre["roofline"], "prefill_from": pre["prefill_from"]})
+                    "roofline": pre["roofline"], "prefill_from": pre["prefill_from"],
+                    "prefill_normed": pre["prefill_normed"]})
     else:
         out.update({"value": None, "ms_per_step": None, "roofline": None})
     out["config"] = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "dk": w.dk, "dv": w.dv, "n": w.n,

@@ -36,7 +36,7 @@
  *     describes the problem (thread-local, valid until the next call on the
  *     same thread).
  *   - Inputs are used as given: q and k are NOT re-normalised (unit norm is
- *     the caller's precondition).  NaN/Inf inputs propagate; a zero
+ *     the caller's precondition), except by the *_normed entry points.  NaN/Inf inputs propagate; a zero
  *     normaliser (possible for n = 2, where K_2(-1) = 0) gives IEEE Inf/NaN.
  *   - Outputs must not alias inputs unless stated.
  *   - Supported shapes: dv = 64; (dk, n) with dk in {16, 32, 64} and
@@ -116,6 +116,43 @@ int tt_prefill_from(const void *Q, const void *K, const void *V, tt_dtype in_dty
                     const float *states_in, float *O, float *states,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* L2 normalisation of q and k with an optional temperature, the input-side
+ * prerequisite of the method ("Expanding Attention", abstract: unit q and k
+ * keep q.k inside the series' convergence radius, and without it more terms
+ * stop helping).  Every row x of d values becomes
+ *     r(scale * x / ||x||_2),
+ * computed with IEEE fp32 operations rounded to nearest even in a fixed
+ * order (s = sum of x_i*x_i in index order, no fused multiply-add;
+ * f = scale / sqrt(s); x_i * f), then rounded by r to the input dtype
+ * (bf16: round to nearest even; fp32: as computed).  The result is a fixed
+ * function of the input bits.  A zero row gives NaN.
+ *   x, out : [rows][d] in_dtype, 16-byte aligned; out may be x (in place)
+ *            but must not otherwise overlap it
+ *   d      : 16, 32 or 64 (TT_ERR_UNSUPPORTED otherwise)
+ *   scale  : finite and > 0 (TT_ERR_INVALID_ARG otherwise)
+ * rows == 0 is a no-op.  The *_normed entry points below apply exactly this
+ * function (with scale = temperature for q and 1 for k) inside the library. */
+int tt_normalize_rows(const void *x, tt_dtype in_dtype, size_t rows, int d, float scale, void *out,
+                      void *stream);
+
+/* Bytes of workspace tt_prefill_normed needs: the tt_prefill workspace
+ * (rounded up to 256 bytes) plus room for normalised copies of Q and K. */
+int tt_prefill_normed_workspace_bytes(int B, int H, int N, int dk, int dv, int n, int chunk,
+                                      size_t *bytes);
+
+/* Prefill on raw (not normalised) Q and K: the kernel is
+ *     K_n(temperature * q.k / (||q|| ||k||)),
+ * i.e. tt_prefill (states_in == NULL) or tt_prefill_from (states_in given)
+ * on q_hat = r(temperature * q/||q||), k_hat = r(k/||k||) as produced by
+ * tt_normalize_rows.  The normalised copies live in the workspace, which
+ * must hold tt_prefill_normed_workspace_bytes().  temperature must be
+ * finite and > 0; the other arguments, layouts and errors are those of
+ * tt_prefill_from.  Q and K are read-only. */
+int tt_prefill_normed(const void *Q, const void *K, const void *V, tt_dtype in_dtype,
+                      int B, int H, int N, int dk, int dv, int n, int chunk, float temperature,
+                      const float *states_in, float *O, float *states,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* One generated token per head ("Expanding Attention", abstract: one
  * rank-one update per state per token, independent of context length):
  *   S += mu(k) (x) [v, 1];  o = phi(q).S[:, :dv] / phi(q).S[:, dv]
@@ -126,6 +163,14 @@ int tt_prefill_from(const void *Q, const void *K, const void *V, tt_dtype in_dty
 int tt_decode_step(const void *q, const void *k, const void *v, tt_dtype in_dtype,
                    int B, int H, int dk, int dv, int n,
                    float *states, float *o, void *stream);
+
+/* tt_decode_step on raw q and k: each workgroup normalises its q (scaled
+ * by temperature) and k with the function of tt_normalize_rows before the
+ * update and readout, so a decode continues a tt_prefill_normed exactly.
+ * temperature must be finite and > 0. */
+int tt_decode_step_normed(const void *q, const void *k, const void *v, tt_dtype in_dtype,
+                          int B, int H, int dk, int dv, int n, float temperature,
+                          float *states, float *o, void *stream);
 
 /* dst[i] = a[i] + b[i] for i < nfloats: the states of two disjoint token
  * sets add ("Expanding Attention", abstract: additivity across chunks).

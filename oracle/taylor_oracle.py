@@ -58,7 +58,7 @@ __all__ = [
     "prefill_from_states", "prefill_from_rows",
     "merge_states", "softmax_attention", "states_to_planes",
     "planes_to_states", "block_row_ranges",
-    "normalize_rows", "round_to_dtype", "normalized_inputs",
+    "normalize_rows", "normalize_rows_f32", "round_to_dtype", "normalized_inputs",
 ]
 
 
@@ -416,6 +416,29 @@ def normalize_rows(X, scale: float = 1.0) -> np.ndarray:
         return X * (float(scale) / np.sqrt(np.sum(X * X, axis=-1, keepdims=True)))
 
 
+def normalize_rows_f32(X, scale: float = 1.0) -> np.ndarray:
+    """``normalize_rows`` evaluated in fp32 with a fixed operation order:
+    s = sum of fl(x_i * x_i) added in index order, f = fl(scale / sqrt(s)),
+    y_i = fl(x_i * f), every operation IEEE fp32 round-to-nearest-even.
+
+    The unit rows are rounded to the input dtype afterwards; that rounding is
+    a discrete decision, so it is taken on the same fp32 value the kernels
+    compute, not on the fp64 quotient (an fp64 quotient lands on the other
+    side of a bf16 rounding boundary for about one coordinate in a hundred).
+    Within (d + 3) fp32 ulps of the fp64 ``normalize_rows``.  Rows of X must
+    be fp32 values (the library's inputs are fp32 or bf16).
+    """
+    X32 = np.asarray(X, dtype=np.float64).astype(np.float32)
+    if not np.array_equal(X32.astype(np.float64), np.asarray(X, dtype=np.float64), equal_nan=True):
+        raise ValueError("rows must hold fp32 values")
+    ss = np.zeros(X32.shape[:-1], dtype=np.float32)
+    for i in range(X32.shape[-1]):
+        ss = ss + X32[..., i] * X32[..., i]
+    with np.errstate(invalid="ignore", divide="ignore"):
+        f = np.float32(scale) / np.sqrt(ss)
+        return (X32 * f[..., None]).astype(np.float64)
+
+
 def round_to_dtype(X, dtype: str) -> np.ndarray:
     """fp64 values rounded to the working dtype and returned as fp64.
 
@@ -434,14 +457,15 @@ def round_to_dtype(X, dtype: str) -> np.ndarray:
 
 
 def normalized_inputs(Q, K, temperature: float, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
-    """(q_hat, k_hat): q_hat = round(tau q/||q||), k_hat = round(k/||k||).
+    """(q_hat, k_hat): q_hat = round(tau q/||q||), k_hat = round(k/||k||),
+    with the quotients taken in fp32 (``normalize_rows_f32``).
 
     The attention of the normalised path is then the definition above on
     these rows, e.g. quadratic_attention(q_hat, k_hat, V, n), whose kernel is
     K_n(tau q.k / (||q|| ||k||)) up to the rounding of the unit rows.
     """
-    return (round_to_dtype(normalize_rows(Q, temperature), dtype),
-            round_to_dtype(normalize_rows(K, 1.0), dtype))
+    return (round_to_dtype(normalize_rows_f32(Q, temperature), dtype),
+            round_to_dtype(normalize_rows_f32(K, 1.0), dtype))
 
 
 # ---------------------------------------------------------------------------

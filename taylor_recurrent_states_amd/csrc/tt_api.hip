@@ -55,10 +55,23 @@ static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-// tt_prefill and tt_prefill_from: states_in is null for zero states.
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static bool valid_scale(float s) { return s > 0.0f && s <= 3.4028235e38f; }  // finite and positive
+
+// Bytes of one normalised copy of Q (or K) in the workspace of the normalised
+// prefill; sized for fp32 so that one query serves both dtypes.
+static size_t normed_copy_bytes(int B, int H, int N, int dk) {
+  return align256((size_t)B * H * N * dk * sizeof(float));
+}
+
+// tt_prefill, tt_prefill_from and tt_prefill_normed: states_in is null for
+// zero states; normed: Q and K are first normalised into the workspace tail
+// (Q scaled by qscale) and the prefill reads those copies.
 static int prefill_impl(const void* Q, const void* K, const void* V, tt_dtype in_dtype, int B, int H, int N,
                         int dk, int dv, int n, int chunk, const float* states_in, float* O, float* states,
-                        void* workspace, size_t workspace_bytes, void* stream, const char* name) {
+                        void* workspace, size_t workspace_bytes, bool normed, float qscale, void* stream,
+                        const char* name) {
   if (!Q || !K || !V || !O || !states) return fail(TT_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (B < 1 || H < 1 || N < 1) return fail(TT_ERR_INVALID_ARG, "B=%d H=%d N=%d must be >= 1", B, H, N);
   int rc = check_dtype(in_dtype);
@@ -69,7 +82,11 @@ static int prefill_impl(const void* Q, const void* K, const void* V, tt_dtype in
   PrefillPlan p;
   rc = plan_prefill(B, H, N, dk, dv, n, chunk, in_dtype, &p);
   if (rc) return rc;
-  const size_t need = p.ws_floats * sizeof(float);
+  const size_t base = p.ws_floats * sizeof(float);
+  const size_t copy = normed ? normed_copy_bytes(B, H, N, dk) : 0;
+  const size_t need = normed ? align256(base) + 2 * copy : base;
+  if (normed && !valid_scale(qscale))
+    return fail(TT_ERR_INVALID_ARG, "temperature %g must be finite and positive", (double)qscale);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(TT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -85,8 +102,35 @@ static int prefill_impl(const void* Q, const void* K, const void* V, tt_dtype in
   }
   char what[64];
   snprintf(what, sizeof(what), "%s launch", name);
+  if (normed) {
+    unsigned char* qn = (unsigned char*)workspace + align256(base);
+    unsigned char* kn = qn + copy;
+    const size_t rows = (size_t)B * H * N;
+    hipError_t e = launch_normalize(in_dtype, dk, Q, qn, qscale, rows, K, kn, 1.0f, rows, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, what);
+    Q = qn;
+    K = kn;
+  }
   return hip_status(launch_prefill(Q, K, V, in_dtype, B * H, N, dk, n, p, states_in, O, states,
                                    (float*)workspace, (hipStream_t)stream),
+                    what);
+}
+
+static int decode_impl(const void* q, const void* k, const void* v, tt_dtype in_dtype, int B, int H, int dk,
+                       int dv, int n, float* states, float* o, bool normed, float qscale, void* stream,
+                       const char* name) {
+  if (!q || !k || !v || !states || !o) return fail(TT_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (B < 1 || H < 1) return fail(TT_ERR_INVALID_ARG, "B=%d H=%d must be >= 1", B, H);
+  int rc = check_dtype(in_dtype);
+  if (rc) return rc;
+  rc = check_shape(dk, dv, n);
+  if (rc) return rc;
+  if (normed && !valid_scale(qscale))
+    return fail(TT_ERR_INVALID_ARG, "temperature %g must be finite and positive", (double)qscale);
+  if ((long long)B * H > 0x7fffffffLL) return fail(TT_ERR_UNSUPPORTED, "B*H too large");
+  char what[64];
+  snprintf(what, sizeof(what), "%s launch", name);
+  return hip_status(launch_decode(q, k, v, in_dtype, B * H, dk, n, states, o, normed, qscale, (hipStream_t)stream),
                     what);
 }
 
@@ -135,7 +179,7 @@ int tt_prefill(const void* Q, const void* K, const void* V, tt_dtype in_dtype, i
                int dv, int n, int chunk, float* O, float* states, void* workspace, size_t workspace_bytes,
                void* stream) {
   return prefill_impl(Q, K, V, in_dtype, B, H, N, dk, dv, n, chunk, nullptr, O, states, workspace,
-                      workspace_bytes, stream, "tt_prefill");
+                      workspace_bytes, false, 1.0f, stream, "tt_prefill");
 }
 
 int tt_prefill_from(const void* Q, const void* K, const void* V, tt_dtype in_dtype, int B, int H, int N, int dk,
@@ -143,20 +187,47 @@ int tt_prefill_from(const void* Q, const void* K, const void* V, tt_dtype in_dty
                     size_t workspace_bytes, void* stream) {
   if (!states_in) return fail(TT_ERR_INVALID_ARG, "states_in is NULL (use tt_prefill for zero states)");
   return prefill_impl(Q, K, V, in_dtype, B, H, N, dk, dv, n, chunk, states_in, O, states, workspace,
-                      workspace_bytes, stream, "tt_prefill_from");
+                      workspace_bytes, false, 1.0f, stream, "tt_prefill_from");
+}
+
+int tt_prefill_normed_workspace_bytes(int B, int H, int N, int dk, int dv, int n, int chunk, size_t* bytes) {
+  int rc = tt_prefill_workspace_bytes(B, H, N, dk, dv, n, chunk, bytes);
+  if (rc) return rc;
+  *bytes = align256(*bytes) + 2 * normed_copy_bytes(B, H, N, dk);
+  return ok();
+}
+
+int tt_prefill_normed(const void* Q, const void* K, const void* V, tt_dtype in_dtype, int B, int H, int N, int dk,
+                      int dv, int n, int chunk, float temperature, const float* states_in, float* O,
+                      float* states, void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(Q, K, V, in_dtype, B, H, N, dk, dv, n, chunk, states_in, O, states, workspace,
+                      workspace_bytes, true, temperature, stream, "tt_prefill_normed");
+}
+
+int tt_normalize_rows(const void* x, tt_dtype in_dtype, size_t rows, int d, float scale, void* out, void* stream) {
+  if (rows == 0) return ok();
+  if (!x || !out) return fail(TT_ERR_INVALID_ARG, "a pointer is NULL");
+  int rc = check_dtype(in_dtype);
+  if (rc) return rc;
+  if (d < 1) return fail(TT_ERR_INVALID_ARG, "d=%d must be >= 1", d);
+  if (d != 16 && d != 32 && d != 64) return fail(TT_ERR_UNSUPPORTED, "d=%d not compiled (16, 32 or 64)", d);
+  if (!valid_scale(scale)) return fail(TT_ERR_INVALID_ARG, "scale %g must be finite and positive", (double)scale);
+  if ((((uintptr_t)x) | ((uintptr_t)out)) & 15u) return fail(TT_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
+  const size_t nb = rows * (size_t)d * (in_dtype == TT_F32 ? 4 : 2);
+  if (x != out && overlap(x, nb, out, nb)) return fail(TT_ERR_INVALID_ARG, "x and out overlap without being equal");
+  return hip_status(launch_normalize(in_dtype, d, x, out, scale, rows, nullptr, nullptr, 1.0f, 0, (hipStream_t)stream),
+                    "tt_normalize_rows launch");
 }
 
 int tt_decode_step(const void* q, const void* k, const void* v, tt_dtype in_dtype, int B, int H, int dk, int dv,
                    int n, float* states, float* o, void* stream) {
-  if (!q || !k || !v || !states || !o) return fail(TT_ERR_INVALID_ARG, "a tensor pointer is NULL");
-  if (B < 1 || H < 1) return fail(TT_ERR_INVALID_ARG, "B=%d H=%d must be >= 1", B, H);
-  int rc = check_dtype(in_dtype);
-  if (rc) return rc;
-  rc = check_shape(dk, dv, n);
-  if (rc) return rc;
-  if ((long long)B * H > 0x7fffffffLL) return fail(TT_ERR_UNSUPPORTED, "B*H too large");
-  return hip_status(launch_decode(q, k, v, in_dtype, B * H, dk, n, states, o, (hipStream_t)stream),
-                    "tt_decode_step launch");
+  return decode_impl(q, k, v, in_dtype, B, H, dk, dv, n, states, o, false, 1.0f, stream, "tt_decode_step");
+}
+
+int tt_decode_step_normed(const void* q, const void* k, const void* v, tt_dtype in_dtype, int B, int H, int dk,
+                          int dv, int n, float temperature, float* states, float* o, void* stream) {
+  return decode_impl(q, k, v, in_dtype, B, H, dk, dv, n, states, o, true, temperature, stream,
+                     "tt_decode_step_normed");
 }
 
 int tt_state_merge(float* dst, const float* a, const float* b, size_t nfloats, void* stream) {

@@ -20,13 +20,16 @@ namespace {
 constexpr int kDV = 64;
 constexpr int kDecodeThreads = 256;
 
-template <int DK, int N, typename TIn>
+// NORM: q and k arrive raw; thread 0 (wave 0) turns q into r(qscale q/|q|)
+// and thread 64 (wave 1) k into r(k/|k|) with normalize_row, the same
+// function the prefill's normalisation pass uses.
+template <int DK, int N, typename TIn, bool NORM>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const TIn* __restrict__ q,
                                                                 const TIn* __restrict__ k,
                                                                 const TIn* __restrict__ v,
                                                                 float* __restrict__ num_plane,
                                                                 float* __restrict__ den_plane,
-                                                                float* __restrict__ o) {
+                                                                float* __restrict__ o, float qscale) {
   constexpr int W = rows_for(DK, N);
   __shared__ float s_q[DK], s_k[DK];
   __shared__ float s_mu[W], s_phi[W];
@@ -39,7 +42,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const TIn* __res
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const auto& tab = RowsOf<DK>::get();
 
-  if (tid < DK) {
+  if constexpr (NORM) {
+    if (tid == 0 || tid == 64) {
+      const TIn* src = (tid == 0 ? q : k) + (size_t)bh * DK;
+      float x[DK];
+#pragma unroll
+      for (int i = 0; i < DK; ++i) x[i] = load_f32(src, i);
+      normalize_row<TIn, DK>(x, tid == 0 ? qscale : 1.0f);
+      float* dst = tid == 0 ? s_q : s_k;
+#pragma unroll
+      for (int i = 0; i < DK; ++i) dst[i] = x[i];
+    }
+  } else if (tid < DK) {
     s_q[tid] = load_f32(q, (size_t)bh * DK + tid);
     s_k[tid] = load_f32(k, (size_t)bh * DK + tid);
   }
@@ -114,6 +128,50 @@ __global__ void feature_map_kernel(const TIn* __restrict__ x, size_t rows, int W
   }
 }
 
+// Rows [0, rows0) of x0 -> out0 with scale s0, then rows [0, rows1) of x1 ->
+// out1 with scale s1; one thread per row (16-byte loads and stores; out may
+// be x: a row is read whole before it is written).
+template <int D, typename TIn>
+__global__ void normalize_kernel(const TIn* x0, TIn* out0, float s0, size_t rows0, const TIn* x1, TIn* out1,
+                                 float s1, size_t rows1) {
+  constexpr int EPS = 16 / (int)sizeof(TIn);  // elements per 16-byte segment
+  constexpr int NSEG = D / EPS;
+  for (size_t r = (size_t)blockIdx.x * blockDim.x + threadIdx.x; r < rows0 + rows1;
+       r += (size_t)gridDim.x * blockDim.x) {
+    const bool first = r < rows0;
+    const size_t row = first ? r : r - rows0;
+    const u32x4* src = reinterpret_cast<const u32x4*>((first ? x0 : x1) + row * D);
+    u32x4 seg[NSEG];
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) seg[i] = src[i];
+    float x[D];
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i)
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) {
+        if constexpr (sizeof(TIn) == 2)
+          x[i * EPS + e] = bf16_to_f32((uint16_t)((seg[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
+        else
+          x[i * EPS + e] = __uint_as_float(seg[i][e]);
+      }
+    normalize_row<TIn, D>(x, first ? s0 : s1);
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) {
+      if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          seg[i][e] = (uint32_t)f32_to_bf16(x[i * 8 + 2 * e]) | ((uint32_t)f32_to_bf16(x[i * 8 + 2 * e + 1]) << 16);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) seg[i][e] = __float_as_uint(x[i * 4 + e]);
+      }
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>((first ? out0 : out1) + row * D);
+#pragma unroll
+    for (int i = 0; i < NSEG; ++i) dst[i] = seg[i];
+  }
+}
+
 __global__ void merge_kernel_vec(float4* dst, const float4* a,
                                  const float4* b, size_t n4) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
@@ -140,20 +198,46 @@ unsigned grid_for(size_t work, unsigned block) {
 }  // namespace
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, tt_dtype dt, int BH, int dk, int n,
-                         float* states, float* o, hipStream_t s) {
+                         float* states, float* o, bool normed, float qscale, hipStream_t s) {
   const int W = rows_for(dk, n);
   float* num = states;
   float* den = states + (size_t)BH * W * kDV;
   return with_dkn(dk, n, [&](auto DKc, auto Nc) {
     constexpr int DK = decltype(DKc)::value, N = decltype(Nc)::value;
-    if (dt == TT_F32)
-      hipLaunchKernelGGL((decode_kernel<DK, N, float>), dim3(BH), dim3(kDecodeThreads), 0, s,
-                         (const float*)q, (const float*)k, (const float*)v, num, den, o);
-    else
-      hipLaunchKernelGGL((decode_kernel<DK, N, uint16_t>), dim3(BH), dim3(kDecodeThreads), 0, s,
-                         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, num, den, o);
+    auto go = [&](auto Tc, auto NORMc) {
+      using T = decltype(Tc);
+      hipLaunchKernelGGL((decode_kernel<DK, N, T, decltype(NORMc)::value>), dim3(BH), dim3(kDecodeThreads), 0, s,
+                         (const T*)q, (const T*)k, (const T*)v, num, den, o, qscale);
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    if (dt == TT_F32) {
+      if (normed) go(float{}, yes{}); else go(float{}, no{});
+    } else {
+      if (normed) go(uint16_t{}, yes{}); else go(uint16_t{}, no{});
+    }
     return hipGetLastError();
   });
+}
+
+hipError_t launch_normalize(tt_dtype dt, int d, const void* x0, void* out0, float s0, size_t rows0,
+                            const void* x1, void* out1, float s1, size_t rows1, hipStream_t s) {
+  const unsigned block = 256;
+  const unsigned grid = grid_for(rows0 + rows1, block);
+#define TT_NORM(D, T)                                                                                     \
+  hipLaunchKernelGGL((normalize_kernel<D, T>), dim3(grid), dim3(block), 0, s, (const T*)x0, (T*)out0, s0, \
+                     rows0, (const T*)x1, (T*)out1, s1, rows1)
+  if (dt == TT_F32) {
+    if (d == 16) TT_NORM(16, float);
+    else if (d == 32) TT_NORM(32, float);
+    else TT_NORM(64, float);
+  } else {
+    if (d == 16) TT_NORM(16, uint16_t);
+    else if (d == 32) TT_NORM(32, uint16_t);
+    else TT_NORM(64, uint16_t);
+  }
+#undef TT_NORM
+  return hipGetLastError();
 }
 
 hipError_t launch_feature_map(const void* x, tt_dtype dt, size_t rows, int dk, int n, int weighted,

@@ -141,6 +141,38 @@ __device__ inline void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
 }
 
 // ---------------------------------------------------------------------------
+// L2 normalisation of one q or k row ("Expanding Attention", abstract: unit
+// q and k keep q.k inside the series' convergence radius; a temperature is
+// folded into the queries as `scale`).  x <- r(scale * x / ||x||_2), where r
+// rounds to the input dtype (bf16: nearest even; fp32: identity).  Every
+// operation is one IEEE fp32 operation rounded to nearest even, in a fixed
+// order: squares x_i*x_i added in index order (no fused multiply-add), the
+// square root, scale / root, and x_i * that factor.  The result is a fixed
+// function of the input bits, the same in every kernel, and a host can
+// reproduce it exactly.  A zero row gives NaN.
+// ---------------------------------------------------------------------------
+
+template <typename TIn, int D>
+__device__ inline void normalize_row(float (&x)[D], float scale) {
+#pragma clang fp contract(off)
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    const float sq = x[i] * x[i];
+    ss = ss + sq;
+  }
+  const float f = scale / sqrtf(ss);
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    const float y = x[i] * f;
+    if constexpr (std::is_same<TIn, uint16_t>::value)
+      x[i] = bf16_to_f32(f32_to_bf16(y));
+    else
+      x[i] = y;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // MFMA wrappers (16x16 output tiles).  Lane l = 16*g + i  (i = l%16, g = l/16).
 //   bf16 16x16x32: A lane holds A[i][8g .. 8g+7]; B lane holds B[8g .. 8g+7][i];
 //   f32  16x16x4 : A lane holds A[i][g];          B lane holds B[g][i];

@@ -16,8 +16,13 @@ int fail(int code, const char* fmt, ...);
 hipError_t launch_feature_map(const void* x, tt_dtype dt, size_t rows, int dk, int n, int weighted,
                               float* out, hipStream_t s);
 hipError_t launch_merge(float* dst, const float* a, const float* b, size_t n, hipStream_t s);
+// normed: q and k are normalised in the kernel (q scaled by qscale).
 hipError_t launch_decode(const void* q, const void* k, const void* v, tt_dtype dt, int BH, int dk, int n,
-                         float* states, float* o, hipStream_t s);
+                         float* states, float* o, bool normed, float qscale, hipStream_t s);
+// Row normalisation of two row sets (d in {16, 32, 64}, 16-byte aligned rows):
+// out0 = r(s0 x0 / |x0|) for rows0 rows, then the same for x1 with s1.
+hipError_t launch_normalize(tt_dtype dt, int d, const void* x0, void* out0, float s0, size_t rows0,
+                            const void* x1, void* out1, float s1, size_t rows1, hipStream_t s);
 
 // Prefill plan: how the sequence and the columns are split over workgroups.
 struct PrefillPlan {

@@ -6,7 +6,8 @@ The calls keep the C names:
 
     tt_state_rows, tt_state_floats, tt_prefill_workspace_bytes,
     tt_prefill, tt_prefill_from, tt_decode_step, tt_state_merge,
-    tt_feature_map, tt_last_error
+    tt_feature_map, tt_last_error, tt_normalize_rows,
+    tt_prefill_normed_workspace_bytes, tt_prefill_normed, tt_decode_step_normed
 
 Loading fails loudly (ImportError / OSError) when the library has not been
 built; there is no fallback implementation.
@@ -25,7 +26,9 @@ TT_F32, TT_BF16 = 0, 1
 TT_OK, TT_ERR_INVALID_ARG, TT_ERR_UNSUPPORTED, TT_ERR_WORKSPACE, TT_ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTED = ("tt_state_rows", "tt_state_floats", "tt_prefill_workspace_bytes", "tt_prefill",
-            "tt_prefill_from", "tt_decode_step", "tt_state_merge", "tt_feature_map", "tt_last_error")
+            "tt_prefill_from", "tt_decode_step", "tt_state_merge", "tt_feature_map", "tt_last_error",
+            "tt_normalize_rows", "tt_prefill_normed_workspace_bytes", "tt_prefill_normed",
+            "tt_decode_step_normed")
 
 _lib = None
 
@@ -65,6 +68,17 @@ def lib() -> ctypes.CDLL:
     L.tt_state_merge.restype = c_int
     L.tt_feature_map.argtypes = [c_void, c_int, c_size, c_int, c_int, c_int, c_float_p, c_void]
     L.tt_feature_map.restype = c_int
+    c_flt = ctypes.c_float
+    L.tt_normalize_rows.argtypes = [c_void, c_int, c_size, c_int, c_flt, c_void, c_void]
+    L.tt_normalize_rows.restype = c_int
+    L.tt_prefill_normed_workspace_bytes.argtypes = [c_int] * 7 + [ctypes.POINTER(c_size)]
+    L.tt_prefill_normed_workspace_bytes.restype = c_int
+    L.tt_prefill_normed.argtypes = [c_void, c_void, c_void, c_int] + [c_int] * 7 + [c_flt, c_float_p, c_float_p,
+                                                                                     c_float_p, c_void, c_size, c_void]
+    L.tt_prefill_normed.restype = c_int
+    L.tt_decode_step_normed.argtypes = [c_void, c_void, c_void, c_int] + [c_int] * 5 + [c_flt, c_float_p, c_float_p,
+                                                                                         c_void]
+    L.tt_decode_step_normed.restype = c_int
     L.tt_last_error.argtypes = []
     L.tt_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -130,7 +144,13 @@ def tt_prefill_workspace_bytes(B: int, H: int, N: int, dk: int, dv: int, n: int,
     return int(out.value)
 
 
-def _prefill_args(Q, K, V, n, chunk, O, states, workspace):
+def tt_prefill_normed_workspace_bytes(B: int, H: int, N: int, dk: int, dv: int, n: int, chunk: int = 64) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().tt_prefill_normed_workspace_bytes(B, H, N, dk, dv, n, chunk, ctypes.byref(out)))
+    return int(out.value)
+
+
+def _prefill_args(Q, K, V, n, chunk, O, states, workspace, normed=False):
     torch = _torch()
     for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
         _dev(t, nm)
@@ -144,7 +164,7 @@ def _prefill_args(Q, K, V, n, chunk, O, states, workspace):
         O = torch.empty((B, H, N, dv), dtype=torch.float32, device=Q.device)
     if states is None:
         states = torch.empty(B * H * tt_state_floats(dk, dv, n), dtype=torch.float32, device=Q.device)
-    need = tt_prefill_workspace_bytes(B, H, N, dk, dv, n, chunk)
+    need = (tt_prefill_normed_workspace_bytes if normed else tt_prefill_workspace_bytes)(B, H, N, dk, dv, n, chunk)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -176,6 +196,55 @@ def tt_prefill_from(Q, K, V, states_in, n: int, chunk: int = 64, O=None, states=
                                  chunk, states_in.data_ptr(), _dev(O, "O").data_ptr(),
                                  _dev(states, "states").data_ptr(), ws_ptr, ws_bytes, _stream(stream)))
     return O, states
+
+
+def tt_prefill_normed(Q, K, V, n: int, temperature: float = 1.0, states_in=None, chunk: int = 64, O=None,
+                      states=None, workspace=None, stream=None):
+    """Prefill on raw Q, K: the library normalises them (Q scaled by
+    ``temperature``) and runs the prefill, from ``states_in`` (flat float32,
+    plane layout) or from zero states when it is None.  Returns (O, states)."""
+    (B, H, N, dk, dv), O, states, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace,
+                                                                   normed=True)
+    sin = None
+    if states_in is not None:
+        _dev(states_in, "states_in")
+        if states_in.dtype != _torch().float32 or states_in.numel() != B * H * tt_state_floats(dk, dv, n):
+            raise ValueError("states_in must hold B*H*W*(dv+1) float32 values")
+        sin = states_in.data_ptr()
+    _check(lib().tt_prefill_normed(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk, dv, n,
+                                   chunk, float(temperature), sin, _dev(O, "O").data_ptr(),
+                                   _dev(states, "states").data_ptr(), ws_ptr, ws_bytes, _stream(stream)))
+    return O, states
+
+
+def tt_normalize_rows(x, scale: float = 1.0, out=None, stream=None):
+    """x [rows, d] (float32 or bfloat16) -> r(scale * x / ||x||) in x's dtype."""
+    torch = _torch()
+    _dev(x, "x")
+    rows, d = x.reshape(-1, x.shape[-1]).shape
+    if out is None:
+        out = torch.empty_like(x)
+    if out.dtype != x.dtype or out.shape != x.shape:
+        raise ValueError("out must match x in dtype and shape")
+    _check(lib().tt_normalize_rows(x.data_ptr(), _dtype_code(x), rows, d, float(scale), _dev(out, "out").data_ptr(),
+                                   _stream(stream)))
+    return out
+
+
+def tt_decode_step_normed(q, k, v, states, n: int, temperature: float = 1.0, o=None, stream=None):
+    """tt_decode_step on raw q, k (normalised in the kernel, q scaled by
+    ``temperature``); states updated in place; returns o [B, H, dv]."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (states, "states")):
+        _dev(t, nm)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    _check(lib().tt_decode_step_normed(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, H, dk, dv, n,
+                                       float(temperature), states.data_ptr(), _dev(o, "o").data_ptr(),
+                                       _stream(stream)))
+    return o
 
 
 def tt_decode_step(q, k, v, states, n: int, o=None, stream=None):

@@ -506,6 +506,22 @@ def pin_normalize_rows():
         assert np.allclose(orc.quadratic_attention(qh, kh, v, int(n_str)), ref, rtol=0, atol=1e-15)
 
 
+def pin_normalize_rows_f32():
+    """The fp32 evaluation stays within (d + 3) fp32 ulps of the fp64
+    normalisation (d roundings in the sum, then sqrt, division and product),
+    for row norms over six decades and temperatures around 1."""
+    g = np.random.Generator(np.random.PCG64(42))
+    for d in (1, 2, 16, 64):
+        X = g.standard_normal((400, d)) * 10.0 ** g.uniform(-3, 3, (400, 1))
+        X = X.astype(np.float32).astype(np.float64)
+        for tau in (1.0, 0.7, 1.5):
+            ref = orc.normalize_rows(X, tau)
+            got = orc.normalize_rows_f32(X, tau)
+            bound = (d + 3) * 2.0 ** -24 * tau
+            assert np.max(np.abs(got - ref)) <= bound, (d, tau)
+    assert np.isnan(orc.normalize_rows_f32([[0.0, 0.0]])).all()
+
+
 def pin_round_to_dtype():
     """bf16 rounding is round-to-nearest-even on the fp32 value: hand ties
     around 1 (ulp 2^-7), and agreement with an integer-bit implementation
@@ -525,5 +541,5 @@ ALL_PINS = [
     pin_decode_equals_recurrence, pin_softmax_library, pin_softmax_convergence,
     pin_normalisation_required, pin_svd_rank, pin_special_cases, pin_convex_hull,
     pin_planes_layout, pin_quadratic_rows, pin_prefill_from_states,
-    pin_normalize_rows, pin_round_to_dtype,
+    pin_normalize_rows, pin_normalize_rows_f32, pin_round_to_dtype,
 ]

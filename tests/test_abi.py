@@ -91,6 +91,34 @@ def test_entry_points_reject_bad_arguments_without_launching():
     assert L.tt_feature_map(None, 0, 0, 16, 3, 0, None, None) == ops.TT_OK
 
 
+def test_normalised_entry_points_reject_bad_arguments_without_launching():
+    L = ops.lib()
+    fake = ctypes.c_void_p(0x1000)
+    f = ctypes.c_float
+    assert L.tt_normalize_rows(None, 0, 0, 16, f(1.0), None, None) == ops.TT_OK  # rows == 0: no-op
+    assert L.tt_normalize_rows(None, 0, 4, 16, f(1.0), fake, None) == ops.TT_ERR_INVALID_ARG
+    assert L.tt_normalize_rows(fake, 0, 4, 24, f(1.0), fake, None) == ops.TT_ERR_UNSUPPORTED
+    assert L.tt_normalize_rows(fake, 3, 4, 16, f(1.0), fake, None) == ops.TT_ERR_INVALID_ARG
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert L.tt_normalize_rows(fake, 0, 4, 16, f(bad), fake, None) == ops.TT_ERR_INVALID_ARG
+        assert "scale" in ops.tt_last_error()
+    assert L.tt_normalize_rows(ctypes.c_void_p(0x1004), 0, 4, 16, f(1.0), fake, None) == ops.TT_ERR_INVALID_ARG
+    # out overlapping x without being x
+    assert L.tt_normalize_rows(fake, 0, 4, 16, f(1.0), ctypes.c_void_p(0x1010), None) == ops.TT_ERR_INVALID_ARG
+    ws = ctypes.c_void_p(0x100000)
+    need = ops.tt_prefill_normed_workspace_bytes(1, 1, 100, 16, 64, 3, 64)
+    assert need > ops.tt_prefill_workspace_bytes(1, 1, 100, 16, 64, 3, 64) + 2 * 100 * 16 * 2
+    rc = L.tt_prefill_normed(fake, fake, fake, 1, 1, 1, 100, 16, 64, 3, 64, f(1.0), None, fake, fake, ws, need - 1,
+                             None)
+    assert rc == ops.TT_ERR_WORKSPACE
+    rc = L.tt_prefill_normed(fake, fake, fake, 1, 1, 1, 100, 16, 64, 3, 64, f(0.0), None, fake, fake, ws, need, None)
+    assert rc == ops.TT_ERR_INVALID_ARG and "temperature" in ops.tt_last_error()
+    rc = L.tt_decode_step_normed(fake, fake, fake, 0, 1, 1, 16, 64, 3, f(-2.0), fake, fake, None)
+    assert rc == ops.TT_ERR_INVALID_ARG and "temperature" in ops.tt_last_error()
+    rc = L.tt_decode_step_normed(None, fake, fake, 0, 1, 1, 16, 64, 3, f(1.0), fake, fake, None)
+    assert rc == ops.TT_ERR_INVALID_ARG
+
+
 def test_product_path_has_no_oracle_or_cpu_fallback():
     """The package never imports the oracle and has no host compute path."""
     pkg = os.path.join(ROOT, "taylor_recurrent_states_amd")

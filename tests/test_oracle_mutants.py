@@ -129,6 +129,7 @@ def _prefill_from_exclusive_states(Q, K, V, S0, n):
 
 
 _orig_normalize = orc.normalize_rows
+_orig_normalize32 = orc.normalize_rows_f32
 _orig_round = orc.round_to_dtype
 
 
@@ -140,6 +141,12 @@ def _normalize_no_sqrt(X, scale=1.0):
 
 def _normalize_inverted_temperature(X, scale=1.0):
     return _orig_normalize(X, 1.0 / float(scale))
+
+
+def _normalize32_no_sqrt(X, scale=1.0):
+    X32 = np.asarray(X, dtype=np.float64).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return (X32 * (np.float32(scale) / np.sum(X32 * X32, axis=-1, keepdims=True))).astype(np.float64)
 
 
 def _round_truncating(X, dtype):
@@ -167,6 +174,7 @@ MUTANTS = {
     "prefill_from_exclusive_states": ("prefill_from_states", _prefill_from_exclusive_states),
     "normalize_no_sqrt": ("normalize_rows", _normalize_no_sqrt),
     "normalize_inverted_temperature": ("normalize_rows", _normalize_inverted_temperature),
+    "normalize_f32_no_sqrt": ("normalize_rows_f32", _normalize32_no_sqrt),
     "round_bf16_truncating": ("round_to_dtype", _round_truncating),
 }
 
@@ -176,7 +184,7 @@ _PINS = [pins.pin_hand_example, pins.pin_kron_features, pins.pin_unit_identity,
          pins.pin_planes_layout, pins.pin_exact_rational, pins.pin_chunk_additivity,
          pins.pin_recurrent_vs_quadratic, pins.pin_softmax_library,
          pins.pin_softmax_convergence, pins.pin_prefill_from_states,
-         pins.pin_normalize_rows, pins.pin_round_to_dtype]
+         pins.pin_normalize_rows, pins.pin_normalize_rows_f32, pins.pin_round_to_dtype]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

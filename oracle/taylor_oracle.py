@@ -59,6 +59,7 @@ __all__ = [
     "merge_states", "softmax_attention", "states_to_planes",
     "planes_to_states", "block_row_ranges",
     "normalize_rows", "normalize_rows_f32", "round_to_dtype", "normalized_inputs",
+    "softmax_rows",
 ]
 
 
@@ -466,6 +467,27 @@ def normalized_inputs(Q, K, temperature: float, dtype: str) -> Tuple[np.ndarray,
     """
     return (round_to_dtype(normalize_rows_f32(Q, temperature), dtype),
             round_to_dtype(normalize_rows_f32(K, 1.0), dtype))
+
+
+def softmax_rows(q_rows, K, V, rows: Sequence[int]) -> np.ndarray:
+    """``softmax_attention`` evaluated for selected query rows of one head:
+    row i is the exp-weighted average of v_0 .. v_i with weights
+    exp(q_i.k_j) (no scale), the baseline the truncated kernel is compared
+    against [ExpAttn abstract; arXivNews "Engineering Trade-offs and
+    Performance"].  The largest score is subtracted before exp.  A decode
+    step of softmax attention at position i is row i of this.
+
+    q_rows: [len(rows), d]; K: [N, d]; V: [N, e].
+    """
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    out = np.empty((len(rows), V.shape[1]), dtype=np.float64)
+    for r, i in enumerate(rows):
+        x = K[: i + 1] @ q_rows[r]
+        p = np.exp(x - x.max())
+        out[r] = (p @ V[: i + 1]) / p.sum()
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -285,6 +285,22 @@ def pin_softmax_library():
     assert rel_err(orc.softmax_attention(q.exact, k.exact, v.exact), ref) <= 1e-13
 
 
+def pin_softmax_rows():
+    """Row-sampled softmax equals torch's causal scaled_dot_product_attention
+    (scale 1, fp64 CPU) on those rows, also where the scores are large
+    (raw, unnormalised inputs scaled by 8: the subtracted maximum matters)."""
+    import torch
+    for scale, norm in ((1.0, True), (8.0, False)):
+        q, k, v = wl.draw_qkv(22, 1, 1, 90, 6, 3, "f32", normalise=norm)
+        Q, K, V = q.exact * scale, k.exact * scale, v.exact
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V), is_causal=True, scale=1.0).numpy()[0, 0]
+        rows = [0, 1, 2, 45, 88, 89]
+        got = orc.softmax_rows(Q[0, 0, rows], K[0, 0], V[0, 0], rows)
+        assert rel_err(got, ref[rows]) <= 1e-13
+        assert np.all(np.isfinite(got))
+
+
 def pin_softmax_convergence(N=128, d=16, e=8, seed=2):
     """With unit q, k: |o_n - o_softmax| <= eps/(1-eps) max_j |v_j - o_softmax|
     per coordinate with eps = e/n! (Taylor remainder on |x| <= 1), and the error
@@ -541,5 +557,5 @@ ALL_PINS = [
     pin_decode_equals_recurrence, pin_softmax_library, pin_softmax_convergence,
     pin_normalisation_required, pin_svd_rank, pin_special_cases, pin_convex_hull,
     pin_planes_layout, pin_quadratic_rows, pin_prefill_from_states,
-    pin_normalize_rows, pin_normalize_rows_f32, pin_round_to_dtype,
+    pin_normalize_rows, pin_normalize_rows_f32, pin_round_to_dtype, pin_softmax_rows,
 ]

@@ -128,6 +128,28 @@ def _prefill_from_exclusive_states(Q, K, V, S0, n):
     return o, S - np.asarray(S0)
 
 
+_orig_softmax_rows = orc.softmax_rows
+
+
+def _softmax_rows_exclusive(q_rows, K, V, rows):
+    # the current key is left out (row 0 keeps its only key)
+    out = []
+    for r, i in enumerate(rows):
+        j = max(i, 1)
+        out.append(_orig_softmax_rows(q_rows[r:r + 1], np.asarray(K)[:j], np.asarray(V)[:j], [j - 1])[0])
+    return np.stack(out)
+
+
+def _softmax_rows_no_max(q_rows, K, V, rows):
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    out = []
+    for r, i in enumerate(rows):
+        p = np.exp(np.float32(K[: i + 1] @ np.asarray(q_rows[r])))  # no max subtracted, fp32 exp overflows
+        out.append((p @ V[: i + 1]) / p.sum())
+    return np.array(out)
+
+
 _orig_normalize = orc.normalize_rows
 _orig_normalize32 = orc.normalize_rows_f32
 _orig_round = orc.round_to_dtype
@@ -175,6 +197,8 @@ MUTANTS = {
     "normalize_no_sqrt": ("normalize_rows", _normalize_no_sqrt),
     "normalize_inverted_temperature": ("normalize_rows", _normalize_inverted_temperature),
     "normalize_f32_no_sqrt": ("normalize_rows_f32", _normalize32_no_sqrt),
+    "softmax_rows_exclusive": ("softmax_rows", _softmax_rows_exclusive),
+    "softmax_rows_no_max": ("softmax_rows", _softmax_rows_no_max),
     "round_bf16_truncating": ("round_to_dtype", _round_truncating),
 }
 
@@ -184,7 +208,8 @@ _PINS = [pins.pin_hand_example, pins.pin_kron_features, pins.pin_unit_identity,
          pins.pin_planes_layout, pins.pin_exact_rational, pins.pin_chunk_additivity,
          pins.pin_recurrent_vs_quadratic, pins.pin_softmax_library,
          pins.pin_softmax_convergence, pins.pin_prefill_from_states,
-         pins.pin_normalize_rows, pins.pin_normalize_rows_f32, pins.pin_round_to_dtype]
+         pins.pin_normalize_rows, pins.pin_normalize_rows_f32, pins.pin_round_to_dtype,
+         pins.pin_softmax_rows]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

@@ -223,6 +223,120 @@ def bench_orders(args, torch, ops, wl):
             "orders": rows}
 
 
+def _loglog_slope(xs, ys):
+    import numpy as np
+    lx, ly = np.log(np.asarray(xs, float)), np.log(np.asarray(ys, float))
+    return float(np.polyfit(lx, ly, 1)[0])
+
+
+def _crossover(ns, t_a, t_b):
+    """Smallest N where t_a / t_b crosses 1, by log-log interpolation between
+    neighbouring points; None if it does not cross in the measured range."""
+    import math
+    for i in range(len(ns) - 1):
+        r0, r1 = t_a[i] / t_b[i], t_a[i + 1] / t_b[i + 1]
+        if (r0 - 1) * (r1 - 1) <= 0 and r0 != r1:
+            f = math.log(r0) / (math.log(r0) - math.log(r1))
+            return round(math.exp(math.log(ns[i]) + f * (math.log(ns[i + 1]) - math.log(ns[i]))), 1)
+    return None
+
+
+def bench_compare(args, torch, ops, wl):
+    """The pages' comparisons with softmax attention, on this GPU: prefill
+    time against N (B=4, H=8, dk=16, dv=64, n=3, bf16) for the truncated
+    kernel and for exact causal softmax, fitted exponents, the crossover and
+    the ratio at N = 8192; decode time per step against the context length
+    (B=64, H=32, fp32) for the recurrent state and for softmax over a KV
+    cache, and the ratio at N = 65536."""
+    w = wl.WORKLOADS["prefill"]
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    pre = []
+    for N in (256, 512, 1024, 2048, 4096, 8192, 16384):
+        Q = torch.randn((w.B, w.H, N, w.dk), generator=g, device=dev)
+        K = torch.randn((w.B, w.H, N, w.dk), generator=g, device=dev)
+        Q = (Q / Q.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        K = (K / K.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        V = torch.randn((w.B, w.H, N, w.dv), generator=g, device=dev).to(torch.bfloat16)
+        O = torch.empty((w.B, w.H, N, w.dv), dtype=torch.float32, device=dev)
+        S = torch.empty(w.B * w.H * ops.tt_state_floats(w.dk, w.dv, w.n), dtype=torch.float32, device=dev)
+        ws = torch.empty(ops.tt_prefill_workspace_bytes(w.B, w.H, N, w.dk, w.dv, w.n, w.chunk), dtype=torch.uint8,
+                         device=dev)
+        f_t = lambda: ops.tt_prefill(Q, K, V, w.n, w.chunk, O=O, states=S, workspace=ws)
+        f_s = lambda: ops.tt_softmax_prefill(Q, K, V, O=O)
+        row = {"N": N}
+        for name, f in (("taylor_n3_us", f_t), ("softmax_us", f_s)):
+            f()
+            t1 = _time_events(f, 3, torch) / 3
+            reps = max(3, min(200, int(0.1 / max(t1, 1e-6))))
+            row[name] = round(_time_events(f, reps, torch) / reps * 1e6, 2)
+        row["ratio_softmax_over_taylor"] = round(row["softmax_us"] / row["taylor_n3_us"], 2)
+        flops = w.B * w.H * N * (N + 1) / 2 * 2 * (w.dk + w.dv)
+        row["softmax_TFLOPs"] = round(flops / (row["softmax_us"] * 1e-6) / 1e12, 1)
+        pre.append(row)
+        print(f"# compare prefill N={N}: taylor {row['taylor_n3_us']} us, softmax {row['softmax_us']} us", file=sys.stderr,
+              flush=True)
+        del Q, K, V, O, S, ws
+    ns = [r["N"] for r in pre]
+    tt = [r["taylor_n3_us"] for r in pre]
+    ts = [r["softmax_us"] for r in pre]
+    big = [i for i, n in enumerate(ns) if n >= 1024]
+    prefill = {"workload": "prefill B4 H8 dk16 dv64 bf16, N swept; truncated kernel n=3 vs exact causal softmax",
+               "points": pre,
+               "exponent_taylor_N1024_16384": round(_loglog_slope([ns[i] for i in big], [tt[i] for i in big]), 3),
+               "exponent_softmax_N1024_16384": round(_loglog_slope([ns[i] for i in big], [ts[i] for i in big]), 3),
+               "crossover_N": _crossover(ns, tt, ts),
+               "ratio_at_8192": next(r["ratio_softmax_over_taylor"] for r in pre if r["N"] == 8192)}
+
+    d = wl.WORKLOADS["decode"]
+    BH = d.B * d.H
+    nf = ops.tt_state_floats(d.dk, d.dv, d.n)
+    states = torch.randn(BH * nf, generator=g, device=dev)
+    q = torch.randn((d.B, d.H, d.dk), generator=g, device=dev)
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = torch.randn((d.B, d.H, d.dk), generator=g, device=dev)
+    k = k / k.norm(dim=-1, keepdim=True)
+    v = torch.randn((d.B, d.H, d.dv), generator=g, device=dev)
+    o = torch.empty((d.B, d.H, d.dv), dtype=torch.float32, device=dev)
+    f_t = lambda: ops.tt_decode_step(q, k, v, states, d.n, o=o)
+    f_t()
+    t_taylor = _time_events(f_t, 100, torch) / 100
+    dec = []
+    capN = 65536 + 1
+    Kc = torch.empty((d.B, d.H, capN, d.dk), dtype=torch.float32, device=dev)
+    Vc = torch.empty((d.B, d.H, capN, d.dv), dtype=torch.float32, device=dev)
+    for b0 in range(d.B):  # fill in slices: a normalised Gaussian cache
+        kk = torch.randn((d.H, capN, d.dk), generator=g, device=dev)
+        Kc[b0] = kk / kk.norm(dim=-1, keepdim=True)
+        Vc[b0] = torch.randn((d.H, capN, d.dv), generator=g, device=dev)
+    del kk
+    ws = torch.empty(ops.tt_softmax_decode_workspace_bytes(d.B, d.H, capN - 1), dtype=torch.uint8, device=dev)
+    for N in (1024, 4096, 16384, 65536):
+        f_s = lambda: ops.tt_softmax_decode_step(q, k, v, Kc, Vc, N, o=o, workspace=ws)
+        f_s()
+        t1 = _time_events(f_s, 2, torch) / 2
+        reps = max(2, min(100, int(0.1 / max(t1, 1e-6))))
+        t_s = _time_events(f_s, reps, torch) / reps
+        kv_bytes = BH * N * (d.dk + d.dv) * 4
+        dec.append({"N": N, "softmax_us": round(t_s * 1e6, 2), "taylor_us": round(t_taylor * 1e6, 2),
+                    "ratio_softmax_over_taylor": round(t_s / t_taylor, 1),
+                    "softmax_kv_GBs": round(kv_bytes / t_s / 1e9, 1),
+                    "softmax_hbm_frac": round(kv_bytes / t_s / 1e9 / HBM_PEAK_GBS, 3)})
+        print(f"# compare decode N={N}: taylor {t_taylor * 1e6:.1f} us, softmax {t_s * 1e6:.1f} us", file=sys.stderr,
+              flush=True)
+    del Kc, Vc
+    decode = {"workload": "decode B64 H32 dk16 dv64 fp32, one step at context N; recurrent state (n=3) vs softmax "
+                          "over an fp32 KV cache",
+              "points": dec,
+              "exponent_softmax": round(_loglog_slope([r["N"] for r in dec], [r["softmax_us"] for r in dec]), 3),
+              "ratio_at_65536": dec[-1]["ratio_softmax_over_taylor"]}
+    return {"compare": {"prefill": prefill, "decode": decode,
+                        "pages": {"prefill_exponents": "softmax N^2.28, states N^0.91", "crossover_N": 728,
+                                  "ratio_at_8192": 20.8, "decode_us_per_token": 7.3, "decode_ratio_at_65536": 76.0,
+                                  "hardware": "not stated"}}}
+
+
 def bench_decode(args, torch, ops, wl):
     """States of a 65536-token prefix per (b, h), then 256 single-token steps."""
     w = wl.WORKLOADS["decode"]
@@ -352,6 +466,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline (profiling runs)")
     ap.add_argument("--only", choices=["prefill", "decode", "others"], default=None)
+    ap.add_argument("--compare", action="store_true",
+                    help="print the comparison with exact softmax attention (prefill N sweep, decode vs context) "
+                         "instead")
     ap.add_argument("--orders", action="store_true",
                     help="print the order sweep (n = 1..5: time per call and error against softmax) instead")
     ap.add_argument("--calibrate", action="store_true",
@@ -369,6 +486,10 @@ def main():
     ops.lib()  # fails loudly if the library is not built
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+
+    if args.compare:
+        print(json.dumps(bench_compare(args, torch, ops, wl)), flush=True)
+        return
 
     if args.orders:
         print(json.dumps(bench_orders(args, torch, ops, wl)), flush=True)

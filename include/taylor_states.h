@@ -186,6 +186,42 @@ int tt_state_merge(float *dst, const float *a, const float *b, size_t nfloats,
 int tt_feature_map(const void *x, tt_dtype in_dtype, size_t rows, int dk, int n,
                    int weighted, float *out, void *stream);
 
+/* ---- Softmax baseline ------------------------------------------------
+ * Exact causal softmax attention, the kernel exp(q.k) that the truncated
+ * series approximates, for timing the method against it on the same GPU
+ * ("Expanding Attention", abstract: prefill time and decode time per token
+ * are compared with softmax attention).  No scale inside exp:
+ *     o_i = sum_{j<=i} exp(q_i.k_j) v_j / sum_{j<=i} exp(q_i.k_j).
+ * Supported: dk in {16, 32, 64}, dv = 64 (TT_ERR_UNSUPPORTED otherwise). */
+
+/* Causal prefill.  Q, K [B][H][N][dk], V [B][H][N][dv]: bf16 only
+ * (TT_ERR_UNSUPPORTED for TT_F32); O [B][H][N][dv] fp32, written.  All
+ * pointers 16-byte aligned.  Scores and the running maximum in fp32;
+ * probabilities enter the value product as bf16 (hi + lo bf16 on the
+ * diagonal block of 64 keys). */
+int tt_softmax_prefill(const void *Q, const void *K, const void *V, tt_dtype in_dtype,
+                       int B, int H, int N, int dk, int dv, float *O, void *stream);
+
+/* Bytes of workspace tt_softmax_decode_step needs at position pos:
+ * B*H*(pos/2048 + 1) records of dv + 2 floats. */
+int tt_softmax_decode_workspace_bytes(int B, int H, int pos, size_t *bytes);
+
+/* One generated token per head against a KV cache.  The token at position
+ * pos is appended (k into Kcache row pos, v into Vcache row pos) and
+ *     o = sum_{j<=pos} exp(q.k_j) v_j / sum_{j<=pos} exp(q.k_j)
+ * is read out over cache rows 0 .. pos-1 and the new token.
+ *   q, k   : [B][H][dk] in_dtype;  v : [B][H][dv] in_dtype
+ *   Kcache : [B][H][capacity][dk] in_dtype, rows 0 .. pos-1 read, row pos written
+ *   Vcache : [B][H][capacity][dv] in_dtype, likewise; both 16-byte aligned
+ *   pos    : 0 <= pos < capacity (TT_ERR_INVALID_ARG otherwise)
+ *   o      : [B][H][dv] fp32, written
+ *   workspace : tt_softmax_decode_workspace_bytes(B, H, pos) bytes or more
+ * B*H must not exceed 65535.  Work grows linearly with pos. */
+int tt_softmax_decode_step(const void *q, const void *k, const void *v, tt_dtype in_dtype,
+                           int B, int H, int dk, int dv, void *Kcache, void *Vcache,
+                           int pos, int capacity, float *o, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 /* Message for the last failed call on this thread ("" if none). */
 const char *tt_last_error(void);
 

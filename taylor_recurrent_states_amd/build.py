@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtaylor_states.so")
-SOURCES = ["tt_api.hip", "tt_decode.hip", "tt_prefill.hip"]
+SOURCES = ["tt_api.hip", "tt_decode.hip", "tt_prefill.hip", "tt_softmax.hip"]
 ARCH = os.environ.get("TT_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

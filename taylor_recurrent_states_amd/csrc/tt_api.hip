@@ -249,6 +249,56 @@ int tt_feature_map(const void* x, tt_dtype in_dtype, size_t rows, int dk, int n,
                     "tt_feature_map launch");
 }
 
+int tt_softmax_prefill(const void* Q, const void* K, const void* V, tt_dtype in_dtype, int B, int H, int N, int dk,
+                       int dv, float* O, void* stream) {
+  if (!Q || !K || !V || !O) return fail(TT_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (B < 1 || H < 1 || N < 1 || dk < 1 || dv < 1)
+    return fail(TT_ERR_INVALID_ARG, "B=%d H=%d N=%d dk=%d dv=%d must be >= 1", B, H, N, dk, dv);
+  int rc = check_dtype(in_dtype);
+  if (rc) return rc;
+  if (in_dtype != TT_BF16) return fail(TT_ERR_UNSUPPORTED, "tt_softmax_prefill takes bf16 inputs only");
+  if ((dk != 16 && dk != 32 && dk != 64) || dv != 64)
+    return fail(TT_ERR_UNSUPPORTED, "(dk=%d, dv=%d) not compiled: dk in {16, 32, 64}, dv = 64", dk, dv);
+  if ((long long)B * H * ((N + 63) / 64) > 0x7fffffffLL) return fail(TT_ERR_UNSUPPORTED, "too many query blocks");
+  if ((((uintptr_t)Q) | ((uintptr_t)K) | ((uintptr_t)V) | ((uintptr_t)O)) & 15u)
+    return fail(TT_ERR_INVALID_ARG, "Q, K, V and O must be 16-byte aligned");
+  return hip_status(launch_softmax_prefill(Q, K, V, B * H, N, dk, O, (hipStream_t)stream),
+                    "tt_softmax_prefill launch");
+}
+
+int tt_softmax_decode_workspace_bytes(int B, int H, int pos, size_t* bytes) {
+  if (!bytes) return fail(TT_ERR_INVALID_ARG, "bytes is NULL");
+  if (B < 1 || H < 1 || pos < 0) return fail(TT_ERR_INVALID_ARG, "B=%d H=%d must be >= 1, pos=%d >= 0", B, H, pos);
+  *bytes = (size_t)B * H * softmax_decode_splits(pos) * (64 + 2) * sizeof(float);
+  return ok();
+}
+
+int tt_softmax_decode_step(const void* q, const void* k, const void* v, tt_dtype in_dtype, int B, int H, int dk,
+                           int dv, void* Kcache, void* Vcache, int pos, int capacity, float* o, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !Kcache || !Vcache || !o) return fail(TT_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (B < 1 || H < 1 || dk < 1 || dv < 1)
+    return fail(TT_ERR_INVALID_ARG, "B=%d H=%d dk=%d dv=%d must be >= 1", B, H, dk, dv);
+  if (pos < 0 || pos >= capacity)
+    return fail(TT_ERR_INVALID_ARG, "pos=%d must lie in [0, capacity=%d)", pos, capacity);
+  int rc = check_dtype(in_dtype);
+  if (rc) return rc;
+  if ((dk != 16 && dk != 32 && dk != 64) || dv != 64)
+    return fail(TT_ERR_UNSUPPORTED, "(dk=%d, dv=%d) not compiled: dk in {16, 32, 64}, dv = 64", dk, dv);
+  if ((long long)B * H > 65535) return fail(TT_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)B * H);
+  if ((((uintptr_t)Kcache) | ((uintptr_t)Vcache)) & 15u)
+    return fail(TT_ERR_INVALID_ARG, "Kcache and Vcache must be 16-byte aligned");
+  size_t need = 0;
+  rc = tt_softmax_decode_workspace_bytes(B, H, pos, &need);
+  if (rc) return rc;
+  if (!workspace || workspace_bytes < need)
+    return fail(TT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  return hip_status(launch_softmax_decode(q, k, v, in_dtype, B * H, dk, Kcache, Vcache, pos, capacity, o,
+                                          (float*)workspace, (hipStream_t)stream),
+                    "tt_softmax_decode_step launch");
+}
+
 const char* tt_last_error(void) { return g_err; }
 
 }  // extern "C"

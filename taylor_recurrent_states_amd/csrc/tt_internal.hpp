@@ -24,6 +24,16 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, tt_dtype d
 hipError_t launch_normalize(tt_dtype dt, int d, const void* x0, void* out0, float s0, size_t rows0,
                             const void* x1, void* out1, float s1, size_t rows1, hipStream_t s);
 
+// Softmax baseline: causal prefill (bf16 inputs, dk in {16, 32, 64}, dv = 64)
+// and one decode step against a KV cache.  Decode partials: one record of
+// dv + 2 floats per (head, split of 2048 keys); softmax_decode_splits(pos)
+// splits cover keys 0 .. pos.
+hipError_t launch_softmax_prefill(const void* Q, const void* K, const void* V, int BH, int N, int dk, float* O,
+                                  hipStream_t s);
+size_t softmax_decode_splits(int pos);
+hipError_t launch_softmax_decode(const void* q, const void* k, const void* v, tt_dtype dt, int BH, int dk,
+                                 void* Kc, void* Vc, int pos, int cap, float* o, float* part, hipStream_t s);
+
 // Prefill plan: how the sequence and the columns are split over workgroups.
 struct PrefillPlan {
   int W;          // feature rows

@@ -7,7 +7,8 @@ The calls keep the C names:
     tt_state_rows, tt_state_floats, tt_prefill_workspace_bytes,
     tt_prefill, tt_prefill_from, tt_decode_step, tt_state_merge,
     tt_feature_map, tt_last_error, tt_normalize_rows,
-    tt_prefill_normed_workspace_bytes, tt_prefill_normed, tt_decode_step_normed
+    tt_prefill_normed_workspace_bytes, tt_prefill_normed, tt_decode_step_normed,
+    tt_softmax_prefill, tt_softmax_decode_workspace_bytes, tt_softmax_decode_step
 
 Loading fails loudly (ImportError / OSError) when the library has not been
 built; there is no fallback implementation.
@@ -28,7 +29,8 @@ TT_OK, TT_ERR_INVALID_ARG, TT_ERR_UNSUPPORTED, TT_ERR_WORKSPACE, TT_ERR_HIP = 0,
 EXPORTED = ("tt_state_rows", "tt_state_floats", "tt_prefill_workspace_bytes", "tt_prefill",
             "tt_prefill_from", "tt_decode_step", "tt_state_merge", "tt_feature_map", "tt_last_error",
             "tt_normalize_rows", "tt_prefill_normed_workspace_bytes", "tt_prefill_normed",
-            "tt_decode_step_normed")
+            "tt_decode_step_normed", "tt_softmax_prefill", "tt_softmax_decode_workspace_bytes",
+            "tt_softmax_decode_step")
 
 _lib = None
 
@@ -79,6 +81,14 @@ def lib() -> ctypes.CDLL:
     L.tt_decode_step_normed.argtypes = [c_void, c_void, c_void, c_int] + [c_int] * 5 + [c_flt, c_float_p, c_float_p,
                                                                                          c_void]
     L.tt_decode_step_normed.restype = c_int
+    L.tt_softmax_prefill.argtypes = [c_void, c_void, c_void, c_int] + [c_int] * 5 + [c_float_p, c_void]
+    L.tt_softmax_prefill.restype = c_int
+    L.tt_softmax_decode_workspace_bytes.argtypes = [c_int, c_int, c_int, ctypes.POINTER(c_size)]
+    L.tt_softmax_decode_workspace_bytes.restype = c_int
+    L.tt_softmax_decode_step.argtypes = [c_void, c_void, c_void, c_int] + [c_int] * 4 + [c_void, c_void, c_int, c_int,
+                                                                                          c_float_p, c_void, c_size,
+                                                                                          c_void]
+    L.tt_softmax_decode_step.restype = c_int
     L.tt_last_error.argtypes = []
     L.tt_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -286,3 +296,51 @@ def tt_feature_map(x, n: int, weighted: bool, out=None, stream=None):
     _check(lib().tt_feature_map(x.data_ptr(), _dtype_code(x), rows, dk, n, int(bool(weighted)),
                                 _dev(out, "out").data_ptr(), _stream(stream)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# softmax baseline
+# ---------------------------------------------------------------------------
+
+def tt_softmax_prefill(Q, K, V, O=None, stream=None):
+    """Causal softmax attention (no scale) of bf16 Q, K [B, H, N, dk] and
+    V [B, H, N, dv]; returns O [B, H, N, dv] float32."""
+    torch = _torch()
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
+        _dev(t, nm)
+    B, H, N, dk = Q.shape
+    dv = V.shape[-1]
+    if O is None:
+        O = torch.empty((B, H, N, dv), dtype=torch.float32, device=Q.device)
+    _check(lib().tt_softmax_prefill(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk, dv,
+                                    _dev(O, "O").data_ptr(), _stream(stream)))
+    return O
+
+
+def tt_softmax_decode_workspace_bytes(B: int, H: int, pos: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().tt_softmax_decode_workspace_bytes(B, H, pos, ctypes.byref(out)))
+    return int(out.value)
+
+
+def tt_softmax_decode_step(q, k, v, Kcache, Vcache, pos: int, o=None, workspace=None, stream=None):
+    """Append (k, v) at row ``pos`` of the caches [B, H, capacity, d] and
+    return the softmax readout o [B, H, dv] float32 over rows 0 .. pos."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (Kcache, "Kcache"), (Vcache, "Vcache")):
+        _dev(t, nm)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    cap = Kcache.shape[2]
+    if tuple(Vcache.shape[:3]) != (B, H, cap):
+        raise ValueError("Kcache and Vcache disagree in shape")
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    need = tt_softmax_decode_workspace_bytes(B, H, pos)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib().tt_softmax_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, H, dk, dv,
+                                        Kcache.data_ptr(), Vcache.data_ptr(), pos, cap, _dev(o, "o").data_ptr(),
+                                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                        _stream(stream)))
+    return o

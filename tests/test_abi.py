@@ -119,6 +119,26 @@ def test_normalised_entry_points_reject_bad_arguments_without_launching():
     assert rc == ops.TT_ERR_INVALID_ARG
 
 
+def test_softmax_entry_points_reject_bad_arguments_without_launching():
+    L = ops.lib()
+    fake = ctypes.c_void_p(0x1000)
+    rc = L.tt_softmax_prefill(fake, fake, fake, 0, 1, 1, 64, 16, 64, fake, None)
+    assert rc == ops.TT_ERR_UNSUPPORTED and "bf16" in ops.tt_last_error()
+    assert L.tt_softmax_prefill(fake, fake, fake, 1, 1, 1, 64, 24, 64, fake, None) == ops.TT_ERR_UNSUPPORTED
+    assert L.tt_softmax_prefill(None, fake, fake, 1, 1, 1, 64, 16, 64, fake, None) == ops.TT_ERR_INVALID_ARG
+    assert L.tt_softmax_prefill(fake, fake, fake, 1, 1, 1, 0, 16, 64, fake, None) == ops.TT_ERR_INVALID_ARG
+    assert ops.tt_softmax_decode_workspace_bytes(2, 3, 0) == 2 * 3 * 66 * 4
+    assert ops.tt_softmax_decode_workspace_bytes(2, 3, 2048) == 2 * 3 * 2 * 66 * 4
+    ws = ctypes.c_void_p(0x100000)
+    args = (fake, fake, fake, 0, 1, 1, 16, 64, fake, fake)
+    assert L.tt_softmax_decode_step(*args, 5, 5, fake, ws, 1 << 20, None) == ops.TT_ERR_INVALID_ARG  # pos == cap
+    assert L.tt_softmax_decode_step(*args, -1, 5, fake, ws, 1 << 20, None) == ops.TT_ERR_INVALID_ARG
+    assert L.tt_softmax_decode_step(*args, 3, 5, fake, ws, 10, None) == ops.TT_ERR_WORKSPACE
+    assert L.tt_softmax_decode_step(*args, 3, 5, fake, None, 0, None) == ops.TT_ERR_WORKSPACE
+    bad = (fake, fake, fake, 0, 1, 1, 16, 64, ctypes.c_void_p(0x1008), fake)
+    assert L.tt_softmax_decode_step(*bad, 3, 5, fake, ws, 1 << 20, None) == ops.TT_ERR_INVALID_ARG
+
+
 def test_product_path_has_no_oracle_or_cpu_fallback():
     """The package never imports the oracle and has no host compute path."""
     pkg = os.path.join(ROOT, "taylor_recurrent_states_amd")

@@ -10,7 +10,9 @@ tokens/s = B*N / (time per step).  The decode workload (B=64 x H=32 states
 of a 65536-token prefix, 256 successive single-token steps) is timed in the
 same run and reported under "decode" as us per step.  Inputs are resident
 in HBM before the timed regions; timing uses HIP events on the stream the
-kernels are launched on.  "roofline" relates algorithmic bytes per launch
+kernels are launched on.  Before its warm-up steps every timed section runs
+its step untimed for 50-200 ms, so the timed steps see the clocks of
+sustained load.  "roofline" relates algorithmic bytes per launch
 to the measured time; "cpu_baseline" times the fp64 oracle on the host on a
 bounded sample.
 """
@@ -53,6 +55,17 @@ def _traffic(kernel_key, src_hash):
     return e.get("bytes_per_launch")
 
 
+def _prewarm(fn, torch, seconds=0.2):
+    """Run fn untimed for about `seconds` of GPU time before the warm-up
+    steps, so that the timed steps see the clocks the GPU settles at under
+    sustained load (a few ms of work after idle run about 15 % slower)."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+
+
 def _time_events(fn, steps, torch):
     s = torch.cuda.current_stream()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -83,6 +96,7 @@ def bench_prefill(args, torch, ops, wl):
     def step():
         ops.tt_prefill(Q, K, V, w.n, w.chunk, O=O, states=S, workspace=ws)
 
+    _prewarm(step, torch)
     for _ in range(args.warmup):
         step()
     t = _time_events(step, args.steps, torch)
@@ -99,7 +113,7 @@ def bench_prefill(args, torch, ops, wl):
     def step_from():
         ops.tt_prefill_from(Q, K, V, S_in, w.n, w.chunk, O=O, states=S, workspace=ws)
 
-    step_from()
+    _prewarm(step_from, torch, 0.05)
     t_from = _time_events(step_from, args.steps, torch) / args.steps
     from_bytes = alg_bytes + S_in.numel() * 4
     # the same workload on raw (not normalised) q, k: the library normalises
@@ -112,7 +126,7 @@ def bench_prefill(args, torch, ops, wl):
     def step_normed():
         ops.tt_prefill_normed(Qr, Kr, V, w.n, 1.0, chunk=w.chunk, O=O, states=S, workspace=ws_n)
 
-    step_normed()
+    _prewarm(step_normed, torch, 0.05)
     t_normed = _time_events(step_normed, args.steps, torch) / args.steps
     # the normalisation pass alone: Q and K rows in one launch
     QK = torch.cat([Qr.reshape(-1, w.dk), Kr.reshape(-1, w.dk)])
@@ -121,7 +135,7 @@ def bench_prefill(args, torch, ops, wl):
     def step_norm():
         ops.tt_normalize_rows(QK, 1.0, out=QKn)
 
-    step_norm()
+    _prewarm(step_norm, torch, 0.05)
     t_norm = _time_events(step_norm, args.steps, torch) / args.steps
     norm_bytes = 2 * QK.numel() * QK.element_size()
     return {
@@ -166,7 +180,7 @@ def bench_prefill_other(name, args, torch, ops, wl):
     def step():
         ops.tt_prefill(Q, K, V, w.n, w.chunk, O=O, states=S, workspace=ws)
 
-    step()
+    _prewarm(step, torch, 0.1)
     steps = max(2, min(args.steps, 10))
     t = _time_events(step, steps, torch) / steps
     W = ops.tt_state_rows(w.dk, w.n)
@@ -209,8 +223,7 @@ def bench_orders(args, torch, ops, wl):
         def step():
             ops.tt_prefill(Q, K, V, n, w.chunk, O=O, states=S, workspace=ws)
 
-        for _ in range(3):
-            step()
+        _prewarm(step, torch, 0.05)
         steps = max(2, min(args.steps, 20))
         t = _time_events(step, steps, torch) / steps
         o_small, _ = ops.tt_prefill(Qs, Ks, Vs, n)
@@ -267,7 +280,7 @@ def bench_compare(args, torch, ops, wl):
         f_s = lambda: ops.tt_softmax_prefill(Q, K, V, O=O)
         row = {"N": N}
         for name, f in (("taylor_n3_us", f_t), ("softmax_us", f_s)):
-            f()
+            _prewarm(f, torch, 0.05)
             t1 = _time_events(f, 3, torch) / 3
             reps = max(3, min(200, int(0.1 / max(t1, 1e-6))))
             row[name] = round(_time_events(f, reps, torch) / reps * 1e6, 2)
@@ -300,7 +313,7 @@ def bench_compare(args, torch, ops, wl):
     v = torch.randn((d.B, d.H, d.dv), generator=g, device=dev)
     o = torch.empty((d.B, d.H, d.dv), dtype=torch.float32, device=dev)
     f_t = lambda: ops.tt_decode_step(q, k, v, states, d.n, o=o)
-    f_t()
+    _prewarm(f_t, torch, 0.05)
     t_taylor = _time_events(f_t, 100, torch) / 100
     dec = []
     capN = 65536 + 1
@@ -314,7 +327,7 @@ def bench_compare(args, torch, ops, wl):
     ws = torch.empty(ops.tt_softmax_decode_workspace_bytes(d.B, d.H, capN - 1), dtype=torch.uint8, device=dev)
     for N in (1024, 4096, 16384, 65536):
         f_s = lambda: ops.tt_softmax_decode_step(q, k, v, Kc, Vc, N, o=o, workspace=ws)
-        f_s()
+        _prewarm(f_s, torch, 0.05)
         t1 = _time_events(f_s, 2, torch) / 2
         reps = max(2, min(100, int(0.1 / max(t1, 1e-6))))
         t_s = _time_events(f_s, reps, torch) / reps
@@ -377,6 +390,7 @@ def bench_decode(args, torch, ops, wl):
         for t in range(steps):
             ops.tt_decode_step(qs[t % T], ks[t % T], vs[t % T], states, w.n, o=o)
 
+    _prewarm(lambda: run(8), torch)
     run(min(args.warmup * 4, T))
     t = _time_events(lambda: run(T), 1, torch)
     t_step = t / T
@@ -405,7 +419,7 @@ def bench_decode(args, torch, ops, wl):
         for t in range(steps):
             ops.tt_decode_step_normed(qr[t % T], kr[t % T], vs[t % T], states, w.n, 1.0, o=o)
 
-    run_normed(8)
+    _prewarm(lambda: run_normed(8), torch, 0.05)
     t_normed = _time_events(lambda: run_normed(T), 1, torch) / T
     src = _source_hash("tt_decode.hip", "tt_device.hpp")
     return {
@@ -462,8 +476,8 @@ def cpu_baselines(pre, wl):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline (profiling runs)")
     ap.add_argument("--only", choices=["prefill", "decode", "others"], default=None)
     ap.add_argument("--compare", action="store_true",

@@ -187,7 +187,18 @@ def bench_prefill_other(name, args, torch, ops, wl):
     flops = 4.0 * W * (w.dv + 1) * w.B * w.H * w.N
     peak = 157.3 if w.dtype == "f32" else 2516.6
     achieved = flops / t / 1e12
+    # the same call with the normalisation folded in (raw q, k; temperature 1)
+    ws_n = torch.empty(ops.tt_prefill_normed_workspace_bytes(w.B, w.H, w.N, w.dk, w.dv, w.n, w.chunk),
+                       dtype=torch.uint8, device=dev)
+    del ws
+
+    def step_n():
+        ops.tt_prefill_normed(Q, K, V, w.n, 1.0, chunk=w.chunk, O=O, states=S, workspace=ws_n)
+
+    _prewarm(step_n, torch, 0.05)
+    t_n = _time_events(step_n, steps, torch) / steps
     return {"workload": w.name, "ms_per_call": round(t * 1e3, 4), "tokens_per_s": round(w.B * w.N / t, 1),
+            "ms_per_call_normed": round(t_n * 1e3, 4),
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                          "frac": round(achieved / peak, 4), "alg_flops_per_launch": flops,
                          "traffic": None}}

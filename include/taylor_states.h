@@ -122,10 +122,12 @@ int tt_prefill_from(const void *Q, const void *K, const void *V, tt_dtype in_dty
  * stop helping).  Every row x of d values becomes
  *     r(scale * x / ||x||_2),
  * computed with IEEE fp32 operations rounded to nearest even in a fixed
- * order (s = sum of x_i*x_i in index order, no fused multiply-add;
- * f = scale / sqrt(s); x_i * f), then rounded by r to the input dtype
- * (bf16: round to nearest even; fp32: as computed).  The result is a fixed
- * function of the input bits.  A zero row gives NaN.
+ * order (s = sum of x_i*x_i, no fused multiply-add, summed in groups of 8
+ * consecutive coordinates in index order, the group sums added as a
+ * balanced pairwise tree, neighbours first; f = scale / sqrt(s); x_i * f),
+ * then rounded by r to the input dtype (bf16: round to nearest even; fp32:
+ * as computed).  The result is a fixed function of the input bits.  A zero
+ * row gives NaN.
  *   x, out : [rows][d] in_dtype, 16-byte aligned; out may be x (in place)
  *            but must not otherwise overlap it
  *   d      : 16, 32 or 64 (TT_ERR_UNSUPPORTED otherwise)

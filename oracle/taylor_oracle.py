@@ -418,9 +418,16 @@ def normalize_rows(X, scale: float = 1.0) -> np.ndarray:
 
 
 def normalize_rows_f32(X, scale: float = 1.0) -> np.ndarray:
-    """``normalize_rows`` evaluated in fp32 with a fixed operation order:
-    s = sum of fl(x_i * x_i) added in index order, f = fl(scale / sqrt(s)),
-    y_i = fl(x_i * f), every operation IEEE fp32 round-to-nearest-even.
+    """``normalize_rows`` evaluated in fp32 with a fixed operation order,
+    every operation IEEE fp32 round-to-nearest-even:
+
+    * squares fl(x_i * x_i) summed in groups of 8 consecutive coordinates,
+      in index order inside a group (a short last group is padded with
+      zeros, which leaves sums unchanged);
+    * the group sums added as a balanced pairwise tree, neighbours first:
+      ((g0 + g1) + (g2 + g3)) + ... (the group count padded with zero groups
+      to a power of two);
+    * f = fl(scale / sqrt(s)), then y_i = fl(x_i * f).
 
     The unit rows are rounded to the input dtype afterwards; that rounding is
     a discrete decision, so it is taken on the same fp32 value the kernels
@@ -432,11 +439,24 @@ def normalize_rows_f32(X, scale: float = 1.0) -> np.ndarray:
     X32 = np.asarray(X, dtype=np.float64).astype(np.float32)
     if not np.array_equal(X32.astype(np.float64), np.asarray(X, dtype=np.float64), equal_nan=True):
         raise ValueError("rows must hold fp32 values")
-    ss = np.zeros(X32.shape[:-1], dtype=np.float32)
-    for i in range(X32.shape[-1]):
-        ss = ss + X32[..., i] * X32[..., i]
+    d = X32.shape[-1]
+    ngroups = 1
+    while ngroups * 8 < d:
+        ngroups *= 2
+    P = np.zeros(X32.shape[:-1] + (ngroups * 8,), dtype=np.float32)
+    P[..., :d] = X32
+    G = P.reshape(X32.shape[:-1] + (ngroups, 8))
+    sums = np.zeros(X32.shape[:-1] + (ngroups,), dtype=np.float32)
+    for e in range(8):
+        sums = sums + G[..., e] * G[..., e]
+    w = 1
+    while w < ngroups:
+        sums = sums.copy()
+        for j in range(0, ngroups - w, 2 * w):
+            sums[..., j] = sums[..., j] + sums[..., j + w]
+        w *= 2
     with np.errstate(invalid="ignore", divide="ignore"):
-        f = np.float32(scale) / np.sqrt(ss)
+        f = np.float32(scale) / np.sqrt(sums[..., 0])
         return (X32 * f[..., None]).astype(np.float64)
 
 

@@ -146,30 +146,64 @@ __device__ inline void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
 // folded into the queries as `scale`).  x <- r(scale * x / ||x||_2), where r
 // rounds to the input dtype (bf16: nearest even; fp32: identity).  Every
 // operation is one IEEE fp32 operation rounded to nearest even, in a fixed
-// order: squares x_i*x_i added in index order (no fused multiply-add), the
-// square root, scale / root, and x_i * that factor.  The result is a fixed
-// function of the input bits, the same in every kernel, and a host can
-// reproduce it exactly.  A zero row gives NaN.
+// order (row_norm_factor: squares summed in groups of 8, group sums by a
+// pairwise tree, no fused multiply-add; then the square root, scale / root,
+// and x_i * that factor).  The result is a fixed function of the input bits,
+// the same in every kernel, and a host can reproduce it exactly.  A zero row
+// gives NaN.
 // ---------------------------------------------------------------------------
+
+// Sum of squares of the 8 coordinates get(8g) .. get(8g+7), in index order.
+template <typename Get>
+__device__ inline float group_sumsq(Get get, int g) {
+#pragma clang fp contract(off)
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float xi = get(8 * g + e);
+    const float sq = xi * xi;
+    s = s + sq;
+  }
+  return s;
+}
+
+// The factor scale / ||x||_2 of a row whose coordinates get(0) .. get(D-1)
+// are fp32 values.  Squares are summed in groups of 8 consecutive
+// coordinates (group_sumsq); the group sums are added as a balanced pairwise
+// tree, neighbours first (((g0+g1)+(g2+g3))+...).  A kernel that spreads a
+// row over D/8 lanes reaches the same bits with a shfl_xor butterfly over
+// lane offsets 1, 2, 4 (IEEE addition commutes).
+template <int D, typename Get>
+__device__ inline float row_norm_factor(Get get, float scale) {
+#pragma clang fp contract(off)
+  constexpr int G = D / 8;
+  static_assert(D % 8 == 0 && (G & (G - 1)) == 0, "groups of 8, a power-of-two count");
+  float g[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) g[j] = group_sumsq(get, j);
+#pragma unroll
+  for (int w = 1; w < G; w *= 2)
+#pragma unroll
+    for (int j = 0; j + w < G; j += 2 * w) g[j] = g[j] + g[j + w];
+  return scale / sqrtf(g[0]);
+}
+
+// One unit coordinate: r(x * f), rounded to the input dtype.
+template <typename TIn>
+__device__ inline float unit_coord(float x, float f) {
+#pragma clang fp contract(off)
+  const float y = x * f;
+  if constexpr (std::is_same<TIn, uint16_t>::value)
+    return bf16_to_f32(f32_to_bf16(y));
+  else
+    return y;
+}
 
 template <typename TIn, int D>
 __device__ inline void normalize_row(float (&x)[D], float scale) {
-#pragma clang fp contract(off)
-  float ss = 0.f;
+  const float f = row_norm_factor<D>([&](int i) { return x[i]; }, scale);
 #pragma unroll
-  for (int i = 0; i < D; ++i) {
-    const float sq = x[i] * x[i];
-    ss = ss + sq;
-  }
-  const float f = scale / sqrtf(ss);
-#pragma unroll
-  for (int i = 0; i < D; ++i) {
-    const float y = x[i] * f;
-    if constexpr (std::is_same<TIn, uint16_t>::value)
-      x[i] = bf16_to_f32(f32_to_bf16(y));
-    else
-      x[i] = y;
-  }
+  for (int i = 0; i < D; ++i) x[i] = unit_coord<TIn>(x[i], f);
 }
 
 // ---------------------------------------------------------------------------

@@ -408,12 +408,15 @@ def bench_decode(args, torch, ops, wl):
     state_bytes = BH * nf * 4
     alg_bytes = 2 * state_bytes + BH * (2 * w.dk + w.dv) * 4 + BH * w.dv * 4
     achieved = alg_bytes / t_step / 1e9
-    # MALL-cold variant: a 512 MB write between steps evicts the 256 MB infinity cache
-    flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=dev)
+    # MALL-cold variant: reading a 512 MB buffer between steps evicts the state
+    # from the 256 MB infinity cache and leaves only clean lines behind (a
+    # write would leave dirty lines whose write-back competes with the step)
+    flush = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device=dev)
     s = torch.cuda.current_stream()
     cold = []
     for t2 in range(8):
-        flush.fill_(float(t2))
+        torch.sum(flush)
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(s)
         ops.tt_decode_step(qs[t2], ks[t2], vs[t2], states, w.n, o=o)

@@ -8,8 +8,7 @@
 // The step is HBM-bound: every float of the state is read once and written
 // once.  One workgroup per head; a wavefront's 64 lanes are the 64 value
 // columns, so each state row (256 B) is one coalesced load and one
-// coalesced store.  Rows are streamed eight at a time per wave to keep many
-// loads in flight.  mu(k) and phi(q) are computed once per head into LDS.
+// coalesced store.  mu(k) and phi(q) are computed once per head into LDS.
 #include "tt_device.hpp"
 #include "tt_internal.hpp"
 
@@ -21,41 +20,64 @@ constexpr int kDV = 64;
 constexpr int kDecodeThreads = 256;
 
 // NORM: q and k arrive raw; thread 0 (wave 0) turns q into r(qscale q/|q|)
-// and thread 64 (wave 1) k into r(k/|k|) with normalize_row, the same
-// function the prefill's normalisation pass uses.
+// and thread 64 (wave 1) k into r(k/|k|) in LDS, with the arithmetic of
+// normalize_row (row_norm_factor, unit_coord), which the prefill's
+// normalisation pass uses.
+//
+// Small states (at most 48 rows per wave, e.g. 153 rows at dk = 16, n = 3):
+// every wave issues the loads of all its state rows (and each thread its
+// normaliser row) before anything else, so the whole step's reads are in
+// flight while q, k and the feature rows are prepared.  Larger states
+// stream their rows eight at a time.  Partial sums are reduced with wave
+// shuffles and one workgroup barrier; the order is fixed, so results are
+// bitwise reproducible.
 template <int DK, int N, typename TIn, bool NORM>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const TIn* __restrict__ q,
+__global__ __launch_bounds__(kDecodeThreads, 8) void decode_kernel(const TIn* __restrict__ q,
                                                                 const TIn* __restrict__ k,
                                                                 const TIn* __restrict__ v,
                                                                 float* __restrict__ num_plane,
                                                                 float* __restrict__ den_plane,
                                                                 float* __restrict__ o, float qscale) {
   constexpr int W = rows_for(DK, N);
+  constexpr int per = (W + 3) / 4;       // rows of the value plane per wave
+  constexpr bool RES = per <= 48;        // all of a wave's rows held in registers
   __shared__ float s_q[DK], s_k[DK];
   __shared__ float s_mu[W], s_phi[W];
   __shared__ float s_red[4][kDV];
-  __shared__ float s_den[kDecodeThreads];
+  __shared__ float s_den[4];
 
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const auto& tab = RowsOf<DK>::get();
+  float* __restrict__ S = num_plane + (size_t)bh * W * kDV;
+  float* __restrict__ D = den_plane + (size_t)bh * W;
+  const int r0 = wave * per;
+  const int r1 = min(W, r0 + per);
 
-  if constexpr (NORM) {
-    if (tid == 0 || tid == 64) {
-      const TIn* src = (tid == 0 ? q : k) + (size_t)bh * DK;
-      float x[DK];
+  // state reads first (small states): they overlap everything up to the update
+  float sv[RES ? per : 1];
+  float dv = 0.f;
+  if constexpr (RES) {
 #pragma unroll
-      for (int i = 0; i < DK; ++i) x[i] = load_f32(src, i);
-      normalize_row<TIn, DK>(x, tid == 0 ? qscale : 1.0f);
-      float* dst = tid == 0 ? s_q : s_k;
-#pragma unroll
-      for (int i = 0; i < DK; ++i) dst[i] = x[i];
-    }
-  } else if (tid < DK) {
+    for (int u = 0; u < per; ++u)
+      if (r0 + u < r1) sv[u] = S[(size_t)(r0 + u) * kDV + lane];
+    if (tid < W) dv = D[tid];
+  }
+  const float vc = load_f32(v, (size_t)bh * kDV + lane);
+
+  if (tid < DK) {
     s_q[tid] = load_f32(q, (size_t)bh * DK + tid);
     s_k[tid] = load_f32(k, (size_t)bh * DK + tid);
+  }
+  if constexpr (NORM) {  // in place in LDS: few registers beside the resident state rows
+    __syncthreads();
+    if (tid == 0 || tid == 64) {
+      float* row = tid == 0 ? s_q : s_k;
+      const float f = row_norm_factor<DK>([&](int i) { return row[i]; }, tid == 0 ? qscale : 1.0f);
+      for (int i = 0; i < DK; ++i) row[i] = unit_coord<TIn>(row[i], f);
+    }
   }
   __syncthreads();
   for (int r = tid; r < W; r += kDecodeThreads) {
@@ -65,50 +87,61 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const TIn* __res
   }
   __syncthreads();
 
-  // value plane: wave w streams rows [r0, r1)
-  const float vc = load_f32(v, (size_t)bh * kDV + lane);
-  float* __restrict__ S = num_plane + (size_t)bh * W * kDV;
-  constexpr int per = (W + 3) / 4;
-  const int r0 = wave * per;
-  const int r1 = min(W, r0 + per);
+  // value plane: wave w updates rows [r0, r1) and reads them out
   float acc = 0.f;
-  int r = r0;
-  for (; r + 8 <= r1; r += 8) {
-    float s[8];
+  if constexpr (RES) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s[u] = S[(size_t)(r + u) * kDV + lane];
+    for (int u = 0; u < per; ++u)
+      if (r0 + u < r1) {
+        const float s = fmaf(s_mu[r0 + u], vc, sv[u]);
+        S[(size_t)(r0 + u) * kDV + lane] = s;
+        acc = fmaf(s_phi[r0 + u], s, acc);
+      }
+  } else {
+    int r = r0;
+    for (; r + 8 <= r1; r += 8) {
+      float s[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      s[u] = fmaf(s_mu[r + u], vc, s[u]);
-      S[(size_t)(r + u) * kDV + lane] = s[u];
-      acc = fmaf(s_phi[r + u], s[u], acc);
+      for (int u = 0; u < 8; ++u) s[u] = S[(size_t)(r + u) * kDV + lane];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s[u] = fmaf(s_mu[r + u], vc, s[u]);
+        S[(size_t)(r + u) * kDV + lane] = s[u];
+        acc = fmaf(s_phi[r + u], s[u], acc);
+      }
+    }
+    for (; r < r1; ++r) {
+      float s = S[(size_t)r * kDV + lane];
+      s = fmaf(s_mu[r], vc, s);
+      S[(size_t)r * kDV + lane] = s;
+      acc = fmaf(s_phi[r], s, acc);
     }
   }
-  for (; r < r1; ++r) {
-    float s = S[(size_t)r * kDV + lane];
-    s = fmaf(s_mu[r], vc, s);
-    S[(size_t)r * kDV + lane] = s;
-    acc = fmaf(s_phi[r], s, acc);
-  }
-  s_red[wave][lane] = acc;
 
   // normaliser plane
-  float* __restrict__ D = den_plane + (size_t)bh * W;
   float accd = 0.f;
-  for (int rr = tid; rr < W; rr += kDecodeThreads) {
-    const float d = D[rr] + s_mu[rr];
-    D[rr] = d;
-    accd = fmaf(s_phi[rr], d, accd);
+  if constexpr (RES) {
+    if (tid < W) {
+      const float d = dv + s_mu[tid];
+      D[tid] = d;
+      accd = s_phi[tid] * d;
+    }
+  } else {
+    for (int rr = tid; rr < W; rr += kDecodeThreads) {
+      const float d = D[rr] + s_mu[rr];
+      D[rr] = d;
+      accd = fmaf(s_phi[rr], d, accd);
+    }
   }
-  s_den[tid] = accd;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) accd += __shfl_xor(accd, off);
+  s_red[wave][lane] = acc;
+  if (lane == 0) s_den[wave] = accd;
   __syncthreads();
-  for (int w = kDecodeThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) s_den[tid] += s_den[tid + w];
-    __syncthreads();
-  }
   if (wave == 0) {
     const float num = (s_red[0][lane] + s_red[1][lane]) + (s_red[2][lane] + s_red[3][lane]);
-    o[(size_t)bh * kDV + lane] = num / s_den[0];
+    const float den = (s_den[0] + s_den[1]) + (s_den[2] + s_den[3]);
+    o[(size_t)bh * kDV + lane] = num / den;
   }
 }
 

@@ -497,10 +497,13 @@ __device__ __attribute__((always_inline)) inline void gen_groups(int part, int n
       return p;
     }
   };
+  // chunk swizzle of the token-major mu tile (PCfg::MUSWZ)
+  const int mswz = C::MUSWZ ? ((lane >> 2) & 3) : 0;
   static_for<0, NG>([&](auto gc) {
     constexpr int GI = decltype(gc)::value;
     if (GI % nparts != part) return;
     constexpr int RB = GI * G;
+    const int MB = (GI ^ mswz) * G;  // where chunk GI of this token lives
     float mu[G];
     static_for<0, G>([&](auto uc) {
       constexpr int U = decltype(uc)::value;
@@ -521,7 +524,7 @@ __device__ __attribute__((always_inline)) inline void gen_groups(int part, int n
       *reinterpret_cast<u32x4*>(sPhi + lane * C::PHS + RB) = pk;
     }
     if constexpr (C::OUT) {
-      *reinterpret_cast<u32x4*>(sMu + lane * C::MUS + RB) =
+      *reinterpret_cast<u32x4*>(sMu + lane * C::MUS + MB) =
           u32x4{pack_bf16x2(mu[0], mu[1]), pack_bf16x2(mu[2], mu[3]), pack_bf16x2(mu[4], mu[5]),
                 pack_bf16x2(mu[6], mu[7])};
     } else {
@@ -539,8 +542,8 @@ __device__ __attribute__((always_inline)) inline void gen_groups(int part, int n
         return u32x4{__builtin_amdgcn_perm(x[1], x[0], 0x07060302u), __builtin_amdgcn_perm(x[3], x[2], 0x07060302u),
                      __builtin_amdgcn_perm(x[5], x[4], 0x07060302u), __builtin_amdgcn_perm(x[7], x[6], 0x07060302u)};
       };
-      *reinterpret_cast<u32x4*>(sMu + lane * C::MUS + RB) = pk(hb);
-      *reinterpret_cast<u32x4*>(sMu + C::MUPL + lane * C::MUS + RB) = pk(lb);
+      *reinterpret_cast<u32x4*>(sMu + lane * C::MUS + MB) = pk(hb);
+      *reinterpret_cast<u32x4*>(sMu + C::MUPL + lane * C::MUS + MB) = pk(lb);
     }
   });
 }
@@ -1196,7 +1199,13 @@ struct PCfg {
   static constexpr int NSLAB = 1;
   static constexpr int PADE = 8;  // 16-byte row padding (bank spread)
   static constexpr int PHS = WP + PADE;   // phi[token][row]
-  static constexpr int MUS = WP + PADE;   // mu[token][row]
+  // mu[token][row]: when WP = 32 (mod 64) the rows are unpadded and the
+  // 16-byte chunk c of token t is stored at chunk c ^ ((t >> 2) & 3), which
+  // spreads the transposing reads (4 tokens x 4 chunks per 16 lanes) over
+  // more banks while the producers' 16-byte stores stay conflict-free; other
+  // widths keep a 16-byte row padding
+  static constexpr bool MUSWZ = WP % 64 == 32;
+  static constexpr int MUS = MUSWZ ? WP : WP + PADE;
   static constexpr int VS = kDV + PADE;   // V[token][col]
   static constexpr int PS = kCH + PADE;   // P[query][key]
   static constexpr int NMU = OUT ? 1 : 2;
@@ -1458,9 +1467,15 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
       const uint2 a = lds_tr16(p), c = lds_tr16(p + 4 * C::VS * 2);
       return u32x4{a.x, a.y, c.x, c.y};
     };
+    // mu chunk swizzle (PCfg::MUSWZ): token 8*lg + li/4 (+4) of a 32-token
+    // block has (t >> 2) & 3 = 2*(lg & 1) (+1)
+    const int mz0 = C::MUSWZ ? ((2 * lg) & 3) : 0;
+    const int mz1 = C::MUSWZ ? ((2 * lg + 1) & 3) : 0;
     auto load_mu = [&](const unsigned char* Mu, int pl, int j, int tau, int tb) {
-      const unsigned char* p = Mu + (pl * C::MUPL + (tb * 32 + trow) * C::MUS + j * 32 + 8 * (li & 3) + 4 * tau) * 2;
-      const uint2 a = lds_tr16(p), c = lds_tr16(p + 4 * C::MUS * 2);
+      const int ch = 4 * j + (li & 3);
+      const unsigned char* r0 = Mu + (pl * C::MUPL + (tb * 32 + trow) * C::MUS) * 2;
+      const uint2 a = lds_tr16(r0 + ((ch ^ mz0) * 8 + 4 * tau) * 2);
+      const uint2 c = lds_tr16(r0 + 4 * C::MUS * 2 + ((ch ^ mz1) * 8 + 4 * tau) * 2);
       return u32x4{a.x, a.y, c.x, c.y};
     };
     constexpr int NPL = C::OUT ? 1 : 2;     // mu planes: hi only in the output pass, hi + lo in the totals pass

@@ -155,6 +155,55 @@ def test_prefill_then_decode_equals_longer_prefill(dtype):
     assert_states(S.cpu().numpy(), orc.states_definition(k.exact, v.exact, n), dk, n, _tol(dtype))
 
 
+@pytest.mark.parametrize("dk,n", [(16, 3), (32, 2), (16, 4)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_equals_decode_steps_from_zero(dk, n, dtype):
+    """The chunked prefill and N single-token decode steps from zero states
+    are two paths to the same outputs and states (cross-path check); both
+    are held to the parity bar against each other."""
+    import torch
+    B, H, N = 1, 2, 130
+    q, k, v = wl.draw_qkv(41 + dk + n, B, H, N, dk, 64, dtype)
+    Qd, Kd, Vd = to_device(q), to_device(k), to_device(v)
+    O, S = ops.tt_prefill(Qd, Kd, Vd, n)
+    Sd = torch.zeros_like(S)
+    outs = [ops.tt_decode_step(Qd[:, :, t].contiguous(), Kd[:, :, t].contiguous(), Vd[:, :, t].contiguous(), Sd,
+                               n).cpu().numpy() for t in range(N)]
+    torch.cuda.synchronize()
+    O_dec = np.stack(outs, axis=2)
+    assert_out(O.cpu().numpy(), O_dec, _tol(dtype), f"prefill vs decode dk{dk} n{n}")
+    W = orc.state_rows(dk, n)
+    S_dec = orc.planes_to_states(Sd.cpu().numpy().astype(np.float64), B, H, W, 64)
+    assert_states(S.cpu().numpy(), S_dec, dk, n, _tol(dtype), f"prefill vs decode dk{dk} n{n}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_independent_of_span_split(dtype):
+    """Two heads prefilled alone (64 spans of one chunk each) and the same
+    two heads inside a 32-head batch (8 spans of 8 chunks): the split of the
+    sequence into spans changes only the rounding (the states add), so the
+    two results agree to the parity bar, and both match the oracle."""
+    import torch
+    N, dk, n = 4096, 16, 3
+    q, k, v = wl.draw_qkv(43, 1, 2, N, dk, 64, dtype)
+    Qd, Kd, Vd = to_device(q), to_device(k), to_device(v)
+    O1, S1 = ops.tt_prefill(Qd, Kd, Vd, n)
+    rep = lambda X: X.repeat(1, 16, 1, 1).contiguous()
+    O2, S2 = ops.tt_prefill(rep(Qd), rep(Kd), rep(Vd), n)
+    torch.cuda.synchronize()
+    O1, O2 = O1.cpu().numpy(), O2.cpu().numpy()
+    assert_out(O2[:, :2], O1, _tol(dtype), "span split")
+    nf = ops.tt_state_floats(dk, 64, n)
+    W = orc.state_rows(dk, n)
+    S2l = orc.planes_to_states(S2.cpu().numpy().astype(np.float64), 1, 32, W, 64)[:, :2]
+    assert_states(S1.cpu().numpy(), S2l, dk, n, _tol(dtype), "span split")
+    assert nf == W * 65
+    rows = [0, 1, 63, 64, 65, 1000, 2047, 2048, N - 1]
+    ref = np.stack([orc.quadratic_rows(q.exact[0, h, rows], k.exact[0, h], v.exact[0, h], rows, n) for h in range(2)])
+    assert_out(O1[0][:, rows], ref, _tol(dtype), "alone vs oracle")
+    assert_out(O2[0, :2][:, rows], ref, _tol(dtype), "batched vs oracle")
+
+
 def test_prefill_bitwise_repeatable_and_workspace_reuse():
     import torch
     q, k, v = wl.draw_qkv(5, 2, 4, 777, 16, 64, "bf16")

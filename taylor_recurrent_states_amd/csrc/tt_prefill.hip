@@ -855,13 +855,18 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
               bd = u32x4{pack_bf16x2(d0.x, d0.y), pack_bf16x2(d0.z, d0.w), pack_bf16x2(d1.x, d1.y),
                          pack_bf16x2(d1.z, d1.w)};
             }
+            // all four fragments are read before the first MFMA: the normaliser
+            // MFMAs below sit behind wave-uniform branches, which the compiler
+            // does not move loads across
+            u32x4 a[4];
 #pragma unroll
-            for (int qt = 0; qt < 4; ++qt) {
-              const u32x4 a = lds_u32x4((const unsigned char*)sPhi,
-                                        ((qt * 16 + li) * C::PHS + kbl * 32 + 8 * lg) * 2);
-              num[qt] = mfma_bf16(a, b, num[qt]);
-              if (qt % C::NVT == ct) den[qt] = mfma_bf16(a, bd, den[qt]);
-            }
+            for (int qt = 0; qt < 4; ++qt)
+              a[qt] = lds_u32x4((const unsigned char*)sPhi, ((qt * 16 + li) * C::PHS + kbl * 32 + 8 * lg) * 2);
+#pragma unroll
+            for (int qt = 0; qt < 4; ++qt) num[qt] = mfma_bf16(a[qt], b, num[qt]);
+#pragma unroll
+            for (int qt = 0; qt < 4; ++qt)
+              if (qt % C::NVT == ct) den[qt] = mfma_bf16(a[qt], bd, den[qt]);
           } else {
             const f32x4 d = *reinterpret_cast<const f32x4*>(Den + row0 + kbl * 16 + 4 * lg);
 #pragma unroll
@@ -904,21 +909,27 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
         f32x4 dacc[C::TPK];
 #pragma unroll
         for (int t = 0; t < C::TPK; ++t) dacc[t] = zero4();
+        // bf16: every hi/lo fragment of the K-block is read before the first
+        // MFMA (the normaliser MFMAs sit behind a wave-uniform branch)
+        u32x4 mfr[BF ? C::TB : 1][2][2];
+        if constexpr (BF) {
+#pragma unroll
+          for (int tb = 0; tb < C::TB; ++tb)
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+              mfr[tb][tau][0] = mu_frag(0, kbl, tau, tb);
+              mfr[tb][tau][1] = mu_frag(1, kbl, tau, tb);
+            }
+        }
 #pragma unroll
         for (int tb = 0; tb < C::TB; ++tb) {
           if constexpr (BF) {
 #pragma unroll
             for (int tau = 0; tau < 2; ++tau) {
-              const u32x4 ah = mu_frag(0, kbl, tau, tb);
-              const u32x4 al = mu_frag(1, kbl, tau, tb);
 #pragma unroll
               for (int c = 0; c < C::J; ++c) {
-                st[sl * C::J + c][tau] = mfma_bf16(ah, vfr[c][tb], st[sl * C::J + c][tau]);
-                st[sl * C::J + c][tau] = mfma_bf16(al, vfr[c][tb], st[sl * C::J + c][tau]);
-              }
-              if (den_own) {
-                dacc[tau] = mfma_bf16(ah, ones_bf, dacc[tau]);
-                dacc[tau] = mfma_bf16(al, ones_bf, dacc[tau]);
+                st[sl * C::J + c][tau] = mfma_bf16(mfr[tb][tau][0], vfr[c][tb], st[sl * C::J + c][tau]);
+                st[sl * C::J + c][tau] = mfma_bf16(mfr[tb][tau][1], vfr[c][tb], st[sl * C::J + c][tau]);
               }
             }
           } else {
@@ -940,6 +951,17 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
             }
           }
         }
+        if constexpr (BF) {
+          if (den_own) {  // normaliser rows of the K-block from the same fragments
+            constexpr int NPF = (int)(sizeof(mfr[0][0]) / sizeof(mfr[0][0][0]));
+#pragma unroll
+            for (int tb = 0; tb < C::TB; ++tb)
+#pragma unroll
+              for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                for (int pl = 0; pl < NPF; ++pl) dacc[tau] = mfma_bf16(mfr[tb][tau][pl], ones_bf, dacc[tau]);
+          }
+        }
         if (den_own && li == 0) {  // four consecutive normaliser rows per tile: one 16-byte access each way
 #pragma unroll
           for (int tau = 0; tau < C::TPK; ++tau) {
@@ -959,23 +981,29 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
         f32x4 dacc[C::TPK];
 #pragma unroll
         for (int t = 0; t < C::TPK; ++t) dacc[t] = zero4();
+        // bf16: the K-block's fragments (and V^T in the totals pass) are read
+        // before the first MFMA (the normaliser MFMAs sit behind a branch)
+        u32x4 mfr[BF ? C::TB : 1][2][OUT ? 1 : 2];
+        u32x4 bvt[BF ? C::TB : 1];
+        if constexpr (BF) {
+#pragma unroll
+          for (int tb = 0; tb < C::TB; ++tb) {
+            if constexpr (OUT) bvt[tb] = vfr[0][tb];
+            else bvt[tb] = lds_u32x4((const unsigned char*)sV, ((ct * 16 + li) * C::VS + tb * 32 + 8 * lg) * 2);
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+              for (int pl = 0; pl < (OUT ? 1 : 2); ++pl) mfr[tb][tau][pl] = mu_frag(pl, kbl, tau, tb);
+          }
+        }
 #pragma unroll
         for (int tb = 0; tb < C::TB; ++tb) {
           if constexpr (BF) {
-            u32x4 b;
-            if constexpr (OUT) b = vfr[0][tb];
-            else b = lds_u32x4((const unsigned char*)sV, ((ct * 16 + li) * C::VS + tb * 32 + 8 * lg) * 2);
 #pragma unroll
-            for (int tau = 0; tau < 2; ++tau) {
-              const u32x4 ah = mu_frag(0, kbl, tau, tb);
-              st[j][tau % C::TPK] = mfma_bf16(ah, b, st[j][tau % C::TPK]);
-              if (den_own) dacc[tau] = mfma_bf16(ah, ones_bf, dacc[tau]);
-              if constexpr (!OUT) {
-                const u32x4 al = mu_frag(1, kbl, tau, tb);
-                st[j][tau % C::TPK] = mfma_bf16(al, b, st[j][tau % C::TPK]);
-                if (den_own) dacc[tau] = mfma_bf16(al, ones_bf, dacc[tau]);
-              }
-            }
+            for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+              for (int pl = 0; pl < (OUT ? 1 : 2); ++pl)
+                st[j][tau % C::TPK] = mfma_bf16(mfr[tb][tau][pl], bvt[tb], st[j][tau % C::TPK]);
           } else {
             const f32x4 b = lds_f32x4((const unsigned char*)sV, ((ct * 16 + li) * C::VS + tb * 16 + 4 * lg) * 4);
             const f32x4 a = lds_f32x4((const unsigned char*)sMu, ((kbl * 16 + li) * C::MUS + tb * 16 + 4 * lg) * 4);
@@ -989,6 +1017,17 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
               dacc[0] = mfma_f32(a.z, ones_f, dacc[0]);
               dacc[0] = mfma_f32(a.w, ones_f, dacc[0]);
             }
+          }
+        }
+        if constexpr (BF) {
+          if (den_own) {  // normaliser rows of the K-block from the same fragments
+            constexpr int NPF = (int)(sizeof(mfr[0][0]) / sizeof(mfr[0][0][0]));
+#pragma unroll
+            for (int tb = 0; tb < C::TB; ++tb)
+#pragma unroll
+              for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                for (int pl = 0; pl < NPF; ++pl) dacc[tau] = mfma_bf16(mfr[tb][tau][pl], ones_bf, dacc[tau]);
           }
         }
         if (den_own && li == 0) {  // four consecutive normaliser rows per tile: one 16-byte access each way

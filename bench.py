@@ -462,14 +462,14 @@ def cpu_baselines(pre, wl):
         blas_threads = cores
     w = wl.WORKLOADS["prefill"]
     q, k, v = pre["inputs"]
-    # prefill: the quadratic-form definition plus the states, head by head
-    # (batch 0), until about 10 s of host time
+    # prefill: the quadratic-form definition plus the states, head by head,
+    # until about 10 s of host time
     t0 = time.perf_counter()
     heads = 0
-    while heads < w.H and (heads == 0 or time.perf_counter() - t0 < 10.0):
-        orc.quadratic_attention(q.exact[0, heads:heads + 1], k.exact[0, heads:heads + 1], v.exact[0, heads:heads + 1],
-                                w.n)
-        orc.states_definition(k.exact[0, heads:heads + 1], v.exact[0, heads:heads + 1], w.n)
+    while heads < w.B * w.H and (heads == 0 or time.perf_counter() - t0 < 10.0):
+        b, h = divmod(heads, w.H)
+        orc.quadratic_attention(q.exact[b, h:h + 1], k.exact[b, h:h + 1], v.exact[b, h:h + 1], w.n)
+        orc.states_definition(k.exact[b, h:h + 1], v.exact[b, h:h + 1], w.n)
         heads += 1
     t_all = time.perf_counter() - t0
     t_head = t_all / heads

@@ -162,46 +162,62 @@ __global__ void feature_map_kernel(const TIn* __restrict__ x, size_t rows, int W
 }
 
 // Rows [0, rows0) of x0 -> out0 with scale s0, then rows [0, rows1) of x1 ->
-// out1 with scale s1; one thread per row (16-byte loads and stores; out may
-// be x: a row is read whole before it is written).
+// out1 with scale s1.  A row is spread over D/8 consecutive lanes, one group
+// of 8 coordinates each (a 16-byte bf16 or two 16-byte fp32 accesses), so a
+// wave reads and writes contiguous memory.  Each lane sums the squares of its
+// group (group_sumsq), a shfl_xor butterfly over the row's lanes adds the
+// group sums in row_norm_factor's pairwise-tree order, and each lane scales
+// its own coordinates: the bits of normalize_row.  out may be x (every
+// coordinate is read before it is written, by the same lane).
 template <int D, typename TIn>
-__global__ void normalize_kernel(const TIn* x0, TIn* out0, float s0, size_t rows0, const TIn* x1, TIn* out1,
-                                 float s1, size_t rows1) {
-  constexpr int EPS = 16 / (int)sizeof(TIn);  // elements per 16-byte segment
-  constexpr int NSEG = D / EPS;
-  for (size_t r = (size_t)blockIdx.x * blockDim.x + threadIdx.x; r < rows0 + rows1;
-       r += (size_t)gridDim.x * blockDim.x) {
+__global__ __launch_bounds__(256) void normalize_kernel(const TIn* x0, TIn* out0, float s0, size_t rows0,
+                                                        const TIn* x1, TIn* out1, float s1, size_t rows1) {
+  constexpr int G = D / 8;                      // lanes per row
+  constexpr int NV = 8 * sizeof(TIn) / 16;      // 16-byte pieces per group
+  const size_t total = (rows0 + rows1) * G;     // one item per (row, group)
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  // every lane of a wave runs the same number of iterations (the butterfly
+  // needs the whole row's lanes): items past the end are computed on row 0
+  // of x0 and not stored
+  const size_t iters = (total + stride - 1) / stride;
+  for (size_t it = 0; it < iters; ++it) {
+    const size_t item = it * stride + (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool live = item < total;
+    const size_t r = live ? item / G : 0;
+    const int g = (int)(item % G);
     const bool first = r < rows0;
     const size_t row = first ? r : r - rows0;
-    const u32x4* src = reinterpret_cast<const u32x4*>((first ? x0 : x1) + row * D);
-    u32x4 seg[NSEG];
+    const u32x4* src = reinterpret_cast<const u32x4*>((first ? x0 : x1) + row * D + 8 * g);
+    u32x4 seg[NV];
 #pragma unroll
-    for (int i = 0; i < NSEG; ++i) seg[i] = src[i];
-    float x[D];
+    for (int i = 0; i < NV; ++i) seg[i] = src[i];
+    float x[8];
 #pragma unroll
-    for (int i = 0; i < NSEG; ++i)
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (sizeof(TIn) == 2)
+        x[e] = bf16_to_f32((uint16_t)((seg[0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
+      else
+        x[e] = __uint_as_float(seg[e >> 2][e & 3]);
+    }
+    float ss = group_sumsq([&](int i) { return x[i & 7]; }, g);
 #pragma unroll
-      for (int e = 0; e < EPS; ++e) {
-        if constexpr (sizeof(TIn) == 2)
-          x[i * EPS + e] = bf16_to_f32((uint16_t)((seg[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
-        else
-          x[i * EPS + e] = __uint_as_float(seg[i][e]);
-      }
-    normalize_row<TIn, D>(x, first ? s0 : s1);
+    for (int o = 1; o < G; o *= 2) ss = ss + __shfl_xor(ss, o);
+    const float f = (first ? s0 : s1) / sqrtf(ss);
+    if (live) {
 #pragma unroll
-    for (int i = 0; i < NSEG; ++i) {
+      for (int e = 0; e < 8; ++e) x[e] = unit_coord<TIn>(x[e], f);
       if constexpr (sizeof(TIn) == 2) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          seg[i][e] = (uint32_t)f32_to_bf16(x[i * 8 + 2 * e]) | ((uint32_t)f32_to_bf16(x[i * 8 + 2 * e + 1]) << 16);
+          seg[0][e] = (uint32_t)f32_to_bf16(x[2 * e]) | ((uint32_t)f32_to_bf16(x[2 * e + 1]) << 16);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) seg[i][e] = __float_as_uint(x[i * 4 + e]);
+        for (int e = 0; e < 8; ++e) seg[e >> 2][e & 3] = __float_as_uint(x[e]);
       }
-    }
-    u32x4* dst = reinterpret_cast<u32x4*>((first ? out0 : out1) + row * D);
+      u32x4* dst = reinterpret_cast<u32x4*>((first ? out0 : out1) + row * D + 8 * g);
 #pragma unroll
-    for (int i = 0; i < NSEG; ++i) dst[i] = seg[i];
+      for (int i = 0; i < NV; ++i) dst[i] = seg[i];
+    }
   }
 }
 
@@ -256,7 +272,7 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, tt_dtype d
 hipError_t launch_normalize(tt_dtype dt, int d, const void* x0, void* out0, float s0, size_t rows0,
                             const void* x1, void* out1, float s1, size_t rows1, hipStream_t s) {
   const unsigned block = 256;
-  const unsigned grid = grid_for(rows0 + rows1, block);
+  const unsigned grid = grid_for((rows0 + rows1) * (size_t)(d / 8), block);
 #define TT_NORM(D, T)                                                                                     \
   hipLaunchKernelGGL((normalize_kernel<D, T>), dim3(grid), dim3(block), 0, s, (const T*)x0, (T*)out0, s0, \
                      rows0, (const T*)x1, (T*)out1, s1, rows1)

@@ -513,8 +513,9 @@ def main():
                          "to scale the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the hot path has no multi-GPU code (see DESIGN.md, "
-              "'How the path would shard'); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU and the hot path has no multi-GPU code; run with --gpus 1. "
+              "(Heads shard with no exchange; sequence segments would exchange one state set per GPU, "
+              "because the states add.)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -20,7 +20,7 @@ Sources (page titles as published):
 Notation: d = key/query width, e = value width, n = number of Taylor terms
 (orders m = 0 .. n-1), W = sum_m C(d+m-1, m) feature rows.
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
 
 * no temperature inside the exponential: the kernel is K_n(q.k) on inputs
   the caller has already L2-normalised; the optional normalised path

@@ -440,7 +440,7 @@ def bench_decode(args, torch, ops, wl):
         "us_per_step": t_step * 1e6, "us_per_step_mall_cold": t_cold * 1e6, "steps": T,
         "us_per_step_normed": round(t_normed * 1e6, 3),
         "workload": w.name,
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel<16,3,float>", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel<16,3,float,false>", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "achieved_mall_cold": round(alg_bytes / t_cold / 1e9, 1),
                      "frac_mall_cold": round(alg_bytes / t_cold / 1e9 / HBM_PEAK_GBS, 4),

@@ -140,6 +140,16 @@ __device__ inline void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
   lo = f32_to_bf16(x - bf16_to_f32(hi));
 }
 
+// split_bf16 of two values at once, packed (a in bits 0..15): the same bits,
+// with one conversion per plane instead of one per value.
+__device__ inline void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
+}
+
+// 1/x by the hardware reciprocal (v_rcp_f32: within 1 ulp for normal x).
+__device__ inline float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
 // ---------------------------------------------------------------------------
 // L2 normalisation of one q or k row ("Expanding Attention", abstract: unit
 // q and k keep q.k inside the series' convergence radius; a temperature is

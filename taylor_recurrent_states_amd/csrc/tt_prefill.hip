@@ -794,11 +794,9 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
         }
         const int kbase = BF ? kb * 32 + 8 * lg + 4 * tau : kb * 16 + 4 * lg;
         if constexpr (BF) {
-          uint16_t h0, l0, h1, l1, h2, l2, h3, l3;
-          split_bf16(p[0], h0, l0); split_bf16(p[1], h1, l1);
-          split_bf16(p[2], h2, l2); split_bf16(p[3], h3, l3);
-          uint2 hi = {(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)};
-          uint2 lo = {(uint32_t)l0 | ((uint32_t)l1 << 16), (uint32_t)l2 | ((uint32_t)l3 << 16)};
+          uint2 hi, lo;
+          split_bf16x2(p[0], p[1], hi.x, lo.x);
+          split_bf16x2(p[2], p[3], hi.y, lo.y);
           *reinterpret_cast<uint2*>(&sP[query * C::PS + kbase]) = hi;
           *reinterpret_cast<uint2*>(&sP[C::PPL + query * C::PS + kbase]) = lo;
         } else {
@@ -1128,7 +1126,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
           if (li == 0) {
             if constexpr (C::NRG == 1) {
 #pragma unroll
-              for (int s = 0; s < 4; ++s) sDenQ[qt * 16 + 4 * lg + s] = 1.0f / (den[qt][s] + den0);
+              for (int s = 0; s < 4; ++s) sDenQ[qt * 16 + 4 * lg + s] = rcp_fast(den[qt][s] + den0);
             } else {
 #pragma unroll
               for (int s = 0; s < 4; ++s)
@@ -1387,13 +1385,11 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
           pr[s] = (key <= query && key < nvalid) ? taylor_poly<C::NT>(x[s]) : 0.f;
         }
         const int kbase = kb * 32 + 8 * lg + 4 * tau;
-        uint16_t h0, l0, h1, l1, h2, l2, h3, l3;
-        split_bf16(pr[0], h0, l0); split_bf16(pr[1], h1, l1);
-        split_bf16(pr[2], h2, l2); split_bf16(pr[3], h3, l3);
-        *reinterpret_cast<uint2*>(&P[query * C::PS + kbase]) =
-            uint2{(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)};
-        *reinterpret_cast<uint2*>(&P[C::PPL + query * C::PS + kbase]) =
-            uint2{(uint32_t)l0 | ((uint32_t)l1 << 16), (uint32_t)l2 | ((uint32_t)l3 << 16)};
+        uint2 hi, lo;
+        split_bf16x2(pr[0], pr[1], hi.x, lo.x);
+        split_bf16x2(pr[2], pr[3], hi.y, lo.y);
+        *reinterpret_cast<uint2*>(&P[query * C::PS + kbase]) = hi;
+        *reinterpret_cast<uint2*>(&P[C::PPL + query * C::PS + kbase]) = lo;
       }
     }
     // features: lane = token, this producer takes 8-row groups g == pw (mod 4).
@@ -1639,7 +1635,7 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
         }
         if (li == 0) {
 #pragma unroll
-          for (int s = 0; s < 4; ++s) sRden[b * kCH + (4 * lg + s) * 4 + ct] = 1.0f / (den[s] + den0);
+          for (int s = 0; s < 4; ++s) sRden[b * kCH + (4 * lg + s) * 4 + ct] = rcp_fast(den[s] + den0);
         }
         // previous chunk: normalise and store (16 bytes per lane and query tile)
         if (ci > 0) {

@@ -217,16 +217,14 @@ __global__ __launch_bounds__(256) void softmax_prefill_kernel(const uint16_t* __
         for (int s = 0; s < 4; ++s) p[4 * tau + s] = __builtin_amdgcn_exp2f(sc[hb][tau][s] - m);
       u32x4 ph, pl;
       if (diag) {
-        uint16_t h[8], lo[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          split_bf16(p[e], h[e], lo[e]);
-          l += bf16_to_f32(h[e]) + bf16_to_f32(lo[e]);
-        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          ph[e] = (uint32_t)h[2 * e] | ((uint32_t)h[2 * e + 1] << 16);
-          pl[e] = (uint32_t)lo[2 * e] | ((uint32_t)lo[2 * e + 1] << 16);
+          uint32_t h2, l2;
+          split_bf16x2(p[2 * e], p[2 * e + 1], h2, l2);
+          ph[e] = h2;
+          pl[e] = l2;
+          l += __uint_as_float(h2 << 16) + __uint_as_float(l2 << 16);
+          l += __uint_as_float(h2 & 0xFFFF0000u) + __uint_as_float(l2 & 0xFFFF0000u);
         }
       } else {
 #pragma unroll

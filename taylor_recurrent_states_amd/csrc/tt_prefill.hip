@@ -1315,11 +1315,8 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
     const int c0 = t_begin + ci * kCH;
     const int tl = t_end - 1;
     const size_t row = (size_t)min(c0 + lane, tl);
-#pragma unroll
-    for (int i = 0; i < C::QV; ++i) {
-      pk[i] = *reinterpret_cast<const u32x4*>(Kh + row * C::DK + 8 * i);
-      if constexpr (OUT) pq[i] = *reinterpret_cast<const u32x4*>(Qh + row * C::DK + 8 * i);
-    }
+    // issued in the order p_build consumes them (loads complete in order):
+    // V, the operands of P, then the key and query rows
 #pragma unroll
     for (int i = 0; i < 2; ++i) {  // V segments: (column group, token), lanes walk tokens
       const int seg = pw * 64 + lane + i * 256;
@@ -1346,6 +1343,11 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
           }
         }
       }
+    }
+#pragma unroll
+    for (int i = 0; i < C::QV; ++i) {
+      pk[i] = *reinterpret_cast<const u32x4*>(Kh + row * C::DK + 8 * i);
+      if constexpr (OUT) pq[i] = *reinterpret_cast<const u32x4*>(Qh + row * C::DK + 8 * i);
     }
   };
   auto p_build = [&](int ci, const Stage& sg) {  // registers -> LDS buffer (ci & 1): V, P, phi, mu

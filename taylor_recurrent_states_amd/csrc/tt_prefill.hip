@@ -1506,22 +1506,25 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
     };
     // mu chunk swizzle (PCfg::MUSWZ): token 8*lg + li/4 (+4) of a 32-token
     // block has (t >> 2) & 3 = 2*(lg & 1) (+1)
-    const int mz0 = C::MUSWZ ? ((2 * lg) & 3) : 0;
-    const int mz1 = C::MUSWZ ? ((2 * lg + 1) & 3) : 0;
+    // (4j + c) ^ z = 4j + (c ^ z) for z < 4: the K-block part of the address
+    // stays a compile-time offset
+    const int cz0 = (li & 3) ^ (C::MUSWZ ? ((2 * lg) & 3) : 0);
+    const int cz1 = (li & 3) ^ (C::MUSWZ ? ((2 * lg + 1) & 3) : 0);
     auto load_mu = [&](const unsigned char* Mu, int pl, int j, int tau, int tb) {
-      const int ch = 4 * j + (li & 3);
-      const unsigned char* r0 = Mu + (pl * C::MUPL + (tb * 32 + trow) * C::MUS) * 2;
-      const uint2 a = lds_tr16(r0 + ((ch ^ mz0) * 8 + 4 * tau) * 2);
-      const uint2 c = lds_tr16(r0 + 4 * C::MUS * 2 + ((ch ^ mz1) * 8 + 4 * tau) * 2);
+      const unsigned char* r0 = Mu + (pl * C::MUPL + (tb * 32 + trow) * C::MUS + 32 * j + 4 * tau) * 2;
+      const uint2 a = lds_tr16(r0 + cz0 * 16);
+      const uint2 c = lds_tr16(r0 + 4 * C::MUS * 2 + cz1 * 16);
       return u32x4{a.x, a.y, c.x, c.y};
     };
     constexpr int NPL = C::OUT ? 1 : 2;     // mu planes: hi only in the output pass, hi + lo in the totals pass
-    for (int ci = 0; ci < nch2; ++ci) {
+    // one chunk step; the LDS buffer index is a compile-time constant (the
+    // loop below is unrolled by two), so LDS addresses are immediates
+    auto chunk_step = [&](const int ci, auto bc) {
+      constexpr int b = decltype(bc)::value;
       if (ci >= nch) {  // padding step
         lds_barrier();
-        continue;
+        return;
       }
-      const int b = ci & 1;
       const int c0 = t_begin + ci * kCH;
       const unsigned char* V = (const unsigned char*)sV(b);
       const unsigned char* Mu = (const unsigned char*)sMu(b);
@@ -1709,6 +1712,10 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
       }
       if constexpr (OUT) publish_den(b ^ 1);
       lds_barrier();
+    };
+    for (int ci = 0; ci < nch2; ci += 2) {
+      chunk_step(ci, std::integral_constant<int, 0>{});
+      chunk_step(ci + 1, std::integral_constant<int, 1>{});
     }
     if constexpr (OUT) {
       // last chunk: normalise and store

@@ -497,8 +497,18 @@ __device__ __attribute__((always_inline)) inline void gen_groups(int part, int n
       return p;
     }
   };
-  // chunk swizzle of the token-major mu tile (PCfg::MUSWZ)
+  // chunk swizzle and row shift of the token-major mu tile (PCfg::MUSWZ,
+  // PCfg::MUSH): 16-byte chunks go out as two 8-byte halves
   const int mswz = C::MUSWZ ? ((lane >> 2) & 3) : 0;
+  typename C::Elem* muRow = sMu + lane * C::MUS + C::MUSH * (lane >> 3);
+  auto st_mu = [&](typename C::Elem* dst, u32x4 v) {
+    if constexpr (C::MUSWZ) {
+      reinterpret_cast<uint2*>(dst)[0] = uint2{v.x, v.y};
+      reinterpret_cast<uint2*>(dst)[1] = uint2{v.z, v.w};
+    } else {
+      *reinterpret_cast<u32x4*>(dst) = v;
+    }
+  };
   static_for<0, NG>([&](auto gc) {
     constexpr int GI = decltype(gc)::value;
     if (GI % nparts != part) return;
@@ -524,9 +534,8 @@ __device__ __attribute__((always_inline)) inline void gen_groups(int part, int n
       *reinterpret_cast<u32x4*>(sPhi + lane * C::PHS + RB) = pk;
     }
     if constexpr (C::OUT) {
-      *reinterpret_cast<u32x4*>(sMu + lane * C::MUS + MB) =
-          u32x4{pack_bf16x2(mu[0], mu[1]), pack_bf16x2(mu[2], mu[3]), pack_bf16x2(mu[4], mu[5]),
-                pack_bf16x2(mu[6], mu[7])};
+      st_mu(muRow + MB, u32x4{pack_bf16x2(mu[0], mu[1]), pack_bf16x2(mu[2], mu[3]), pack_bf16x2(mu[4], mu[5]),
+                              pack_bf16x2(mu[6], mu[7])});
     } else {
       // exact split: rows are products of at most two bf16 values (n <= 3 here),
       // so mu has at most 16 significant bits; hi = mu truncated to bf16 and
@@ -542,8 +551,8 @@ __device__ __attribute__((always_inline)) inline void gen_groups(int part, int n
         return u32x4{__builtin_amdgcn_perm(x[1], x[0], 0x07060302u), __builtin_amdgcn_perm(x[3], x[2], 0x07060302u),
                      __builtin_amdgcn_perm(x[5], x[4], 0x07060302u), __builtin_amdgcn_perm(x[7], x[6], 0x07060302u)};
       };
-      *reinterpret_cast<u32x4*>(sMu + lane * C::MUS + MB) = pk(hb);
-      *reinterpret_cast<u32x4*>(sMu + C::MUPL + lane * C::MUS + MB) = pk(lb);
+      st_mu(muRow + MB, pk(hb));
+      st_mu(muRow + C::MUPL + MB, pk(lb));
     }
   });
 }
@@ -1243,10 +1252,18 @@ struct PCfg {
   // widths keep a 16-byte row padding
   static constexpr bool MUSWZ = WP % 64 == 32;
   static constexpr int MUS = MUSWZ ? WP : WP + PADE;
+  // with the swizzle, each block of 8 tokens also starts 8 bytes (MUSH = 4
+  // elements) after the end of the previous one: token t's row begins at
+  // t * MUS + MUSH * (t >> 3). The 32 lanes of a transposing read (tokens
+  // 0-3 and 8-11 of a 16-token group, the same chunks and the same half)
+  // then fall on opposite halves of each 16-byte bank group. Rows are stored
+  // as 8-byte-aligned pairs; each plane ends with 32 elements of slack.
+  static constexpr int MUSH = MUSWZ ? 4 : 0;
   static constexpr int VS = kDV + PADE;   // V[token][col]
   static constexpr int PS = kCH + PADE;   // P[query][key]
   static constexpr int NMU = OUT ? 1 : 2;
-  static constexpr int MUPL = kCH * MUS;
+  static constexpr int MUPL = kCH * MUS + (MUSWZ ? 32 : 0);
+  static_assert(!MUSWZ || MUSH * (kCH / 8 - 1) <= 32 - 4, "row shift slack");
   static constexpr int PPL = kCH * PS;
   static constexpr int al(int b) { return (b + 15) / 16 * 16; }
   // one buffer of each kind; two of each are allocated
@@ -1511,7 +1528,9 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
     const int cz0 = (li & 3) ^ (C::MUSWZ ? ((2 * lg) & 3) : 0);
     const int cz1 = (li & 3) ^ (C::MUSWZ ? ((2 * lg + 1) & 3) : 0);
     auto load_mu = [&](const unsigned char* Mu, int pl, int j, int tau, int tb) {
-      const unsigned char* r0 = Mu + (pl * C::MUPL + (tb * 32 + trow) * C::MUS + 32 * j + 4 * tau) * 2;
+      // token tb * 32 + trow (+4) lies in 8-token block 4 * tb + lg
+      const unsigned char* r0 =
+          Mu + (pl * C::MUPL + (tb * 32 + trow) * C::MUS + C::MUSH * (4 * tb + lg) + 32 * j + 4 * tau) * 2;
       const uint2 a = lds_tr16(r0 + cz0 * 16);
       const uint2 c = lds_tr16(r0 + 4 * C::MUS * 2 + cz1 * 16);
       return u32x4{a.x, a.y, c.x, c.y};
@@ -1569,13 +1588,12 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
         f32x4 num[4], den = zero4();
 #pragma unroll
         for (int q = 0; q < 4; ++q) num[q] = zero4();
-        // normaliser fragments of every K-block: the same normaliser rows in
-        // every column of the B tile, so every column of the product holds
-        // the readout (lanes li == 0 use it)
-        u32x4 bdn[C::NKB];
-#pragma unroll
-        for (int j = 0; j < C::NKB; ++j)
-          bdn[j] = *reinterpret_cast<const u32x4*>(sDenB + b * C::WP + j * 32 + 8 * lg);
+        // normaliser fragment of K-block j: the same normaliser rows in every
+        // column of the B tile, so every column of the product holds the
+        // readout (lanes li == 0 use it); fetched one K-block ahead
+        auto load_bdn = [&](int j) { return *reinterpret_cast<const u32x4*>(sDenB + b * C::WP + j * 32 + 8 * lg); };
+        u32x4 bdn[2];
+        bdn[0] = load_bdn(0);
         const float den0 = sDen0[b];
         // m = 0 row (fp32): S[0][col] for this lane's four columns
         f32x4 m0;
@@ -1595,7 +1613,10 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
 #pragma unroll
         for (int j = 0; j < C::NKB; ++j) {
           if (j + 2 < C::NKB) load_phi(j + 2, af[(j + 2) % 3]);
-          if (j + 1 < C::NKB) fetch_mu(j + 1, mf[(j + 1) & 1]);
+          if (j + 1 < C::NKB) {
+            fetch_mu(j + 1, mf[(j + 1) & 1]);
+            bdn[(j + 1) & 1] = load_bdn(j + 1);
+          }
           u32x4 bs;  // S[rows 8lg..8lg+7 of K-block j][column ct*16 + li], as the A operand (S^T)
           bs.x = pack_bf16x2(st[j][0].x, st[j][0].y);
           bs.y = pack_bf16x2(st[j][0].z, st[j][0].w);
@@ -1606,10 +1627,10 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
           // normaliser readout of this wave's query tile: ct is wave-uniform,
           // so this is a scalar branch to one of four MFMAs (no operand select)
           switch (ct) {
-            case 0: den = mfma_bf16(af[j % 3][0], bdn[j], den); break;
-            case 1: den = mfma_bf16(af[j % 3][1], bdn[j], den); break;
-            case 2: den = mfma_bf16(af[j % 3][2], bdn[j], den); break;
-            default: den = mfma_bf16(af[j % 3][3], bdn[j], den); break;
+            case 0: den = mfma_bf16(af[j % 3][0], bdn[j & 1], den); break;
+            case 1: den = mfma_bf16(af[j % 3][1], bdn[j & 1], den); break;
+            case 2: den = mfma_bf16(af[j % 3][2], bdn[j & 1], den); break;
+            default: den = mfma_bf16(af[j % 3][3], bdn[j & 1], den); break;
           }
           update_block(j, mf[j & 1]);
         }

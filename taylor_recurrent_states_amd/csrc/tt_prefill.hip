@@ -1221,8 +1221,9 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
 // Outputs are normalised one chunk late, once all four consumers have
 // published 1/den.
 //
-// Every LDS tile is written token-major with 16-byte stores (V as loaded,
-// mu and phi as generated); operands whose contraction index is the token
+// Every LDS tile is written token-major, 16 bytes per lane and store (V as
+// loaded, mu and phi as generated; a shifted mu row goes out as two 8-byte
+// halves in one instruction); operands whose contraction index is the token
 // (V, mu^T) are read back with transposing LDS reads.  The readout and P.V
 // produce O^T tiles (value columns x queries), so each lane ends up with four
 // consecutive columns of one query and stores them as one 16-byte write.
@@ -1247,9 +1248,8 @@ struct PCfg {
   static constexpr int PHS = WP + PADE;   // phi[token][row]
   // mu[token][row]: when WP = 32 (mod 64) the rows are unpadded and the
   // 16-byte chunk c of token t is stored at chunk c ^ ((t >> 2) & 3), which
-  // spreads the transposing reads (4 tokens x 4 chunks per 16 lanes) over
-  // more banks while the producers' 16-byte stores stay conflict-free; other
-  // widths keep a 16-byte row padding
+  // spreads each 16-lane group of a transposing read (4 tokens x 4 chunks)
+  // over all 16-byte bank groups; other widths keep a 16-byte row padding
   static constexpr bool MUSWZ = WP % 64 == 32;
   static constexpr int MUS = MUSWZ ? WP : WP + PADE;
   // with the swizzle, each block of 8 tokens also starts 8 bytes (MUSH = 4

@@ -7,6 +7,8 @@ compared element by element against the quadratic form; the full-size
 workloads compare every state element and sampled output rows (the oracle
 evaluates those rows one by one from the definition).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -62,15 +64,18 @@ def test_tiny_workload():
 
 def _sample_rows(N, rng, extra=24):
     base = {0, 1, 2, 31, 32, 63, 64, 65, 127, 128, N // 2, N // 2 + 1, N - 65, N - 64, N - 2, N - 1}
+    # both sides of every multiple of 512 tokens: the span boundaries of the
+    # full-size plans (spans of 512 or 1024 tokens)
+    base |= {r for m in range(512, N, 512) for r in (m - 1, m)}
     base |= set(int(x) for x in rng.integers(0, N, extra))
     return sorted(r for r in base if 0 <= r < N)
 
 
-def _full_workload(name, heads_checked=None, state_heads=None):
-    """Run the named workload at full size; compare sampled output rows of
-    ``heads_checked`` (default: all heads) and every state element of
+def _full_workload(name, heads_checked=None, state_heads=None, w=None):
+    """Run the named workload (or ``w``) at full size; compare sampled output
+    rows of ``heads_checked`` (default: all heads) and every state element of
     ``state_heads`` (default: the same heads) against the oracle."""
-    w = wl.WORKLOADS[name]
+    w = wl.WORKLOADS[name] if w is None else w
     print(f"\n[{name}] drawing inputs", flush=True)
     q, k, v = wl.draw_qkv(w.seed, w.B, w.H, w.N, w.dk, w.dv, w.dtype)
     O, S = _prefill(q, k, v, w.n)
@@ -104,6 +109,18 @@ def _full_workload(name, heads_checked=None, state_heads=None):
 def test_prefill_workload_full_size():
     """B=4, H=8, N=8192, dk=16, n=3, bf16: every state element, sampled rows of every head."""
     _full_workload("prefill")
+
+
+@pytest.mark.parametrize("B,H,N", [(4, 8, 8155), (2, 8, 8129)])
+def test_prefill_workload_ragged_length(B, H, N):
+    """The prefill workload's shape with a length that ends inside a chunk.
+    With B*H = 32 the plan has 8 spans of 1024 tokens and the last one ends
+    27 tokens into its final chunk; with B*H = 16 it has 16 spans of 512 and
+    the last ends 1 token into its final chunk.  Sampled rows of every head
+    (span boundaries and the ragged tail included), every state element of
+    8 heads."""
+    w = dataclasses.replace(wl.WORKLOADS["prefill"], name=f"prefill B{B} H{H} N{N}", B=B, H=H, N=N, seed=11)
+    _full_workload(w.name, state_heads=range(0, B * H, B * H // 8), w=w)
 
 
 def test_order5_workload_full_size():

@@ -1441,7 +1441,6 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
   const int ct = pw;
   const u32x4 ones_bf = (li == 0) ? u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}
                                   : u32x4{0u, 0u, 0u, 0u};
-  const u32x4 ones_all = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
   // Producer and consumer waves run separate loops with the same number of
   // workgroup barriers (one per chunk, plus one after the prologue), so their
@@ -1652,8 +1651,9 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
               num[qt] = mfma_bf16(bvk[kb], ph[qt][kb], num[qt]);
               num[qt] = mfma_bf16(bvk[kb], pl[qt][kb], num[qt]);
               if (qt == ct) {
-                den = mfma_bf16(ph[qt][kb], ones_all, den);
-                den = mfma_bf16(pl[qt][kb], ones_all, den);
+                // column 0 of the product holds P.1 (only lanes li == 0 read den)
+                den = mfma_bf16(ph[qt][kb], ones_bf, den);
+                den = mfma_bf16(pl[qt][kb], ones_bf, den);
               }
             }
           }

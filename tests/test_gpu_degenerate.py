@@ -1,0 +1,111 @@
+"""GPU parity on the method's degenerate inputs, against closed forms.
+
+Under the truncated kernel K_n(x) = sum_{m<n} x^m / m! (the n-term Taylor
+series that replaces exp; "Expanding Attention: A Taylor-Series Route to
+Linear-Time Transformers with a Fixed Number of Recurrent States", abstract),
+a causal output is the weighted mean of the values with weights
+K_n(q_t . k_j), j <= t.  Two inputs fix every weight of a query to one value,
+so the output is the running mean of the values whatever q and n:
+
+- identical keys: every weight of query t is K_n(q_t . k);
+- queries orthogonal to every key: every weight is K_n(0) = 1 (only the
+  order-0 term survives, so this also checks that row in isolation).
+
+Zero values give outputs that are exactly zero, and states whose value plane
+is exactly zero.  The outputs are compared with these closed forms (fp64 over
+the rounded inputs); the states with the oracle's state definition.
+"""
+import numpy as np
+import pytest
+
+import oracle.taylor_oracle as orc
+from gpu_util import assert_out, assert_states
+from taylor_recurrent_states_amd import ops
+
+pytestmark = pytest.mark.gpu
+
+# pipe_kernel shapes (bf16 rows <= 256) and sweep_kernel shapes (fp32, or more rows)
+SHAPES = [(16, 2), (16, 3), (32, 2), (64, 2), (16, 5)]
+
+
+def _tol(dtype):
+    return ("rel", 1e-5) if dtype == "f32" else ("abs", 5e-3)
+
+
+def _dev(x64, dtype):
+    """fp64 array -> (device tensor in the working dtype, its exact values in fp64)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x64, dtype=np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.cuda(), t.to(torch.float64).numpy()
+
+
+def _unit(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def _running_mean(v):
+    """[..., N, dv] -> mean of v[..., :t+1, :] for every t (fp64)."""
+    N = v.shape[-2]
+    return np.cumsum(v, axis=-2) / np.arange(1, N + 1, dtype=np.float64)[:, None]
+
+
+@pytest.mark.parametrize("dk,n", SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_identical_keys_give_the_running_mean(dk, n, dtype):
+    """All keys of a head equal: outputs are the running mean of v, through a
+    multi-span prefill (B*H = 2: spans of one chunk) and then decode steps
+    with the same key."""
+    import torch
+    B, H, N, extra, dv = 1, 2, 300, 4, 64
+    rng = np.random.default_rng(1000 + 10 * dk + n)
+    key = _unit(rng.standard_normal((B, H, 1, dk)))
+    q, qx = _dev(_unit(rng.standard_normal((B, H, N + extra, dk))), dtype)
+    k, kx = _dev(np.broadcast_to(key, (B, H, N + extra, dk)), dtype)
+    v, vx = _dev(rng.standard_normal((B, H, N + extra, dv)), dtype)
+    O, S = ops.tt_prefill(q[:, :, :N].contiguous(), k[:, :, :N].contiguous(), v[:, :, :N].contiguous(), n)
+    outs = [ops.tt_decode_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(), S, n)
+            for t in range(N, N + extra)]
+    torch.cuda.synchronize()
+    ref = _running_mean(vx)
+    assert_out(O.cpu().numpy(), ref[:, :, :N], _tol(dtype), f"identical keys dk{dk} n{n} prefill")
+    assert_out(torch.stack(outs, dim=2).cpu().numpy(), ref[:, :, N:], _tol(dtype), f"identical keys dk{dk} n{n} decode")
+    assert_states(S.cpu().numpy(), orc.states_definition(kx, vx, n), dk, n, _tol(dtype), "identical keys")
+
+
+@pytest.mark.parametrize("dk,n", SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_queries_orthogonal_to_keys_give_the_running_mean(dk, n, dtype):
+    """q = e_0 and k = e_1 for every token: every weight is K_n(0) = 1."""
+    import torch
+    B, H, N, dv = 1, 2, 200, 64
+    rng = np.random.default_rng(2000 + 10 * dk + n)
+    e = np.eye(dk)
+    q, _ = _dev(np.broadcast_to(e[0], (B, H, N, dk)), dtype)
+    k, kx = _dev(np.broadcast_to(e[1], (B, H, N, dk)), dtype)
+    v, vx = _dev(rng.standard_normal((B, H, N, dv)), dtype)
+    O, S = ops.tt_prefill(q, k, v, n)
+    torch.cuda.synchronize()
+    assert_out(O.cpu().numpy(), _running_mean(vx), _tol(dtype), f"orthogonal dk{dk} n{n}")
+    assert_states(S.cpu().numpy(), orc.states_definition(kx, vx, n), dk, n, _tol(dtype), "orthogonal")
+
+
+@pytest.mark.parametrize("dk,n", [(16, 3), (64, 2), (16, 5)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_values_give_zero_outputs(dk, n, dtype):
+    """v = 0: every output and every value-plane state element is exactly 0;
+    the normaliser plane still holds the sum of mu(k) (oracle)."""
+    import torch
+    B, H, N, dv = 1, 2, 130, 64
+    rng = np.random.default_rng(3000 + 10 * dk + n)
+    q, _ = _dev(_unit(rng.standard_normal((B, H, N, dk))), dtype)
+    k, kx = _dev(_unit(rng.standard_normal((B, H, N, dk))), dtype)
+    v, vx = _dev(np.zeros((B, H, N, dv)), dtype)
+    O, S = ops.tt_prefill(q, k, v, n)
+    torch.cuda.synchronize()
+    assert not O.abs().max().item(), "outputs of zero values must be exactly zero"
+    W = ops.tt_state_rows(dk, n)
+    flat = S.cpu().numpy()
+    assert not np.abs(flat[:B * H * W * dv]).max(), "value plane must be exactly zero"
+    assert_states(flat, orc.states_definition(kx, vx, n), dk, n, _tol(dtype), "zero values")

@@ -116,6 +116,27 @@ int tt_prefill_from(const void *Q, const void *K, const void *V, tt_dtype in_dty
                     const float *states_in, float *O, float *states,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* tt_prefill_from without the final division: for each query the numerator
+ * and the normaliser of the expression above are returned separately,
+ *   num_i = phi(q_i).S_in[:, :dv] + sum_{j<=i} K_n(q_i.k_j) v_j
+ *   den_i = phi(q_i).S_in[:, dv]  + sum_{j<=i} K_n(q_i.k_j)
+ * so that results computed over separate segments can still be combined
+ * (num and den add across key segments; o_i = num_i / den_i), the step
+ * that context-parallel prefill needs ("Expanding Attention", abstract: the
+ * states add across segments).  Arguments as for tt_prefill_from, with
+ *   states_in : may be NULL (zero states, as tt_prefill);
+ *   num       : [B][H][N][dv] fp32, device, 16-byte aligned (in place of O);
+ *   den       : [B][H][N] fp32, device, 4-byte aligned; NULL is
+ *               TT_ERR_INVALID_ARG; it must not overlap num, the states,
+ *               states_in or the workspace (TT_ERR_INVALID_ARG).
+ * The numerators and normalisers are those the normalised call divides
+ * (its O is num * (1/den) with the hardware reciprocal); the states are the
+ * same.  Uses the same workspace size as tt_prefill. */
+int tt_prefill_from_unnormalized(const void *Q, const void *K, const void *V, tt_dtype in_dtype,
+                                 int B, int H, int N, int dk, int dv, int n, int chunk,
+                                 const float *states_in, float *num, float *den, float *states,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
 /* L2 normalisation of q and k with an optional temperature, the input-side
  * prerequisite of the method ("Expanding Attention", abstract: unit q and k
  * keep q.k inside the series' convergence radius, and without it more terms

@@ -320,17 +320,19 @@ def decode_step(q, k, v, S, n: int) -> Tuple[np.ndarray, np.ndarray]:
     return num / den[..., None], S_new
 
 
-def prefill_from_states(Q, K, V, S0, n: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Prefill of new tokens that continues from the states S0 of earlier ones.
+def prefill_from_numden(Q, K, V, S0, n: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Numerator and normaliser of a prefill that continues from states S0.
 
-    Q, K: [..., N, d]; V: [..., N, e]; S0: [..., W, e+1].  For row i,
-    num_i = phi(q_i).S0[:, :e] + sum_{j<=i} K_n(q_i.k_j) v_j and
-    den_i = phi(q_i).S0[:, e] + sum_{j<=i} K_n(q_i.k_j); o_i = num_i / den_i.
-    The returned states are S0 plus the states of the new tokens.  The earlier
-    tokens enter only through their summed state, which is what lets a
-    prefill resume after decoding or start from another segment's total
-    [ExpAttn abstract: additive states, constant-size recurrent state;
-    HN-thread, reply on the "+1" column for the den part].
+    Q, K: [..., N, d]; V: [..., N, e]; S0: [..., W, e+1], or None for zero
+    states.  For row i,
+        num_i = phi(q_i).S0[:, :e] + sum_{j<=i} K_n(q_i.k_j) v_j,
+        den_i = phi(q_i).S0[:, e]  + sum_{j<=i} K_n(q_i.k_j),
+    before any division.  Both are sums over keys, so results computed over
+    separate key segments add, which is how segments are combined; the
+    returned states are S0 plus the states of the new tokens [ExpAttn
+    abstract: additive states, constant-size recurrent state; HN-thread,
+    reply on the "+1" column for the den part].  Returns (num [..., N, e],
+    den [..., N], states [..., W, e+1]).
     """
     Qh, lead = _heads(Q)
     Kh, _ = _heads(K)
@@ -338,18 +340,33 @@ def prefill_from_states(Q, K, V, S0, n: int) -> Tuple[np.ndarray, np.ndarray]:
     H, N, d = Qh.shape
     e = Vh.shape[2]
     W = state_rows(d, n)
-    S0h = np.asarray(S0, dtype=np.float64).reshape(H, W, e + 1)
+    S0h = np.zeros((H, W, e + 1)) if S0 is None else np.asarray(S0, dtype=np.float64).reshape(H, W, e + 1)
     mask = np.tril(np.ones((N, N), dtype=bool))
-    O = np.empty((H, N, e))
+    num = np.empty((H, N, e))
+    den = np.empty((H, N))
     S_all = np.empty((H, W, e + 1))
     for h in range(H):
         phi = feature_map(Qh[h], n, weighted=True)
         vp = np.concatenate([Vh[h], np.ones((N, 1))], axis=1)
         P = np.where(mask, taylor_kernel(Qh[h] @ Kh[h].T, n), 0.0)
         acc = phi @ S0h[h] + P @ vp
-        O[h] = acc[:, :e] / acc[:, e:]
+        num[h] = acc[:, :e]
+        den[h] = acc[:, e]
         S_all[h] = S0h[h] + states_definition(Kh[h], Vh[h], n)
-    return O.reshape(lead + (N, e)), S_all.reshape(lead + (W, e + 1))
+    return num.reshape(lead + (N, e)), den.reshape(lead + (N,)), S_all.reshape(lead + (W, e + 1))
+
+
+def prefill_from_states(Q, K, V, S0, n: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Prefill of new tokens that continues from the states S0 of earlier ones.
+
+    o_i = num_i / den_i with num and den from ``prefill_from_numden``; the
+    returned states are S0 plus the states of the new tokens.  The earlier
+    tokens enter only through their summed state, which is what lets a
+    prefill resume after decoding or start from another segment's total
+    [ExpAttn abstract: additive states, constant-size recurrent state].
+    """
+    num, den, S_all = prefill_from_numden(Q, K, V, S0, n)
+    return num / den[..., None], S_all
 
 
 def prefill_from_rows(q_rows, K, V, S0, rows: Sequence[int], n: int) -> np.ndarray:

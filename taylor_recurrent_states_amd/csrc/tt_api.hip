@@ -69,9 +69,9 @@ static size_t normed_copy_bytes(int B, int H, int N, int dk) {
 // zero states; normed: Q and K are first normalised into the workspace tail
 // (Q scaled by qscale) and the prefill reads those copies.
 static int prefill_impl(const void* Q, const void* K, const void* V, tt_dtype in_dtype, int B, int H, int N,
-                        int dk, int dv, int n, int chunk, const float* states_in, float* O, float* states,
-                        void* workspace, size_t workspace_bytes, bool normed, float qscale, void* stream,
-                        const char* name) {
+                        int dk, int dv, int n, int chunk, const float* states_in, float* O, float* den,
+                        float* states, void* workspace, size_t workspace_bytes, bool normed, float qscale,
+                        void* stream, const char* name) {
   if (!Q || !K || !V || !O || !states) return fail(TT_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (B < 1 || H < 1 || N < 1) return fail(TT_ERR_INVALID_ARG, "B=%d H=%d N=%d must be >= 1", B, H, N);
   int rc = check_dtype(in_dtype);
@@ -92,6 +92,14 @@ static int prefill_impl(const void* Q, const void* K, const void* V, tt_dtype in
                 workspace ? workspace_bytes : (size_t)0);
   if ((((uintptr_t)Q) | ((uintptr_t)K) | ((uintptr_t)V) | ((uintptr_t)O) | ((uintptr_t)workspace)) & 15u)
     return fail(TT_ERR_INVALID_ARG, "Q, K, V, O and workspace must be 16-byte aligned");
+  if (den) {
+    const size_t db = (size_t)B * H * N * sizeof(float);
+    const size_t sb = (size_t)B * H * tt_state_floats(dk, dv, n) * sizeof(float);
+    if (((uintptr_t)den) & 3u) return fail(TT_ERR_INVALID_ARG, "den must be 4-byte aligned");
+    if (overlap(den, db, O, (size_t)B * H * N * dv * sizeof(float)) || overlap(den, db, states, sb) ||
+        (states_in && overlap(den, db, states_in, sb)) || (workspace && overlap(den, db, workspace, need)))
+      return fail(TT_ERR_INVALID_ARG, "den overlaps O, the states or the workspace");
+  }
   if (states_in) {
     const size_t sb = (size_t)B * H * tt_state_floats(dk, dv, n) * sizeof(float);
     if (states_in != states && overlap(states_in, sb, states, sb))
@@ -111,7 +119,7 @@ static int prefill_impl(const void* Q, const void* K, const void* V, tt_dtype in
     Q = qn;
     K = kn;
   }
-  return hip_status(launch_prefill(Q, K, V, in_dtype, B * H, N, dk, n, p, states_in, O, states,
+  return hip_status(launch_prefill(Q, K, V, in_dtype, B * H, N, dk, n, p, states_in, O, den, states,
                                    (float*)workspace, (hipStream_t)stream),
                     what);
 }
@@ -178,7 +186,7 @@ int tt_prefill_workspace_bytes(int B, int H, int N, int dk, int dv, int n, int c
 int tt_prefill(const void* Q, const void* K, const void* V, tt_dtype in_dtype, int B, int H, int N, int dk,
                int dv, int n, int chunk, float* O, float* states, void* workspace, size_t workspace_bytes,
                void* stream) {
-  return prefill_impl(Q, K, V, in_dtype, B, H, N, dk, dv, n, chunk, nullptr, O, states, workspace,
+  return prefill_impl(Q, K, V, in_dtype, B, H, N, dk, dv, n, chunk, nullptr, O, nullptr, states, workspace,
                       workspace_bytes, false, 1.0f, stream, "tt_prefill");
 }
 
@@ -186,8 +194,17 @@ int tt_prefill_from(const void* Q, const void* K, const void* V, tt_dtype in_dty
                     int dv, int n, int chunk, const float* states_in, float* O, float* states, void* workspace,
                     size_t workspace_bytes, void* stream) {
   if (!states_in) return fail(TT_ERR_INVALID_ARG, "states_in is NULL (use tt_prefill for zero states)");
-  return prefill_impl(Q, K, V, in_dtype, B, H, N, dk, dv, n, chunk, states_in, O, states, workspace,
+  return prefill_impl(Q, K, V, in_dtype, B, H, N, dk, dv, n, chunk, states_in, O, nullptr, states, workspace,
                       workspace_bytes, false, 1.0f, stream, "tt_prefill_from");
+}
+
+int tt_prefill_from_unnormalized(const void* Q, const void* K, const void* V, tt_dtype in_dtype, int B, int H,
+                                 int N, int dk, int dv, int n, int chunk, const float* states_in, float* num,
+                                 float* den, float* states, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (!den) return fail(TT_ERR_INVALID_ARG, "den is NULL");
+  return prefill_impl(Q, K, V, in_dtype, B, H, N, dk, dv, n, chunk, states_in, num, den, states, workspace,
+                      workspace_bytes, false, 1.0f, stream, "tt_prefill_from_unnormalized");
 }
 
 int tt_prefill_normed_workspace_bytes(int B, int H, int N, int dk, int dv, int n, int chunk, size_t* bytes) {
@@ -200,7 +217,7 @@ int tt_prefill_normed_workspace_bytes(int B, int H, int N, int dk, int dv, int n
 int tt_prefill_normed(const void* Q, const void* K, const void* V, tt_dtype in_dtype, int B, int H, int N, int dk,
                       int dv, int n, int chunk, float temperature, const float* states_in, float* O,
                       float* states, void* workspace, size_t workspace_bytes, void* stream) {
-  return prefill_impl(Q, K, V, in_dtype, B, H, N, dk, dv, n, chunk, states_in, O, states, workspace,
+  return prefill_impl(Q, K, V, in_dtype, B, H, N, dk, dv, n, chunk, states_in, O, nullptr, states, workspace,
                       workspace_bytes, true, temperature, stream, "tt_prefill_normed");
 }
 

@@ -49,8 +49,10 @@ struct PrefillPlan {
 
 int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype dt, PrefillPlan* p);
 // states_in: carried-in states in the plane layout, or null for zero states.
+// den_out: null for normalised outputs; otherwise O receives the numerators
+// and den_out [BH][N] the normalisers.
 hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype dt, int BH, int N, int dk,
-                          int n, const PrefillPlan& p, const float* states_in, float* O, float* states,
-                          float* ws, hipStream_t s);
+                          int n, const PrefillPlan& p, const float* states_in, float* O, float* den_out,
+                          float* states, float* ws, hipStream_t s);
 
 }  // namespace tt

@@ -43,7 +43,9 @@
 namespace tt {
 namespace {
 
-enum { MODE_TOTALS = 0, MODE_OUTPUT = 1 };
+// MODE_OUTPUT_UNN: the output pass with unnormalised outputs (numerators to O,
+// normalisers to a separate buffer); the pipe kernel only
+enum { MODE_TOTALS = 0, MODE_OUTPUT = 1, MODE_OUTPUT_UNN = 2 };
 
 constexpr int kCH = 64;  // tokens per chunk
 constexpr int kDV = 64;  // value columns
@@ -562,7 +564,8 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
                                                         const typename C::TIn* __restrict__ Kg,
                                                         const typename C::TIn* __restrict__ Vg, int N,
                                                         int span, int nspan, float* __restrict__ ws,
-                                                        float* __restrict__ part, float* __restrict__ Og) {
+                                                        float* __restrict__ part, float* __restrict__ Og,
+                                                        float* __restrict__ Dg) {
   using TIn = typename C::TIn;
   using Elem = typename C::Elem;
   constexpr bool BF = C::BF;
@@ -1134,8 +1137,13 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
           }
           if (li == 0) {
             if constexpr (C::NRG == 1) {
+              // Dg non-null: outputs stay unnormalised and the normalisers go to Dg
 #pragma unroll
-              for (int s = 0; s < 4; ++s) sDenQ[qt * 16 + 4 * lg + s] = rcp_fast(den[qt][s] + den0);
+              for (int s = 0; s < 4; ++s) {
+                const float dq = den[qt][s] + den0;
+                sDenQ[qt * 16 + 4 * lg + s] = Dg ? 1.0f : rcp_fast(dq);
+                if (Dg && qt * 16 + 4 * lg + s < nvalid) Dg[(size_t)bh * N + c0 + qt * 16 + 4 * lg + s] = dq;
+              }
             } else {
 #pragma unroll
               for (int s = 0; s < 4; ++s)
@@ -1234,7 +1242,8 @@ struct PCfg {
   using TIn = uint16_t;
   using Elem = uint16_t;
   static constexpr bool BF = true;
-  static constexpr bool OUT = (MODE_ == MODE_OUTPUT);
+  static constexpr bool OUT = (MODE_ != MODE_TOTALS);
+  static constexpr bool UNN = (MODE_ == MODE_OUTPUT_UNN);
   static constexpr int DK = DK_, NT = NT_;
   static constexpr int NTHR = 512;
   static constexpr int NW = 8;
@@ -1288,7 +1297,7 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
                                                        const uint16_t* __restrict__ Kg,
                                                        const uint16_t* __restrict__ Vg, int N, int span,
                                                        int nspan, float* __restrict__ ws,
-                                                       float* __restrict__ Og) {
+                                                       float* __restrict__ Og, float* __restrict__ Dg) {
   using Elem = uint16_t;
   constexpr bool OUT = C::OUT;
   __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS];
@@ -1660,8 +1669,19 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
           num[qt] += m0;
         }
         if (li == 0) {
+          // unnormalised mode: outputs keep their numerators and the
+          // normalisers go to Dg
 #pragma unroll
-          for (int s = 0; s < 4; ++s) sRden[b * kCH + (4 * lg + s) * 4 + ct] = rcp_fast(den[s] + den0);
+          for (int s = 0; s < 4; ++s) {
+            const float dq = den[s] + den0;
+            if constexpr (C::UNN) {
+              sRden[b * kCH + (4 * lg + s) * 4 + ct] = 1.0f;
+              const int t = c0 + ct * 16 + 4 * lg + s;
+              if (t < t_end) Dg[(size_t)bh * N + t] = dq;
+            } else {
+              sRden[b * kCH + (4 * lg + s) * 4 + ct] = rcp_fast(dq);
+            }
+          }
         }
         // previous chunk: normalise and store (16 bytes per lane and query tile)
         if (ci > 0) {
@@ -1877,7 +1897,8 @@ struct Shape {
 
 // O = (sum over row groups of the partial numerators) / (sum of the partial
 // normalisers), four columns per thread.
-__global__ void combine_kernel(const float* __restrict__ part, int BH, int N, int nrg, float* __restrict__ O) {
+__global__ void combine_kernel(const float* __restrict__ part, int BH, int N, int nrg, float* __restrict__ O,
+                               float* __restrict__ Dg) {
   const size_t total = (size_t)BH * N * (kDV / 4);
   const float* pden = part + (size_t)BH * nrg * N * kDV;
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
@@ -1891,7 +1912,12 @@ __global__ void combine_kernel(const float* __restrict__ part, int BH, int N, in
       acc += *reinterpret_cast<const f32x4*>(part + row * kDV + 4 * c4);
       d += pden[row];
     }
-    *reinterpret_cast<f32x4*>(O + (bh * N + t) * kDV + 4 * c4) = acc * (1.0f / d);
+    if (Dg) {  // unnormalised: the numerator to O, the normaliser to Dg
+      *reinterpret_cast<f32x4*>(O + (bh * N + t) * kDV + 4 * c4) = acc;
+      if (c4 == 0) Dg[bh * N + t] = d;
+    } else {
+      *reinterpret_cast<f32x4*>(O + (bh * N + t) * kDV + 4 * c4) = acc * (1.0f / d);
+    }
   }
 }
 
@@ -1949,8 +1975,8 @@ int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype
 }
 
 hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype dt, int BH, int N, int dk, int n,
-                          const PrefillPlan& p, const float* states_in, float* O, float* states, float* ws,
-                          hipStream_t s) {
+                          const PrefillPlan& p, const float* states_in, float* O, float* den_out, float* states,
+                          float* ws, hipStream_t s) {
   return with_dkn(dk, n, [&](auto DKc, auto Nc) {
     constexpr int DK = decltype(DKc)::value, NT = decltype(Nc)::value;
     auto scan = [&](int WP, int octdk) {
@@ -1967,34 +1993,39 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype 
       const unsigned nblk = (unsigned)((size_t)BH * p.nspan * p.ngroups * S::NRG);
       float* part = ws + (size_t)BH * p.nspan * S::Out::WP * (kDV + 1);  // row-group partial outputs
       hipLaunchKernelGGL((sweep_kernel<typename S::Tot>), dim3(nblk), dim3(S::Tot::NTHR), 0, s, (const TIn*)Q,
-                         (const TIn*)K, (const TIn*)V, N, p.span, p.nspan, ws, part, O);
+                         (const TIn*)K, (const TIn*)V, N, p.span, p.nspan, ws, part, O, den_out);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       e = scan((int)S::Out::WP, S::Out::OCT ? DK : 0);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((sweep_kernel<typename S::Out>), dim3(nblk), dim3(S::Out::NTHR), 0, s, (const TIn*)Q,
-                         (const TIn*)K, (const TIn*)V, N, p.span, p.nspan, ws, part, O);
+                         (const TIn*)K, (const TIn*)V, N, p.span, p.nspan, ws, part, O, den_out);
       e = hipGetLastError();
       if (e != hipSuccess || S::NRG == 1) return e;
       const size_t total = (size_t)BH * N * (kDV / 4);
       unsigned g = (unsigned)((total + 255) / 256);
       if (g > 16384) g = 16384;
-      hipLaunchKernelGGL(combine_kernel, dim3(g), dim3(256), 0, s, (const float*)part, BH, N, S::NRG, O);
+      hipLaunchKernelGGL(combine_kernel, dim3(g), dim3(256), 0, s, (const float*)part, BH, N, S::NRG, O, den_out);
       return hipGetLastError();
     };
     if (dt == TT_BF16) {
       if constexpr (use_pipe<DK, NT>()) {
         using PT = PCfg<DK, NT, MODE_TOTALS>;
         using PO = PCfg<DK, NT, MODE_OUTPUT>;
+        using PU = PCfg<DK, NT, MODE_OUTPUT_UNN>;
         const unsigned nblk = (unsigned)((size_t)BH * p.nspan);
         hipLaunchKernelGGL((pipe_kernel<PT>), dim3(nblk), dim3(PT::NTHR), 0, s, (const uint16_t*)Q,
-                           (const uint16_t*)K, (const uint16_t*)V, N, p.span, p.nspan, ws, O);
+                           (const uint16_t*)K, (const uint16_t*)V, N, p.span, p.nspan, ws, O, den_out);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = scan((int)PO::WP, 0);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((pipe_kernel<PO>), dim3(nblk), dim3(PO::NTHR), 0, s, (const uint16_t*)Q,
-                           (const uint16_t*)K, (const uint16_t*)V, N, p.span, p.nspan, ws, O);
+        if (den_out)
+          hipLaunchKernelGGL((pipe_kernel<PU>), dim3(nblk), dim3(PU::NTHR), 0, s, (const uint16_t*)Q,
+                             (const uint16_t*)K, (const uint16_t*)V, N, p.span, p.nspan, ws, O, den_out);
+        else
+          hipLaunchKernelGGL((pipe_kernel<PO>), dim3(nblk), dim3(PO::NTHR), 0, s, (const uint16_t*)Q,
+                             (const uint16_t*)K, (const uint16_t*)V, N, p.span, p.nspan, ws, O, den_out);
         return hipGetLastError();
       } else {
         return go(uint16_t{});

@@ -27,7 +27,7 @@ TT_F32, TT_BF16 = 0, 1
 TT_OK, TT_ERR_INVALID_ARG, TT_ERR_UNSUPPORTED, TT_ERR_WORKSPACE, TT_ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTED = ("tt_state_rows", "tt_state_floats", "tt_prefill_workspace_bytes", "tt_prefill",
-            "tt_prefill_from", "tt_decode_step", "tt_state_merge", "tt_feature_map", "tt_last_error",
+            "tt_prefill_from", "tt_prefill_from_unnormalized", "tt_decode_step", "tt_state_merge", "tt_feature_map", "tt_last_error",
             "tt_normalize_rows", "tt_prefill_normed_workspace_bytes", "tt_prefill_normed",
             "tt_decode_step_normed", "tt_softmax_prefill", "tt_softmax_decode_workspace_bytes",
             "tt_softmax_decode_step")
@@ -64,6 +64,9 @@ def lib() -> ctypes.CDLL:
     L.tt_prefill_from.argtypes = [c_void, c_void, c_void, c_int] + [c_int] * 7 + [c_float_p, c_float_p, c_float_p,
                                                                                    c_void, c_size, c_void]
     L.tt_prefill_from.restype = c_int
+    L.tt_prefill_from_unnormalized.argtypes = [c_void, c_void, c_void, c_int] + [c_int] * 7 + [c_float_p] * 4 + [
+        c_void, c_size, c_void]
+    L.tt_prefill_from_unnormalized.restype = c_int
     L.tt_decode_step.argtypes = [c_void, c_void, c_void, c_int] + [c_int] * 5 + [c_float_p, c_float_p, c_void]
     L.tt_decode_step.restype = c_int
     L.tt_state_merge.argtypes = [c_float_p, c_float_p, c_float_p, c_size, c_void]
@@ -179,14 +182,17 @@ def _prefill_args(Q, K, V, n, chunk, O, states, workspace, normed=False):
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    return (B, H, N, dk, dv), O, states, ws_ptr, ws_bytes
+    # the caller holds ``workspace`` until the launch is queued: a workspace
+    # allocated here must not return to torch's pool before that, or the next
+    # allocation (an output buffer) could be handed the same memory
+    return (B, H, N, dk, dv), O, states, workspace, ws_ptr, ws_bytes
 
 
 def tt_prefill(Q, K, V, n: int, chunk: int = 64, O=None, states=None, workspace=None, stream=None):
     """Causal prefill of Q, K [B, H, N, dk] and V [B, H, N, dv] (float32 or
     bfloat16, same dtype).  Returns (O [B, H, N, dv] float32, states flat
     float32 in the library's plane layout)."""
-    (B, H, N, dk, dv), O, states, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace)
+    (B, H, N, dk, dv), O, states, ws, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace)
     _check(lib().tt_prefill(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk, dv, n, chunk,
                             _dev(O, "O").data_ptr(), _dev(states, "states").data_ptr(), ws_ptr, ws_bytes,
                             _stream(stream)))
@@ -199,7 +205,7 @@ def tt_prefill_from(Q, K, V, states_in, n: int, chunk: int = 64, O=None, states=
     ``states`` may be ``states_in`` itself to continue in place.  Returns
     (O, states)."""
     _dev(states_in, "states_in")
-    (B, H, N, dk, dv), O, states, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace)
+    (B, H, N, dk, dv), O, states, ws, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace)
     if states_in.dtype != _torch().float32 or states_in.numel() != B * H * tt_state_floats(dk, dv, n):
         raise ValueError("states_in must hold B*H*W*(dv+1) float32 values")
     _check(lib().tt_prefill_from(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk, dv, n,
@@ -208,12 +214,36 @@ def tt_prefill_from(Q, K, V, states_in, n: int, chunk: int = 64, O=None, states=
     return O, states
 
 
+def tt_prefill_from_unnormalized(Q, K, V, states_in, n: int, chunk: int = 64, num=None, den=None, states=None,
+                                 workspace=None, stream=None):
+    """tt_prefill_from without the division: returns (num [B, H, N, dv],
+    den [B, H, N], states); o = num / den[..., None].  ``states_in`` may be
+    None (zero states)."""
+    torch = _torch()
+    (B, H, N, dk, dv), num, states, ws, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, num, states, workspace)
+    if den is None:
+        den = torch.empty((B, H, N), dtype=torch.float32, device=Q.device)
+    sin = 0
+    if states_in is not None:
+        _dev(states_in, "states_in")
+        if states_in.dtype != torch.float32 or states_in.numel() != B * H * tt_state_floats(dk, dv, n):
+            raise ValueError("states_in must hold B*H*W*(dv+1) float32 values")
+        sin = states_in.data_ptr()
+    if den.dtype != torch.float32 or den.numel() != B * H * N:
+        raise ValueError("den must hold B*H*N float32 values")
+    _check(lib().tt_prefill_from_unnormalized(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk,
+                                              dv, n, chunk, sin, _dev(num, "num").data_ptr(),
+                                              _dev(den, "den").data_ptr(), _dev(states, "states").data_ptr(), ws_ptr,
+                                              ws_bytes, _stream(stream)))
+    return num, den, states
+
+
 def tt_prefill_normed(Q, K, V, n: int, temperature: float = 1.0, states_in=None, chunk: int = 64, O=None,
                       states=None, workspace=None, stream=None):
     """Prefill on raw Q, K: the library normalises them (Q scaled by
     ``temperature``) and runs the prefill, from ``states_in`` (flat float32,
     plane layout) or from zero states when it is None.  Returns (O, states)."""
-    (B, H, N, dk, dv), O, states, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace,
+    (B, H, N, dk, dv), O, states, ws, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace,
                                                                    normed=True)
     sin = None
     if states_in is not None:

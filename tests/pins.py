@@ -494,6 +494,34 @@ def pin_prefill_from_states():
 # Trade-offs and Performance"]
 # ---------------------------------------------------------------------------
 
+def pin_prefill_from_numden(N=7, p=4, d=3, e=2, seed=21):
+    """Numerator and normaliser of a resumed prefill against brute force over
+    the whole sequence: num_i = sum over every key j of the prefix and of the
+    new tokens up to i of K_n(q_i.k_j) v_j, den_i the same sum of weights,
+    with K_n written out as its power series; the division gives
+    prefill_from_states, and zero states give the plain prefill's sums
+    [ExpAttn abstract: additive states]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((p + N, d)); q /= np.linalg.norm(q, axis=1, keepdims=True)
+    k = rng.standard_normal((p + N, d)); k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((p + N, e))
+    for n in (1, 2, 3, 4):
+        kn = lambda x: sum(x ** m / math.factorial(m) for m in range(n))
+        S0 = orc.states_definition(k[:p], v[:p], n)
+        num, den, S = orc.prefill_from_numden(q[p:], k[p:], v[p:], S0, n)
+        for i in range(N):
+            t = p + i
+            w = [kn(float(q[t] @ k[j])) for j in range(t + 1)]
+            ref_num = sum(wj * v[j] for j, wj in enumerate(w))
+            assert np.max(np.abs(num[i] - ref_num)) <= 1e-13 * max(1.0, np.max(np.abs(ref_num)))
+            assert abs(den[i] - sum(w)) <= 1e-13 * max(1.0, abs(sum(w)))
+        o, S2 = orc.prefill_from_states(q[p:], k[p:], v[p:], S0, n)
+        assert np.array_equal(o, num / den[:, None]) and np.array_equal(S, S2)
+        num0, den0, _ = orc.prefill_from_numden(q, k, v, None, n)
+        w0 = [sum(kn(float(q[t] @ k[j])) for j in range(t + 1)) for t in range(p + N)]
+        assert np.max(np.abs(den0 - np.array(w0))) <= 1e-13 * max(w0)
+
+
 def pin_normalize_rows():
     """Hand values, unit norms, invariance to positive scale (exact for
     powers of two), the NaN of a zero row, and a temperature worked by hand
@@ -556,6 +584,6 @@ ALL_PINS = [
     pin_unit_identity, pin_recurrent_vs_quadratic, pin_chunk_additivity,
     pin_decode_equals_recurrence, pin_softmax_library, pin_softmax_convergence,
     pin_normalisation_required, pin_svd_rank, pin_special_cases, pin_convex_hull,
-    pin_planes_layout, pin_quadratic_rows, pin_prefill_from_states,
+    pin_planes_layout, pin_quadratic_rows, pin_prefill_from_states, pin_prefill_from_numden,
     pin_normalize_rows, pin_normalize_rows_f32, pin_round_to_dtype, pin_softmax_rows,
 ]

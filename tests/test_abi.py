@@ -91,6 +91,23 @@ def test_entry_points_reject_bad_arguments_without_launching():
     assert L.tt_feature_map(None, 0, 0, 16, 3, 0, None, None) == ops.TT_OK
 
 
+def test_unnormalized_prefill_rejects_bad_arguments_without_launching():
+    L = ops.lib()
+    fake = ctypes.c_void_p(0x1000)
+    args = (fake, fake, fake, 0, 1, 1, 64, 16, 64, 3, 64)
+    # den NULL
+    rc = L.tt_prefill_from_unnormalized(*args, None, ctypes.c_void_p(0x100000), None, fake, fake, 1 << 30, None)
+    assert rc == ops.TT_ERR_INVALID_ARG and "den" in ops.tt_last_error()
+    # den not 4-byte aligned
+    rc = L.tt_prefill_from_unnormalized(*args, None, ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200002), fake, fake,
+                                        1 << 30, None)
+    assert rc == ops.TT_ERR_INVALID_ARG
+    # den overlapping the numerators
+    rc = L.tt_prefill_from_unnormalized(*args, None, ctypes.c_void_p(0x100000), ctypes.c_void_p(0x100010), fake,
+                                        ctypes.c_void_p(0x90000000), 1 << 30, None)
+    assert rc == ops.TT_ERR_INVALID_ARG and "overlap" in ops.tt_last_error()
+
+
 def test_normalised_entry_points_reject_bad_arguments_without_launching():
     L = ops.lib()
     fake = ctypes.c_void_p(0x1000)

@@ -106,3 +106,39 @@ def test_prefill_from_workload_full_size():
     S_ref = np.stack([orc.merge_states(S0h[h], orc.states_definition(Kx[h], Vx[h], w.n)) for h in range(BH)])
     assert_states(S.cpu().numpy(), S_ref, w.dk, w.n, w.tol, "prefill_from")
     print("[prefill_from] states ok", flush=True)
+
+
+def _rel_to_max(x, ref):
+    return float(np.max(np.abs(x - ref)) / max(1e-300, np.max(np.abs(ref))))
+
+
+@pytest.mark.parametrize("dk,n", [(16, 2), (16, 3), (32, 2), (64, 2), (64, 3), (16, 5)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("carried", [True, False])
+def test_prefill_from_unnormalized(dk, n, dtype, carried):
+    """tt_prefill_from_unnormalized: the numerators and normalisers against
+    the oracle's (relative to their largest element: 1e-5 for fp32 inputs,
+    5e-3 for bf16), num / den at the output bar, the same states as the
+    normalised call, and the normalised call's O equal to num * (1/den)
+    within the hardware reciprocal's rounding.  The shapes cover the pipe
+    kernel, the sweep kernel and the row-group combine (dk 64 n 3, dk 16 n 5)."""
+    import torch
+    B, H, P, N = 1, 2, 150, 200
+    S0, S0d = _prefix_states(3400 + dk * 10 + n, B, H, P, dk, 64, n, dtype) if carried else (None, None)
+    q, k, v = wl.draw_qkv(3500 + dk * 10 + n, B, H, N, dk, 64, dtype)
+    Qd, Kd, Vd = to_device(q), to_device(k), to_device(v)
+    num, den, S = ops.tt_prefill_from_unnormalized(Qd, Kd, Vd, S0d, n)
+    if carried:
+        O, S_n = ops.tt_prefill_from(Qd, Kd, Vd, S0d, n)
+    else:
+        O, S_n = ops.tt_prefill(Qd, Kd, Vd, n)
+    torch.cuda.synchronize()
+    num_ref, den_ref, S_ref = orc.prefill_from_numden(q.exact, k.exact, v.exact, S0, n)
+    bar = 1e-5 if dtype == "f32" else 5e-3
+    num_g, den_g = num.cpu().numpy().astype(np.float64), den.cpu().numpy().astype(np.float64)
+    assert _rel_to_max(num_g, num_ref) <= bar, f"num dk{dk} n{n}"
+    assert _rel_to_max(den_g, den_ref) <= bar, f"den dk{dk} n{n}"
+    assert_out(num_g / den_g[..., None], num_ref / den_ref[..., None], _tol(dtype), f"num/den dk{dk} n{n}")
+    assert_states(S.cpu().numpy(), S_ref, dk, n, _tol(dtype), f"dk{dk} n{n}")
+    assert torch.equal(S, S_n)
+    assert _rel_to_max(O.cpu().numpy().astype(np.float64), num_g / den_g[..., None]) <= 1e-6

@@ -178,6 +178,18 @@ def _round_truncating(X, dtype):
     return u.view(np.float32).astype(np.float64)
 
 
+_orig_numden = orc.prefill_from_numden
+
+
+def _numden_den_without_states(Q, K, V, S0, n):
+    # the normaliser forgets the carried-in states' "+1" column
+    num, den, S = _orig_numden(Q, K, V, S0, n)
+    if S0 is None:
+        return num, den, S
+    phi = orc.feature_map(np.asarray(Q, dtype=np.float64), n, weighted=True)
+    return num, den - phi @ np.asarray(S0, dtype=np.float64)[..., -1], S
+
+
 MUTANTS = {
     "taylor_dropped_term": ("taylor_kernel", _taylor_dropped_term),
     "taylor_wrong_factorial": ("taylor_kernel", _taylor_wrong_factorial),
@@ -194,6 +206,7 @@ MUTANTS = {
     "planes_interleaved": ("states_to_planes", _planes_interleaved),
     "prefill_from_den_without_states": ("prefill_from_states", _prefill_from_den_without_states),
     "prefill_from_exclusive_states": ("prefill_from_states", _prefill_from_exclusive_states),
+    "numden_den_without_states": ("prefill_from_numden", _numden_den_without_states),
     "normalize_no_sqrt": ("normalize_rows", _normalize_no_sqrt),
     "normalize_inverted_temperature": ("normalize_rows", _normalize_inverted_temperature),
     "normalize_f32_no_sqrt": ("normalize_rows_f32", _normalize32_no_sqrt),
@@ -207,7 +220,7 @@ _PINS = [pins.pin_hand_example, pins.pin_kron_features, pins.pin_unit_identity,
          pins.pin_special_cases, pins.pin_decode_equals_recurrence,
          pins.pin_planes_layout, pins.pin_exact_rational, pins.pin_chunk_additivity,
          pins.pin_recurrent_vs_quadratic, pins.pin_softmax_library,
-         pins.pin_softmax_convergence, pins.pin_prefill_from_states,
+         pins.pin_softmax_convergence, pins.pin_prefill_from_states, pins.pin_prefill_from_numden,
          pins.pin_normalize_rows, pins.pin_normalize_rows_f32, pins.pin_round_to_dtype,
          pins.pin_softmax_rows]
 

@@ -116,6 +116,15 @@ def bench_prefill(args, torch, ops, wl):
     _prewarm(step_from, torch, 0.05)
     t_from = _time_events(step_from, args.steps, torch) / args.steps
     from_bytes = alg_bytes + S_in.numel() * 4
+    # the same, returning numerators and normalisers (no division)
+    den = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    def step_unn():
+        ops.tt_prefill_from_unnormalized(Q, K, V, S_in, w.n, w.chunk, num=O, den=den, states=S, workspace=ws)
+
+    _prewarm(step_unn, torch, 0.05)
+    t_unn = _time_events(step_unn, args.steps, torch) / args.steps
+    unn_bytes = from_bytes + den.numel() * 4
     # the same workload on raw (not normalised) q, k: the library normalises
     # them (one pass over Q and K into the workspace), then runs the prefill
     qr, kr, _ = wl.draw_qkv(w.seed, w.B, w.H, w.N, w.dk, w.dv, w.dtype, normalise=False)
@@ -143,6 +152,9 @@ def bench_prefill(args, torch, ops, wl):
         "prefill_from": {"ms_per_call": round(t_from * 1e3, 5), "tokens_per_s": round(tokens / t_from, 1),
                          "hbm_frac": round(from_bytes / t_from / 1e9 / HBM_PEAK_GBS, 4),
                          "alg_bytes_per_launch": from_bytes},
+        "prefill_from_unnormalized": {"ms_per_call": round(t_unn * 1e3, 5), "tokens_per_s": round(tokens / t_unn, 1),
+                                      "hbm_frac": round(unn_bytes / t_unn / 1e9 / HBM_PEAK_GBS, 4),
+                                      "alg_bytes_per_launch": unn_bytes},
         "prefill_normed": {"ms_per_call": round(t_normed * 1e3, 5), "tokens_per_s": round(tokens / t_normed, 1),
                            "inputs": "raw Gaussian q, k (normalised by the library), temperature 1",
                            "normalize_pass": {"us_per_launch": round(t_norm * 1e6, 2),
@@ -566,6 +578,7 @@ def main():
     if pre is not None:
         out.update({"value": round(pre["value"], 1), "ms_per_step": round(pre["t_step"] * 1e3, 5),
                     "roofline": pre["roofline"], "prefill_from": pre["prefill_from"],
+                    "prefill_from_unnormalized": pre["prefill_from_unnormalized"],
                     "prefill_normed": pre["prefill_normed"]})
     else:
         out.update({"value": None, "ms_per_step": None, "roofline": None})

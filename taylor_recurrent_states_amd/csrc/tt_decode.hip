@@ -56,28 +56,35 @@ __global__ __launch_bounds__(kDecodeThreads, 8) void decode_kernel(const TIn* __
   const int r0 = wave * per;
   const int r1 = min(W, r0 + per);
 
-  // state reads first (small states): they overlap everything up to the update
+  // state reads first (small states): they overlap everything up to the
+  // update. With NORM they follow the normalisation of q and k, so that the
+  // resident rows do not share registers with it (at 8 waves per SIMD they
+  // would spill); the other resident workgroups cover the later start.
   float sv[RES ? per : 1];
   float dv = 0.f;
-  if constexpr (RES) {
+  auto load_state = [&]() {
+    if constexpr (RES) {
 #pragma unroll
-    for (int u = 0; u < per; ++u)
-      if (r0 + u < r1) sv[u] = S[(size_t)(r0 + u) * kDV + lane];
-    if (tid < W) dv = D[tid];
-  }
+      for (int u = 0; u < per; ++u)
+        if (r0 + u < r1) sv[u] = S[(size_t)(r0 + u) * kDV + lane];
+      if (tid < W) dv = D[tid];
+    }
+  };
+  if constexpr (!NORM) load_state();
   const float vc = load_f32(v, (size_t)bh * kDV + lane);
 
   if (tid < DK) {
     s_q[tid] = load_f32(q, (size_t)bh * DK + tid);
     s_k[tid] = load_f32(k, (size_t)bh * DK + tid);
   }
-  if constexpr (NORM) {  // in place in LDS: few registers beside the resident state rows
+  if constexpr (NORM) {  // in place in LDS
     __syncthreads();
     if (tid == 0 || tid == 64) {
       float* row = tid == 0 ? s_q : s_k;
       const float f = row_norm_factor<DK>([&](int i) { return row[i]; }, tid == 0 ? qscale : 1.0f);
       for (int i = 0; i < DK; ++i) row[i] = unit_coord<TIn>(row[i], f);
     }
+    load_state();
   }
   __syncthreads();
   for (int r = tid; r < W; r += kDecodeThreads) {

@@ -24,8 +24,9 @@ Readings where the pages leave a step open:
 
 * no temperature inside the exponential: the kernel is K_n(q.k) on inputs
   the caller has already L2-normalised; the optional normalised path
-  (``normalized_inputs``) makes the unit rows itself, folds a temperature
-  tau into the queries, and rounds the unit rows back to the input dtype;
+  (``normalized_inputs``) makes the unit rows itself in fp64, folds a
+  temperature tau into the queries, and rounds the unit rows to the input
+  dtype the way the inputs are rounded;
 * "n terms" means the orders 0 .. n-1;
 * the state stores *raw* symmetric monomials mu_t(k) = prod_l k_{t_l}; the
   multinomial weight 1/alpha(t)! lives on the query side,
@@ -55,10 +56,10 @@ __all__ = [
     "multinomial_weights", "feature_map", "taylor_kernel",
     "quadratic_attention", "quadratic_rows", "states_definition",
     "recurrent_attention", "chunked_attention", "decode_step",
-    "prefill_from_states", "prefill_from_rows",
+    "prefill_from_numden", "prefill_from_states", "prefill_from_rows",
     "merge_states", "softmax_attention", "states_to_planes",
     "planes_to_states", "block_row_ranges",
-    "normalize_rows", "normalize_rows_f32", "round_to_dtype", "normalized_inputs",
+    "normalize_rows", "round_to_dtype", "normalized_inputs",
     "softmax_rows",
 ]
 
@@ -178,12 +179,12 @@ def quadratic_attention(Q, K, V, n: int) -> np.ndarray:
     Kh, _ = _heads(K)
     Vh, _ = _heads(V)
     N = Qh.shape[1]
-    mask = np.tril(np.ones((N, N), dtype=bool))
     out = np.empty(Vh.shape, dtype=np.float64)
     for h in range(Qh.shape[0]):
         P = taylor_kernel(Qh[h] @ Kh[h].T, n)
-        P = np.where(mask, P, 0.0)
-        out[h] = (P @ Vh[h]) / P.sum(axis=1, keepdims=True)
+        for i in range(N):  # row i sums over keys 0 .. i only
+            p = P[i, : i + 1]
+            out[h, i] = (p @ Vh[h, : i + 1]) / p.sum()
     return out.reshape(lead + Vh.shape[1:])
 
 
@@ -341,15 +342,16 @@ def prefill_from_numden(Q, K, V, S0, n: int) -> Tuple[np.ndarray, np.ndarray, np
     e = Vh.shape[2]
     W = state_rows(d, n)
     S0h = np.zeros((H, W, e + 1)) if S0 is None else np.asarray(S0, dtype=np.float64).reshape(H, W, e + 1)
-    mask = np.tril(np.ones((N, N), dtype=bool))
     num = np.empty((H, N, e))
     den = np.empty((H, N))
     S_all = np.empty((H, W, e + 1))
     for h in range(H):
         phi = feature_map(Qh[h], n, weighted=True)
         vp = np.concatenate([Vh[h], np.ones((N, 1))], axis=1)
-        P = np.where(mask, taylor_kernel(Qh[h] @ Kh[h].T, n), 0.0)
-        acc = phi @ S0h[h] + P @ vp
+        P = taylor_kernel(Qh[h] @ Kh[h].T, n)
+        acc = phi @ S0h[h]
+        for i in range(N):  # row i sums over the new keys 0 .. i only
+            acc[i] = acc[i] + P[i, : i + 1] @ vp[: i + 1]
         num[h] = acc[:, :e]
         den[h] = acc[:, e]
         S_all[h] = S0h[h] + states_definition(Kh[h], Vh[h], n)
@@ -434,49 +436,6 @@ def normalize_rows(X, scale: float = 1.0) -> np.ndarray:
         return X * (float(scale) / np.sqrt(np.sum(X * X, axis=-1, keepdims=True)))
 
 
-def normalize_rows_f32(X, scale: float = 1.0) -> np.ndarray:
-    """``normalize_rows`` evaluated in fp32 with a fixed operation order,
-    every operation IEEE fp32 round-to-nearest-even:
-
-    * squares fl(x_i * x_i) summed in groups of 8 consecutive coordinates,
-      in index order inside a group (a short last group is padded with
-      zeros, which leaves sums unchanged);
-    * the group sums added as a balanced pairwise tree, neighbours first:
-      ((g0 + g1) + (g2 + g3)) + ... (the group count padded with zero groups
-      to a power of two);
-    * f = fl(scale / sqrt(s)), then y_i = fl(x_i * f).
-
-    The unit rows are rounded to the input dtype afterwards; that rounding is
-    a discrete decision, so it is taken on the same fp32 value the kernels
-    compute, not on the fp64 quotient (an fp64 quotient lands on the other
-    side of a bf16 rounding boundary for about one coordinate in a hundred).
-    Within (d + 3) fp32 ulps of the fp64 ``normalize_rows``.  Rows of X must
-    be fp32 values (the library's inputs are fp32 or bf16).
-    """
-    X32 = np.asarray(X, dtype=np.float64).astype(np.float32)
-    if not np.array_equal(X32.astype(np.float64), np.asarray(X, dtype=np.float64), equal_nan=True):
-        raise ValueError("rows must hold fp32 values")
-    d = X32.shape[-1]
-    ngroups = 1
-    while ngroups * 8 < d:
-        ngroups *= 2
-    P = np.zeros(X32.shape[:-1] + (ngroups * 8,), dtype=np.float32)
-    P[..., :d] = X32
-    G = P.reshape(X32.shape[:-1] + (ngroups, 8))
-    sums = np.zeros(X32.shape[:-1] + (ngroups,), dtype=np.float32)
-    for e in range(8):
-        sums = sums + G[..., e] * G[..., e]
-    w = 1
-    while w < ngroups:
-        sums = sums.copy()
-        for j in range(0, ngroups - w, 2 * w):
-            sums[..., j] = sums[..., j] + sums[..., j + w]
-        w *= 2
-    with np.errstate(invalid="ignore", divide="ignore"):
-        f = np.float32(scale) / np.sqrt(sums[..., 0])
-        return (X32 * f[..., None]).astype(np.float64)
-
-
 def round_to_dtype(X, dtype: str) -> np.ndarray:
     """fp64 values rounded to the working dtype and returned as fp64.
 
@@ -496,14 +455,15 @@ def round_to_dtype(X, dtype: str) -> np.ndarray:
 
 def normalized_inputs(Q, K, temperature: float, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
     """(q_hat, k_hat): q_hat = round(tau q/||q||), k_hat = round(k/||k||),
-    with the quotients taken in fp32 (``normalize_rows_f32``).
+    the fp64 unit rows of ``normalize_rows`` rounded to the working dtype the
+    way the inputs are (``round_to_dtype``).
 
     The attention of the normalised path is then the definition above on
     these rows, e.g. quadratic_attention(q_hat, k_hat, V, n), whose kernel is
     K_n(tau q.k / (||q|| ||k||)) up to the rounding of the unit rows.
     """
-    return (round_to_dtype(normalize_rows_f32(Q, temperature), dtype),
-            round_to_dtype(normalize_rows_f32(K, 1.0), dtype))
+    return (round_to_dtype(normalize_rows(Q, temperature), dtype),
+            round_to_dtype(normalize_rows(K, 1.0), dtype))
 
 
 def softmax_rows(q_rows, K, V, rows: Sequence[int]) -> np.ndarray:

@@ -550,20 +550,29 @@ def pin_normalize_rows():
         assert np.allclose(orc.quadratic_attention(qh, kh, v, int(n_str)), ref, rtol=0, atol=1e-15)
 
 
-def pin_normalize_rows_f32():
-    """The fp32 evaluation stays within (d + 3) fp32 ulps of the fp64
-    normalisation (d roundings in the sum, then sqrt, division and product),
-    for row norms over six decades and temperatures around 1."""
-    g = np.random.Generator(np.random.PCG64(42))
-    for d in (1, 2, 16, 64):
-        X = g.standard_normal((400, d)) * 10.0 ** g.uniform(-3, 3, (400, 1))
-        X = X.astype(np.float32).astype(np.float64)
-        for tau in (1.0, 0.7, 1.5):
-            ref = orc.normalize_rows(X, tau)
-            got = orc.normalize_rows_f32(X, tau)
-            bound = (d + 3) * 2.0 ** -24 * tau
-            assert np.max(np.abs(got - ref)) <= bound, (d, tau)
-    assert np.isnan(orc.normalize_rows_f32([[0.0, 0.0]])).all()
+def pin_normalized_inputs():
+    """The normalised inputs are the fp64 unit rows rounded the way inputs
+    are rounded (fp32, then bf16, each to nearest even), worked by hand:
+    (21, 28) has norm 35, so the unit row is (3/5, 4/5); 3/5 =
+    1.0011001100...b x 2^-1 rounds up to 1.0011010b x 2^-1 = 0.6015625 in
+    bf16, and 4/5 = 1.1001100110...b x 2^-1 rounds up to 1.1001101b x 2^-1
+    = 0.80078125.  With temperature 2 the query row is (6/5, 8/5) =
+    1.0011001100...b x 2^0 and 1.1001100110...b x 2^0, giving 1.203125 and
+    1.6015625.  fp32 rows are the fp32 roundings of 3/5 and 4/5."""
+    q = np.array([[21.0, 28.0], [-3.0, 4.0]])
+    qh, kh = orc.normalized_inputs(q, q, 2.0, "bf16")
+    assert np.array_equal(kh, [[0.6015625, 0.80078125], [-0.6015625, 0.80078125]])
+    assert np.array_equal(qh, [[1.203125, 1.6015625], [-1.203125, 1.6015625]])
+    qf, kf = orc.normalized_inputs(q, q, 1.0, "f32")
+    assert np.array_equal(kf[0], np.array([0.6, 0.8], dtype=np.float32).astype(np.float64))
+    assert np.array_equal(qf, kf)
+    # an fp64 unit row that is not a dtype value is rounded, not truncated:
+    # every coordinate lies within half a bf16 ulp of the fp64 unit row
+    X = np.random.Generator(np.random.PCG64(43)).standard_normal((300, 16))
+    _, kb = orc.normalized_inputs(X, X, 1.0, "bf16")
+    u = orc.normalize_rows(X)
+    half_ulp = 2.0 ** (np.floor(np.log2(np.abs(u))) - 8)
+    assert np.all(np.abs(kb - u) <= half_ulp * (1 + 2.0 ** -20))
 
 
 def pin_round_to_dtype():
@@ -585,5 +594,5 @@ ALL_PINS = [
     pin_decode_equals_recurrence, pin_softmax_library, pin_softmax_convergence,
     pin_normalisation_required, pin_svd_rank, pin_special_cases, pin_convex_hull,
     pin_planes_layout, pin_quadratic_rows, pin_prefill_from_states, pin_prefill_from_numden,
-    pin_normalize_rows, pin_normalize_rows_f32, pin_round_to_dtype, pin_softmax_rows,
+    pin_normalize_rows, pin_normalized_inputs, pin_round_to_dtype, pin_softmax_rows,
 ]

@@ -151,7 +151,6 @@ def _softmax_rows_no_max(q_rows, K, V, rows):
 
 
 _orig_normalize = orc.normalize_rows
-_orig_normalize32 = orc.normalize_rows_f32
 _orig_round = orc.round_to_dtype
 
 
@@ -165,12 +164,6 @@ def _normalize_inverted_temperature(X, scale=1.0):
     return _orig_normalize(X, 1.0 / float(scale))
 
 
-def _normalize32_no_sqrt(X, scale=1.0):
-    X32 = np.asarray(X, dtype=np.float64).astype(np.float32)
-    with np.errstate(invalid="ignore", divide="ignore"):
-        return (X32 * (np.float32(scale) / np.sum(X32 * X32, axis=-1, keepdims=True))).astype(np.float64)
-
-
 def _round_truncating(X, dtype):
     if dtype != "bf16":
         return _orig_round(X, dtype)
@@ -179,6 +172,13 @@ def _round_truncating(X, dtype):
 
 
 _orig_numden = orc.prefill_from_numden
+_orig_normalized_inputs = orc.normalized_inputs
+
+
+def _normalized_inputs_tau_on_keys(Q, K, temperature, dtype):
+    # the temperature also scales the keys
+    return (orc.round_to_dtype(orc.normalize_rows(Q, temperature), dtype),
+            orc.round_to_dtype(orc.normalize_rows(K, temperature), dtype))
 
 
 def _numden_den_without_states(Q, K, V, S0, n):
@@ -209,7 +209,7 @@ MUTANTS = {
     "numden_den_without_states": ("prefill_from_numden", _numden_den_without_states),
     "normalize_no_sqrt": ("normalize_rows", _normalize_no_sqrt),
     "normalize_inverted_temperature": ("normalize_rows", _normalize_inverted_temperature),
-    "normalize_f32_no_sqrt": ("normalize_rows_f32", _normalize32_no_sqrt),
+    "normalized_inputs_tau_on_keys": ("normalized_inputs", _normalized_inputs_tau_on_keys),
     "softmax_rows_exclusive": ("softmax_rows", _softmax_rows_exclusive),
     "softmax_rows_no_max": ("softmax_rows", _softmax_rows_no_max),
     "round_bf16_truncating": ("round_to_dtype", _round_truncating),
@@ -221,7 +221,7 @@ _PINS = [pins.pin_hand_example, pins.pin_kron_features, pins.pin_unit_identity,
          pins.pin_planes_layout, pins.pin_exact_rational, pins.pin_chunk_additivity,
          pins.pin_recurrent_vs_quadratic, pins.pin_softmax_library,
          pins.pin_softmax_convergence, pins.pin_prefill_from_states, pins.pin_prefill_from_numden,
-         pins.pin_normalize_rows, pins.pin_normalize_rows_f32, pins.pin_round_to_dtype,
+         pins.pin_normalize_rows, pins.pin_normalized_inputs, pins.pin_round_to_dtype,
          pins.pin_softmax_rows]
 
 

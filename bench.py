@@ -106,6 +106,7 @@ def bench_prefill(args, torch, ops, wl):
     # algorithmic bytes per call: q, k (bf16) + v (bf16) read, O (fp32) written, final states written
     alg_bytes = head_tokens * (2 * w.dk * 2 + w.dv * 2 + w.dv * 4) + w.B * w.H * ops.tt_state_floats(w.dk, w.dv, w.n) * 4
     achieved = alg_bytes / t_step / 1e9
+    alg_flops = 4.0 * ops.tt_state_rows(w.dk, w.n) * (w.dv + 1) * head_tokens
     src = _source_hash("tt_prefill.hip", "tt_device.hpp")
     # the same workload continued from carried-in states (read once more)
     S_in = S.clone()
@@ -165,7 +166,12 @@ def bench_prefill(args, torch, ops, wl):
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": _traffic("prefill", src), "alg_bytes_per_launch": alg_bytes,
-                     "source_hash": src},
+                     "source_hash": src,
+                     # the contraction work of the same call against the bf16 MFMA peak
+                     # (4 W (dv+1) flops per head-token: readout plus state update)
+                     "mfma": {"alg_flops_per_launch": alg_flops,
+                              "achieved_TFLOPs": round(alg_flops / t_step / 1e12, 2), "peak_TFLOPs": 2516.6,
+                              "frac": round(alg_flops / t_step / 1e12 / 2516.6, 4)}},
         "inputs": (q, k, v),
     }
 
@@ -218,45 +224,54 @@ def bench_prefill_other(name, args, torch, ops, wl):
 
 def bench_orders(args, torch, ops, wl):
     """The variant axis: time per call of the prefill workload's shape
-    (B=4, H=8, N=8192, dk=16, bf16) for n = 1 .. 5 Taylor terms, and the
-    largest deviation from exact softmax attention of the GPU outputs on a
-    small seeded case (B=1, H=4, N=512).  The softmax reference is torch's
-    causal attention with scale 1 in fp64 on the CPU."""
+    (B=4, H=8, N=8192, dv=64) for n = 1 .. 5 Taylor terms at dk=16 (bf16)
+    and n = 1 .. 6 at dk=8 (fp32), and the largest deviation from exact
+    softmax attention of the GPU outputs on a small seeded case (B=1, H=4,
+    N=512).  The softmax reference is torch's causal attention with scale 1
+    in fp64 on the CPU."""
     import math
     import numpy as np
     w = wl.WORKLOADS["prefill"]
     dev = torch.device("cuda:0")
 
     def to_dev(r):
+        if r.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(r.device)).to(dev)
         return torch.from_numpy(np.ascontiguousarray(r.device).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    q, k, v = wl.draw_qkv(w.seed, w.B, w.H, w.N, w.dk, w.dv, w.dtype)
-    Q, K, V = to_dev(q), to_dev(k), to_dev(v)
-    qs, ks, vs = wl.draw_qkv(4000, 1, 4, 512, w.dk, w.dv, w.dtype)
-    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a.exact, dtype=np.float64)) for a in (qs, ks, vs))
-    o_soft = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=1.0).numpy()
-    Qs, Ks, Vs = to_dev(qs), to_dev(ks), to_dev(vs)
     rows = []
-    for n in range(1, 6):
-        O = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.float32, device=dev)
-        S = torch.empty(w.B * w.H * ops.tt_state_floats(w.dk, w.dv, n), dtype=torch.float32, device=dev)
-        ws = torch.empty(ops.tt_prefill_workspace_bytes(w.B, w.H, w.N, w.dk, w.dv, n, w.chunk), dtype=torch.uint8,
-                         device=dev)
+    for dk, dtype, nmax in ((16, "bf16", 5), (8, "f32", 6)):
+        q, k, v = wl.draw_qkv(w.seed, w.B, w.H, w.N, dk, w.dv, dtype)
+        Q, K, V = to_dev(q), to_dev(k), to_dev(v)
+        qs, ks, vs = wl.draw_qkv(4000, 1, 4, 512, dk, w.dv, dtype)
+        tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a.exact, dtype=np.float64)) for a in (qs, ks, vs))
+        o_soft = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=1.0).numpy()
+        Qs, Ks, Vs = to_dev(qs), to_dev(ks), to_dev(vs)
+        for n in range(1, nmax + 1):
+            O = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.float32, device=dev)
+            S = torch.empty(w.B * w.H * ops.tt_state_floats(dk, w.dv, n), dtype=torch.float32, device=dev)
+            ws = torch.empty(ops.tt_prefill_workspace_bytes(w.B, w.H, w.N, dk, w.dv, n, w.chunk), dtype=torch.uint8,
+                             device=dev)
 
-        def step():
-            ops.tt_prefill(Q, K, V, n, w.chunk, O=O, states=S, workspace=ws)
+            def step():
+                ops.tt_prefill(Q, K, V, n, w.chunk, O=O, states=S, workspace=ws)
 
-        _prewarm(step, torch, 0.05)
-        steps = max(2, min(args.steps, 20))
-        t = _time_events(step, steps, torch) / steps
-        o_small, _ = ops.tt_prefill(Qs, Ks, Vs, n)
-        err = float(np.max(np.abs(o_small.cpu().numpy().astype(np.float64) - o_soft)))
-        rows.append({"n": n, "state_rows": ops.tt_state_rows(w.dk, n), "ms_per_call": round(t * 1e3, 4),
-                     "tokens_per_s": round(w.B * w.N / t, 1), "max_abs_err_vs_softmax": err,
-                     "taylor_eps": math.e / math.factorial(n)})
-        print(f"# n={n}: {t * 1e6:.1f} us/call, max|o - softmax| = {err:.2e}", file=sys.stderr, flush=True)
-    return {"workload": w.name.replace("n3", "n1..5"), "softmax_check": "B1 H4 N512 dk16 bf16, seed 4000",
-            "orders": rows}
+            _prewarm(step, torch, 0.05)
+            steps = max(2, min(args.steps, 20))
+            t = _time_events(step, steps, torch) / steps
+            o_small, _ = ops.tt_prefill(Qs, Ks, Vs, n)
+            err = float(np.max(np.abs(o_small.cpu().numpy().astype(np.float64) - o_soft)))
+            W = ops.tt_state_rows(dk, n)
+            flops = 4.0 * W * (w.dv + 1) * w.B * w.H * w.N
+            rows.append({"dk": dk, "dtype": dtype, "n": n, "state_rows": W, "ms_per_call": round(t * 1e3, 4),
+                         "tokens_per_s": round(w.B * w.N / t, 1),
+                         "alg_TFLOPs": round(flops / t / 1e12, 2),
+                         "max_abs_err_vs_softmax": err, "taylor_eps": math.e / math.factorial(n)})
+            print(f"# dk={dk} {dtype} n={n}: {t * 1e6:.1f} us/call, max|o - softmax| = {err:.2e}", file=sys.stderr,
+                  flush=True)
+            del O, S, ws
+    return {"workload": "prefill B4 H8 N8192 dv64: dk16 bf16 n=1..5, dk8 fp32 n=1..6",
+            "softmax_check": "B1 H4 N512 (same dk and dtype), seed 4000", "orders": rows}
 
 
 def _loglog_slope(xs, ys):
@@ -408,21 +423,51 @@ def bench_decode(args, torch, ops, wl):
     vs = torch.randn((T, w.B, w.H, w.dv), generator=g, device=dev)
     o = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+    state_bytes = BH * nf * 4
+    alg_bytes = 2 * state_bytes + BH * (2 * w.dk + w.dv) * 4 + BH * w.dv * 4
 
     def run(steps):
         for t in range(steps):
             ops.tt_decode_step(qs[t % T], ks[t % T], vs[t % T], states, w.n, o=o)
 
+    # 1. one state set, steps back to back: the 81.5 MB state stays in the
+    #    256 MB infinity cache (MALL) between steps
     _prewarm(lambda: run(8), torch)
     run(min(args.warmup * 4, T))
-    t = _time_events(lambda: run(T), 1, torch)
-    t_step = t / T
-    state_bytes = BH * nf * 4
-    alg_bytes = 2 * state_bytes + BH * (2 * w.dk + w.dv) * 4 + BH * w.dv * 4
+    t_warm = _time_events(lambda: run(T), 1, torch) / T
+    # 2. steady state from HBM: R distinct state sets (R x 81.5 MB, larger
+    #    than the MALL), step t on set t % R, so every step reads a state
+    #    last touched R - 1 steps (>= 245 MB of traffic) earlier
+    R = 5
+    sets = [states] + [states.clone() for _ in range(R - 1)]
+
+    def run_rot(steps):
+        for t in range(steps):
+            ops.tt_decode_step(qs[t % T], ks[t % T], vs[t % T], sets[t % R], w.n, o=o)
+
+    _prewarm(lambda: run_rot(2 * R), torch)
+    run_rot(min(args.warmup * 4, T))
+    t_step = _time_events(lambda: run_rot(T), 1, torch) / T
     achieved = alg_bytes / t_step / 1e9
-    # MALL-cold variant: reading a 512 MB buffer between steps evicts the state
-    # from the 256 MB infinity cache and leaves only clean lines behind (a
-    # write would leave dirty lines whose write-back competes with the step)
+    # 3. the same T steps captured once as a HIP graph and replayed (no
+    #    per-launch host cost); rotating sets and the single set
+    graphs = {}
+    for name, fn in (("rotating", run_rot), ("single", run)):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(2 * R)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn(T)
+        torch.cuda.synchronize()
+        _prewarm(gr.replay, torch, 0.05)
+        graphs[name] = _time_events(gr.replay, 4, torch) / (4 * T)
+        del gr
+    # 4. one step right after a 512 MB read that evicts the state (includes
+    #    the latency of a single launch after an idle GPU)
     flush = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device=dev)
     s = torch.cuda.current_stream()
     cold = []
@@ -435,7 +480,7 @@ def bench_decode(args, torch, ops, wl):
         e1.record(s)
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1) / 1e3)
-    del flush
+    del flush, sets
     t_cold = sorted(cold)[len(cold) // 2]
     # raw q, k normalised inside the decode kernel (temperature 1)
     qr = torch.randn((T, w.B, w.H, w.dk), generator=g, device=dev)
@@ -448,14 +493,20 @@ def bench_decode(args, torch, ops, wl):
     _prewarm(lambda: run_normed(8), torch, 0.05)
     t_normed = _time_events(lambda: run_normed(T), 1, torch) / T
     src = _source_hash("tt_decode.hip", "tt_device.hpp")
+    frac = lambda t: round(alg_bytes / t / 1e9 / HBM_PEAK_GBS, 4)
     return {
-        "us_per_step": t_step * 1e6, "us_per_step_mall_cold": t_cold * 1e6, "steps": T,
+        "us_per_step": t_step * 1e6, "steps": T,
+        "timing": f"{T} back-to-back steps rotating over {R} distinct state sets ({R * state_bytes / 1e6:.0f} MB, "
+                  f"larger than the 256 MB MALL): steady-state HBM",
+        "us_per_step_mall_warm": round(t_warm * 1e6, 3), "frac_mall_warm": frac(t_warm),
+        "us_per_step_graph": round(graphs["rotating"] * 1e6, 3), "frac_graph": frac(graphs["rotating"]),
+        "us_per_step_graph_mall_warm": round(graphs["single"] * 1e6, 3),
+        "us_per_step_single_after_flush": round(t_cold * 1e6, 3),
         "us_per_step_normed": round(t_normed * 1e6, 3),
         "workload": w.name,
         "roofline": {"bound": "hbm", "kernel": "decode_kernel<16,3,float,false>", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "achieved_mall_cold": round(alg_bytes / t_cold / 1e9, 1),
-                     "frac_mall_cold": round(alg_bytes / t_cold / 1e9 / HBM_PEAK_GBS, 4),
+                     "state_source": "HBM (rotating state sets)",
                      "traffic": _traffic("decode", src), "alg_bytes_per_launch": alg_bytes,
                      "source_hash": src},
     }
@@ -466,12 +517,26 @@ def cpu_baselines(pre, wl):
     import numpy as np
     import oracle.taylor_oracle as orc
     cores = len(os.sched_getaffinity(0))
+    blas = "unknown"
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
         blas_threads = max([i.get("num_threads", 1) for i in info] or [1])
+        b = [i for i in info if i.get("user_api") == "blas"]
+        if b:
+            blas = f"{b[0].get('internal_api')} {b[0].get('version')} ({b[0].get('threading_layer')}, " \
+                   f"{b[0].get('architecture')})"
     except Exception:
         blas_threads = cores
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     w = wl.WORKLOADS["prefill"]
     q, k, v = pre["inputs"]
     # prefill: the quadratic-form definition plus the states, head by head,
@@ -487,7 +552,7 @@ def cpu_baselines(pre, wl):
     t_head = t_all / heads
     # tokens/s of the whole workload: one head-sequence is 1/(B*H) of the work
     pre_cpu = {"value": round(w.B * w.N / (t_head * w.B * w.H), 2), "unit": "tokens/s",
-               "cores": blas_threads, "kind": "oracle",
+               "cores": blas_threads, "kind": "oracle", "cpu": cpu_model, "blas": blas,
                "sample": f"{heads} of {w.B * w.H} heads (N={w.N}): quadratic form + state definition, fp64, "
                          f"{t_all:.1f} s; scaled to B*H heads"}
     # decode: the oracle's decode step vectorised over all 2048 states, 2 steps
@@ -503,6 +568,7 @@ def cpu_baselines(pre, wl):
         steps += 1
     t_dec = (time.perf_counter() - t0) / steps
     dec_cpu = {"value": round(t_dec * 1e6, 1), "unit": "us/step", "cores": blas_threads, "kind": "oracle",
+               "cpu": cpu_model, "blas": blas,
                "sample": f"{steps} full decode steps over all {d.B * d.H} states, fp64 "
                          f"({t_dec * steps:.1f} s)"}
     return pre_cpu, dec_cpu, cores
@@ -519,7 +585,8 @@ def main():
                     help="print the comparison with exact softmax attention (prefill N sweep, decode vs context) "
                          "instead")
     ap.add_argument("--orders", action="store_true",
-                    help="print the order sweep (n = 1..5: time per call and error against softmax) instead")
+                    help="print the order sweep (dk16 n = 1..5, dk8 n = 1..6: time per call and error against "
+                         "softmax) instead")
     ap.add_argument("--calibrate", action="store_true",
                     help="run only tt_state_merge over 2 x 256 MiB -> 256 MiB (known HBM bytes), "
                          "to scale the FETCH_SIZE / WRITE_SIZE counters")

@@ -36,12 +36,23 @@
  *     describes the problem (thread-local, valid until the next call on the
  *     same thread).
  *   - Inputs are used as given: q and k are NOT re-normalised (unit norm is
- *     the caller's precondition), except by the *_normed entry points.  NaN/Inf inputs propagate; a zero
- *     normaliser (possible for n = 2, where K_2(-1) = 0) gives IEEE Inf/NaN.
+ *     the caller's precondition), except by the *_normed entry points.
+ *   - Non-finite inputs propagate.  A NaN or Inf in token j reaches the
+ *     outputs of tokens i >= j and the states, as the definition says; in
+ *     addition, a non-finite value v_j can reach the outputs of the earlier
+ *     queries of its own prefill chunk (the intra-chunk product multiplies
+ *     their masked zero weights by v_j), in the value columns where v_j is
+ *     not finite.  Outputs of earlier chunks are not affected.  A normaliser
+ *     that is exactly zero (possible for n = 2, where K_2(-1) = 0) gives
+ *     0/0 = NaN; with bf16 inputs, after the first chunk of a span, the
+ *     rounding of the state readout can leave a tiny nonzero normaliser
+ *     instead.
  *   - Outputs must not alias inputs unless stated.
- *   - Supported shapes: dv = 64; (dk, n) with dk in {16, 32, 64} and
- *     W <= 4845, i.e. dk=16: n in 1..5, dk=32: n in 1..3, dk=64: n in 1..3.
- *     Other shapes return TT_ERR_UNSUPPORTED.
+ *   - Supported shapes: dv = 64; (dk, n) with dk in {8, 16, 32, 64}:
+ *     dk=8: n in 1..6 (W up to 1287), dk=16: n in 1..5 (W up to 4845),
+ *     dk=32 and dk=64: n in 1..3.  The dk = 8 prefill takes fp32 inputs
+ *     (bf16 returns TT_ERR_UNSUPPORTED); its decode takes both.  Other
+ *     shapes return TT_ERR_UNSUPPORTED.
  */
 #ifndef TAYLOR_STATES_H
 #define TAYLOR_STATES_H
@@ -142,16 +153,18 @@ int tt_prefill_from_unnormalized(const void *Q, const void *K, const void *V, tt
  * keep q.k inside the series' convergence radius, and without it more terms
  * stop helping).  Every row x of d values becomes
  *     r(scale * x / ||x||_2),
- * computed with IEEE fp32 operations rounded to nearest even in a fixed
- * order (s = sum of x_i*x_i, no fused multiply-add, summed in groups of 8
- * consecutive coordinates in index order, the group sums added as a
- * balanced pairwise tree, neighbours first; f = scale / sqrt(s); x_i * f),
- * then rounded by r to the input dtype (bf16: round to nearest even; fp32:
- * as computed).  The result is a fixed function of the input bits.  A zero
- * row gives NaN.
+ * where r rounds once to the nearest value of the input dtype (ties to
+ * even; bf16 from the fp64 value directly, not through a rounded fp32
+ * value).  The quotient is evaluated in fp64
+ * in a fixed order (s = sum of x_i*x_i, exact squares, summed in groups of 8
+ * consecutive coordinates and a balanced pairwise tree over the groups;
+ * f = scale / sqrt(s); x_i * f), within about 10 fp64 ulps of the exact
+ * unit coordinate, so the result is the correctly rounded unit row except
+ * for coordinates whose exact value lies that close to a rounding boundary.
+ * The result is a fixed function of the input bits.  A zero row gives NaN.
  *   x, out : [rows][d] in_dtype, 16-byte aligned; out may be x (in place)
  *            but must not otherwise overlap it
- *   d      : 16, 32 or 64 (TT_ERR_UNSUPPORTED otherwise)
+ *   d      : 8, 16, 32 or 64 (TT_ERR_UNSUPPORTED otherwise)
  *   scale  : finite and > 0 (TT_ERR_INVALID_ARG otherwise)
  * rows == 0 is a no-op.  The *_normed entry points below apply exactly this
  * function (with scale = temperature for q and 1 for k) inside the library. */

@@ -25,8 +25,8 @@ Readings where the pages leave a step open:
 * no temperature inside the exponential: the kernel is K_n(q.k) on inputs
   the caller has already L2-normalised; the optional normalised path
   (``normalized_inputs``) makes the unit rows itself in fp64, folds a
-  temperature tau into the queries, and rounds the unit rows to the input
-  dtype the way the inputs are rounded;
+  temperature tau into the queries, and rounds each unit coordinate once to
+  the nearest value of the input dtype;
 * "n terms" means the orders 0 .. n-1;
 * the state stores *raw* symmetric monomials mu_t(k) = prod_l k_{t_l}; the
   multinomial weight 1/alpha(t)! lives on the query side,
@@ -437,26 +437,39 @@ def normalize_rows(X, scale: float = 1.0) -> np.ndarray:
 
 
 def round_to_dtype(X, dtype: str) -> np.ndarray:
-    """fp64 values rounded to the working dtype and returned as fp64.
+    """fp64 values rounded once to the nearest value of the working dtype,
+    ties to even, returned as fp64.
 
-    "f32": round to nearest even fp32.  "bf16": to fp32, then to bf16 by
-    round to nearest even (torch's CPU cast).  The normalised inputs are
-    rounded back to the dtype the caller's q and k came in, so a prefill on
-    raw inputs sees the same values as one on inputs normalised beforehand.
+    "f32": numpy's fp64 -> fp32 cast.  "bf16": 8 significant bits (the
+    fp32 exponent range): with |x| = m 2^p, m in [0.5, 1), the spacing of
+    bf16 values around x is u = 2^(p-8) (at least 2^-133, the subnormal
+    spacing), and x is rounded to rint(x / u) u, where rint rounds half to
+    even; x / u is exact (a power-of-two scaling).  Values beyond the largest
+    bf16 round to infinity.  This is the correctly rounded unit row of the
+    normalised path; rounding to fp32 first would round twice.
     """
-    import torch
-    x32 = torch.from_numpy(np.ascontiguousarray(X, dtype=np.float64)).to(torch.float32)
+    X = np.asarray(X, dtype=np.float64)
     if dtype == "f32":
-        return x32.to(torch.float64).numpy()
+        with np.errstate(over="ignore"):
+            return X.astype(np.float32).astype(np.float64)
     if dtype == "bf16":
-        return x32.to(torch.bfloat16).to(torch.float64).numpy()
+        out = X.copy()
+        fin = np.isfinite(X) & (X != 0.0)
+        x = X[fin]
+        _, p = np.frexp(np.abs(x))
+        u = np.ldexp(1.0, np.maximum(p - 8, -133))
+        r = np.rint(x / u) * u
+        big = (2.0 - 2.0 ** -7) * 2.0 ** 127
+        r = np.where(np.abs(r) > big, np.copysign(np.inf, r), r)
+        out[fin] = r
+        return out
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
 def normalized_inputs(Q, K, temperature: float, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
     """(q_hat, k_hat): q_hat = round(tau q/||q||), k_hat = round(k/||k||),
-    the fp64 unit rows of ``normalize_rows`` rounded to the working dtype the
-    way the inputs are (``round_to_dtype``).
+    the fp64 unit rows of ``normalize_rows`` rounded once to the nearest
+    value of the working dtype (``round_to_dtype``).
 
     The attention of the normalised path is then the definition above on
     these rows, e.g. quadratic_attention(q_hat, k_hat, V, n), whose kernel is

@@ -1,15 +1,19 @@
 """Builds libtaylor_states.so in-tree with hipcc for gfx950.
 
-    python -m taylor_recurrent_states_amd.build [-v]
+    python -m taylor_recurrent_states_amd.build [-v] [--resource-usage]
 
 Every source is compiled on each call (this is the "does it build" check);
 objects go to ``_build/`` next to this file, the library next to this file.
+``--resource-usage`` also prints, per kernel, the registers, scratch
+(spill) bytes, occupancy and LDS the compiler assigned (its
+kernel-resource-usage remarks).
 """
 
 from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -31,9 +35,11 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
+def _compile(src: str, verbose: bool, remarks: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if remarks:
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,14 +47,42 @@ def _compile(src: str, verbose: bool) -> str:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
     if verbose and r.stderr.strip():
         print(r.stderr, file=sys.stderr)
+    if remarks:
+        _REMARKS[src] = r.stderr
     return obj
 
 
-def build(verbose: bool = False) -> str:
+_REMARKS = {}
+_FIELDS = {"VGPRs": "vgpr", "AGPRs": "agpr", "SGPRs": "sgpr", "ScratchSize [bytes/lane]": "scratch",
+           "Occupancy [waves/SIMD]": "occupancy", "LDS Size [bytes/block]": "lds"}
+
+
+def resource_usage():
+    """[(source, demangled kernel, {field: value})] from the compiler's
+    kernel-resource-usage remarks of the last build(resource=True)."""
+    out = []
+    for src, text in _REMARKS.items():
+        cur = None
+        for line in text.splitlines():
+            m = re.search(r"Function Name: (\S+)", line)
+            if m:
+                name = subprocess.run(["c++filt", m.group(1)], capture_output=True, text=True).stdout.strip()
+                name = re.sub(r"tt::\(anonymous namespace\)::", "", name)
+                cur = {}
+                out.append((src, re.sub(r"\(.*", "", name), cur))
+                continue
+            for key, field in _FIELDS.items():
+                m = re.search(re.escape(key) + r": (\d+)", line)
+                if m and cur is not None:
+                    cur[field] = int(m.group(1))
+    return out
+
+
+def build(verbose: bool = False, resource: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, verbose, resource), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
@@ -61,4 +95,11 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    lib = build(verbose="-v" in sys.argv, resource="--resource-usage" in sys.argv)
+    if "--resource-usage" in sys.argv:
+        print(f"{'source':15} {'vgpr':>4} {'agpr':>4} {'sgpr':>4} {'scratch':>7} {'occ':>3} {'lds':>6}  kernel")
+        for src, name, f in resource_usage():
+            print(f"{src:15} {f.get('vgpr', 0):4d} {f.get('agpr', 0):4d} {f.get('sgpr', 0):4d} "
+                  f"{f.get('scratch', 0):7d} {f.get('occupancy', 0):3d} {f.get('lds', 0):6d}  {name}")
+    else:
+        print(lib)

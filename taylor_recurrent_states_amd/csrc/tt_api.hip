@@ -31,6 +31,7 @@ static int hip_status(hipError_t e, const char* what) {
 
 static bool shape_supported(int dk, int dv, int n) {
   if (dv != 64 || n < 1) return false;
+  if (dk == 8) return n <= 6;
   if (dk == 16) return n <= 5;
   if (dk == 32 || dk == 64) return n <= 3;
   return false;
@@ -40,8 +41,9 @@ static int check_shape(int dk, int dv, int n) {
   if (dk < 1 || dv < 1 || n < 1) return fail(TT_ERR_INVALID_ARG, "dk=%d dv=%d n=%d must be >= 1", dk, dv, n);
   if (!shape_supported(dk, dv, n))
     return fail(TT_ERR_UNSUPPORTED,
-                "(dk=%d, dv=%d, n=%d) not compiled: dv must be 64; dk=16 with n<=5, dk=32/64 with n<=3", dk,
-                dv, n);
+                "(dk=%d, dv=%d, n=%d) not compiled: dv must be 64; dk=8 with n<=6, dk=16 with n<=5, dk=32/64 "
+                "with n<=3",
+                dk, dv, n);
   return TT_OK;
 }
 
@@ -174,11 +176,15 @@ int tt_prefill_workspace_bytes(int B, int H, int N, int dk, int dv, int n, int c
   int rc = check_shape(dk, dv, n);
   if (rc) return rc;
   // the query takes no dtype: report the larger of the fp32 and bf16 plans
+  // (dk = 8 runs on fp32 inputs only)
   PrefillPlan pf, pb;
   rc = plan_prefill(B, H, N, dk, dv, n, chunk, TT_F32, &pf);
   if (rc) return rc;
-  rc = plan_prefill(B, H, N, dk, dv, n, chunk, TT_BF16, &pb);
-  if (rc) return rc;
+  pb.ws_floats = 0;
+  if (dk >= 16) {
+    rc = plan_prefill(B, H, N, dk, dv, n, chunk, TT_BF16, &pb);
+    if (rc) return rc;
+  }
   *bytes = (pf.ws_floats > pb.ws_floats ? pf.ws_floats : pb.ws_floats) * sizeof(float);
   return ok();
 }
@@ -227,7 +233,8 @@ int tt_normalize_rows(const void* x, tt_dtype in_dtype, size_t rows, int d, floa
   int rc = check_dtype(in_dtype);
   if (rc) return rc;
   if (d < 1) return fail(TT_ERR_INVALID_ARG, "d=%d must be >= 1", d);
-  if (d != 16 && d != 32 && d != 64) return fail(TT_ERR_UNSUPPORTED, "d=%d not compiled (16, 32 or 64)", d);
+  if (d != 8 && d != 16 && d != 32 && d != 64)
+    return fail(TT_ERR_UNSUPPORTED, "d=%d not compiled (8, 16, 32 or 64)", d);
   if (!valid_scale(scale)) return fail(TT_ERR_INVALID_ARG, "scale %g must be finite and positive", (double)scale);
   if ((((uintptr_t)x) | ((uintptr_t)out)) & 15u) return fail(TT_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
   const size_t nb = rows * (size_t)d * (in_dtype == TT_F32 ? 4 : 2);

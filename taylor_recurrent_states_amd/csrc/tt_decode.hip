@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kDecodeThreads, 8) void decode_kernel(const TIn* __
     __syncthreads();
     if (tid == 0 || tid == 64) {
       float* row = tid == 0 ? s_q : s_k;
-      const float f = row_norm_factor<DK>([&](int i) { return row[i]; }, tid == 0 ? qscale : 1.0f);
+      const double f = row_norm_factor<DK>([&](int i) { return row[i]; }, tid == 0 ? qscale : 1.0f);
       for (int i = 0; i < DK; ++i) row[i] = unit_coord<TIn>(row[i], f);
     }
     load_state();
@@ -89,8 +89,8 @@ __global__ __launch_bounds__(kDecodeThreads, 8) void decode_kernel(const TIn* __
   __syncthreads();
   for (int r = tid; r < W; r += kDecodeThreads) {
     const uint32_t code = tab.code[r];
-    s_mu[r] = monomial(code, [&](int i) { return s_k[i]; });
-    s_phi[r] = tab.weight[r] * monomial(code, [&](int i) { return s_q[i]; });
+    s_mu[r] = monomial<DK>(code, [&](int i) { return s_k[i]; });
+    s_phi[r] = tab.weight[r] * monomial<DK>(code, [&](int i) { return s_q[i]; });
   }
   __syncthreads();
 
@@ -162,7 +162,7 @@ __global__ void feature_map_kernel(const TIn* __restrict__ x, size_t rows, int W
     const size_t row = e / W;
     const int t = (int)(e - row * W);
     const uint32_t code = tab.code[t];
-    float val = monomial(code, [&](int i) { return load_f32(x, row * DK + i); });
+    float val = monomial<DK>(code, [&](int i) { return load_f32(x, row * DK + i); });
     if (weighted) val *= tab.weight[t];
     out[e] = val;
   }
@@ -206,10 +206,10 @@ __global__ __launch_bounds__(256) void normalize_kernel(const TIn* x0, TIn* out0
       else
         x[e] = __uint_as_float(seg[e >> 2][e & 3]);
     }
-    float ss = group_sumsq([&](int i) { return x[i & 7]; }, g);
+    double ss = group_sumsq([&](int i) { return x[i & 7]; }, g);
 #pragma unroll
     for (int o = 1; o < G; o *= 2) ss = ss + __shfl_xor(ss, o);
-    const float f = (first ? s0 : s1) / sqrtf(ss);
+    const double f = (double)(first ? s0 : s1) / sqrt(ss);
     if (live) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = unit_coord<TIn>(x[e], f);
@@ -284,11 +284,13 @@ hipError_t launch_normalize(tt_dtype dt, int d, const void* x0, void* out0, floa
   hipLaunchKernelGGL((normalize_kernel<D, T>), dim3(grid), dim3(block), 0, s, (const T*)x0, (T*)out0, s0, \
                      rows0, (const T*)x1, (T*)out1, s1, rows1)
   if (dt == TT_F32) {
-    if (d == 16) TT_NORM(16, float);
+    if (d == 8) TT_NORM(8, float);
+    else if (d == 16) TT_NORM(16, float);
     else if (d == 32) TT_NORM(32, float);
     else TT_NORM(64, float);
   } else {
-    if (d == 16) TT_NORM(16, uint16_t);
+    if (d == 8) TT_NORM(8, uint16_t);
+    else if (d == 16) TT_NORM(16, uint16_t);
     else if (d == 32) TT_NORM(32, uint16_t);
     else TT_NORM(64, uint16_t);
   }
@@ -304,11 +306,13 @@ hipError_t launch_feature_map(const void* x, tt_dtype dt, size_t rows, int dk, i
 #define TT_FEAT(DK, T) \
   hipLaunchKernelGGL((feature_map_kernel<DK, T>), dim3(grid), dim3(block), 0, s, (const T*)x, rows, W, weighted, out)
   if (dt == TT_F32) {
-    if (dk == 16) TT_FEAT(16, float);
+    if (dk == 8) TT_FEAT(8, float);
+    else if (dk == 16) TT_FEAT(16, float);
     else if (dk == 32) TT_FEAT(32, float);
     else TT_FEAT(64, float);
   } else {
-    if (dk == 16) TT_FEAT(16, uint16_t);
+    if (dk == 8) TT_FEAT(8, uint16_t);
+    else if (dk == 16) TT_FEAT(16, uint16_t);
     else if (dk == 32) TT_FEAT(32, uint16_t);
     else TT_FEAT(64, uint16_t);
   }

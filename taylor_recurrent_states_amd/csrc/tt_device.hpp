@@ -20,9 +20,10 @@ namespace tt {
 // ---------------------------------------------------------------------------
 // Compile-time row tables.  One table per supported key width holds the rows
 // of the largest supported order; smaller orders use a prefix (blocks are in
-// ascending m).  Entry: code = idx0 | idx1<<6 | idx2<<12 | idx3<<18 | m<<24
-// | w<<27, where w indexes 1/alpha(t)! in {1, 1/2, 1/4, 1/6, 1/24}; weight =
-// 1/alpha(t)! rounded to fp32.
+// ascending m).  Entry: code = idx0 | idx1 << B | idx2 << 2B | ... | m << 24
+// | w << 27, with B = index_bits(dk) bits per index (enough for dk - 1), m
+// the order and w indexing 1/alpha(t)! in {1, 1/2, 1/4, 1/6, 1/12, 1/24,
+// 1/120}; weight = 1/alpha(t)! rounded to fp32.
 // ---------------------------------------------------------------------------
 
 constexpr int binom(int a, int b) {
@@ -34,19 +35,30 @@ constexpr int binom(int a, int b) {
 
 constexpr int rows_for(int dk, int n) { return binom(dk + n - 1, n - 1); }
 
+// bits per index in a row code, and the number of Taylor terms compiled for
+// each key width (the largest order is max_terms - 1)
+constexpr int index_bits(int dk) { return dk <= 8 ? 3 : dk <= 16 ? 4 : dk <= 32 ? 5 : 6; }
+constexpr int max_terms(int dk) { return dk <= 8 ? 6 : dk <= 16 ? 5 : 3; }
+static_assert(index_bits(8) * 5 <= 24 && index_bits(16) * 4 <= 24 && index_bits(64) * 2 <= 24, "code fields");
+
+constexpr uint32_t weight_index(int denom) {
+  return denom == 1 ? 0u : denom == 2 ? 1u : denom == 4 ? 2u : denom == 6 ? 3u : denom == 12 ? 4u : denom == 24 ? 5u : 6u;
+}
+
 template <int DK, int NMAX>
 struct RowTable {
   static constexpr int W = rows_for(DK, NMAX);
+  static constexpr int IB = index_bits(DK);
   uint32_t code[W];
   float weight[W];
   constexpr RowTable() : code(), weight() {
     int r = 0;
     for (int m = 0; m < NMAX; ++m) {
-      int t[4] = {0, 0, 0, 0};
+      int t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       bool more = true;
       while (more) {
         uint32_t c = (uint32_t)m << 24;
-        for (int l = 0; l < m; ++l) c |= (uint32_t)t[l] << (6 * l);
+        for (int l = 0; l < m; ++l) c |= (uint32_t)t[l] << (IB * l);
         // 1 / prod over runs of equal indices of (run length)!
         int denom = 1, run = 1;
         for (int l = 1; l <= m; ++l) {
@@ -57,8 +69,7 @@ struct RowTable {
             run = 1;
           }
         }
-        const uint32_t widx = denom == 1 ? 0u : denom == 2 ? 1u : denom == 4 ? 2u : denom == 6 ? 3u : 4u;
-        code[r] = c | (widx << 27);
+        code[r] = c | (weight_index(denom) << 27);
         weight[r] = 1.0f / (float)denom;
         ++r;
         // next non-decreasing tuple in lexicographic order
@@ -78,34 +89,43 @@ struct RowTable {
 static_assert(rows_for(16, 3) == 153, "W(16,3)");
 static_assert(rows_for(16, 5) == 4845, "W(16,5)");
 static_assert(rows_for(64, 3) == 2145, "W(64,3)");
+static_assert(rows_for(8, 6) == 1287, "W(8,6)");
 
 // Device copies, constant-initialised in each code object (read-only).
+static __device__ const RowTable<8, 6> kRows8 = RowTable<8, 6>();
 static __device__ const RowTable<16, 5> kRows16 = RowTable<16, 5>();
 static __device__ const RowTable<32, 3> kRows32 = RowTable<32, 3>();
 static __device__ const RowTable<64, 3> kRows64 = RowTable<64, 3>();
 
 template <int DK> struct RowsOf;
+template <> struct RowsOf<8> { static __device__ const RowTable<8, 6>& get() { return kRows8; } };
 template <> struct RowsOf<16> { static __device__ const RowTable<16, 5>& get() { return kRows16; } };
 template <> struct RowsOf<32> { static __device__ const RowTable<32, 3>& get() { return kRows32; } };
 template <> struct RowsOf<64> { static __device__ const RowTable<64, 3>& get() { return kRows64; } };
 
 __host__ __device__ constexpr int row_order(uint32_t code) { return (int)((code >> 24) & 7u); }
-__host__ __device__ constexpr int row_index_c(uint32_t code, int l) { return (int)((code >> (6 * l)) & 63u); }
+// index l of a row code of key width DK
+template <int DK>
+__host__ __device__ constexpr int row_index_c(uint32_t code, int l) {
+  return (int)((code >> (index_bits(DK) * l)) & ((1u << index_bits(DK)) - 1u));
+}
 // 1/alpha(t)! from the weight index of a row code
 __host__ __device__ constexpr float row_weight(uint32_t code) {
   const uint32_t w = (code >> 27) & 7u;
-  return w == 0 ? 1.0f : w == 1 ? 0.5f : w == 2 ? 0.25f : w == 3 ? 1.0f / 6.0f : 1.0f / 24.0f;
+  return w == 0 ? 1.0f : w == 1 ? 0.5f : w == 2 ? 0.25f : w == 3 ? 1.0f / 6.0f : w == 4 ? 1.0f / 12.0f
+       : w == 5 ? 1.0f / 24.0f : 1.0f / 120.0f;
 }
 // code of a padding row (order 7: contributes nothing)
 constexpr uint32_t kPadRow = 7u << 24;
-__device__ inline int row_index(uint32_t code, int l) { return (int)((code >> (6 * l)) & 63u); }
+template <int DK>
+__device__ inline int row_index(uint32_t code, int l) { return row_index_c<DK>(code, l); }
 
-// mu_t(x) for a row code, reading coordinates through `get(i)`.
-template <typename Get>
+// mu_t(x) for a row code of key width DK, reading coordinates through `get(i)`.
+template <int DK, typename Get>
 __device__ inline float monomial(uint32_t code, Get get) {
   const int m = row_order(code);
   float p = 1.0f;
-  for (int l = 0; l < m; ++l) p *= get(row_index(code, l));
+  for (int l = 0; l < m; ++l) p *= get(row_index<DK>(code, l));
   return p;
 }
 
@@ -154,64 +174,82 @@ __device__ inline float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
 // L2 normalisation of one q or k row ("Expanding Attention", abstract: unit
 // q and k keep q.k inside the series' convergence radius; a temperature is
 // folded into the queries as `scale`).  x <- r(scale * x / ||x||_2), where r
-// rounds to the input dtype (bf16: nearest even; fp32: identity).  Every
-// operation is one IEEE fp32 operation rounded to nearest even, in a fixed
-// order (row_norm_factor: squares summed in groups of 8, group sums by a
-// pairwise tree, no fused multiply-add; then the square root, scale / root,
-// and x_i * that factor).  The result is a fixed function of the input bits,
-// the same in every kernel, and a host can reproduce it exactly.  A zero row
-// gives NaN.
+// rounds once to the nearest value of the input dtype (ties to even).  The
+// quotient is evaluated in
+// fp64 (row_norm_factor: squares of the fp32 coordinates, which are exact in
+// fp64, summed in groups of 8 and a pairwise tree over the groups; then the
+// square root, scale / root and x_i * that factor, each an IEEE fp64
+// operation).  That value lies within about 10 fp64 ulps of the exact unit
+// coordinate, so r gives the correctly rounded unit row except where the
+// exact value lies that close to a rounding boundary.  The operation order
+// is fixed, so every kernel gives the same bits.  A zero row gives NaN.
 // ---------------------------------------------------------------------------
 
-// Sum of squares of the 8 coordinates get(8g) .. get(8g+7), in index order.
+// Sum of squares of the 8 coordinates get(8g) .. get(8g+7), in index order,
+// in fp64 (each square of an fp32 value is exact).
 template <typename Get>
-__device__ inline float group_sumsq(Get get, int g) {
-#pragma clang fp contract(off)
-  float s = 0.f;
+__device__ inline double group_sumsq(Get get, int g) {
+  double s = 0.0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float xi = get(8 * g + e);
-    const float sq = xi * xi;
-    s = s + sq;
+    const double xi = (double)get(8 * g + e);
+    s = s + xi * xi;
   }
   return s;
 }
 
-// The factor scale / ||x||_2 of a row whose coordinates get(0) .. get(D-1)
-// are fp32 values.  Squares are summed in groups of 8 consecutive
+// The factor scale / ||x||_2 (fp64) of a row whose coordinates get(0) ..
+// get(D-1) are fp32 values.  Squares are summed in groups of 8 consecutive
 // coordinates (group_sumsq); the group sums are added as a balanced pairwise
 // tree, neighbours first (((g0+g1)+(g2+g3))+...).  A kernel that spreads a
 // row over D/8 lanes reaches the same bits with a shfl_xor butterfly over
 // lane offsets 1, 2, 4 (IEEE addition commutes).
 template <int D, typename Get>
-__device__ inline float row_norm_factor(Get get, float scale) {
-#pragma clang fp contract(off)
+__device__ inline double row_norm_factor(Get get, float scale) {
   constexpr int G = D / 8;
   static_assert(D % 8 == 0 && (G & (G - 1)) == 0, "groups of 8, a power-of-two count");
-  float g[G];
+  double g[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) g[j] = group_sumsq(get, j);
 #pragma unroll
   for (int w = 1; w < G; w *= 2)
 #pragma unroll
     for (int j = 0; j + w < G; j += 2 * w) g[j] = g[j] + g[j + w];
-  return scale / sqrtf(g[0]);
+  return (double)scale / sqrt(g[0]);
 }
 
-// One unit coordinate: r(x * f), rounded to the input dtype.
+// fp64 -> bf16 rounded once to nearest even.  The fp64 value is first
+// rounded to fp32 by rounding to odd (toward zero, then the last bit set if
+// the conversion was inexact): that keeps the information the second
+// rounding needs, so fp32 -> bf16 to nearest even then gives the correctly
+// rounded bf16 of the fp64 value.  (Rounding to nearest fp32 first could
+// land exactly on a bf16 midpoint and round a second time.)  The bit
+// operations also keep the compiler from folding the two conversions.
+__device__ inline float round_bf16_from_f64(double y) {
+  float t = (float)y;
+  const double back = (double)t;
+  if (back != y) {
+    uint32_t b = __float_as_uint(t);
+    if (fabs(back) > fabs(y)) b -= 1u;  // one fp32 step toward zero
+    t = __uint_as_float(b | 1u);
+  }
+  return bf16_to_f32(f32_to_bf16(t));
+}
+
+// One unit coordinate: r(x * f) with x * f in fp64, rounded once to the
+// input dtype (nearest even).
 template <typename TIn>
-__device__ inline float unit_coord(float x, float f) {
-#pragma clang fp contract(off)
-  const float y = x * f;
+__device__ inline float unit_coord(float x, double f) {
+  const double y = (double)x * f;
   if constexpr (std::is_same<TIn, uint16_t>::value)
-    return bf16_to_f32(f32_to_bf16(y));
+    return round_bf16_from_f64(y);
   else
-    return y;
+    return (float)y;
 }
 
 template <typename TIn, int D>
 __device__ inline void normalize_row(float (&x)[D], float scale) {
-  const float f = row_norm_factor<D>([&](int i) { return x[i]; }, scale);
+  const double f = row_norm_factor<D>([&](int i) { return x[i]; }, scale);
 #pragma unroll
   for (int i = 0; i < D; ++i) x[i] = unit_coord<TIn>(x[i], f);
 }
@@ -237,6 +275,18 @@ __device__ inline f32x4 mfma_f32(float a, float b, f32x4 c) {
 }
 
 __device__ inline f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+// split_bf16x2 of eight values (x0.xyzw, then x1.xyzw) into packed hi and lo
+// planes of four dwords each (the same bits as eight split_bf16 calls).
+__device__ inline void split_bf16x8(f32x4 x0, f32x4 x1, u32x4& hi, u32x4& lo) {
+  uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+  split_bf16x2(x0.x, x0.y, h0, l0);
+  split_bf16x2(x0.z, x0.w, h1, l1);
+  split_bf16x2(x1.x, x1.y, h2, l2);
+  split_bf16x2(x1.z, x1.w, h3, l3);
+  hi = u32x4{h0, h1, h2, h3};
+  lo = u32x4{l0, l1, l2, l3};
+}
 
 // Workgroup barrier ordering LDS only: each wave waits for its own LDS
 // operations, not for its global loads and stores in flight (a plain
@@ -278,6 +328,7 @@ inline hipError_t with_dkn(int dk, int n, Fn&& fn) {
   using std::integral_constant;
 #define TT_CASE(D, NN) \
   if (dk == D && n == NN) return fn(integral_constant<int, D>{}, integral_constant<int, NN>{});
+  TT_CASE(8, 1) TT_CASE(8, 2) TT_CASE(8, 3) TT_CASE(8, 4) TT_CASE(8, 5) TT_CASE(8, 6)
   TT_CASE(16, 1) TT_CASE(16, 2) TT_CASE(16, 3) TT_CASE(16, 4) TT_CASE(16, 5)
   TT_CASE(32, 1) TT_CASE(32, 2) TT_CASE(32, 3)
   TT_CASE(64, 1) TT_CASE(64, 2) TT_CASE(64, 3)

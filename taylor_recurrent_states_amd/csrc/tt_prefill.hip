@@ -199,7 +199,7 @@ struct Cfg {
 template <int NT>
 __device__ inline float taylor_poly(float x) {
   // K_n(x) = sum_{m<n} x^m/m!  by Horner, coefficients 1/m! in fp32
-  constexpr float c[5] = {1.0f, 1.0f, 0.5f, 1.0f / 6.0f, 1.0f / 24.0f};
+  constexpr float c[6] = {1.0f, 1.0f, 0.5f, 1.0f / 6.0f, 1.0f / 24.0f, 1.0f / 120.0f};
   float p = c[NT - 1];
 #pragma unroll
   for (int m = NT - 2; m >= 0; --m) p = fmaf(p, x, c[m]);
@@ -231,7 +231,7 @@ __device__ __attribute__((always_inline)) inline void gen_unrolled(int sl, int w
   constexpr bool BF = C::BF;
   constexpr int G = BF ? 8 : 4;  // rows per 16-byte group
   constexpr int NG = C::SR / G;
-  constexpr RowTable<C::DK, (C::DK == 16 ? 5 : 3)> tab{};
+  constexpr RowTable<C::DK, max_terms(C::DK)> tab{};
   float xk[C::DK], xq[C::DK];
   if constexpr (BF) {
 #pragma unroll
@@ -268,7 +268,7 @@ __device__ __attribute__((always_inline)) inline void gen_unrolled(int sl, int w
       return 0.f;
     } else {
       float p = 1.f;
-      static_for<0, m>([&](auto lc) { p *= x[row_index_c(code, decltype(lc)::value)]; });
+      static_for<0, m>([&](auto lc) { p *= x[row_index_c<C::DK>(code, decltype(lc)::value)]; });
       return p;
     }
   };
@@ -437,18 +437,18 @@ __device__ __attribute__((always_inline)) inline void gen_runs(int sl, int w, in
       if (m == 0) {
         mu = kmask;
       } else if (m < 7) {
-        const uint32_t key = (code & ((1u << (6 * (m - 1))) - 1u)) | ((uint32_t)m << 24);
+        const uint32_t key = (code & ((1u << (index_bits(C::DK) * (m - 1))) - 1u)) | ((uint32_t)m << 24);
         if (key != pkey) {
           pkey = key;
           pq = 1.f;
           pk = 1.f;
           for (int l = 0; l < m - 1; ++l) {
-            const int ix = row_index(code, l);
+            const int ix = row_index<C::DK>(code, l);
             pk *= to_f32(xk[ix]);
             if constexpr (C::OUT) pq *= to_f32(xq[ix]);
           }
         }
-        const int il = row_index(code, m - 1);
+        const int il = row_index<C::DK>(code, m - 1);
         mu = pk * to_f32(xk[il]);
         if constexpr (C::OUT) phv = row_weight(code) * pq * to_f32(xq[il]);
       }
@@ -485,7 +485,7 @@ __device__ __attribute__((always_inline)) inline void gen_groups(int part, int n
                                   typename C::Elem* sPhi, typename C::Elem* sMu) {
   constexpr int G = 8;
   constexpr int NG = C::WP / G;
-  constexpr RowTable<C::DK, (C::DK == 16 ? 5 : 3)> tab{};
+  constexpr RowTable<C::DK, max_terms(C::DK)> tab{};
   const float kmask = lane < nvalid ? 1.f : 0.f;
   auto mono = [&](const float* x, auto Rc) -> float {
     constexpr int R = decltype(Rc)::value;
@@ -495,7 +495,7 @@ __device__ __attribute__((always_inline)) inline void gen_groups(int part, int n
       return 0.f;
     } else {
       float p = 1.f;
-      static_for<0, m>([&](auto lc) { p *= x[row_index_c(code, decltype(lc)::value)]; });
+      static_for<0, m>([&](auto lc) { p *= x[row_index_c<C::DK>(code, decltype(lc)::value)]; });
       return p;
     }
   };
@@ -853,17 +853,17 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
           const int j = sl * C::J + jl;
           const int kbl = rp * C::J + jl;  // K-block within the slab
           if constexpr (BF) {
-            u32x4 b;
-            b.x = pack_bf16x2(st[j][0].x, st[j][0].y);
-            b.y = pack_bf16x2(st[j][0].z, st[j][0].w);
-            b.z = pack_bf16x2(st[j][C::TPK - 1].x, st[j][C::TPK - 1].y);
-            b.w = pack_bf16x2(st[j][C::TPK - 1].z, st[j][C::TPK - 1].w);
-            u32x4 bd = {0u, 0u, 0u, 0u};  // normaliser rows of the K-block in column 0
+            // the state and the normaliser rows enter the readout as hi + lo
+            // bf16 (16 significant bits): rounded to one bf16 each, values and
+            // normaliser would round independently and move an output by
+            // about 2^-9 |o|
+            u32x4 b, bl;
+            split_bf16x8(st[j][0], st[j][C::TPK - 1], b, bl);
+            u32x4 bd = {0u, 0u, 0u, 0u}, bdl = {0u, 0u, 0u, 0u};  // normaliser rows of the K-block in column 0
             if (li == 0) {
               const f32x4 d0 = *reinterpret_cast<const f32x4*>(Den + row0 + kbl * 32 + 8 * lg);
               const f32x4 d1 = *reinterpret_cast<const f32x4*>(Den + row0 + kbl * 32 + 8 * lg + 4);
-              bd = u32x4{pack_bf16x2(d0.x, d0.y), pack_bf16x2(d0.z, d0.w), pack_bf16x2(d1.x, d1.y),
-                         pack_bf16x2(d1.z, d1.w)};
+              split_bf16x8(d0, d1, bd, bdl);
             }
             // all four fragments are read before the first MFMA: the normaliser
             // MFMAs below sit behind wave-uniform branches, which the compiler
@@ -875,8 +875,13 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
 #pragma unroll
             for (int qt = 0; qt < 4; ++qt) num[qt] = mfma_bf16(a[qt], b, num[qt]);
 #pragma unroll
+            for (int qt = 0; qt < 4; ++qt) num[qt] = mfma_bf16(a[qt], bl, num[qt]);
+#pragma unroll
             for (int qt = 0; qt < 4; ++qt)
-              if (qt % C::NVT == ct) den[qt] = mfma_bf16(a[qt], bd, den[qt]);
+              if (qt % C::NVT == ct) {
+                den[qt] = mfma_bf16(a[qt], bd, den[qt]);
+                den[qt] = mfma_bf16(a[qt], bdl, den[qt]);
+              }
           } else {
             const f32x4 d = *reinterpret_cast<const f32x4*>(Den + row0 + kbl * 16 + 4 * lg);
 #pragma unroll
@@ -1284,8 +1289,8 @@ struct PCfg {
   static constexpr int O_PHI = O_V + 2 * B_V;
   static constexpr int O_MU = O_PHI + 2 * B_PHI;
   static constexpr int O_P = O_MU + 2 * B_MU;
-  static constexpr int O_DEN = O_P + 2 * B_P;             // bf16 normaliser rows [2][WP]
-  static constexpr int O_DEN0 = O_DEN + al(2 * WP * 2);    // fp32 normaliser of row 0 [2]
+  static constexpr int O_DEN = O_P + 2 * B_P;             // bf16 normaliser rows [2][hi, lo][WP]
+  static constexpr int O_DEN0 = O_DEN + al(4 * WP * 2);    // fp32 normaliser of row 0 [2]
   static constexpr int O_RDEN = O_DEN0 + 16;               // 1/den per query [2][64]
   static constexpr int LDS = O_RDEN + (OUT ? al(2 * kCH * 4) : 0);
   static_assert(LDS <= 160 * 1024, "LDS budget");
@@ -1305,7 +1310,7 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
   auto sPhi = [&](int b) { return reinterpret_cast<Elem*>(lds + C::O_PHI + b * C::B_PHI); };
   auto sMu = [&](int b) { return reinterpret_cast<Elem*>(lds + C::O_MU + b * C::B_MU); };
   auto sP = [&](int b) { return reinterpret_cast<Elem*>(lds + C::O_P + b * C::B_P); };
-  uint16_t* sDenB = reinterpret_cast<uint16_t*>(lds + C::O_DEN);  // [2][WP] bf16 normaliser rows
+  uint16_t* sDenB = reinterpret_cast<uint16_t*>(lds + C::O_DEN);  // [2][hi, lo][WP] bf16 normaliser rows
   float* sDen0 = reinterpret_cast<float*>(lds + C::O_DEN0);         // [2] row-0 normaliser (token count)
   float* sRden = reinterpret_cast<float*>(lds + C::O_RDEN);         // [2][query%16][query/16]
 
@@ -1482,16 +1487,17 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
     f32x4 dstate[NJD][2];
 #pragma unroll
     for (int jd = 0; jd < NJD; ++jd) dstate[jd][0] = dstate[jd][1] = zero4();
-    auto publish_den = [&](int buf) {  // bf16 readout fragments and the fp32 row 0
+    auto publish_den = [&](int buf) {  // hi + lo bf16 readout fragments and the fp32 row 0
       if (li == 0) {
 #pragma unroll
         for (int jd = 0; jd < NJD; ++jd) {
           const int j = 4 * jd + ct;
           if (j < C::NKB) {
             const f32x4 d0 = dstate[jd][0], d1 = dstate[jd][1];
-            *reinterpret_cast<u32x4*>(sDenB + buf * C::WP + j * 32 + 8 * lg) =
-                u32x4{pack_bf16x2(d0.x, d0.y), pack_bf16x2(d0.z, d0.w), pack_bf16x2(d1.x, d1.y),
-                      pack_bf16x2(d1.z, d1.w)};
+            u32x4 hi, lo;
+            split_bf16x8(d0, d1, hi, lo);
+            *reinterpret_cast<u32x4*>(sDenB + 2 * buf * C::WP + j * 32 + 8 * lg) = hi;
+            *reinterpret_cast<u32x4*>(sDenB + (2 * buf + 1) * C::WP + j * 32 + 8 * lg) = lo;
           }
         }
         if (ct == 0 && lg == 0) sDen0[buf] = dstate[0][0].x;
@@ -1599,17 +1605,19 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
         // normaliser fragment of K-block j: the same normaliser rows in every
         // column of the B tile, so every column of the product holds the
         // readout (lanes li == 0 use it); fetched one K-block ahead
-        auto load_bdn = [&](int j) { return *reinterpret_cast<const u32x4*>(sDenB + b * C::WP + j * 32 + 8 * lg); };
+        auto load_bdn = [&](int j, int pl) {
+          return *reinterpret_cast<const u32x4*>(sDenB + (2 * b + pl) * C::WP + j * 32 + 8 * lg);
+        };
         u32x4 bdn[2];
-        bdn[0] = load_bdn(0);
+        bdn[0] = load_bdn(0, 0);
         const float den0 = sDen0[b];
         // m = 0 row (fp32): S[0][col] for this lane's four columns
         f32x4 m0;
 #pragma unroll
         for (int s = 0; s < 4; ++s) m0[s] = __shfl(st[0][0].x, 4 * lg + s);
         // readout of K-block j, then its update (the readout has taken st[j]
-        // into bs first); phi fragments two K-blocks ahead, mu one block ahead
-        u32x4 af[3][4];
+        // into bs first); phi and mu fragments one K-block ahead
+        u32x4 af[2][4];
         u32x4 mf[2][2][2][NPL];
         auto load_phi = [&](int j, u32x4* dst) {
 #pragma unroll
@@ -1617,28 +1625,35 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
         };
         load_phi(0, af[0]);
         fetch_mu(0, mf[0]);
-        if (C::NKB > 1) load_phi(1, af[1]);
 #pragma unroll
         for (int j = 0; j < C::NKB; ++j) {
-          if (j + 2 < C::NKB) load_phi(j + 2, af[(j + 2) % 3]);
           if (j + 1 < C::NKB) {
+            load_phi(j + 1, af[(j + 1) & 1]);
             fetch_mu(j + 1, mf[(j + 1) & 1]);
-            bdn[(j + 1) & 1] = load_bdn(j + 1);
+            bdn[(j + 1) & 1] = load_bdn(j + 1, 0);
           }
-          u32x4 bs;  // S[rows 8lg..8lg+7 of K-block j][column ct*16 + li], as the A operand (S^T)
-          bs.x = pack_bf16x2(st[j][0].x, st[j][0].y);
-          bs.y = pack_bf16x2(st[j][0].z, st[j][0].w);
-          bs.z = pack_bf16x2(st[j][1].x, st[j][1].y);
-          bs.w = pack_bf16x2(st[j][1].z, st[j][1].w);
+          // lo plane of the normaliser rows, read here and used after the
+          // value readout's MFMAs
+          const u32x4 bdl = load_bdn(j, 1);
+          // S[rows 8lg..8lg+7 of K-block j][column ct*16 + li] as the A
+          // operand (S^T), split into hi + lo bf16 (16 significant bits), so
+          // the readout does not round the state to 8 bits: the values and
+          // their normaliser would round independently, which can move an
+          // output by about 2^-9 |o|
+          u32x4 bs, bsl;
+          split_bf16x8(st[j][0], st[j][1], bs, bsl);
 #pragma unroll
-          for (int qt = 0; qt < 4; ++qt) num[qt] = mfma_bf16(bs, af[j % 3][qt], num[qt]);
-          // normaliser readout of this wave's query tile: ct is wave-uniform,
-          // so this is a scalar branch to one of four MFMAs (no operand select)
+          for (int qt = 0; qt < 4; ++qt) num[qt] = mfma_bf16(bs, af[j & 1][qt], num[qt]);
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt) num[qt] = mfma_bf16(bsl, af[j & 1][qt], num[qt]);
+          // normaliser readout of this wave's query tile (hi, then lo plane):
+          // ct is wave-uniform, so this is a scalar branch to one of four
+          // MFMA pairs (no operand select)
           switch (ct) {
-            case 0: den = mfma_bf16(af[j % 3][0], bdn[j & 1], den); break;
-            case 1: den = mfma_bf16(af[j % 3][1], bdn[j & 1], den); break;
-            case 2: den = mfma_bf16(af[j % 3][2], bdn[j & 1], den); break;
-            default: den = mfma_bf16(af[j % 3][3], bdn[j & 1], den); break;
+            case 0: den = mfma_bf16(af[j & 1][0], bdn[j & 1], den); den = mfma_bf16(af[j & 1][0], bdl, den); break;
+            case 1: den = mfma_bf16(af[j & 1][1], bdn[j & 1], den); den = mfma_bf16(af[j & 1][1], bdl, den); break;
+            case 2: den = mfma_bf16(af[j & 1][2], bdn[j & 1], den); den = mfma_bf16(af[j & 1][2], bdl, den); break;
+            default: den = mfma_bf16(af[j & 1][3], bdn[j & 1], den); den = mfma_bf16(af[j & 1][3], bdl, den); break;
           }
           update_block(j, mf[j & 1]);
         }
@@ -1930,11 +1945,14 @@ constexpr bool use_pipe() { return (rows_for(DK, NT) + 31) / 32 * 32 <= 256; }
 int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype dt, PrefillPlan* p) {
   (void)dv;
   if (chunk != kCH) return fail(TT_ERR_UNSUPPORTED, "chunk=%d not compiled (64 only)", chunk);
+  if (dt == TT_BF16 && dk < 16) return fail(TT_ERR_UNSUPPORTED, "dk=%d prefill takes fp32 inputs only", dk);
   int wp = 0, ngroups = 0, nrg = 1, wg_per_cu = 2;
   hipError_t e = with_dkn(dk, n, [&](auto DKc, auto Nc) {
     constexpr int DK = decltype(DKc)::value, NT = decltype(Nc)::value;
     if (dt == TT_BF16) {
-      if constexpr (use_pipe<DK, NT>()) {
+      if constexpr (DK < 16) {
+        return hipErrorInvalidValue;  // refused above
+      } else if constexpr (use_pipe<DK, NT>()) {
         wp = PCfg<DK, NT, MODE_OUTPUT>::WP;
         ngroups = 1;
         wg_per_cu = 1;
@@ -2009,7 +2027,9 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype 
       return hipGetLastError();
     };
     if (dt == TT_BF16) {
-      if constexpr (use_pipe<DK, NT>()) {
+      if constexpr (DK < 16) {
+        return hipErrorInvalidValue;  // refused by plan_prefill
+      } else if constexpr (use_pipe<DK, NT>()) {
         using PT = PCfg<DK, NT, MODE_TOTALS>;
         using PO = PCfg<DK, NT, MODE_OUTPUT>;
         using PU = PCfg<DK, NT, MODE_OUTPUT_UNN>;

@@ -108,7 +108,10 @@ def _check(rc: int) -> None:
 
 
 # ---------------------------------------------------------------------------
-# torch plumbing
+# torch plumbing.  The C entry points take raw pointers and no buffer sizes,
+# so every caller-supplied buffer is checked here (dtype, element count,
+# shape, contiguity, device) before the library is called: a wrong size
+# would otherwise become an out-of-bounds device access.
 # ---------------------------------------------------------------------------
 
 def _torch():
@@ -122,21 +125,97 @@ def _dtype_code(t) -> int:
         return TT_F32
     if t.dtype == torch.bfloat16:
         return TT_BF16
-    raise TypeError(f"unsupported input dtype {t.dtype} (float32 or bfloat16)")
+    raise ValueError(f"unsupported input dtype {t.dtype} (float32 or bfloat16)")
 
 
-def _dev(t, name: str):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+def _contig(t, name: str):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
 
 
-def _stream(stream) -> int:
-    if stream is not None:
-        return int(getattr(stream, "cuda_stream", stream))
-    return _torch().cuda.current_stream().cuda_stream
+def _on_gpu(ref, *named):
+    """Every tensor on the GPU, on the device of ``ref`` (checked after the
+    dtypes and sizes, so that those errors do not need a GPU)."""
+    for t, name in ((ref, "input"),) + named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, the inputs on {ref.device}")
+
+
+def _f32(t, name: str, numel: int):
+    """A caller-supplied float32 buffer of exactly ``numel`` elements."""
+    torch = _torch()
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32, got {t.dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} float32 values, got {t.numel()}")
+    return _contig(t, name)
+
+
+class _Launch:
+    """The stream of one call, and the tensors allocated for it.
+
+    Tensors allocated here come from torch's caching allocator on the
+    current stream; when the caller passes another stream they are marked
+    as used on it (record_stream), so that the allocator does not hand their
+    memory to a later allocation while the kernels may still run."""
+
+    def __init__(self, stream):
+        self.stream = stream
+        self._resolved = None
+
+    def _resolve(self):
+        if self._resolved is None:
+            torch = _torch()
+            cur = torch.cuda.current_stream().cuda_stream
+            s = self.stream
+            if s is None:
+                self._resolved = (cur, None)
+            else:
+                obj = s if isinstance(s, torch.cuda.Stream) else torch.cuda.ExternalStream(
+                    int(getattr(s, "cuda_stream", s)))
+                self._resolved = (obj.cuda_stream, obj if obj.cuda_stream != cur else None)
+        return self._resolved
+
+    @property
+    def handle(self) -> int:
+        return self._resolve()[0]
+
+    def alloc(self, shape, dtype, device):
+        t = _torch().empty(shape, dtype=dtype, device=device)
+        other = self._resolve()[1]
+        if other is not None:
+            t.record_stream(other)
+        return t
+
+
+def _qkv(Q, K, V):
+    """Shapes of prefill inputs Q, K [B, H, N, dk] and V [B, H, N, dv] of one dtype."""
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
+        if t.dim() != 4:
+            raise ValueError(f"{nm} must be 4-D [B, H, N, d], got shape {tuple(t.shape)}")
+    _dtype_code(Q)
+    if not (Q.dtype == K.dtype == V.dtype):
+        raise ValueError(f"Q, K, V must share a dtype (got {Q.dtype}, {K.dtype}, {V.dtype})")
+    B, H, N, dk = Q.shape
+    dv = V.shape[-1]
+    if tuple(K.shape) != (B, H, N, dk) or tuple(V.shape[:3]) != (B, H, N):
+        raise ValueError(f"shape mismatch: Q {tuple(Q.shape)}, K {tuple(K.shape)}, V {tuple(V.shape)}")
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
+        _contig(t, nm)
+    return B, H, N, dk, dv
+
+
+def _states_in(t, Q, K, V, n):
+    """Size check of carried-in states for inputs Q, K, V (None passes)."""
+    if t is not None:
+        B, H, _, dk, dv = _qkv(Q, K, V)
+        _f32(t, "states_in", B * H * tt_state_floats(dk, dv, n))
+    return t
 
 
 # ---------------------------------------------------------------------------
@@ -163,23 +242,24 @@ def tt_prefill_normed_workspace_bytes(B: int, H: int, N: int, dk: int, dv: int, 
     return int(out.value)
 
 
-def _prefill_args(Q, K, V, n, chunk, O, states, workspace, normed=False):
+def _prefill_args(Q, K, V, n, chunk, O, states, workspace, launch, normed=False, extra=()):
     torch = _torch()
-    for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
-        _dev(t, nm)
-    if not (Q.dtype == K.dtype == V.dtype):
-        raise TypeError("Q, K, V must share a dtype")
-    B, H, N, dk = Q.shape
-    dv = V.shape[-1]
-    if tuple(K.shape) != (B, H, N, dk) or tuple(V.shape[:3]) != (B, H, N):
-        raise ValueError("shape mismatch between Q, K, V")
-    if O is None:
-        O = torch.empty((B, H, N, dv), dtype=torch.float32, device=Q.device)
-    if states is None:
-        states = torch.empty(B * H * tt_state_floats(dk, dv, n), dtype=torch.float32, device=Q.device)
+    B, H, N, dk, dv = _qkv(Q, K, V)
+    nstate = B * H * tt_state_floats(dk, dv, n)
+    if O is not None:
+        _f32(O, "O", B * H * N * dv)
+    if states is not None:
+        _f32(states, "states", nstate)
+    if workspace is not None:
+        _contig(workspace, "workspace")
     need = (tt_prefill_normed_workspace_bytes if normed else tt_prefill_workspace_bytes)(B, H, N, dk, dv, n, chunk)
+    _on_gpu(Q, (K, "K"), (V, "V"), (O, "O"), (states, "states"), (workspace, "workspace"), *extra)
+    if O is None:
+        O = launch.alloc((B, H, N, dv), torch.float32, Q.device)
+    if states is None:
+        states = launch.alloc((nstate,), torch.float32, Q.device)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+        workspace = launch.alloc((need,), torch.uint8, Q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     # the caller holds ``workspace`` until the launch is queued: a workspace
@@ -192,10 +272,11 @@ def tt_prefill(Q, K, V, n: int, chunk: int = 64, O=None, states=None, workspace=
     """Causal prefill of Q, K [B, H, N, dk] and V [B, H, N, dv] (float32 or
     bfloat16, same dtype).  Returns (O [B, H, N, dv] float32, states flat
     float32 in the library's plane layout)."""
-    (B, H, N, dk, dv), O, states, ws, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace)
+    launch = _Launch(stream)
+    (B, H, N, dk, dv), O, states, ws, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace,
+                                                                       launch)
     _check(lib().tt_prefill(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk, dv, n, chunk,
-                            _dev(O, "O").data_ptr(), _dev(states, "states").data_ptr(), ws_ptr, ws_bytes,
-                            _stream(stream)))
+                            O.data_ptr(), states.data_ptr(), ws_ptr, ws_bytes, launch.handle))
     return O, states
 
 
@@ -204,13 +285,15 @@ def tt_prefill_from(Q, K, V, states_in, n: int, chunk: int = 64, O=None, states=
     """Prefill continuing from carried-in states (flat float32, plane layout).
     ``states`` may be ``states_in`` itself to continue in place.  Returns
     (O, states)."""
-    _dev(states_in, "states_in")
-    (B, H, N, dk, dv), O, states, ws, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace)
-    if states_in.dtype != _torch().float32 or states_in.numel() != B * H * tt_state_floats(dk, dv, n):
-        raise ValueError("states_in must hold B*H*W*(dv+1) float32 values")
+    launch = _Launch(stream)
+    if states_in is None:
+        raise ValueError("states_in is None (use tt_prefill for zero states)")
+    _states_in(states_in, Q, K, V, n)
+    (B, H, N, dk, dv), O, states, ws, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace,
+                                                                       launch, extra=((states_in, "states_in"),))
     _check(lib().tt_prefill_from(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk, dv, n,
-                                 chunk, states_in.data_ptr(), _dev(O, "O").data_ptr(),
-                                 _dev(states, "states").data_ptr(), ws_ptr, ws_bytes, _stream(stream)))
+                                 chunk, states_in.data_ptr(), O.data_ptr(), states.data_ptr(), ws_ptr, ws_bytes,
+                                 launch.handle))
     return O, states
 
 
@@ -220,21 +303,19 @@ def tt_prefill_from_unnormalized(Q, K, V, states_in, n: int, chunk: int = 64, nu
     den [B, H, N], states); o = num / den[..., None].  ``states_in`` may be
     None (zero states)."""
     torch = _torch()
-    (B, H, N, dk, dv), num, states, ws, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, num, states, workspace)
+    launch = _Launch(stream)
+    _states_in(states_in, Q, K, V, n)
+    if den is not None:
+        B, H, N, _, _ = _qkv(Q, K, V)
+        _f32(den, "den", B * H * N)
+    (B, H, N, dk, dv), num, states, ws, ws_ptr, ws_bytes = _prefill_args(
+        Q, K, V, n, chunk, num, states, workspace, launch, extra=((states_in, "states_in"), (den, "den")))
     if den is None:
-        den = torch.empty((B, H, N), dtype=torch.float32, device=Q.device)
-    sin = 0
-    if states_in is not None:
-        _dev(states_in, "states_in")
-        if states_in.dtype != torch.float32 or states_in.numel() != B * H * tt_state_floats(dk, dv, n):
-            raise ValueError("states_in must hold B*H*W*(dv+1) float32 values")
-        sin = states_in.data_ptr()
-    if den.dtype != torch.float32 or den.numel() != B * H * N:
-        raise ValueError("den must hold B*H*N float32 values")
+        den = launch.alloc((B, H, N), torch.float32, Q.device)
+    sin = states_in.data_ptr() if states_in is not None else 0
     _check(lib().tt_prefill_from_unnormalized(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk,
-                                              dv, n, chunk, sin, _dev(num, "num").data_ptr(),
-                                              _dev(den, "den").data_ptr(), _dev(states, "states").data_ptr(), ws_ptr,
-                                              ws_bytes, _stream(stream)))
+                                              dv, n, chunk, sin, num.data_ptr(), den.data_ptr(), states.data_ptr(),
+                                              ws_ptr, ws_bytes, launch.handle))
     return num, den, states
 
 
@@ -243,88 +324,113 @@ def tt_prefill_normed(Q, K, V, n: int, temperature: float = 1.0, states_in=None,
     """Prefill on raw Q, K: the library normalises them (Q scaled by
     ``temperature``) and runs the prefill, from ``states_in`` (flat float32,
     plane layout) or from zero states when it is None.  Returns (O, states)."""
+    launch = _Launch(stream)
+    _states_in(states_in, Q, K, V, n)
     (B, H, N, dk, dv), O, states, ws, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace,
-                                                                   normed=True)
-    sin = None
-    if states_in is not None:
-        _dev(states_in, "states_in")
-        if states_in.dtype != _torch().float32 or states_in.numel() != B * H * tt_state_floats(dk, dv, n):
-            raise ValueError("states_in must hold B*H*W*(dv+1) float32 values")
-        sin = states_in.data_ptr()
+                                                                       launch, normed=True,
+                                                                       extra=((states_in, "states_in"),))
+    sin = states_in.data_ptr() if states_in is not None else None
     _check(lib().tt_prefill_normed(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk, dv, n,
-                                   chunk, float(temperature), sin, _dev(O, "O").data_ptr(),
-                                   _dev(states, "states").data_ptr(), ws_ptr, ws_bytes, _stream(stream)))
+                                   chunk, float(temperature), sin, O.data_ptr(), states.data_ptr(), ws_ptr, ws_bytes,
+                                   launch.handle))
     return O, states
 
 
 def tt_normalize_rows(x, scale: float = 1.0, out=None, stream=None):
     """x [rows, d] (float32 or bfloat16) -> r(scale * x / ||x||) in x's dtype."""
-    torch = _torch()
-    _dev(x, "x")
+    launch = _Launch(stream)
+    _dtype_code(x)
+    _contig(x, "x")
     rows, d = x.reshape(-1, x.shape[-1]).shape
+    if out is not None:
+        if out.dtype != x.dtype or out.shape != x.shape:
+            raise ValueError("out must match x in dtype and shape")
+        _contig(out, "out")
+    _on_gpu(x, (out, "out"))
     if out is None:
-        out = torch.empty_like(x)
-    if out.dtype != x.dtype or out.shape != x.shape:
-        raise ValueError("out must match x in dtype and shape")
-    _check(lib().tt_normalize_rows(x.data_ptr(), _dtype_code(x), rows, d, float(scale), _dev(out, "out").data_ptr(),
-                                   _stream(stream)))
+        out = launch.alloc(tuple(x.shape), x.dtype, x.device)
+    _check(lib().tt_normalize_rows(x.data_ptr(), _dtype_code(x), rows, d, float(scale), out.data_ptr(),
+                                   launch.handle))
     return out
+
+
+def _decode_args(q, k, v, states, n, o, launch):
+    """Shapes of one decode step: q, k [B, H, dk], v [B, H, dv] of one dtype,
+    states of B*H heads, o [B, H, dv] float32."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dim() != 3:
+            raise ValueError(f"{nm} must be 3-D [B, H, d], got shape {tuple(t.shape)}")
+    _dtype_code(q)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError(f"q, k, v must share a dtype (got {q.dtype}, {k.dtype}, {v.dtype})")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if tuple(k.shape) != (B, H, dk) or tuple(v.shape[:2]) != (B, H):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    _f32(states, "states", B * H * tt_state_floats(dk, dv, n))
+    if o is not None:
+        _f32(o, "o", B * H * dv)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _contig(t, nm)
+    _on_gpu(q, (k, "k"), (v, "v"), (states, "states"), (o, "o"))
+    if o is None:
+        o = launch.alloc((B, H, dv), torch.float32, q.device)
+    return B, H, dk, dv, o
 
 
 def tt_decode_step_normed(q, k, v, states, n: int, temperature: float = 1.0, o=None, stream=None):
     """tt_decode_step on raw q, k (normalised in the kernel, q scaled by
     ``temperature``); states updated in place; returns o [B, H, dv]."""
-    torch = _torch()
-    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (states, "states")):
-        _dev(t, nm)
-    B, H, dk = q.shape
-    dv = v.shape[-1]
-    if o is None:
-        o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    launch = _Launch(stream)
+    B, H, dk, dv, o = _decode_args(q, k, v, states, n, o, launch)
     _check(lib().tt_decode_step_normed(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, H, dk, dv, n,
-                                       float(temperature), states.data_ptr(), _dev(o, "o").data_ptr(),
-                                       _stream(stream)))
+                                       float(temperature), states.data_ptr(), o.data_ptr(), launch.handle))
     return o
 
 
 def tt_decode_step(q, k, v, states, n: int, o=None, stream=None):
     """One token per head: q, k [B, H, dk], v [B, H, dv]; states updated in
     place; returns o [B, H, dv] float32."""
-    torch = _torch()
-    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (states, "states")):
-        _dev(t, nm)
-    B, H, dk = q.shape
-    dv = v.shape[-1]
-    if o is None:
-        o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    launch = _Launch(stream)
+    B, H, dk, dv, o = _decode_args(q, k, v, states, n, o, launch)
     _check(lib().tt_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, H, dk, dv, n,
-                                states.data_ptr(), _dev(o, "o").data_ptr(), _stream(stream)))
+                                states.data_ptr(), o.data_ptr(), launch.handle))
     return o
 
 
 def tt_state_merge(a, b, dst=None, stream=None):
     """dst = a + b elementwise over float32 state buffers (dst may be a or b)."""
     torch = _torch()
-    _dev(a, "a"), _dev(b, "b")
-    if a.numel() != b.numel():
-        raise ValueError("state buffers differ in size")
+    launch = _Launch(stream)
+    _f32(a, "a", a.numel())
+    _f32(b, "b", a.numel())
+    if dst is not None:
+        _f32(dst, "dst", a.numel())
+    _on_gpu(a, (b, "b"), (dst, "dst"))
     if dst is None:
-        dst = torch.empty_like(a)
-    _check(lib().tt_state_merge(_dev(dst, "dst").data_ptr(), a.data_ptr(), b.data_ptr(), a.numel(),
-                                _stream(stream)))
+        dst = launch.alloc(tuple(a.shape), torch.float32, a.device)
+    _check(lib().tt_state_merge(dst.data_ptr(), a.data_ptr(), b.data_ptr(), a.numel(), launch.handle))
     return dst
 
 
 def tt_feature_map(x, n: int, weighted: bool, out=None, stream=None):
     """x [rows, dk] -> [rows, W] float32 features (mu, or phi if weighted)."""
     torch = _torch()
-    _dev(x, "x")
+    launch = _Launch(stream)
+    if x.dim() != 2:
+        raise ValueError(f"x must be 2-D [rows, dk], got shape {tuple(x.shape)}")
+    _dtype_code(x)
     rows, dk = x.shape
     W = tt_state_rows(dk, n)
+    if out is not None:
+        _f32(out, "out", rows * W)
+    _contig(x, "x")
+    _on_gpu(x, (out, "out"))
     if out is None:
-        out = torch.empty((rows, W), dtype=torch.float32, device=x.device)
-    _check(lib().tt_feature_map(x.data_ptr(), _dtype_code(x), rows, dk, n, int(bool(weighted)),
-                                _dev(out, "out").data_ptr(), _stream(stream)))
+        out = launch.alloc((rows, W), torch.float32, x.device)
+    _check(lib().tt_feature_map(x.data_ptr(), _dtype_code(x), rows, dk, n, int(bool(weighted)), out.data_ptr(),
+                                launch.handle))
     return out
 
 
@@ -336,14 +442,15 @@ def tt_softmax_prefill(Q, K, V, O=None, stream=None):
     """Causal softmax attention (no scale) of bf16 Q, K [B, H, N, dk] and
     V [B, H, N, dv]; returns O [B, H, N, dv] float32."""
     torch = _torch()
-    for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
-        _dev(t, nm)
-    B, H, N, dk = Q.shape
-    dv = V.shape[-1]
+    launch = _Launch(stream)
+    B, H, N, dk, dv = _qkv(Q, K, V)
+    if O is not None:
+        _f32(O, "O", B * H * N * dv)
+    _on_gpu(Q, (K, "K"), (V, "V"), (O, "O"))
     if O is None:
-        O = torch.empty((B, H, N, dv), dtype=torch.float32, device=Q.device)
+        O = launch.alloc((B, H, N, dv), torch.float32, Q.device)
     _check(lib().tt_softmax_prefill(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk, dv,
-                                    _dev(O, "O").data_ptr(), _stream(stream)))
+                                    O.data_ptr(), launch.handle))
     return O
 
 
@@ -357,20 +464,37 @@ def tt_softmax_decode_step(q, k, v, Kcache, Vcache, pos: int, o=None, workspace=
     """Append (k, v) at row ``pos`` of the caches [B, H, capacity, d] and
     return the softmax readout o [B, H, dv] float32 over rows 0 .. pos."""
     torch = _torch()
-    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (Kcache, "Kcache"), (Vcache, "Vcache")):
-        _dev(t, nm)
+    launch = _Launch(stream)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dim() != 3:
+            raise ValueError(f"{nm} must be 3-D [B, H, d], got shape {tuple(t.shape)}")
+    _dtype_code(q)
+    if not (q.dtype == k.dtype == v.dtype == Kcache.dtype == Vcache.dtype):
+        raise ValueError("q, k, v and the caches must share a dtype")
     B, H, dk = q.shape
     dv = v.shape[-1]
+    if tuple(k.shape) != (B, H, dk) or tuple(v.shape[:2]) != (B, H):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if Kcache.dim() != 4 or Vcache.dim() != 4:
+        raise ValueError("Kcache and Vcache must be 4-D [B, H, capacity, d]")
     cap = Kcache.shape[2]
-    if tuple(Vcache.shape[:3]) != (B, H, cap):
-        raise ValueError("Kcache and Vcache disagree in shape")
-    if o is None:
-        o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    if tuple(Kcache.shape) != (B, H, cap, dk) or tuple(Vcache.shape) != (B, H, cap, dv):
+        raise ValueError(f"cache shapes {tuple(Kcache.shape)}, {tuple(Vcache.shape)} do not match q, k, v")
+    if o is not None:
+        _f32(o, "o", B * H * dv)
     need = tt_softmax_decode_workspace_bytes(B, H, pos)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (Kcache, "Kcache"), (Vcache, "Vcache"), (workspace, "workspace")):
+        if t is not None:
+            _contig(t, nm)
+    if workspace is not None and workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold {need} bytes")
+    _on_gpu(q, (k, "k"), (v, "v"), (Kcache, "Kcache"), (Vcache, "Vcache"), (o, "o"), (workspace, "workspace"))
+    if o is None:
+        o = launch.alloc((B, H, dv), torch.float32, q.device)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = launch.alloc((max(need, 1),), torch.uint8, q.device)
     _check(lib().tt_softmax_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, H, dk, dv,
-                                        Kcache.data_ptr(), Vcache.data_ptr(), pos, cap, _dev(o, "o").data_ptr(),
+                                        Kcache.data_ptr(), Vcache.data_ptr(), pos, cap, o.data_ptr(),
                                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                        _stream(stream)))
+                                        launch.handle))
     return o

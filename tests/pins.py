@@ -551,14 +551,13 @@ def pin_normalize_rows():
 
 
 def pin_normalized_inputs():
-    """The normalised inputs are the fp64 unit rows rounded the way inputs
-    are rounded (fp32, then bf16, each to nearest even), worked by hand:
-    (21, 28) has norm 35, so the unit row is (3/5, 4/5); 3/5 =
-    1.0011001100...b x 2^-1 rounds up to 1.0011010b x 2^-1 = 0.6015625 in
-    bf16, and 4/5 = 1.1001100110...b x 2^-1 rounds up to 1.1001101b x 2^-1
-    = 0.80078125.  With temperature 2 the query row is (6/5, 8/5) =
-    1.0011001100...b x 2^0 and 1.1001100110...b x 2^0, giving 1.203125 and
-    1.6015625.  fp32 rows are the fp32 roundings of 3/5 and 4/5."""
+    """The normalised inputs are the fp64 unit rows rounded once to the
+    nearest value of the dtype, worked by hand: (21, 28) has norm 35, so the
+    unit row is (3/5, 4/5); 3/5 = 1.0011001100...b x 2^-1 rounds up to
+    1.0011010b x 2^-1 = 0.6015625 in bf16, and 4/5 = 1.1001100110...b x 2^-1
+    rounds up to 1.1001101b x 2^-1 = 0.80078125.  With temperature 2 the
+    query row is (6/5, 8/5), giving 1.203125 and 1.6015625.  fp32 rows are
+    the fp32 roundings of 3/5 and 4/5."""
     q = np.array([[21.0, 28.0], [-3.0, 4.0]])
     qh, kh = orc.normalized_inputs(q, q, 2.0, "bf16")
     assert np.array_equal(kh, [[0.6015625, 0.80078125], [-0.6015625, 0.80078125]])
@@ -566,26 +565,50 @@ def pin_normalized_inputs():
     qf, kf = orc.normalized_inputs(q, q, 1.0, "f32")
     assert np.array_equal(kf[0], np.array([0.6, 0.8], dtype=np.float32).astype(np.float64))
     assert np.array_equal(qf, kf)
-    # an fp64 unit row that is not a dtype value is rounded, not truncated:
-    # every coordinate lies within half a bf16 ulp of the fp64 unit row
+    # every coordinate lies within half a bf16 spacing of the fp64 unit row
     X = np.random.Generator(np.random.PCG64(43)).standard_normal((300, 16))
     _, kb = orc.normalized_inputs(X, X, 1.0, "bf16")
     u = orc.normalize_rows(X)
-    half_ulp = 2.0 ** (np.floor(np.log2(np.abs(u))) - 8)
-    assert np.all(np.abs(kb - u) <= half_ulp * (1 + 2.0 ** -20))
+    half = 2.0 ** (np.floor(np.log2(np.abs(u))) - 8)
+    assert np.all(np.abs(kb - u) <= half * (1 + 2.0 ** -20))
+
+
+def _bf16_nearest_brute(x: float) -> float:
+    """Nearest bf16 value to a finite nonzero fp64 x (normal range) by
+    enumeration: the bf16 values are the fp32 values whose low 16 bits are
+    zero; take the two around x and compare exact distances (ties: the one
+    with an even last mantissa bit)."""
+    f = np.float32(x)
+    b = int(np.array(f).view(np.uint32)) & 0xFFFF0000
+    cands = set()
+    for d in (-0x10000, 0, 0x10000, 0x20000):
+        c = float(np.array(np.uint32((b + d) & 0xFFFFFFFF)).view(np.float32))
+        if np.isfinite(c):
+            cands.add(c)
+    best = min(cands, key=lambda c: (abs(c - x), (int(np.array(np.float32(c)).view(np.uint32)) >> 16) & 1))
+    return best
 
 
 def pin_round_to_dtype():
-    """bf16 rounding is round-to-nearest-even on the fp32 value: hand ties
-    around 1 (ulp 2^-7), and agreement with an integer-bit implementation
-    of the same rule on random values; f32 rounding is numpy's cast."""
+    """bf16 rounding is a single round to nearest even from fp64: hand ties
+    around 1 (spacing 2^-7), a value that rounding to fp32 first would round
+    the other way (1 + 2^-8 + 2^-30: fp32 would make it the exact tie 1 +
+    2^-8 and then round down to 1), agreement with a brute-force nearest
+    search on random values, and with the fp32 bit rule on values that are
+    already fp32; f32 rounding is numpy's cast."""
     ulp = 2.0 ** -7
-    x = np.array([1 + ulp / 2, 1 + 1.5 * ulp, 1 + ulp / 2 + 2.0 ** -20, -(1 + 1.5 * ulp), 3.0])
-    assert np.array_equal(orc.round_to_dtype(x, "bf16"), [1.0, 1 + 2 * ulp, 1 + ulp, -(1 + 2 * ulp), 3.0])
-    r = np.random.Generator(np.random.PCG64(41)).standard_normal(4096) * 3.0
-    bits = wl.f32_to_bf16_bits(r.astype(np.float32))
-    assert np.array_equal(orc.round_to_dtype(r, "bf16"), wl.bf16_bits_to_f32(bits).astype(np.float64))
+    x = np.array([1 + ulp / 2, 1 + 1.5 * ulp, 1 + ulp / 2 + 2.0 ** -20, -(1 + 1.5 * ulp), 3.0, 1 + 2.0 ** -8 + 2.0 ** -30])
+    assert np.array_equal(orc.round_to_dtype(x, "bf16"), [1.0, 1 + 2 * ulp, 1 + ulp, -(1 + 2 * ulp), 3.0, 1 + ulp])
+    r = np.random.Generator(np.random.PCG64(41)).standard_normal(2000) * 3.0
+    got = orc.round_to_dtype(r, "bf16")
+    assert all(got[i] == _bf16_nearest_brute(float(r[i])) for i in range(len(r)))
+    r32 = r.astype(np.float32)
+    bits = wl.f32_to_bf16_bits(r32)
+    assert np.array_equal(orc.round_to_dtype(r32.astype(np.float64), "bf16"),
+                          wl.bf16_bits_to_f32(bits).astype(np.float64))
     assert np.array_equal(orc.round_to_dtype(r, "f32"), r.astype(np.float32).astype(np.float64))
+    assert np.isnan(orc.round_to_dtype(np.array([np.nan]), "bf16")).all()
+    assert np.array_equal(orc.round_to_dtype(np.array([0.0, np.inf, -np.inf]), "bf16"), [0.0, np.inf, -np.inf])
 
 
 ALL_PINS = [

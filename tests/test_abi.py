@@ -165,3 +165,18 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
                 assert "taylor_oracle" not in text, f
+
+
+def test_small_key_width_plans():
+    """dk = 8 runs up to six terms (C(13, 5) = 1287 feature rows); its
+    prefill takes fp32 inputs only, refused before anything is launched."""
+    assert ops.tt_state_rows(8, 6) == 1287
+    assert ops.tt_state_floats(8, 64, 6) == 1287 * 65
+    assert ops.tt_prefill_workspace_bytes(1, 16, 4096, 8, 64, 6, 64) > 0
+    with pytest.raises(ops.TTError) as e:
+        ops.tt_prefill_workspace_bytes(1, 1, 16, 8, 64, 7, 64)
+    assert e.value.code == ops.TT_ERR_UNSUPPORTED
+    L = ops.lib()
+    fake = ctypes.c_void_p(0x1000)
+    rc = L.tt_prefill(fake, fake, fake, ops.TT_BF16, 1, 1, 100, 8, 64, 3, 64, fake, fake, fake, 1 << 30, None)
+    assert rc == ops.TT_ERR_UNSUPPORTED and "fp32" in ops.tt_last_error()

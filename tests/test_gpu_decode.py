@@ -13,7 +13,7 @@ from taylor_recurrent_states_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(16, 1), (16, 2), (16, 3), (16, 4), (16, 5), (32, 3), (64, 2), (64, 3)]
+SHAPES = [(8, 3), (8, 6), (16, 1), (16, 2), (16, 3), (16, 4), (16, 5), (32, 3), (64, 2), (64, 3)]
 
 
 @pytest.mark.parametrize("dk,n", SHAPES)
@@ -111,3 +111,46 @@ def test_merge(nfloats):
         A2 = torch.from_numpy(a).cuda()
         got = ops.tt_state_merge(A2[1:], Bt[1:]).cpu().numpy()
         assert np.array_equal(got, a[1:] + b[1:])
+
+
+def test_decode_graph_replays_match_eager():
+    """Eight decode steps captured once as a HIP graph (the launch the bench
+    times as its graph variant) and replayed three times, with eager work
+    and synchronisation between replays: after every replay the outputs and
+    the states equal those of the same steps run eagerly, bit for bit."""
+    import torch
+    B, H, dk, dv, n, T = 4, 8, 16, 64, 3, 8
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9300)
+    nf = ops.tt_state_floats(dk, dv, n)
+    S_graph = torch.randn(B * H * nf, generator=g, device="cuda").abs()
+    S_eager = S_graph.clone()
+    qs = torch.nn.functional.normalize(torch.randn((T, B, H, dk), generator=g, device="cuda"), dim=-1)
+    ks = torch.nn.functional.normalize(torch.randn((T, B, H, dk), generator=g, device="cuda"), dim=-1)
+    vs = torch.randn((T, B, H, dv), generator=g, device="cuda")
+    o_graph = torch.empty((T, B, H, dv), device="cuda")
+    o_eager = torch.empty_like(o_graph)
+
+    def steps(S, out):
+        for t in range(T):
+            ops.tt_decode_step(qs[t], ks[t], vs[t], S, n, o=out[t])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture, on a scratch copy
+        scratch = S_graph.clone()
+        steps(scratch, torch.empty_like(o_graph))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        steps(S_graph, o_graph)
+    torch.cuda.synchronize()
+    for r in range(3):
+        gr.replay()
+        torch.cuda.synchronize()
+        steps(S_eager, o_eager)
+        _ = (scratch * 2).sum().item()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o_graph, o_eager), f"replay {r}: outputs"
+        assert torch.equal(S_graph, S_eager), f"replay {r}: states"

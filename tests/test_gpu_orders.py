@@ -2,12 +2,13 @@
 attention as the number of Taylor terms n grows ("Expanding Attention",
 abstract: accuracy improves exponentially in the number of terms).
 
-For n = 1 .. 5 (dk = 16) the GPU outputs must (a) match the oracle's own
+For n = 1 .. 5 (dk = 16, fp32 and bf16) and n = 1 .. 6 (dk = 8, fp32, 1287
+feature rows at n = 6) the GPU outputs must (a) match the oracle's own
 n-term truncation to the parity bar and (b) lie within the Taylor-remainder
 bound of the softmax output: with unit q, k and eps = e/n!,
 |o_n - o_softmax| <= eps/(1-eps) * max_{j<=i} |v_j - o_softmax,i| per
-coordinate (plus the parity tolerance), and the error must fall from n = 3
-to n = 5.
+coordinate (plus the parity tolerance), and the error must fall with every
+term from n = 3 on.
 """
 import math
 
@@ -15,17 +16,17 @@ import numpy as np
 import pytest
 
 import oracle.taylor_oracle as orc
-from gpu_util import assert_out, to_device
+from gpu_util import assert_out, assert_states, to_device
 from taylor_recurrent_states_amd import ops
 from taylor_recurrent_states_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_order_sweep_approaches_softmax(dtype):
+@pytest.mark.parametrize("dk,dtype,nmax", [(16, "f32", 5), (16, "bf16", 5), (8, "f32", 6)])
+def test_order_sweep_approaches_softmax(dk, dtype, nmax):
     import torch
-    B, H, N, dk, dv = 1, 4, 512, 16, 64
+    B, H, N, dv = 1, 4, 512, 64
     tol = ("rel", 1e-5) if dtype == "f32" else ("abs", 5e-3)
     q, k, v = wl.draw_qkv(4000, B, H, N, dk, dv, dtype)
     o_s = orc.softmax_attention(q.exact, k.exact, v.exact)
@@ -36,17 +37,20 @@ def test_order_sweep_approaches_softmax(dtype):
         spread[:, :, i] = np.max(np.abs(V[:, :, : i + 1] - o_s[:, :, i : i + 1]), axis=2)
     Qd, Kd, Vd = to_device(q), to_device(k), to_device(v)
     errs = {}
-    for n in range(1, 6):
-        O, _ = ops.tt_prefill(Qd, Kd, Vd, n)
+    for n in range(1, nmax + 1):
+        O, S = ops.tt_prefill(Qd, Kd, Vd, n)
         torch.cuda.synchronize()
         O = O.cpu().numpy().astype(np.float64)
         ref = orc.quadratic_attention(q.exact, k.exact, v.exact, n)
-        par = assert_out(O, ref, tol, f"n{n}")
+        par = assert_out(O, ref, tol, f"dk{dk} n{n}")
+        if dk == 8:  # the states of the order-6 sweep against the definition too
+            assert_states(S.cpu().numpy(), orc.states_definition(k.exact, v.exact, n), dk, n, tol, f"dk{dk} n{n}")
         slack = par if tol[0] == "abs" else par * float(np.max(np.abs(ref)))
         errs[n] = float(np.max(np.abs(O - o_s)))
         eps = math.e / math.factorial(n)
         if eps < 1:
             assert np.all(np.abs(O - o_s) <= eps / (1 - eps) * spread + slack + 1e-6), f"n{n} outside the remainder bound"
     with np.printoptions(precision=3):
-        print("\n  max |o_n - o_softmax| on the GPU: " + ", ".join(f"n={n}: {e:.2e}" for n, e in errs.items()))
-    assert errs[4] < errs[3] and errs[5] < errs[4]
+        print(f"\n  dk{dk} {dtype}: max |o_n - o_softmax| on the GPU: " + ", ".join(f"n={n}: {e:.2e}" for n, e in errs.items()))
+    for n in range(4, nmax + 1):
+        assert errs[n] < errs[n - 1], (n, errs)

@@ -43,6 +43,24 @@ def test_prefill_small(dk, n, dtype):
     assert_states(S, orc.states_definition(k.exact, v.exact, n), dk, n, _tol(dtype), f"dk{dk} n{n}")
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6])
+def test_prefill_small_dk8(n):
+    """dk = 8 (fp32 inputs), up to six Taylor terms: C(13, 5) = 1287 feature
+    rows at n = 6."""
+    B, H, N, dk = 1, 2, 200, 8
+    q, k, v = wl.draw_qkv(1500 + n, B, H, N, dk, 64, "f32")
+    O, S = _prefill(q, k, v, n)
+    assert_out(O, orc.quadratic_attention(q.exact, k.exact, v.exact, n), _tol("f32"), f"dk8 n{n}")
+    assert_states(S, orc.states_definition(k.exact, v.exact, n), dk, n, _tol("f32"), f"dk8 n{n}")
+
+
+def test_prefill_dk8_bf16_is_unsupported():
+    q, k, v = wl.draw_qkv(1600, 1, 1, 64, 8, 64, "bf16")
+    with pytest.raises(ops.TTError) as e:
+        ops.tt_prefill(to_device(q), to_device(k), to_device(v), 3)
+    assert e.value.code == ops.TT_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 127, 128, 129, 300, 1000])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_prefill_lengths(N, dtype):
@@ -71,13 +89,16 @@ def _sample_rows(N, rng, extra=24):
     return sorted(r for r in base if 0 <= r < N)
 
 
-def _full_workload(name, heads_checked=None, state_heads=None, w=None):
+def _full_workload(name, heads_checked=None, state_heads=None, w=None, vmap=None):
     """Run the named workload (or ``w``) at full size; compare sampled output
     rows of ``heads_checked`` (default: all heads) and every state element of
-    ``state_heads`` (default: the same heads) against the oracle."""
+    ``state_heads`` (default: the same heads) against the oracle.  ``vmap``
+    transforms the drawn values (fp64) before they are rounded again."""
     w = wl.WORKLOADS[name] if w is None else w
     print(f"\n[{name}] drawing inputs", flush=True)
     q, k, v = wl.draw_qkv(w.seed, w.B, w.H, w.N, w.dk, w.dv, w.dtype)
+    if vmap is not None:
+        v = wl.round_to(vmap(v.exact), w.dtype)
     O, S = _prefill(q, k, v, w.n)
     print(f"[{name}] GPU prefill done", flush=True)
     rng = np.random.Generator(np.random.PCG64([w.seed, 99]))
@@ -109,6 +130,15 @@ def _full_workload(name, heads_checked=None, state_heads=None, w=None):
 def test_prefill_workload_full_size():
     """B=4, H=8, N=8192, dk=16, n=3, bf16: every state element, sampled rows of every head."""
     _full_workload("prefill")
+
+
+@pytest.mark.parametrize("shift,scale", [(3.0, 1.0), (0.0, 4.0)])
+def test_prefill_workload_full_size_offset_values(shift, scale):
+    """The prefill workload with values shift + scale * N(0, 1): outputs
+    near 3, or four times the spread, where the bf16 readout of the state
+    is weakest.  Every state element, sampled rows of every head."""
+    w = dataclasses.replace(wl.WORKLOADS["prefill"], name=f"prefill v~{shift}+{scale}N(0,1)", seed=21)
+    _full_workload(w.name, w=w, vmap=lambda x: shift + scale * x)
 
 
 @pytest.mark.parametrize("B,H,N", [(4, 8, 8155), (2, 8, 8129)])

@@ -7,6 +7,7 @@ import pytest
 
 import oracle.taylor_oracle as orc
 import pins
+from taylor_recurrent_states_amd import workloads as wl
 
 _orig_taylor = orc.taylor_kernel
 _orig_feat = orc.feature_map
@@ -164,6 +165,14 @@ def _normalize_inverted_temperature(X, scale=1.0):
     return _orig_normalize(X, 1.0 / float(scale))
 
 
+def _round_via_f32(X, dtype):
+    # rounds to fp32 first, then to bf16: two roundings
+    if dtype != "bf16":
+        return _orig_round(X, dtype)
+    x32 = np.asarray(X, dtype=np.float64).astype(np.float32)
+    return wl.bf16_bits_to_f32(wl.f32_to_bf16_bits(x32)).astype(np.float64)
+
+
 def _round_truncating(X, dtype):
     if dtype != "bf16":
         return _orig_round(X, dtype)
@@ -213,6 +222,7 @@ MUTANTS = {
     "softmax_rows_exclusive": ("softmax_rows", _softmax_rows_exclusive),
     "softmax_rows_no_max": ("softmax_rows", _softmax_rows_no_max),
     "round_bf16_truncating": ("round_to_dtype", _round_truncating),
+    "round_bf16_twice": ("round_to_dtype", _round_via_f32),
 }
 
 # cheap pins first; each mutant must make at least one of them fail

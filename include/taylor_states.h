@@ -108,6 +108,28 @@ int tt_prefill(const void *Q, const void *K, const void *V, tt_dtype in_dtype,
                float *O, float *states, void *workspace, size_t workspace_bytes,
                void *stream);
 
+/* Bytes of the fixed device scratch array that tt_prefill_noalloc uses in
+ * place of a workspace (64 MiB per GPU). */
+#define TT_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* tt_prefill for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, kernels and results as tt_prefill, with the
+ * workspace taken from a fixed array of TT_NOALLOC_SCRATCH_BYTES in device
+ * memory that the library holds on each GPU it runs on until the process
+ * ends.  The call allocates nothing: the caller passes Q, K, V, O and
+ * states as for tt_prefill (same layouts, alignment and errors).  A shape
+ * whose tt_prefill_workspace_bytes() exceeds TT_NOALLOC_SCRATCH_BYTES
+ * returns TT_ERR_WORKSPACE before anything is launched.  The first call on
+ * a device looks the array up on the current device, which `stream` must
+ * belong to.  Every call on one GPU shares that GPU's array, and each call
+ * overwrites what it needs of it (nothing has to start at zero): calls
+ * that may overlap on one GPU (other streams, other threads) race and give
+ * undefined results, so serialise them. */
+int tt_prefill_noalloc(const void *Q, const void *K, const void *V, tt_dtype in_dtype,
+                       int B, int H, int N, int dk, int dv, int n, int chunk,
+                       float *O, float *states, void *stream);
+
 /* Prefill that continues from carried-in states: the same computation as
  * tt_prefill for tokens that follow earlier ones whose summed states are
  * states_in ("Expanding Attention", abstract: the states are sums over

@@ -1,8 +1,11 @@
 // C entry points of libtaylor_states.so: argument validation, planning and
-// launch on the caller's stream.  No allocation, no global state (apart from
-// the thread-local error message).
+// launch on the caller's stream.  No allocation, no global state apart from
+// the thread-local error message and the fixed device scratch array of the
+// no-allocation prefill (below).
 #include <stdarg.h>
 #include <stdio.h>
+
+#include <mutex>
 
 #include "tt_device.hpp"
 #include "tt_internal.hpp"
@@ -144,6 +147,47 @@ static int decode_impl(const void* q, const void* k, const void* v, tt_dtype in_
                     what);
 }
 
+// Device scratch of tt_prefill_noalloc: one array per GPU, loaded with the
+// code object and held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol); it uses the device address that hipGetSymbolAddress returns for
+// the current device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[TT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+// Device address of `scratch` on the current device (null on error, with
+// the error recorded for tt_last_error()).
+static void* scratch_for_current_device(int* rc) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *rc = hip_status(e, "hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *rc = fail(TT_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) {
+    *rc = hip_status(g_scratch_err[dev] != hipSuccess ? g_scratch_err[dev] : hipErrorInvalidSymbol,
+                     "hipGetSymbolAddress(scratch)");
+    return nullptr;
+  }
+  *rc = TT_OK;
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace tt
 
 using namespace tt;
@@ -194,6 +238,23 @@ int tt_prefill(const void* Q, const void* K, const void* V, tt_dtype in_dtype, i
                void* stream) {
   return prefill_impl(Q, K, V, in_dtype, B, H, N, dk, dv, n, chunk, nullptr, O, nullptr, states, workspace,
                       workspace_bytes, false, 1.0f, stream, "tt_prefill");
+}
+
+int tt_prefill_noalloc(const void* Q, const void* K, const void* V, tt_dtype in_dtype, int B, int H, int N, int dk,
+                       int dv, int n, int chunk, float* O, float* states, void* stream) {
+  if (B < 1 || H < 1 || N < 1) return fail(TT_ERR_INVALID_ARG, "B=%d H=%d N=%d must be >= 1", B, H, N);
+  size_t need = 0;
+  int rc = tt_prefill_workspace_bytes(B, H, N, dk, dv, n, chunk, &need);
+  if (rc) return rc;
+  if (need > (size_t)TT_NOALLOC_SCRATCH_BYTES)
+    return fail(TT_ERR_WORKSPACE,
+                "this shape needs %zu bytes of scratch; tt_prefill_noalloc holds %zu (use tt_prefill with a "
+                "workspace)",
+                need, (size_t)TT_NOALLOC_SCRATCH_BYTES);
+  void* ws = scratch_for_current_device(&rc);
+  if (!ws) return rc;
+  return prefill_impl(Q, K, V, in_dtype, B, H, N, dk, dv, n, chunk, nullptr, O, nullptr, states, ws,
+                      (size_t)TT_NOALLOC_SCRATCH_BYTES, false, 1.0f, stream, "tt_prefill_noalloc");
 }
 
 int tt_prefill_from(const void* Q, const void* K, const void* V, tt_dtype in_dtype, int B, int H, int N, int dk,

@@ -8,7 +8,8 @@ The calls keep the C names:
     tt_prefill, tt_prefill_from, tt_decode_step, tt_state_merge,
     tt_feature_map, tt_last_error, tt_normalize_rows,
     tt_prefill_normed_workspace_bytes, tt_prefill_normed, tt_decode_step_normed,
-    tt_softmax_prefill, tt_softmax_decode_workspace_bytes, tt_softmax_decode_step
+    tt_softmax_prefill, tt_softmax_decode_workspace_bytes, tt_softmax_decode_step,
+    tt_prefill_noalloc
 
 Loading fails loudly (ImportError / OSError) when the library has not been
 built; there is no fallback implementation.
@@ -30,7 +31,7 @@ EXPORTED = ("tt_state_rows", "tt_state_floats", "tt_prefill_workspace_bytes", "t
             "tt_prefill_from", "tt_prefill_from_unnormalized", "tt_decode_step", "tt_state_merge", "tt_feature_map", "tt_last_error",
             "tt_normalize_rows", "tt_prefill_normed_workspace_bytes", "tt_prefill_normed",
             "tt_decode_step_normed", "tt_softmax_prefill", "tt_softmax_decode_workspace_bytes",
-            "tt_softmax_decode_step")
+            "tt_softmax_decode_step", "tt_prefill_noalloc")
 
 _lib = None
 
@@ -92,6 +93,8 @@ def lib() -> ctypes.CDLL:
                                                                                           c_float_p, c_void, c_size,
                                                                                           c_void]
     L.tt_softmax_decode_step.restype = c_int
+    L.tt_prefill_noalloc.argtypes = [c_void, c_void, c_void, c_int] + [c_int] * 7 + [c_float_p, c_float_p, c_void]
+    L.tt_prefill_noalloc.restype = c_int
     L.tt_last_error.argtypes = []
     L.tt_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -277,6 +280,26 @@ def tt_prefill(Q, K, V, n: int, chunk: int = 64, O=None, states=None, workspace=
                                                                        launch)
     _check(lib().tt_prefill(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk, dv, n, chunk,
                             O.data_ptr(), states.data_ptr(), ws_ptr, ws_bytes, launch.handle))
+    return O, states
+
+
+TT_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def tt_prefill_noalloc(Q, K, V, n: int, chunk: int, O, states, stream=None):
+    """tt_prefill that allocates nothing: O [B, H, N, dv] and states (flat,
+    B*H*W*(dv+1)) float32 are required, and the library's fixed device
+    scratch array serves as the workspace.  Calls that overlap on one GPU
+    race.  Returns (O, states)."""
+    if O is None or states is None:
+        raise ValueError("tt_prefill_noalloc allocates nothing: pass O and states")
+    launch = _Launch(stream)
+    B, H, N, dk, dv = _qkv(Q, K, V)
+    _f32(O, "O", B * H * N * dv)
+    _f32(states, "states", B * H * tt_state_floats(dk, dv, n))
+    _on_gpu(Q, (K, "K"), (V, "V"), (O, "O"), (states, "states"))
+    _check(lib().tt_prefill_noalloc(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk, dv, n,
+                                    chunk, O.data_ptr(), states.data_ptr(), launch.handle))
     return O, states
 
 

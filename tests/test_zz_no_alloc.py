@@ -1,0 +1,53 @@
+"""tt_prefill_noalloc: the prefill for callers that cannot allocate device
+memory, with its workspace in the library's fixed device scratch array.
+Checked through the C ABI against tt_prefill (the entry point it varies),
+bit for bit: the same kernels and plans run, only the workspace differs.
+Two calls in a row, the second smaller, so the second runs on scratch left
+over from the first; a shape whose workspace exceeds the array is refused
+before anything is launched."""
+import numpy as np
+import pytest
+
+from gpu_util import to_device
+from taylor_recurrent_states_amd import ops
+from taylor_recurrent_states_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_both(B, H, N, dk, n, dtype, seed):
+    import torch
+    q, k, v = wl.draw_qkv(seed, B, H, N, dk, 64, dtype)
+    Q, K, V = to_device(q), to_device(k), to_device(v)
+    O_ref, S_ref = ops.tt_prefill(Q, K, V, n)
+    O = torch.full_like(O_ref, float("nan"))
+    S = torch.full_like(S_ref, float("nan"))
+    ops.tt_prefill_noalloc(Q, K, V, n, 64, O, S)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O_ref), f"B{B} H{H} N{N} dk{dk} n{n} {dtype}: outputs differ"
+    assert torch.equal(S, S_ref), f"B{B} H{H} N{N} dk{dk} n{n} {dtype}: states differ"
+
+
+def test_noalloc_matches_prefill_twice_then_smaller():
+    print("\n[noalloc] prefill workload shape, bf16", flush=True)
+    _run_both(4, 8, 8192, 16, 3, "bf16", 31)
+    print("[noalloc] smaller second call, fp32 sweep path", flush=True)
+    _run_both(1, 2, 1000, 16, 5, "f32", 32)
+    print("[noalloc] smaller third call, bf16 ragged", flush=True)
+    _run_both(1, 3, 777, 32, 3, "bf16", 33)
+
+
+def test_noalloc_refuses_shapes_beyond_the_scratch():
+    import torch
+    B, H, N, dk, n = 1, 16, 8192, 64, 3  # row-group partials alone exceed the array
+    need = ops.tt_prefill_workspace_bytes(B, H, N, dk, 64, n)
+    assert need > ops.TT_NOALLOC_SCRATCH_BYTES
+    Q = torch.zeros((B, H, N, dk), dtype=torch.bfloat16, device="cuda")
+    V = torch.zeros((B, H, N, 64), dtype=torch.bfloat16, device="cuda")
+    O = torch.zeros((B, H, N, 64), device="cuda")
+    S = torch.zeros(B * H * ops.tt_state_floats(dk, 64, n), device="cuda")
+    with pytest.raises(ops.TTError) as e:
+        ops.tt_prefill_noalloc(Q, Q, V, n, 64, O, S)
+    assert e.value.code == ops.TT_ERR_WORKSPACE and "scratch" in str(e.value)
+    torch.cuda.synchronize()
+    assert not O.abs().max().item()  # nothing ran

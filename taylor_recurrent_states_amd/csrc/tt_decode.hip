@@ -9,6 +9,9 @@
 // once.  One workgroup per head; a wavefront's 64 lanes are the 64 value
 // columns, so each state row (256 B) is one coalesced load and one
 // coalesced store.  mu(k) and phi(q) are computed once per head into LDS.
+// The updated state is written with non-temporal stores: at steady state the
+// states of all heads do not fit the memory-side cache, and stores that take
+// cache lines there slow the step's loads down.
 #include "tt_device.hpp"
 #include "tt_internal.hpp"
 
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(kDecodeThreads, 8) void decode_kernel(const TIn* __
     for (int u = 0; u < per; ++u)
       if (r0 + u < r1) {
         const float s = fmaf(s_mu[r0 + u], vc, sv[u]);
-        S[(size_t)(r0 + u) * kDV + lane] = s;
+        store_nt(&S[(size_t)(r0 + u) * kDV + lane], s);
         acc = fmaf(s_phi[r0 + u], s, acc);
       }
   } else {
@@ -113,14 +116,14 @@ __global__ __launch_bounds__(kDecodeThreads, 8) void decode_kernel(const TIn* __
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         s[u] = fmaf(s_mu[r + u], vc, s[u]);
-        S[(size_t)(r + u) * kDV + lane] = s[u];
+        store_nt(&S[(size_t)(r + u) * kDV + lane], s[u]);
         acc = fmaf(s_phi[r + u], s[u], acc);
       }
     }
     for (; r < r1; ++r) {
       float s = S[(size_t)r * kDV + lane];
       s = fmaf(s_mu[r], vc, s);
-      S[(size_t)r * kDV + lane] = s;
+      store_nt(&S[(size_t)r * kDV + lane], s);
       acc = fmaf(s_phi[r], s, acc);
     }
   }
@@ -130,13 +133,13 @@ __global__ __launch_bounds__(kDecodeThreads, 8) void decode_kernel(const TIn* __
   if constexpr (RES) {
     if (tid < W) {
       const float d = dv + s_mu[tid];
-      D[tid] = d;
+      store_nt(&D[tid], d);
       accd = s_phi[tid] * d;
     }
   } else {
     for (int rr = tid; rr < W; rr += kDecodeThreads) {
       const float d = D[rr] + s_mu[rr];
-      D[rr] = d;
+      store_nt(&D[rr], d);
       accd = fmaf(s_phi[rr], d, accd);
     }
   }

@@ -1175,7 +1175,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
           for (int qt = 0; qt < 4; ++qt) {
             const f32x4 rd = *reinterpret_cast<const f32x4*>(sDenQ + qt * 16 + 4 * lg);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) ob[(qt * 16 + s) * kDV] = num[qt][s] * rd[s];
+            for (int s = 0; s < 4; ++s) store_nt(&ob[(qt * 16 + s) * kDV], num[qt][s] * rd[s]);
           }
         } else {
 #pragma unroll
@@ -1183,7 +1183,7 @@ __global__ __launch_bounds__(C::NTHR) void sweep_kernel(const typename C::TIn* _
             const f32x4 rd = *reinterpret_cast<const f32x4*>(sDenQ + qt * 16 + 4 * lg);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-              if (qt * 16 + 4 * lg + s < nvalid) ob[(qt * 16 + s) * kDV] = num[qt][s] * rd[s];
+              if (qt * 16 + 4 * lg + s < nvalid) store_nt(&ob[(qt * 16 + s) * kDV], num[qt][s] * rd[s]);
           }
         }
         }
@@ -1704,7 +1704,7 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
 #pragma unroll
           for (int qt = 0; qt < 4; ++qt) {
             float* ob = Og + ((size_t)bh * N + c0 - kCH + qt * 16 + li) * kDV + ct * 16 + 4 * lg;
-            *reinterpret_cast<f32x4*>(ob) = nprev[qt] * rd[qt];
+            store_nt(ob, nprev[qt] * rd[qt]);
           }
         }
 #pragma unroll
@@ -1782,7 +1782,7 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
       for (int qt = 0; qt < 4; ++qt) {
         if (qt * 16 + li < nvalid) {
           float* ob = Og + ((size_t)bh * N + lc0 + qt * 16 + li) * kDV + ct * 16 + 4 * lg;
-          *reinterpret_cast<f32x4*>(ob) = nprev[qt] * rd[qt];
+          store_nt(ob, nprev[qt] * rd[qt]);
         }
       }
     } else {
@@ -1928,10 +1928,10 @@ __global__ void combine_kernel(const float* __restrict__ part, int BH, int N, in
       d += pden[row];
     }
     if (Dg) {  // unnormalised: the numerator to O, the normaliser to Dg
-      *reinterpret_cast<f32x4*>(O + (bh * N + t) * kDV + 4 * c4) = acc;
+      store_nt(O + (bh * N + t) * kDV + 4 * c4, acc);
       if (c4 == 0) Dg[bh * N + t] = d;
     } else {
-      *reinterpret_cast<f32x4*>(O + (bh * N + t) * kDV + 4 * c4) = acc * (1.0f / d);
+      store_nt(O + (bh * N + t) * kDV + 4 * c4, acc * (1.0f / d));
     }
   }
 }

@@ -99,7 +99,15 @@ int tt_prefill_workspace_bytes(int B, int H, int N, int dk, int dv, int n,
  *            states of all N tokens (prefill starts from zero states)
  *   workspace : device scratch of at least tt_prefill_workspace_bytes();
  *            contents undefined on return
- *   chunk : tokens per chunk of the intra-chunk quadratic block; 64.
+ *   chunk : tokens per chunk of the intra-chunk quadratic block: 16, 32,
+ *           64 or 128.  Results do not depend on it beyond fp32 rounding
+ *           (it moves work between the quadratic block and the state).
+ *           bf16 inputs take 32, 64 or 128.  128 runs the shapes whose
+ *           tiles fit the 160 KB of LDS of a CU: fp32 dk=8 n<=4, dk=16
+ *           n<=3, dk=32 n=1; bf16 dk=16 n<=3, dk=32 n<=2, dk=64 n=1.
+ *           Other values and combinations return TT_ERR_UNSUPPORTED.  64
+ *           is the tuned default (bf16 with W <= 256 then runs the
+ *           warp-specialised kernel).
  * Q, K, V, O and workspace must be 16-byte aligned (TT_ERR_INVALID_ARG).
  * Any N >= 1 is accepted (the tail chunk is masked).  Results do not
  * depend on how the work is split beyond fp32 rounding. */

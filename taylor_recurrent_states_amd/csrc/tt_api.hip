@@ -219,17 +219,17 @@ int tt_prefill_workspace_bytes(int B, int H, int N, int dk, int dv, int n, int c
   if (B < 1 || H < 1 || N < 1) return fail(TT_ERR_INVALID_ARG, "B=%d H=%d N=%d must be >= 1", B, H, N);
   int rc = check_shape(dk, dv, n);
   if (rc) return rc;
-  // the query takes no dtype: report the larger of the fp32 and bf16 plans
-  // (dk = 8 runs on fp32 inputs only)
+  // the query takes no dtype: report the larger of the fp32 and bf16 plans,
+  // over the dtypes this shape and chunk length run with (an error only if
+  // neither does)
   PrefillPlan pf, pb;
-  rc = plan_prefill(B, H, N, dk, dv, n, chunk, TT_F32, &pf);
-  if (rc) return rc;
-  pb.ws_floats = 0;
-  if (dk >= 16) {
-    rc = plan_prefill(B, H, N, dk, dv, n, chunk, TT_BF16, &pb);
-    if (rc) return rc;
-  }
-  *bytes = (pf.ws_floats > pb.ws_floats ? pf.ws_floats : pb.ws_floats) * sizeof(float);
+  const int rf = plan_prefill(B, H, N, dk, dv, n, chunk, TT_F32, &pf);
+  const int rb = plan_prefill(B, H, N, dk, dv, n, chunk, TT_BF16, &pb);
+  if (rf && rb) return plan_prefill(B, H, N, dk, dv, n, chunk, TT_F32, &pf);  // the fp32 message
+  size_t w = 0;
+  if (!rf) w = pf.ws_floats;
+  if (!rb && pb.ws_floats > w) w = pb.ws_floats;
+  *bytes = w * sizeof(float);
   return ok();
 }
 

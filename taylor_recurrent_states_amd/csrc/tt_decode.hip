@@ -22,10 +22,10 @@ namespace {
 constexpr int kDV = 64;
 constexpr int kDecodeThreads = 256;
 
-// NORM: q and k arrive raw; thread 0 (wave 0) turns q into r(qscale q/|q|)
-// and thread 64 (wave 1) k into r(k/|k|) in LDS, with the arithmetic of
-// normalize_row (row_norm_factor, unit_coord), which the prefill's
-// normalisation pass uses.
+// NORM: q and k arrive raw; wave 0 turns q into r(qscale q/|q|) and wave 1
+// k into r(k/|k|) in LDS, dk/8 lanes per row with the arithmetic of
+// normalize_kernel (the prefill's normalisation pass): group sums of squares
+// in fp64, a butterfly over the groups, then unit_coord.
 //
 // Small states (at most 48 rows per wave, e.g. 153 rows at dk = 16, n = 3):
 // every wave issues the loads of all its state rows (and each thread its
@@ -80,12 +80,20 @@ __global__ __launch_bounds__(kDecodeThreads, 8) void decode_kernel(const TIn* __
     s_q[tid] = load_f32(q, (size_t)bh * DK + tid);
     s_k[tid] = load_f32(k, (size_t)bh * DK + tid);
   }
-  if constexpr (NORM) {  // in place in LDS
+  if constexpr (NORM) {  // in place in LDS: wave 0 normalises q, wave 1 k
     __syncthreads();
-    if (tid == 0 || tid == 64) {
-      float* row = tid == 0 ? s_q : s_k;
-      const double f = row_norm_factor<DK>([&](int i) { return row[i]; }, tid == 0 ? qscale : 1.0f);
-      for (int i = 0; i < DK; ++i) row[i] = unit_coord<TIn>(row[i], f);
+    constexpr int G = DK / 8;  // lanes per row, one group of 8 coordinates each
+    if (wave < 2 && lane < G) {
+      float* row = wave == 0 ? s_q : s_k;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = row[8 * lane + e];
+      double ss = group_sumsq([&](int i) { return x[i & 7]; }, lane);
+#pragma unroll
+      for (int off = 1; off < G; off *= 2) ss = ss + __shfl_xor(ss, off);
+      const double f = (double)(wave == 0 ? qscale : 1.0f) / sqrt(ss);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) row[8 * lane + e] = unit_coord<TIn>(x[e], f);
     }
     load_state();
   }
@@ -176,8 +184,9 @@ __global__ void feature_map_kernel(const TIn* __restrict__ x, size_t rows, int W
 // of 8 coordinates each (a 16-byte bf16 or two 16-byte fp32 accesses), so a
 // wave reads and writes contiguous memory.  Each lane sums the squares of its
 // group (group_sumsq), a shfl_xor butterfly over the row's lanes adds the
-// group sums in row_norm_factor's pairwise-tree order, and each lane scales
-// its own coordinates: the bits of normalize_row.  out may be x (every
+// group sums as a pairwise tree, and each lane scales its own coordinates
+// (unit_coord); the decode kernel's normalisation does the same, so both
+// give the same bits.  out may be x (every
 // coordinate is read before it is written, by the same lane).
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void normalize_kernel(const TIn* x0, TIn* out0, float s0, size_t rows0,

@@ -184,14 +184,16 @@ __device__ inline float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
 // q and k keep q.k inside the series' convergence radius; a temperature is
 // folded into the queries as `scale`).  x <- r(scale * x / ||x||_2), where r
 // rounds once to the nearest value of the input dtype (ties to even).  The
-// quotient is evaluated in
-// fp64 (row_norm_factor: squares of the fp32 coordinates, which are exact in
-// fp64, summed in groups of 8 and a pairwise tree over the groups; then the
-// square root, scale / root and x_i * that factor, each an IEEE fp64
-// operation).  That value lies within about 10 fp64 ulps of the exact unit
-// coordinate, so r gives the correctly rounded unit row except where the
-// exact value lies that close to a rounding boundary.  The operation order
-// is fixed, so every kernel gives the same bits.  A zero row gives NaN.
+// quotient is evaluated in fp64: squares of the fp32 coordinates (exact in
+// fp64) summed in groups of 8 consecutive coordinates (group_sumsq), the
+// group sums added as a balanced pairwise tree, neighbours first
+// (((g0+g1)+(g2+g3))+..., which a shfl_xor butterfly over lane offsets 1, 2,
+// 4 gives when each lane holds one group), then f = scale / sqrt(sum) and
+// x_i * f (unit_coord), each an IEEE fp64 operation.  That value lies within
+// about 10 fp64 ulps of the exact unit coordinate, so r gives the correctly
+// rounded unit row except where the exact value lies that close to a
+// rounding boundary.  The operation order is fixed, so every kernel gives the
+// same bits.  A zero row gives NaN.
 // ---------------------------------------------------------------------------
 
 // Sum of squares of the 8 coordinates get(8g) .. get(8g+7), in index order,
@@ -205,26 +207,6 @@ __device__ inline double group_sumsq(Get get, int g) {
     s = s + xi * xi;
   }
   return s;
-}
-
-// The factor scale / ||x||_2 (fp64) of a row whose coordinates get(0) ..
-// get(D-1) are fp32 values.  Squares are summed in groups of 8 consecutive
-// coordinates (group_sumsq); the group sums are added as a balanced pairwise
-// tree, neighbours first (((g0+g1)+(g2+g3))+...).  A kernel that spreads a
-// row over D/8 lanes reaches the same bits with a shfl_xor butterfly over
-// lane offsets 1, 2, 4 (IEEE addition commutes).
-template <int D, typename Get>
-__device__ inline double row_norm_factor(Get get, float scale) {
-  constexpr int G = D / 8;
-  static_assert(D % 8 == 0 && (G & (G - 1)) == 0, "groups of 8, a power-of-two count");
-  double g[G];
-#pragma unroll
-  for (int j = 0; j < G; ++j) g[j] = group_sumsq(get, j);
-#pragma unroll
-  for (int w = 1; w < G; w *= 2)
-#pragma unroll
-    for (int j = 0; j + w < G; j += 2 * w) g[j] = g[j] + g[j + w];
-  return (double)scale / sqrt(g[0]);
 }
 
 // fp64 -> bf16 rounded once to nearest even.  The fp64 value is first
@@ -254,13 +236,6 @@ __device__ inline float unit_coord(float x, double f) {
     return round_bf16_from_f64(y);
   else
     return (float)y;
-}
-
-template <typename TIn, int D>
-__device__ inline void normalize_row(float (&x)[D], float scale) {
-  const double f = row_norm_factor<D>([&](int i) { return x[i]; }, scale);
-#pragma unroll
-  for (int i = 0; i < D; ++i) x[i] = unit_coord<TIn>(x[i], f);
 }
 
 // ---------------------------------------------------------------------------

@@ -55,4 +55,18 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype 
                           int n, const PrefillPlan& p, const float* states_in, float* O, float* den_out,
                           float* states, float* ws, hipStream_t s);
 
+// The sweep-kernel prefill path for chunks of 16, 32 and 128 tokens (one
+// compilation unit each): plan figures and launches, as for 64 tokens.
+hipError_t sweep_shape_chunk16(int dk, int n, tt_dtype dt, int* wp, int* ngroups, int* nrg);
+hipError_t sweep_shape_chunk32(int dk, int n, tt_dtype dt, int* wp, int* ngroups, int* nrg);
+hipError_t sweep_shape_chunk128(int dk, int n, tt_dtype dt, int* wp, int* ngroups, int* nrg);
+#define TT_SWEEP_LAUNCH_DECL(NAME)                                                                              \
+  hipError_t NAME(const void* Q, const void* K, const void* V, tt_dtype dt, int BH, int N, int dk, int n,         \
+                  const PrefillPlan& p, const float* states_in, float* O, float* den_out, float* states, float* ws, \
+                  hipStream_t s);
+TT_SWEEP_LAUNCH_DECL(sweep_launch_chunk16)
+TT_SWEEP_LAUNCH_DECL(sweep_launch_chunk32)
+TT_SWEEP_LAUNCH_DECL(sweep_launch_chunk128)
+#undef TT_SWEEP_LAUNCH_DECL
+
 }  // namespace tt

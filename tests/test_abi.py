@@ -177,6 +177,27 @@ def test_small_key_width_plans():
         ops.tt_prefill_workspace_bytes(1, 1, 16, 8, 64, 7, 64)
     assert e.value.code == ops.TT_ERR_UNSUPPORTED
     L = ops.lib()
-    fake = ctypes.c_void_p(0x1000)
-    rc = L.tt_prefill(fake, fake, fake, ops.TT_BF16, 1, 1, 100, 8, 64, 3, 64, fake, fake, fake, 1 << 30, None)
+    misaligned, fake = ctypes.c_void_p(0x1001), ctypes.c_void_p(0x1000)  # never reaches a launch
+    rc = L.tt_prefill(misaligned, fake, fake, ops.TT_BF16, 1, 1, 100, 8, 64, 3, 64, fake, fake, fake, 1 << 30, None)
     assert rc == ops.TT_ERR_UNSUPPORTED and "fp32" in ops.tt_last_error()
+
+
+def test_chunk_lengths_are_validated_before_launch():
+    """chunk in {16, 32, 64, 128}; bf16 takes 32 or more; 128 runs the shapes
+    whose tiles fit the LDS and refuses the others, all before any launch."""
+    L = ops.lib()
+    # Q misaligned: a shape the plan accepts fails the alignment check that
+    # follows it (INVALID_ARG), so no call here can reach a launch
+    misaligned, fake = ctypes.c_void_p(0x1001), ctypes.c_void_p(0x1000)
+
+    def rc(dt, dk, n, chunk):
+        return L.tt_prefill(misaligned, fake, fake, dt, 1, 1, 100, dk, 64, n, chunk, fake, fake, fake, 1 << 40, None)
+
+    for chunk in (0, 8, 48, 96, 256):
+        assert rc(ops.TT_F32, 16, 3, chunk) == ops.TT_ERR_UNSUPPORTED
+    assert rc(ops.TT_BF16, 16, 3, 16) == ops.TT_ERR_UNSUPPORTED
+    assert rc(ops.TT_BF16, 16, 3, 128) == ops.TT_ERR_INVALID_ARG
+    assert rc(ops.TT_BF16, 64, 3, 128) == ops.TT_ERR_UNSUPPORTED
+    assert rc(ops.TT_F32, 8, 6, 16) == ops.TT_ERR_INVALID_ARG
+    for chunk in (16, 32, 64, 128):
+        assert ops.tt_prefill_workspace_bytes(2, 4, 1000, 16, 64, 3, chunk) > 0

@@ -289,3 +289,105 @@ def test_prefill_rejects_misaligned_outputs(which):
     with pytest.raises(ops.TTError) as e:
         ops.tt_prefill(to_device(q), to_device(k), to_device(v), 3, O=O, states=S)
     assert e.value.code == ops.TT_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# Chunk length ("Expanding Attention", abstract: the states add, so the split
+# of the sequence into chunks is free; the chunk length moves work between
+# the intra-chunk quadratic block and the state readout and update).
+# 64 tokens: pipe kernel (bf16, W <= 256) or sweep kernel; 16, 32 and 128:
+# sweep kernel compiled per chunk length.  bf16 needs chunks of 32 or more;
+# 128-token chunks run the shapes whose tiles fit the LDS of a CU, and the
+# others are refused before anything is launched.
+# ---------------------------------------------------------------------------
+
+CHUNK_SHAPES = [(8, 6), (16, 1), (16, 3), (16, 5), (32, 2), (64, 3)]
+
+
+def _refused(dk, n, dtype, chunk):
+    """Whether the library refuses the shape, asked without launching: Q is
+    misaligned, which the entry point reports (INVALID_ARG) only after the
+    plan check (UNSUPPORTED), so the call never reaches a launch."""
+    L = ops.lib()
+    import ctypes
+    misaligned, fake = ctypes.c_void_p(0x1001), ctypes.c_void_p(0x1000)
+    rc = L.tt_prefill(misaligned, fake, fake, ops.TT_F32 if dtype == "f32" else ops.TT_BF16, 1, 1, 100, dk, 64, n,
+                      chunk, fake, fake, fake, 1 << 40, None)
+    assert rc in (ops.TT_ERR_UNSUPPORTED, ops.TT_ERR_INVALID_ARG), rc
+    return rc == ops.TT_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64, 128])
+@pytest.mark.parametrize("dk,n", CHUNK_SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_chunk_lengths(chunk, dk, n, dtype):
+    """Every chunk length against the oracle on 300 tokens (ragged for every
+    length), B*H = 2, every output and state element."""
+    import torch
+    B, H, N = 1, 2, 300
+    q, k, v = wl.draw_qkv(5000 + 10 * dk + n, B, H, N, dk, 64, dtype)
+    if _refused(dk, n, dtype, chunk):
+        assert (dtype == "bf16" and (dk < 16 or chunk < 32)) or chunk == 128, "refused unexpectedly"
+        with pytest.raises(ops.TTError) as e:
+            ops.tt_prefill(to_device(q), to_device(k), to_device(v), n, chunk)
+        assert e.value.code == ops.TT_ERR_UNSUPPORTED
+        return
+    O, S = ops.tt_prefill(to_device(q), to_device(k), to_device(v), n, chunk)
+    torch.cuda.synchronize()
+    tag = f"chunk{chunk} dk{dk} n{n} {dtype}"
+    assert_out(O.cpu().numpy(), orc.quadratic_attention(q.exact, k.exact, v.exact, n), _tol(dtype), tag)
+    assert_states(S.cpu().numpy(), orc.states_definition(k.exact, v.exact, n), dk, n, _tol(dtype), tag)
+
+
+def test_tiny_workload_every_chunk_length():
+    """The tiny workload (N = 256, dk 16, n 3, fp32) with chunks of 16, 32,
+    64 and 128: each against the quadratic form and the oracle's chunked
+    form of the same chunk length, and the four results against each other."""
+    import torch
+    w = wl.WORKLOADS["tiny"]
+    q, k, v = wl.draw_qkv(w.seed, w.B, w.H, w.N, w.dk, w.dv, w.dtype)
+    ref = orc.quadratic_attention(q.exact, k.exact, v.exact, w.n)
+    outs = {}
+    for chunk in (16, 32, 64, 128):
+        O, S = ops.tt_prefill(to_device(q), to_device(k), to_device(v), w.n, chunk)
+        torch.cuda.synchronize()
+        O = O.cpu().numpy()
+        o_chunked, _ = orc.chunked_attention(q.exact, k.exact, v.exact, w.n, chunk)
+        assert_out(O, ref, w.tol, f"chunk {chunk}")
+        assert_out(O, o_chunked, w.tol, f"chunk {chunk} vs chunked oracle")
+        assert_states(S.cpu().numpy(), orc.states_definition(k.exact, v.exact, w.n), w.dk, w.n, w.tol, f"chunk {chunk}")
+        outs[chunk] = O
+    for c in (16, 32, 128):
+        assert_out(outs[c], outs[64].astype(np.float64), w.tol, f"chunk {c} vs 64")
+
+
+def test_prefill_workload_chunk_lengths():
+    """The prefill workload (B4 H8 N8192 dk16 n3 bf16) with chunks of 32 and
+    128 besides the default 64: sampled rows of every head and every state
+    element against the oracle, and all outputs of the three lengths within
+    the bar of each other."""
+    import torch
+    w = wl.WORKLOADS["prefill"]
+    print("\n[chunks] drawing inputs", flush=True)
+    q, k, v = wl.draw_qkv(w.seed, w.B, w.H, w.N, w.dk, w.dv, w.dtype)
+    Qd, Kd, Vd = to_device(q), to_device(k), to_device(v)
+    outs = {}
+    for chunk in (32, 64, 128):
+        O, S = ops.tt_prefill(Qd, Kd, Vd, w.n, chunk)
+        torch.cuda.synchronize()
+        outs[chunk] = (O.cpu().numpy(), S.cpu().numpy())
+        print(f"[chunks] chunk {chunk} done", flush=True)
+    BH = w.B * w.H
+    S_ref = orc.states_definition(k.exact, v.exact, w.n)
+    rng = np.random.Generator(np.random.PCG64([w.seed, 97]))
+    Qx, Kx, Vx = (a.exact.reshape(BH, w.N, -1) for a in (q, k, v))
+    for chunk, (O, S) in outs.items():
+        assert_states(S, S_ref, w.dk, w.n, w.tol, f"chunk {chunk}")
+        Og = O.reshape(BH, w.N, w.dv)
+        for h in range(BH):
+            rows = _sample_rows(w.N, rng, extra=8)
+            ref = orc.quadratic_rows(Qx[h, rows], Kx[h], Vx[h], rows, w.n)
+            assert_out(Og[h, rows], ref, w.tol, f"chunk {chunk} head {h}")
+        print(f"[chunks] chunk {chunk} against the oracle ok", flush=True)
+    for chunk in (32, 128):
+        assert_out(outs[chunk][0], outs[64][0].astype(np.float64), w.tol, f"chunk {chunk} vs 64")

@@ -93,10 +93,11 @@ def draw_qkv(seed, B: int, H: int, N: int, dk: int, dv: int, dtype: str,
     return round_to(q, dtype), round_to(k, dtype), round_to(v, dtype)
 
 
-def draw_prefix_kv(b: int, h: int, N: int, dk: int, dv: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Decode-workload prefix of one (b, h): k then v, PCG64([2, b, h]);
+def draw_prefix_kv(b: int, h: int, N: int, dk: int, dv: int, part: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Decode-workload prefix of one (b, h): k then v, PCG64([2, b, h])
+    (PCG64([2, b, h, part]) for a further part of the prefix, part >= 1);
     k normalised; both rounded to fp32 and returned as fp64 values."""
-    g = np.random.Generator(np.random.PCG64([2, b, h]))
+    g = np.random.Generator(np.random.PCG64([2, b, h] if part == 0 else [2, b, h, part]))
     k = l2_normalise(g.standard_normal((N, dk)))
     v = g.standard_normal((N, dv))
     return (k.astype(np.float32).astype(np.float64),

@@ -67,30 +67,93 @@ def assert_out(o_gpu, o_ref, tol: Tuple[str, float], label=""):
 
 
 # ---------------------------------------------------------------------------
+# Oracle work of the full-size tests, spread over CPU processes.  The oracle
+# is single-threaded numpy; heads are independent, so the reference of each
+# head is computed in its own process (spawned: the children import only
+# numpy and the oracle, never the GPU runtime).
+# ---------------------------------------------------------------------------
+
+def _one_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(1)
+    except ImportError:  # pragma: no cover
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def _states_job(args):
+    K, V, n = args
+    with _one_thread():
+        return orc.states_definition(K, V, n, block=4096)
+
+
+def _rows_job(args):
+    q_rows, K, V, rows, n = args
+    with _one_thread():
+        return orc.quadratic_rows(q_rows, K, V, rows, n)
+
+
+def _prefix_job(args):
+    b, h, N, dk, dv, n, part = args
+    k, v = wl.draw_prefix_kv(b, h, N, dk, dv, part)
+    with _one_thread():
+        return orc.states_definition(k, v, n, block=4096)
+
+
+def oracle_map(fn, jobs, workers: int = 16):
+    """[fn(job) for job in jobs], computed in up to ``workers`` spawned
+    processes (at most 16: the CPU share of one GPU)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    jobs = list(jobs)
+    if len(jobs) <= 1:
+        return [fn(j) for j in jobs]
+    from concurrent.futures.process import BrokenProcessPool
+    workers = max(1, min(workers, 16, len(jobs), os.cpu_count() or 1))
+    try:
+        with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+            return list(ex.map(fn, jobs))
+    except (BrokenProcessPool, OSError) as e:  # no child processes here: the same work in this process
+        print(f"[oracle] process pool unavailable ({e!r}); computing serially", flush=True)
+        return [fn(j) for j in jobs]
+
+
+def oracle_states(K, V, n: int, heads):
+    """Oracle states of the listed heads: K [BH, N, d], V [BH, N, e] (fp64)."""
+    return oracle_map(_states_job, [(K[h], V[h], n) for h in heads])
+
+
+def oracle_rows(Q, K, V, rows_of, n: int, heads):
+    """Oracle outputs at the sampled rows ``rows_of[h]`` of the listed heads."""
+    return oracle_map(_rows_job, [(Q[h, rows_of[h]], K[h], V[h], rows_of[h], n) for h in heads])
+
+
+# ---------------------------------------------------------------------------
 # Decode workload prefix: states of a seeded N-token prefix per (b, h),
 # built by the oracle in fp64 and rounded to fp32 (the GPU's state dtype).
 # ---------------------------------------------------------------------------
 
-def _prefix_one(args):
-    b, h, N, dk, dv, n = args
-    k, v = wl.draw_prefix_kv(b, h, N, dk, dv)
-    return orc.states_definition(k, v, n, block=4096)
+def decode_prefix_states(B: int, H: int, N: int, dk: int, dv: int, n: int, distinct: int = 16,
+                         tail: int = 256) -> np.ndarray:
+    """[B, H, W, dv+1] fp64 values of fp32-rounded prefix states, a different
+    one for every head.
 
-
-def decode_prefix_states(B: int, H: int, N: int, dk: int, dv: int, n: int, distinct: int = 16) -> np.ndarray:
-    """[B, H, W, dv+1] fp64 values of fp32-rounded prefix states.
-
-    The oracle builds the states of ``distinct`` seeded N-token prefixes
-    (heads (0, 0) .. (0, distinct-1)) and they are tiled over the B*H heads:
-    heads are independent, so every head is still a valid state of a seeded
-    N-token causal prefix, and the oracle checks all of them.
+    Head (b, h)'s prefix is N - ``tail`` tokens shared with every
+    ``distinct``-th head (the oracle builds ``distinct`` seeded prefixes,
+    PCG64([2, 0, i])) followed by ``tail`` tokens of its own
+    (PCG64([2, b, h, 1])).  States add over token sets, so the sum of the two
+    states is the state of that N-token causal prefix; building all B*H
+    prefixes in full would take the CPU oracle hours.
     """
-    from concurrent.futures import ThreadPoolExecutor
     distinct = min(distinct, B * H)
-    jobs = [(0, h, N, dk, dv, n) for h in range(distinct)]
-    with ThreadPoolExecutor(max_workers=min(8, distinct)) as ex:
-        res = list(ex.map(_prefix_one, jobs))
-    base = np.stack(res)
-    idx = np.arange(B * H) % distinct
-    S = base[idx].reshape(B, H, *res[0].shape)
-    return S.astype(np.float32).astype(np.float64)
+    base = np.stack(oracle_map(_prefix_job, [(0, i, N - tail, dk, dv, n, 0) for i in range(distinct)]))
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    Kt = np.empty((B * H, tail, dk))
+    Vt = np.empty((B * H, tail, dv))
+    for i, (b, h) in enumerate(heads):
+        Kt[i], Vt[i] = wl.draw_prefix_kv(b, h, tail, dk, dv, part=1)
+    chunks = np.array_split(np.arange(B * H), 16)
+    tails = np.concatenate(oracle_map(_states_job, [(Kt[c], Vt[c], n) for c in chunks]))
+    S = base[np.arange(B * H) % distinct] + tails
+    return S.reshape(B, H, *S.shape[1:]).astype(np.float32).astype(np.float64)

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle.taylor_oracle as orc
-from gpu_util import assert_out, assert_states, to_device
+from gpu_util import assert_out, assert_states, oracle_rows, oracle_states, to_device
 from taylor_recurrent_states_amd import ops
 from taylor_recurrent_states_amd import workloads as wl
 
@@ -108,20 +108,16 @@ def _full_workload(name, heads_checked=None, state_heads=None, w=None, vmap=None
     Vx = v.exact.reshape(BH, w.N, w.dv)
     Og = O.reshape(BH, w.N, w.dv)
     heads = list(range(BH)) if heads_checked is None else list(heads_checked)
+    rows_of = {h: _sample_rows(w.N, rng) for h in heads}
+    refs = oracle_rows(Qx, Kx, Vx, rows_of, w.n, heads)
     worst = 0.0
-    for h in heads:
-        rows = _sample_rows(w.N, rng)
-        ref = orc.quadratic_rows(Qx[h, rows], Kx[h], Vx[h], rows, w.n)
-        worst = max(worst, assert_out(Og[h, rows], ref, w.tol, f"{name} head {h}"))
+    for h, ref in zip(heads, refs):
+        worst = max(worst, assert_out(Og[h, rows_of[h]], ref, w.tol, f"{name} head {h}"))
     print(f"[{name}] sampled rows of {len(heads)} heads ok (worst {worst:.2e})", flush=True)
     W = orc.state_rows(w.dk, w.n)
     heads = heads if state_heads is None else list(state_heads)
     S_got = orc.planes_to_states(S, 1, BH, W, w.dv)[0][heads]
-    refs = []
-    for h in heads:
-        refs.append(orc.states_definition(Kx[h], Vx[h], w.n))
-        print(f"[{name}] oracle states of head {h}", flush=True)
-    S_ref = np.stack(refs)
+    S_ref = np.stack(oracle_states(Kx, Vx, w.n, heads))
     errs = assert_states(orc.states_to_planes(S_got[None]), S_ref[None], w.dk, w.n, w.tol, name)
     print(f"[{name}] states of {len(heads)} heads ok", flush=True)
     return q, k, v, S, S_ref, heads, errs
@@ -147,26 +143,28 @@ def test_prefill_workload_ragged_length(B, H, N):
     With B*H = 32 the plan has 8 spans of 1024 tokens and the last one ends
     27 tokens into its final chunk; with B*H = 16 it has 16 spans of 512 and
     the last ends 1 token into its final chunk.  Sampled rows of every head
-    (span boundaries and the ragged tail included), every state element of
-    8 heads."""
+    (span boundaries and the ragged tail included) and every state element
+    of every head."""
     w = dataclasses.replace(wl.WORKLOADS["prefill"], name=f"prefill B{B} H{H} N{N}", B=B, H=H, N=N, seed=11)
-    _full_workload(w.name, state_heads=range(0, B * H, B * H // 8), w=w)
+    _full_workload(w.name, w=w)
 
 
+@pytest.mark.timeout(600)
 def test_order5_workload_full_size():
-    """B=1, H=16, N=16384, dk=16, n=5, fp32: sampled rows of every head,
-    every state element of 6 heads."""
-    _full_workload("order5", state_heads=(0, 3, 6, 9, 12, 15))
+    """B=1, H=16, N=16384, dk=16, n=5, fp32: sampled rows and every state
+    element of every head."""
+    _full_workload("order5")
 
 
+@pytest.mark.timeout(600)
 def test_wide_workload_full_size_and_split_merge():
-    """B=1, H=16, N=65536, dk=64, n=3, bf16 (states and rows checked on 4 of
-    the 16 heads); then the states of 8 random chunk splits merged with
-    tt_state_merge equal the single pass on every head (GPU vs GPU) and the
-    oracle on the checked heads."""
+    """B=1, H=16, N=65536, dk=64, n=3, bf16: sampled rows and every state
+    element of every head; then the states of 8 random chunk splits merged
+    with tt_state_merge equal the single pass (GPU vs GPU) and the oracle, on
+    every head."""
     import torch
     w = wl.WORKLOADS["wide"]
-    q, k, v, S_single, S_ref, heads, _ = _full_workload("wide", heads_checked=(0, 5, 10, 15))
+    q, k, v, S_single, S_ref, heads, _ = _full_workload("wide")
     Qd, Kd, Vd = to_device(q), to_device(k), to_device(v)
     cuts = [0] + wl.draw_split_points(w.N, w.extra["splits"] - 1) + [w.N]
     merged = None

@@ -1673,14 +1673,18 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
         fetch_mu(0, mf[0]);
 #pragma unroll
         for (int j = 0; j < C::NKB; ++j) {
+          // lo plane of the normaliser rows, read before the next K-block's
+          // fragments (LDS reads complete in order: read after them, the
+          // normaliser MFMA would wait for all of them) and used after the
+          // value readout's MFMAs
+          const u32x4 bdl = load_bdn(j, 1);
+          // keep the scheduler from moving that read behind the prefetch
+          __builtin_amdgcn_sched_barrier(0);
           if (j + 1 < C::NKB) {
             load_phi(j + 1, af[(j + 1) & 1]);
             fetch_mu(j + 1, mf[(j + 1) & 1]);
             bdn[(j + 1) & 1] = load_bdn(j + 1, 0);
           }
-          // lo plane of the normaliser rows, read here and used after the
-          // value readout's MFMAs
-          const u32x4 bdl = load_bdn(j, 1);
           // S[rows 8lg..8lg+7 of K-block j][column ct*16 + li] as the A
           // operand (S^T), split into hi + lo bf16 (16 significant bits), so
           // the readout does not round the state to 8 bits: the values and

@@ -1,14 +1,17 @@
-// Prefill plans and launches.  The kernels live in tt_prefill_kernels.hpp;
-// this unit compiles the paths for chunks of 64 tokens (the warp-specialised
-// pipe kernel for bf16 inputs with at most 256 feature rows, the sweep kernel
-// for everything else), and dispatches other chunk lengths to the units that
-// compile the sweep kernel for them (tt_prefill_c16, _c32, _c128).
+// Prefill plans and launches.  The kernels live in tt_prefill_kernels.hpp and
+// tt_prefill_stream.hpp; this unit compiles the paths for chunks of 64 tokens
+// (the warp-specialised pipe kernel for bf16 inputs with at most 256 feature
+// rows, the streamed-state output pass for bf16 with n = 3 and dk = 32 or 64,
+// the sweep kernel for everything else), and dispatches other chunk lengths
+// to the units that compile the sweep kernel for them (tt_prefill_c16, _c32,
+// _c128).
 //
 // "Expanding Attention: A Taylor-Series Route to Linear-Time Transformers
 // with a Fixed Number of Recurrent States" (abstract): the states add across
 // token sets, so the chunking is free; the chunk length only moves work
 // between the intra-chunk quadratic block and the state readout and update.
 #include "tt_prefill_kernels.hpp"
+#include "tt_prefill_stream.hpp"
 
 namespace tt {
 
@@ -20,10 +23,21 @@ int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype
   if (dt == TT_BF16 && chunk < 32)
     return fail(TT_ERR_UNSUPPORTED, "chunk=%d with bf16 inputs (32, 64 or 128: token blocks of 32)", chunk);
   int wp = 0, ngroups = 0, nrg = 1, wg_per_cu = 2;
+  bool stream = false;
   hipError_t e = hipSuccess;
   if (chunk == 64) {
     e = with_dkn(dk, n, [&](auto DKc, auto Nc) {
       constexpr int DK = decltype(DKc)::value, NT = decltype(Nc)::value;
+      if constexpr (use_stream<DK, NT>()) {
+        if (dt == TT_BF16) {  // large bf16 feature sets: the streamed-state output pass
+          using S = Shape<uint16_t, DK, NT, 64>;
+          wp = S::Tot::WP;
+          ngroups = 1;
+          nrg = S::NRG;
+          stream = true;
+          return hipSuccess;
+        }
+      }
       if constexpr (use_pipe<DK, NT>()) {
         if (dt == TT_BF16) {
           wp = PCfg<DK, NT, MODE_OUTPUT>::WP;
@@ -43,6 +57,18 @@ int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype
   }
   if (e != hipSuccess) return fail(TT_ERR_UNSUPPORTED, "(dk=%d, n=%d, chunk=%d) not compiled", dk, n, chunk);
   const long long BH = (long long)B * H;
+  if (stream) {  // spans of kStL tokens: the output pass's causal block is one span
+    p->W = rows_for(dk, n);
+    p->Wpad = wp;
+    p->chunk = chunk;
+    p->span = kStL;
+    p->nspan = (N + kStL - 1) / kStL;
+    p->ngroups = ngroups;
+    p->nrg = nrg;
+    p->part_floats = 0;
+    p->ws_floats = (size_t)BH * p->nspan * (size_t)wp * (kDV + 1);
+    return TT_OK;
+  }
   const int nchunk = (N + chunk - 1) / chunk;
   // enough workgroups to fill the 256 CUs once
   const long long slots = 256LL * wg_per_cu;
@@ -72,6 +98,9 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype 
     return sweep_launch_chunk128(Q, K, V, dt, BH, N, dk, n, p, states_in, O, den_out, states, ws, s);
   return with_dkn(dk, n, [&](auto DKc, auto Nc) -> hipError_t {
     constexpr int DK = decltype(DKc)::value, NT = decltype(Nc)::value;
+    if constexpr (use_stream<DK, NT>()) {
+      if (dt == TT_BF16) return stream_launch<DK>(Q, K, V, BH, N, p, states_in, O, den_out, states, ws, s);
+    }
     if constexpr (use_pipe<DK, NT>()) {
       if (dt == TT_BF16) {
         using PT = PCfg<DK, NT, MODE_TOTALS>;

@@ -1,0 +1,476 @@
+// Prefill for large feature sets with bf16 inputs (n = 3, dk = 32 and 64:
+// 561 and 2,145 rows, octet order inside the library): the output pass reads
+// the state instead of carrying it.
+//
+// "Expanding Attention: A Taylor-Series Route to Linear-Time Transformers
+// with a Fixed Number of Recurrent States" (abstract): states of disjoint
+// token sets add, so the output of query i in span s splits into the readout
+// of the state of all spans before s and the quadratic form over the keys of
+// span s up to i (comment thread on the paper, item 46888355: (Q'K)V = Q'(KV)
+// for everything but the span's own causal block):
+//
+//   num/den(i) = phi(q_i).S_prefix(s) + sum_{span start <= j <= i} K_n(q_i.k_j) [v_j, 1]
+//
+// Three launches:
+//   1. span totals: the sweep kernel's totals pass over spans of kStL tokens
+//      (hi + lo bf16 mu, exact products, fp32 accumulation);
+//   2. stream_scan_kernel: exclusive prefix over spans, in place, rewritten
+//      as MFMA operand fragments (hi + lo bf16, 16 significant bits); the sum
+//      over all spans is the final state, written in feature order;
+//   3. stream_out_kernel: one workgroup per 128 queries.  Phase A is the
+//      in-span causal block, flash-style (S^T = K Q^T and O^T += V^T P^T on
+//      MFMA, P = K_n(S) in registers, hi + lo bf16 on the diagonal block);
+//      phase B is the readout GEMM phi(Q) S_prefix over all feature rows,
+//      with phi generated per 32-row block into LDS and the state fragments
+//      streamed from the workspace (L2); the two are added and divided.
+// No state update runs in the output pass and no row-group partial outputs
+// exist; the workspace holds one state per (head, span).
+#pragma once
+
+#include "tt_prefill_kernels.hpp"
+
+namespace tt {
+namespace {
+
+constexpr int kStL = 1024;  // tokens per span
+constexpr int kStQ = 128;   // queries per output workgroup
+constexpr int kStK = 64;    // keys per key block of the in-span causal block
+constexpr int kStT = kStL / kStQ;  // output workgroups per span
+
+template <int DK>
+struct StCfg {
+  static constexpr int W = oct_rows(DK);  // internal rows (octets)
+  static constexpr int NO = W / 8;
+  static constexpr int NKB = (W + 31) / 32;  // 32-row blocks of the readout
+  static constexpr int XD = DK / 32;         // 32-coordinate pieces of a q or k row
+  static constexpr int KS = DK + 8;          // K and Q tile row stride (bf16)
+  static constexpr int VS = kDV + 8;         // V tile row stride
+  static constexpr int PHS = 32 + 8;         // phi tile row stride: one 32-row block
+  static constexpr int B_K = kStK * KS * 2, B_V = kStK * VS * 2;
+  static constexpr int LDS_A = 2 * (B_K + B_V);             // phase A: K, V double-buffered
+  static constexpr int B_Q = kStQ * KS * 2, B_PHI = kStQ * PHS * 2;
+  static constexpr int LDS_B = B_Q + 2 * B_PHI;             // phase B: Q tile, phi double-buffered
+  static constexpr int OXS = kDV + 4;                       // exchange row stride (floats)
+  static constexpr int LDS_X = (kStQ * OXS + kStQ) * 4;     // exchange: numerators, normalisers
+  static constexpr int LDS = LDS_A > LDS_B ? (LDS_A > LDS_X ? LDS_A : LDS_X) : (LDS_B > LDS_X ? LDS_B : LDS_X);
+  static constexpr int KSEG = kStK * DK / 8, VSEG = kStK * kDV / 8, QSEG = kStQ * DK / 8;
+  static constexpr int NKS = KSEG / 256, NVS = VSEG / 256, NQS = QSEG / 256;
+  static_assert(KSEG % 256 == 0 && VSEG % 256 == 0 && QSEG % 256 == 0, "16-byte segments per thread");
+};
+
+// ---------------------------------------------------------------------------
+// Fragment layout of a prefix state in the workspace.  The span state of
+// (head, span) is [WP][64] fp32 values, then [WP] fp32 normalisers (the
+// totals pass writes it so).  The scan rewrites the 32 x 16 region of rows
+// 32j .. 32j+31 and columns 16ct .. 16ct+15 as the A operand of the readout
+// MFMA (S^T: lane (i, g) holds rows 32j + 8g .. 8g+7 of column 16ct + i),
+// hi plane then lo plane, 16 bytes per lane each: lane l's piece h sits in
+// row 32j + 16h + l/4 at columns 16ct + 4(l%4) .. +3.  Normaliser rows
+// 32j .. 32j+31 become eight hi bf16 then eight lo bf16 per group g of 8
+// rows (the same for every lane of the group).
+// ---------------------------------------------------------------------------
+__device__ inline size_t st_frag_off(int j, int ct, int l, int h) {
+  return (size_t)(32 * j + 16 * h + (l >> 2)) * kDV + 16 * ct + 4 * (l & 3);
+}
+__device__ inline size_t st_den_off(int WP, int j, int g, int h) {
+  return (size_t)WP * kDV + 32 * j + 8 * g + 4 * h;
+}
+
+// Exclusive scan over spans, in place, into fragments; final states (feature
+// order, plane layout), starting from `init` (plane layout, or null).  One
+// workgroup per (head, 32-row block), wave = column tile; wave 0's lanes 0-3
+// also take the block's normaliser rows.  Each lane reads the elements whose
+// fragment it writes, but at other addresses of the same region; every read
+// of a span completes before the wave's first write to it.
+template <int DK>
+__global__ __launch_bounds__(256) void stream_scan_kernel(float* ws, int nspan, int WP, int BH, int W,
+                                                          const float* init, float* states) {
+  using C = StCfg<DK>;
+  const int bh = blockIdx.x / C::NKB, j = blockIdx.x % C::NKB;
+  const int lane = threadIdx.x & 63, ct = threadIdx.x >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const bool den_lane = ct == 0 && lane < 4;
+  const size_t per = (size_t)WP * (kDV + 1);
+  float* base = ws + (size_t)bh * nspan * per;
+  const int col = 16 * ct + li;
+  int ra[8], rd[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    ra[u] = abi_row<DK>(32 * j + 8 * lg + u);
+    rd[u] = abi_row<DK>(32 * j + 8 * lane + u);
+  }
+  float run[8], rund[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    run[u] = (init != nullptr && ra[u] >= 0) ? init[((size_t)bh * W + ra[u]) * kDV + col] : 0.f;
+    rund[u] = (init != nullptr && den_lane && rd[u] >= 0) ? init[(size_t)BH * W * kDV + (size_t)bh * W + rd[u]] : 0.f;
+  }
+  constexpr int G = 4;  // spans whose loads are in flight together
+  for (int s0 = 0; s0 < nspan; s0 += G) {
+    float t[G][8], td[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (s0 + g < nspan) {
+        const float* p = base + (size_t)(s0 + g) * per;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[g][u] = p[(size_t)(32 * j + 8 * lg + u) * kDV + col];
+        if (den_lane) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) td[g][u] = p[(size_t)WP * kDV + 32 * j + 8 * lane + u];
+        }
+      }
+    }
+    // every read of these spans has returned before any fragment is written
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (s0 + g < nspan) {
+        float* p = base + (size_t)(s0 + g) * per;
+        u32x4 hi, lo;
+        split_bf16x8(f32x4{run[0], run[1], run[2], run[3]}, f32x4{run[4], run[5], run[6], run[7]}, hi, lo);
+        *reinterpret_cast<u32x4*>(p + st_frag_off(j, ct, lane, 0)) = hi;
+        *reinterpret_cast<u32x4*>(p + st_frag_off(j, ct, lane, 1)) = lo;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) run[u] += t[g][u];
+        if (den_lane) {
+          split_bf16x8(f32x4{rund[0], rund[1], rund[2], rund[3]}, f32x4{rund[4], rund[5], rund[6], rund[7]}, hi, lo);
+          *reinterpret_cast<u32x4*>(p + st_den_off(WP, j, lane, 0)) = hi;
+          *reinterpret_cast<u32x4*>(p + st_den_off(WP, j, lane, 1)) = lo;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) rund[u] += td[g][u];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    if (ra[u] >= 0) states[((size_t)bh * W + ra[u]) * kDV + col] = run[u];
+    if (den_lane && rd[u] >= 0) states[(size_t)BH * W * kDV + (size_t)bh * W + rd[u]] = rund[u];
+  }
+}
+
+// Output pass: one workgroup of 4 waves per 128 queries of a span.
+template <int DK, bool UNN>
+__global__ __launch_bounds__(256) void stream_out_kernel(const uint16_t* __restrict__ Qg,
+                                                         const uint16_t* __restrict__ Kg,
+                                                         const uint16_t* __restrict__ Vg, int BH, int N, int nspan,
+                                                         int WP, const float* __restrict__ ws, bool has_init,
+                                                         float* __restrict__ Og, float* __restrict__ Dg) {
+  using C = StCfg<DK>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+
+  // block -> (head, span, tile): the kStT tiles of a span share blockIdx % 8,
+  // so they are dealt to one XCD and its L2 serves the span's prefix state to
+  // all of them; within a span the tiles with the longest causal block come
+  // first
+  const int b = blockIdx.x;
+  const int sg = (b / (8 * kStT)) * 8 + (b & 7);
+  const int tile = kStT - 1 - (b >> 3) % kStT;
+  if (sg >= BH * nspan) return;
+  const int bh = sg / nspan, s = sg % nspan;
+  const int q0 = s * kStL + tile * kStQ;
+  if (q0 >= N) return;
+  const uint16_t* Qh = Qg + (size_t)bh * N * DK;
+  const uint16_t* Kh = Kg + (size_t)bh * N * DK;
+  const uint16_t* Vh = Vg + (size_t)bh * N * kDV;
+
+  // ---------------- phase A: the span's causal block ----------------
+  // wave w owns queries q0 + 32w .. +31 (two 16-query tiles) and all 64
+  // value columns as O^T tiles (columns x queries)
+  const int qw0 = q0 + 32 * w;
+  u32x4 qf[2][C::XD];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int h = 0; h < C::XD; ++h)
+      qf[qt][h] = *reinterpret_cast<const u32x4*>(Qh + (size_t)min(qw0 + 16 * qt + li, N - 1) * DK + 32 * h + 8 * lg);
+  f32x4 oA[2][4], dA[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    dA[qt] = zero4();
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) oA[qt][ct] = zero4();
+  }
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  {
+    auto sK = [&](int buf) { return lds + buf * (C::B_K + C::B_V); };
+    auto sV = [&](int buf) { return lds + buf * (C::B_K + C::B_V) + C::B_K; };
+    const int kbeg = s * kStL;
+    const int kend = min(q0 + kStQ, N);
+    const int nkb = (kend - kbeg + kStK - 1) / kStK;
+    u32x4 rk[C::NKS], rv[C::NVS];
+    auto issue = [&](int kb) {  // rows past N are clamped (such keys exceed every valid query: masked)
+      const int k0 = kbeg + kb * kStK;
+#pragma unroll
+      for (int i = 0; i < C::NKS; ++i) {
+        const int seg = tid + 256 * i, tok = seg / (DK / 8), part = seg % (DK / 8);
+        rk[i] = *reinterpret_cast<const u32x4*>(Kh + (size_t)min(k0 + tok, N - 1) * DK + part * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < C::NVS; ++i) {
+        const int seg = tid + 256 * i, tok = seg >> 3, part = seg & 7;
+        rv[i] = *reinterpret_cast<const u32x4*>(Vh + (size_t)min(k0 + tok, N - 1) * kDV + part * 8);
+      }
+    };
+    auto commit = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < C::NKS; ++i) {
+        const int seg = tid + 256 * i, tok = seg / (DK / 8), part = seg % (DK / 8);
+        *reinterpret_cast<u32x4*>(sK(buf) + (tok * C::KS + part * 8) * 2) = rk[i];
+      }
+#pragma unroll
+      for (int i = 0; i < C::NVS; ++i) {
+        const int seg = tid + 256 * i, tok = seg >> 3, part = seg & 7;
+        *reinterpret_cast<u32x4*>(sV(buf) + (tok * C::VS + part * 8) * 2) = rv[i];
+      }
+    };
+    // V^T fragment (A operand of O^T += V^T P^T), keys hb*32 .. +31, columns ct*16 .. +15
+    const int trow = 8 * lg + (li >> 2);
+    auto load_vt = [&](const unsigned char* V, int hb, int ct) {
+      const unsigned char* p = V + ((hb * 32 + trow) * C::VS + ct * 16 + 4 * (li & 3)) * 2;
+      const uint2 a = lds_tr16(p), c = lds_tr16(p + 4 * C::VS * 2);
+      return u32x4{a.x, a.y, c.x, c.y};
+    };
+    issue(0);
+    commit(0);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int buf = kb & 1;
+      if (kb + 1 < nkb) issue(kb + 1);
+      const int k0 = kbeg + kb * kStK;
+      if (k0 <= qw0 + 31) {  // some key of the block reaches a query of this wave (wave-uniform)
+        const bool diag = k0 + kStK - 1 > qw0;  // keys after the wave's first query: mask, hi + lo P
+        const unsigned char* K = sK(buf);
+        const unsigned char* V = sV(buf);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          // P^T fragments (B operand): lane (query i, g) holds keys hb*32 + 8g .. +7
+          u32x4 ph[2], pl[2];
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) {
+            float p[8];
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+              const int arow = hb * 32 + rho(tau, li);
+              f32x4 x = zero4();
+#pragma unroll
+              for (int h = 0; h < C::XD; ++h) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(K + (arow * C::KS + 32 * h + 8 * lg) * 2);
+                x = mfma_bf16(a, qf[qt][h], x);
+              }
+              const int query = qw0 + 16 * qt + li;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int key = k0 + hb * 32 + 8 * lg + 4 * tau + e;
+                const float v = taylor_poly<3>(x[e]);
+                p[4 * tau + e] = (diag && key > query) ? 0.f : v;
+              }
+            }
+            if (diag) {
+              uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+              split_bf16x2(p[0], p[1], h0, l0);
+              split_bf16x2(p[2], p[3], h1, l1);
+              split_bf16x2(p[4], p[5], h2, l2);
+              split_bf16x2(p[6], p[7], h3, l3);
+              ph[qt] = u32x4{h0, h1, h2, h3};
+              pl[qt] = u32x4{l0, l1, l2, l3};
+            } else {
+              ph[qt] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                             pack_bf16x2(p[6], p[7])};
+              pl[qt] = u32x4{0u, 0u, 0u, 0u};
+            }
+            // normaliser: every row of ones^T P^T is the column sum, the same P as the numerator
+            dA[qt] = mfma_bf16(ones, ph[qt], dA[qt]);
+            if (diag) dA[qt] = mfma_bf16(ones, pl[qt], dA[qt]);
+          }
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const u32x4 a = load_vt(V, hb, ct);
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+              oA[qt][ct] = mfma_bf16(a, ph[qt], oA[qt][ct]);
+              if (diag) oA[qt][ct] = mfma_bf16(a, pl[qt], oA[qt][ct]);
+            }
+          }
+        }
+      }
+      if (kb + 1 < nkb) {
+        commit(buf ^ 1);
+        __syncthreads();
+      }
+    }
+  }
+  __syncthreads();  // phase A's tiles are free
+
+  // ---------------- phase B: readout of the prefix state ----------------
+  // wave w owns value columns 16w .. 16w+15 of all 128 queries (eight O^T
+  // tiles) and the normalisers of query tiles 2w, 2w+1
+  f32x4 nB[8], dB[2];
+#pragma unroll
+  for (int qt = 0; qt < 8; ++qt) nB[qt] = zero4();
+  dB[0] = dB[1] = zero4();
+  if (s > 0 || has_init) {
+    uint16_t* sQ = reinterpret_cast<uint16_t*>(lds);
+    auto sPhi = [&](int buf) { return reinterpret_cast<uint16_t*>(lds + C::B_Q + buf * C::B_PHI); };
+#pragma unroll
+    for (int i = 0; i < C::NQS; ++i) {
+      const int seg = tid + 256 * i, tok = seg / (DK / 8), part = seg % (DK / 8);
+      *reinterpret_cast<u32x4*>(sQ + tok * C::KS + part * 8) =
+          *reinterpret_cast<const u32x4*>(Qh + (size_t)min(q0 + tok, N - 1) * DK + part * 8);
+    }
+    // phi of 32-row block j: wave w builds octet 4j + w for the 128 tokens
+    // (lane = token, two passes); the octet's descriptor is wave-uniform
+    const uint32_t* tab = OctOf<DK>::get().d;
+    auto gen = [&](int j, uint16_t* P) {
+      const int o = 4 * j + w;
+      const uint32_t d = o < C::NO ? tab[o] : 0xFFu;
+      const int m = d & 0xFF, a = (d >> 8) & 0xFF, b0 = (int)(d >> 16);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int tok = 64 * h + lane;
+        const uint16_t* x = sQ + tok * C::KS;
+        float ph[8];
+        if (m == 2) {
+          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+          const uint32_t xa = x[a];
+          const bf16x2_t lo2 = __builtin_bit_cast(bf16x2_t, xa);        // {x_a, 0}
+          const bf16x2_t hi2 = __builtin_bit_cast(bf16x2_t, xa << 16);  // {0, x_a}
+          const u32x4 xb = *reinterpret_cast<const u32x4*>(x + b0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t wv = xb[e];
+            const bf16x2_t v = __builtin_bit_cast(bf16x2_t, wv);
+            ph[2 * e] = __builtin_amdgcn_fdot2_f32_bf16(lo2, v, 0.f, false);      // x_a x_b exactly
+            ph[2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(hi2, v, 0.f, false);
+          }
+          if (b0 <= a) {  // the octet holding (a, a): rows b < a are zero, weight 1/2 on b == a
+#pragma unroll
+            for (int u = 0; u < 8; ++u) ph[u] = b0 + u > a ? ph[u] : (b0 + u == a ? 0.5f * ph[u] : 0.f);
+          }
+        } else if (m == 1) {
+          const u32x4 xb = *reinterpret_cast<const u32x4*>(x + b0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ph[2 * e] = __uint_as_float(xb[e] << 16);
+            ph[2 * e + 1] = __uint_as_float(xb[e] & 0xFFFF0000u);
+          }
+        } else {  // order 0 (row 0, weight 1) or past the last octet
+#pragma unroll
+          for (int u = 0; u < 8; ++u) ph[u] = (m == 0 && u == 0) ? 1.f : 0.f;
+        }
+        *reinterpret_cast<u32x4*>(P + tok * C::PHS + 8 * w) =
+            u32x4{pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3]), pack_bf16x2(ph[4], ph[5]),
+                  pack_bf16x2(ph[6], ph[7])};
+      }
+    };
+    const float* S = ws + ((size_t)bh * nspan + s) * (size_t)WP * (kDV + 1);
+    auto load_s = [&](int j, u32x4& hi, u32x4& lo, u32x4& dhi, u32x4& dlo) {
+      hi = *reinterpret_cast<const u32x4*>(S + st_frag_off(j, w, lane, 0));
+      lo = *reinterpret_cast<const u32x4*>(S + st_frag_off(j, w, lane, 1));
+      dhi = *reinterpret_cast<const u32x4*>(S + st_den_off(WP, j, lg, 0));
+      dlo = *reinterpret_cast<const u32x4*>(S + st_den_off(WP, j, lg, 1));
+    };
+    u32x4 shi, slo, dhi, dlo;
+    load_s(0, shi, slo, dhi, dlo);
+    __syncthreads();  // Q tile staged
+    gen(0, sPhi(0));
+    __syncthreads();
+    for (int j = 0; j < C::NKB; ++j) {
+      const uint16_t* P = sPhi(j & 1);
+      if (j + 1 < C::NKB) gen(j + 1, sPhi((j + 1) & 1));
+      u32x4 nhi, nlo, ndhi, ndlo;
+      if (j + 1 < C::NKB) load_s(j + 1, nhi, nlo, ndhi, ndlo);
+      u32x4 af[8];
+#pragma unroll
+      for (int qt = 0; qt < 8; ++qt)
+        af[qt] = *reinterpret_cast<const u32x4*>(P + (qt * 16 + li) * C::PHS + 8 * lg);
+#pragma unroll
+      for (int qt = 0; qt < 8; ++qt) nB[qt] = mfma_bf16(shi, af[qt], nB[qt]);
+#pragma unroll
+      for (int qt = 0; qt < 8; ++qt) nB[qt] = mfma_bf16(slo, af[qt], nB[qt]);
+      // normalisers of query tiles 2w, 2w+1 (w is wave-uniform: a scalar branch)
+      switch (w) {
+        case 0: dB[0] = mfma_bf16(dhi, af[0], dB[0]); dB[0] = mfma_bf16(dlo, af[0], dB[0]);
+                dB[1] = mfma_bf16(dhi, af[1], dB[1]); dB[1] = mfma_bf16(dlo, af[1], dB[1]); break;
+        case 1: dB[0] = mfma_bf16(dhi, af[2], dB[0]); dB[0] = mfma_bf16(dlo, af[2], dB[0]);
+                dB[1] = mfma_bf16(dhi, af[3], dB[1]); dB[1] = mfma_bf16(dlo, af[3], dB[1]); break;
+        case 2: dB[0] = mfma_bf16(dhi, af[4], dB[0]); dB[0] = mfma_bf16(dlo, af[4], dB[0]);
+                dB[1] = mfma_bf16(dhi, af[5], dB[1]); dB[1] = mfma_bf16(dlo, af[5], dB[1]); break;
+        default: dB[0] = mfma_bf16(dhi, af[6], dB[0]); dB[0] = mfma_bf16(dlo, af[6], dB[0]);
+                 dB[1] = mfma_bf16(dhi, af[7], dB[1]); dB[1] = mfma_bf16(dlo, af[7], dB[1]); break;
+      }
+      if (j + 1 < C::NKB) {
+        shi = nhi; slo = nlo; dhi = ndhi; dlo = ndlo;
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---------------- combine: phase B's tiles to the row split of phase A ----------------
+  float* sX = reinterpret_cast<float*>(lds);
+  float* sXd = sX + kStQ * C::OXS;
+#pragma unroll
+  for (int qt = 0; qt < 8; ++qt)
+    *reinterpret_cast<f32x4*>(sX + (qt * 16 + li) * C::OXS + 16 * w + 4 * lg) = nB[qt];
+  if (lg == 0) {
+    sXd[(2 * w) * 16 + li] = dB[0].x;
+    sXd[(2 * w + 1) * 16 + li] = dB[1].x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int ql = 32 * w + 16 * qt + li;
+    const int q = q0 + ql;
+    if (q >= N) continue;
+    const float den = dA[qt].x + sXd[ql];
+    const float r = UNN ? 1.0f : 1.0f / den;
+    float* orow = Og + ((size_t)bh * N + q) * kDV;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const f32x4 num = oA[qt][ct] + *reinterpret_cast<const f32x4*>(sX + ql * C::OXS + 16 * ct + 4 * lg);
+      store_nt(orow + 16 * ct + 4 * lg, num * r);
+    }
+    if (UNN && lg == 0) Dg[(size_t)bh * N + q] = den;
+  }
+}
+
+// The shapes of this path: bf16 inputs with n = 3 and dk = 32 or 64, in
+// 64-token chunks (the totals pass).
+template <int DK, int NT>
+constexpr bool use_stream() { return NT == 3 && (DK == 32 || DK == 64); }
+
+template <int DK>
+hipError_t stream_launch(const void* Q, const void* K, const void* V, int BH, int N, const PrefillPlan& p,
+                         const float* states_in, float* O, float* den_out, float* states, float* ws, hipStream_t s) {
+  using S = Shape<uint16_t, DK, 3, 64>;
+  using T = typename S::Tot;
+  static_assert(StCfg<DK>::NKB * 32 <= T::WP, "the readout's row blocks lie inside the span state");
+  static_assert(S::NVT == 4, "one column group: the totals pass covers all 64 value columns");
+  const unsigned nblk = (unsigned)((size_t)BH * p.nspan * p.ngroups * S::NRG);
+  hipLaunchKernelGGL((sweep_kernel<T>), dim3(nblk), dim3(T::NTHR), 0, s, (const uint16_t*)Q, (const uint16_t*)K,
+                     (const uint16_t*)V, N, p.span, p.nspan, ws, (float*)nullptr, O, den_out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((stream_scan_kernel<DK>), dim3((unsigned)(BH * StCfg<DK>::NKB)), dim3(256), 0, s, ws, p.nspan,
+                     (int)T::WP, BH, p.W, states_in, states);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned sgs = (unsigned)((BH * p.nspan + 7) / 8 * 8);
+  const dim3 grid(sgs * kStT);
+  if (den_out)
+    hipLaunchKernelGGL((stream_out_kernel<DK, true>), grid, dim3(256), 0, s, (const uint16_t*)Q, (const uint16_t*)K,
+                       (const uint16_t*)V, BH, N, p.nspan, (int)T::WP, (const float*)ws, states_in != nullptr, O,
+                       den_out);
+  else
+    hipLaunchKernelGGL((stream_out_kernel<DK, false>), grid, dim3(256), 0, s, (const uint16_t*)Q, (const uint16_t*)K,
+                       (const uint16_t*)V, BH, N, p.nspan, (int)T::WP, (const float*)ws, states_in != nullptr, O,
+                       den_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace tt

@@ -107,7 +107,7 @@ def bench_prefill(args, torch, ops, wl):
     alg_bytes = head_tokens * (2 * w.dk * 2 + w.dv * 2 + w.dv * 4) + w.B * w.H * ops.tt_state_floats(w.dk, w.dv, w.n) * 4
     achieved = alg_bytes / t_step / 1e9
     alg_flops = 4.0 * ops.tt_state_rows(w.dk, w.n) * (w.dv + 1) * head_tokens
-    src = _source_hash("tt_prefill.hip", "tt_prefill_kernels.hpp", "tt_device.hpp")
+    src = _source_hash("tt_prefill.hip", "tt_prefill_kernels.hpp", "tt_prefill_stream.hpp", "tt_device.hpp")
     # the same workload continued from carried-in states (read once more)
     S_in = S.clone()
 
@@ -215,7 +215,7 @@ def bench_prefill_other(name, args, torch, ops, wl):
 
     _prewarm(step_n, torch, 0.05)
     t_n = _time_events(step_n, steps, torch) / steps
-    src = _source_hash("tt_prefill.hip", "tt_prefill_kernels.hpp", "tt_device.hpp")
+    src = _source_hash("tt_prefill.hip", "tt_prefill_kernels.hpp", "tt_prefill_stream.hpp", "tt_device.hpp")
     # algorithmic bytes: q, k, v in, O (fp32) out, final states out
     alg_bytes = w.B * w.H * w.N * (2 * w.dk + w.dv) * (4 if w.dtype == "f32" else 2) + w.B * w.H * w.N * w.dv * 4 \
         + w.B * w.H * ops.tt_state_floats(w.dk, w.dv, w.n) * 4

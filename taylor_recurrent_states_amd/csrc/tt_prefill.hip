@@ -30,10 +30,9 @@ int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype
       constexpr int DK = decltype(DKc)::value, NT = decltype(Nc)::value;
       if constexpr (use_stream<DK, NT>()) {
         if (dt == TT_BF16) {  // large bf16 feature sets: the streamed-state output pass
-          using S = Shape<uint16_t, DK, NT, 64>;
-          wp = S::Tot::WP;
+          wp = StTot<DK>::WP;
           ngroups = 1;
-          nrg = S::NRG;
+          nrg = StTot<DK>::NRB;
           stream = true;
           return hipSuccess;
         }

@@ -12,8 +12,8 @@
 //   num/den(i) = phi(q_i).S_prefix(s) + sum_{span start <= j <= i} K_n(q_i.k_j) [v_j, 1]
 //
 // Three launches:
-//   1. span totals: the sweep kernel's totals pass over spans of kStL tokens
-//      (hi + lo bf16 mu, exact products, fp32 accumulation);
+//   1. stream_totals_kernel: the state of each span of kStL tokens (hi + lo
+//      bf16 mu, exact products, fp32 accumulation);
 //   2. stream_scan_kernel: exclusive prefix over spans, in place, rewritten
 //      as MFMA operand fragments (hi + lo bf16, 16 significant bits); the sum
 //      over all spans is the final state, written in feature order;
@@ -36,6 +36,16 @@ constexpr int kStL = 1024;  // tokens per span
 constexpr int kStQ = 128;   // queries per output workgroup
 constexpr int kStK = 64;    // keys per key block of the in-span causal block
 constexpr int kStT = kStL / kStQ;  // output workgroups per span
+
+// x_a * x[b], x_a * x[b+1] for a packed bf16 pair {x[b], x[b+1]}: a bf16
+// dot product with one zero term is the exact product (16 significant bits)
+// in fp32.  The 3-operand form with an inline zero accumulator; the
+// compiler's choice for the builtin is the 2-operand form, which needs a
+// zeroed destination register per product.
+__device__ inline void prod_pair(uint32_t xa_lo, uint32_t xa_hi, uint32_t pair, float& p0, float& p1) {
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(p0) : "v"(xa_lo), "v"(pair));
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(p1) : "v"(xa_hi), "v"(pair));
+}
 
 template <int DK>
 struct StCfg {
@@ -74,6 +84,217 @@ __device__ inline size_t st_frag_off(int j, int ct, int l, int h) {
 }
 __device__ inline size_t st_den_off(int WP, int j, int g, int h) {
   return (size_t)WP * kDV + 32 * j + 8 * g + 4 * h;
+}
+
+// Span totals: one workgroup of 4 waves per (head, span, 128 feature rows);
+// wave w owns the 32-row block j = 4*rb + w for all 64 value columns (eight
+// accumulator tiles) and its normaliser.  Per 64-token block the waves stage
+// K and V in LDS; each wave then builds the mu rows of its own block (lane =
+// token, one octet at a time, hi + lo bf16: a product of two bf16 values is
+// exact in fp32 and splits exactly into two bf16) into a wave-private tile
+// and contracts them with V by MFMA, so no workgroup barrier separates the
+// features from their use.  The mu tile is token-major with the chunk
+// swizzle and row shift of the pipe kernel (conflict-free transposing reads).
+template <int DK>
+struct StTot {
+  static constexpr int NW = 4;
+  static constexpr int KS = DK + 8;                    // K tile row stride (bf16)
+  static constexpr int VS = kDV + 8;                   // V tile row stride
+  static constexpr int MUS = 32, MUSH = 4;             // mu rows: 32 elements, +4 every 8 tokens
+  static constexpr int MUPL = kStK * MUS + 32;         // elements per mu plane (with the shift's slack)
+  static constexpr int B_K = kStK * KS * 2, B_V = kStK * VS * 2;
+  static constexpr int B_MU = 2 * MUPL * 2;            // hi and lo planes of one wave
+  static constexpr int LDS = 2 * (B_K + B_V) + NW * B_MU;
+  static constexpr int KSEG = kStK * DK / 8, VSEG = kStK * kDV / 8;
+  static constexpr int NKS = (KSEG + NW * 64 - 1) / (NW * 64), NVS = VSEG / (NW * 64);
+  static constexpr int NRB = (StCfg<DK>::NKB + NW - 1) / NW;  // 256-row groups
+  static constexpr int WP = NRB * NW * 32;                     // padded rows of a span state
+  static_assert(VSEG % (NW * 64) == 0, "V segments per thread");
+};
+
+template <int DK>
+__global__ __launch_bounds__(256, 2) void stream_totals_kernel(const uint16_t* __restrict__ Kg,
+                                                            const uint16_t* __restrict__ Vg, int BH, int N,
+                                                            int nspan, float* __restrict__ ws) {
+  using C = StTot<DK>;
+  constexpr int NKB = StCfg<DK>::NKB, NO = StCfg<DK>::NO;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  // block -> (head, span, row group): the row groups of a span share
+  // blockIdx % 8 (one XCD, whose L2 then serves the span's K and V to all)
+  const int b = blockIdx.x;
+  const int rb = (b >> 3) % C::NRB;
+  const int hs = (b / (8 * C::NRB)) * 8 + (b & 7);
+  if (hs >= BH * nspan) return;
+  const int bh = hs / nspan, s = hs % nspan;
+  const int t_begin = s * kStL, t_end = min(N, t_begin + kStL);
+  const int ntb = (t_end - t_begin + kStK - 1) / kStK;
+  const int j = rb * C::NW + w;       // this wave's 32-row block
+  const bool active = j < NKB;        // wave-uniform; blocks past the last octet hold zero rows
+  const uint16_t* Kh = Kg + (size_t)bh * N * DK;
+  const uint16_t* Vh = Vg + (size_t)bh * N * kDV;
+  auto sK = [&](int buf) { return lds + buf * (C::B_K + C::B_V); };
+  auto sV = [&](int buf) { return lds + buf * (C::B_K + C::B_V) + C::B_K; };
+  uint16_t* sMu = reinterpret_cast<uint16_t*>(lds + 2 * (C::B_K + C::B_V) + w * C::B_MU);
+
+  u32x4 rk[C::NKS], rv[C::NVS];
+  auto issue = [&](int tb) {  // rows past the span end are clamped to its last token (their mu is zero)
+    const int k0 = t_begin + tb * kStK;
+#pragma unroll
+    for (int i = 0; i < C::NKS; ++i) {
+      const int seg = tid + C::NW * 64 * i;
+      if (seg < C::KSEG) {
+        const int tok = seg / (DK / 8), part = seg % (DK / 8);
+        rk[i] = *reinterpret_cast<const u32x4*>(Kh + (size_t)min(k0 + tok, t_end - 1) * DK + part * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::NVS; ++i) {
+      const int seg = tid + C::NW * 64 * i, tok = seg >> 3, part = seg & 7;
+      rv[i] = *reinterpret_cast<const u32x4*>(Vh + (size_t)min(k0 + tok, t_end - 1) * kDV + part * 8);
+    }
+  };
+  // K rows of tokens past the span end are stored as zeros, so their mu rows
+  // of order 1 and 2 vanish; the order-0 row is masked where it is built
+  auto commit = [&](int buf, int tb) {
+    const int k0 = t_begin + tb * kStK;
+#pragma unroll
+    for (int i = 0; i < C::NKS; ++i) {
+      const int seg = tid + C::NW * 64 * i;
+      if (seg < C::KSEG) {
+        const int tok = seg / (DK / 8), part = seg % (DK / 8);
+        *reinterpret_cast<u32x4*>(sK(buf) + (tok * C::KS + part * 8) * 2) =
+            k0 + tok < t_end ? rk[i] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::NVS; ++i) {
+      const int seg = tid + C::NW * 64 * i, tok = seg >> 3, part = seg & 7;
+      *reinterpret_cast<u32x4*>(sV(buf) + (tok * C::VS + part * 8) * 2) = rv[i];
+    }
+  };
+
+  f32x4 st[2][4], dn[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    dn[t] = zero4();
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) st[t][ct] = zero4();
+  }
+  const u32x4 ones_bf = (li == 0) ? u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}
+                                  : u32x4{0u, 0u, 0u, 0u};
+  const uint32_t* tab = OctOf<DK>::get().d;
+  // this lane's token row in the mu tile; chunk c of it sits at c ^ mswz
+  const int mswz = (lane >> 2) & 3;
+  uint16_t* muRow = sMu + lane * C::MUS + C::MUSH * (lane >> 3);
+  // transposing-read addresses (see the pipe kernel): token 8*lg + li/4 (+4)
+  // of a 32-token half, chunks (li & 3) ^ z
+  const int trow = 8 * lg + (li >> 2);
+  const int cz0 = (li & 3) ^ ((2 * lg) & 3);
+  const int cz1 = (li & 3) ^ ((2 * lg + 1) & 3);
+  auto load_mu = [&](int pl, int tau, int th) {
+    const unsigned char* r0 = reinterpret_cast<const unsigned char*>(sMu) +
+                              (pl * C::MUPL + (th * 32 + trow) * C::MUS + C::MUSH * (4 * th + lg) + 4 * tau) * 2;
+    const uint2 a = lds_tr16(r0 + cz0 * 16);
+    const uint2 c = lds_tr16(r0 + 4 * C::MUS * 2 + cz1 * 16);
+    return u32x4{a.x, a.y, c.x, c.y};
+  };
+  auto load_v = [&](const unsigned char* V, int th, int ct) {
+    const unsigned char* p = V + ((th * 32 + trow) * C::VS + ct * 16 + 4 * (li & 3)) * 2;
+    const uint2 a = lds_tr16(p), c = lds_tr16(p + 4 * C::VS * 2);
+    return u32x4{a.x, a.y, c.x, c.y};
+  };
+
+  issue(0);
+  commit(0, 0);
+  __syncthreads();
+  for (int tb = 0; tb < ntb; ++tb) {
+    const int buf = tb & 1;
+    if (tb + 1 < ntb) issue(tb + 1);
+    if (active) {
+      const uint16_t* x = reinterpret_cast<const uint16_t*>(sK(buf)) + lane * C::KS;
+      const bool kvalid = t_begin + tb * kStK + lane < t_end;  // tokens past the span end: zero rows
+      // mu rows of octets 4j .. 4j+3 for this lane's token, hi and lo planes
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int o = 4 * j + c;
+        const uint32_t d = o < NO ? tab[o] : 0xFFu;  // wave-uniform
+        const int m = d & 0xFF, a = (d >> 8) & 0xFF, b0 = (int)(d >> 16);
+        float mu[8];
+        if (m == 2) {
+          const uint32_t xa = x[a];  // {x_a, 0}; shifted: {0, x_a}
+          const u32x4 xb = *reinterpret_cast<const u32x4*>(x + b0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) prod_pair(xa, xa << 16, xb[e], mu[2 * e], mu[2 * e + 1]);
+          if (b0 <= a) {  // the octet holding (a, a): rows b < a are zero
+#pragma unroll
+            for (int u = 0; u < 8; ++u) mu[u] = b0 + u >= a ? mu[u] : 0.f;
+          }
+        } else if (m == 1) {
+          const u32x4 xb = *reinterpret_cast<const u32x4*>(x + b0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            mu[2 * e] = __uint_as_float(xb[e] << 16);
+            mu[2 * e + 1] = __uint_as_float(xb[e] & 0xFFFF0000u);
+          }
+        } else {  // order 0 (row 0: the token count) or past the last octet
+#pragma unroll
+          for (int u = 0; u < 8; ++u) mu[u] = (m == 0 && u == 0 && kvalid) ? 1.f : 0.f;
+        }
+        uint32_t hb[8], lb[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          hb[u] = __float_as_uint(mu[u]) & 0xFFFF0000u;
+          lb[u] = __float_as_uint(mu[u] - __uint_as_float(hb[u]));
+        }
+        uint16_t* dst = muRow + 8 * (c ^ mswz);
+        reinterpret_cast<uint2*>(dst)[0] = uint2{__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
+                                                 __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)};
+        reinterpret_cast<uint2*>(dst)[1] = uint2{__builtin_amdgcn_perm(hb[5], hb[4], 0x07060302u),
+                                                 __builtin_amdgcn_perm(hb[7], hb[6], 0x07060302u)};
+        reinterpret_cast<uint2*>(dst + C::MUPL)[0] = uint2{__builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u),
+                                                           __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u)};
+        reinterpret_cast<uint2*>(dst + C::MUPL)[1] = uint2{__builtin_amdgcn_perm(lb[5], lb[4], 0x07060302u),
+                                                           __builtin_amdgcn_perm(lb[7], lb[6], 0x07060302u)};
+      }
+      // the tile is wave-private: this wave's LDS writes done, then its reads
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const unsigned char* V = sV(buf);
+#pragma unroll
+      for (int th = 0; th < 2; ++th) {
+        u32x4 vf[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) vf[ct] = load_v(V, th, ct);
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+          for (int pl = 0; pl < 2; ++pl) {
+            const u32x4 af = load_mu(pl, tau, th);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) st[tau][ct] = mfma_bf16(af, vf[ct], st[tau][ct]);
+            dn[tau] = mfma_bf16(af, ones_bf, dn[tau]);
+          }
+      }
+    }
+    if (tb + 1 < ntb) {
+      commit(buf ^ 1, tb + 1);
+      __syncthreads();
+    }
+  }
+  if (!active) return;
+  float* S = ws + (size_t)hs * C::WP * (kDV + 1);
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 32 * j + 8 * lg + 4 * tau + e;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) S[(size_t)row * kDV + 16 * ct + li] = st[tau][ct][e];
+      if (li == 0) S[(size_t)C::WP * kDV + row] = dn[tau][e];
+    }
 }
 
 // Exclusive scan over spans, in place, into fragments; final states (feature
@@ -151,7 +372,7 @@ __global__ __launch_bounds__(256) void stream_scan_kernel(float* ws, int nspan, 
 
 // Output pass: one workgroup of 4 waves per 128 queries of a span.
 template <int DK, bool UNN>
-__global__ __launch_bounds__(256) void stream_out_kernel(const uint16_t* __restrict__ Qg,
+__global__ __launch_bounds__(256, 3) void stream_out_kernel(const uint16_t* __restrict__ Qg,
                                                          const uint16_t* __restrict__ Kg,
                                                          const uint16_t* __restrict__ Vg, int BH, int N, int nspan,
                                                          int WP, const float* __restrict__ ws, bool has_init,
@@ -335,18 +556,10 @@ __global__ __launch_bounds__(256) void stream_out_kernel(const uint16_t* __restr
         const uint16_t* x = sQ + tok * C::KS;
         float ph[8];
         if (m == 2) {
-          typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-          const uint32_t xa = x[a];
-          const bf16x2_t lo2 = __builtin_bit_cast(bf16x2_t, xa);        // {x_a, 0}
-          const bf16x2_t hi2 = __builtin_bit_cast(bf16x2_t, xa << 16);  // {0, x_a}
+          const uint32_t xa = x[a];  // {x_a, 0}; shifted: {0, x_a}
           const u32x4 xb = *reinterpret_cast<const u32x4*>(x + b0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t wv = xb[e];
-            const bf16x2_t v = __builtin_bit_cast(bf16x2_t, wv);
-            ph[2 * e] = __builtin_amdgcn_fdot2_f32_bf16(lo2, v, 0.f, false);      // x_a x_b exactly
-            ph[2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(hi2, v, 0.f, false);
-          }
+          for (int e = 0; e < 4; ++e) prod_pair(xa, xa << 16, xb[e], ph[2 * e], ph[2 * e + 1]);
           if (b0 <= a) {  // the octet holding (a, a): rows b < a are zero, weight 1/2 on b == a
 #pragma unroll
             for (int u = 0; u < 8; ++u) ph[u] = b0 + u > a ? ph[u] : (b0 + u == a ? 0.5f * ph[u] : 0.f);
@@ -446,21 +659,18 @@ constexpr bool use_stream() { return NT == 3 && (DK == 32 || DK == 64); }
 template <int DK>
 hipError_t stream_launch(const void* Q, const void* K, const void* V, int BH, int N, const PrefillPlan& p,
                          const float* states_in, float* O, float* den_out, float* states, float* ws, hipStream_t s) {
-  using S = Shape<uint16_t, DK, 3, 64>;
-  using T = typename S::Tot;
+  using T = StTot<DK>;
   static_assert(StCfg<DK>::NKB * 32 <= T::WP, "the readout's row blocks lie inside the span state");
-  static_assert(S::NVT == 4, "one column group: the totals pass covers all 64 value columns");
-  const unsigned nblk = (unsigned)((size_t)BH * p.nspan * p.ngroups * S::NRG);
-  hipLaunchKernelGGL((sweep_kernel<T>), dim3(nblk), dim3(T::NTHR), 0, s, (const uint16_t*)Q, (const uint16_t*)K,
-                     (const uint16_t*)V, N, p.span, p.nspan, ws, (float*)nullptr, O, den_out);
+  const unsigned hsg = (unsigned)((BH * p.nspan + 7) / 8 * 8);  // (head, span) pairs, padded to the 8 XCDs
+  hipLaunchKernelGGL((stream_totals_kernel<DK>), dim3(hsg * T::NRB), dim3(T::NW * 64), 0, s, (const uint16_t*)K,
+                     (const uint16_t*)V, BH, N, p.nspan, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((stream_scan_kernel<DK>), dim3((unsigned)(BH * StCfg<DK>::NKB)), dim3(256), 0, s, ws, p.nspan,
                      (int)T::WP, BH, p.W, states_in, states);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned sgs = (unsigned)((BH * p.nspan + 7) / 8 * 8);
-  const dim3 grid(sgs * kStT);
+  const dim3 grid(hsg * kStT);
   if (den_out)
     hipLaunchKernelGGL((stream_out_kernel<DK, true>), grid, dim3(256), 0, s, (const uint16_t*)Q, (const uint16_t*)K,
                        (const uint16_t*)V, BH, N, p.nspan, (int)T::WP, (const float*)ws, states_in != nullptr, O,

@@ -1,8 +1,9 @@
 // Prefill plans and launches.  The kernels live in tt_prefill_kernels.hpp and
 // tt_prefill_stream.hpp; this unit compiles the paths for chunks of 64 tokens
 // (the warp-specialised pipe kernel for bf16 inputs with at most 256 feature
-// rows, the streamed-state output pass for bf16 with n = 3 and dk = 32 or 64,
-// the sweep kernel for everything else), and dispatches other chunk lengths
+// rows, the streamed-state output pass for bf16 with n = 3 and dk = 32 or 64
+// and for fp32 with more than 256 rows, the sweep kernel for everything
+// else), and dispatches other chunk lengths
 // to the units that compile the sweep kernel for them (tt_prefill_c16, _c32,
 // _c128).
 //
@@ -33,6 +34,16 @@ int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype
           wp = StTot<DK>::WP;
           ngroups = 1;
           nrg = StTot<DK>::NRB;
+          stream = true;
+          return hipSuccess;
+        }
+      }
+      if constexpr (use_stream_f32<DK, NT>()) {
+        if (dt == TT_F32) {  // large fp32 feature sets: the same, on fp32 MFMA
+          using S = Shape<float, DK, NT, 64>;
+          wp = S::Tot::WP;
+          ngroups = kDV / S::Tot::GC;
+          nrg = S::NRG;
           stream = true;
           return hipSuccess;
         }
@@ -99,6 +110,9 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype 
     constexpr int DK = decltype(DKc)::value, NT = decltype(Nc)::value;
     if constexpr (use_stream<DK, NT>()) {
       if (dt == TT_BF16) return stream_launch<DK>(Q, K, V, BH, N, p, states_in, O, den_out, states, ws, s);
+    }
+    if constexpr (use_stream_f32<DK, NT>()) {
+      if (dt == TT_F32) return stream_launch_f32<DK, NT>(Q, K, V, BH, N, p, states_in, O, den_out, states, ws, s);
     }
     if constexpr (use_pipe<DK, NT>()) {
       if (dt == TT_BF16) {

@@ -651,6 +651,385 @@ __global__ __launch_bounds__(256, 3) void stream_out_kernel(const uint16_t* __re
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp32 inputs with more than 256 feature rows: the same three launches on
+// fp32 MFMA (16x16x4), rows in feature order, no hi/lo splits (fp32
+// operands are exact).  The span totals come from the sweep kernel's totals
+// pass over spans of kStL tokens.  The prefix state is rewritten per
+// 16-row block and 16-column tile as the readout's A operand (lane (i, g)
+// holds rows 16j + 4g .. 4g+3 of column 16ct + i: one 16-byte load); the
+// normaliser rows are read in place.
+// ---------------------------------------------------------------------------
+template <int DK, int NT>
+struct StF {
+  static constexpr int W = rows_for(DK, NT);
+  static constexpr int NKB = (W + 15) / 16;  // 16-row blocks of the readout
+  static constexpr int XS = DK + 1;          // K and Q tile row stride (floats; odd: column reads hit distinct banks)
+  static constexpr int VS = kDV + 4;         // V tile row stride
+  static constexpr int PHS = 16 + 4;         // phi tile row stride: one 16-row block
+  static constexpr int B_K = kStK * XS * 4, B_V = kStK * VS * 4;
+  static constexpr int LDS_A = 2 * (B_K + B_V);
+  static constexpr int B_Q = kStQ * XS * 4, B_PHI = kStQ * PHS * 4;
+  static constexpr int LDS_B = B_Q + 2 * B_PHI;
+  static constexpr int OXS = kDV + 4;
+  static constexpr int LDS_X = (kStQ * OXS + kStQ) * 4;
+  static constexpr int LDS = LDS_A > LDS_B ? (LDS_A > LDS_X ? LDS_A : LDS_X) : (LDS_B > LDS_X ? LDS_B : LDS_X);
+  static constexpr int KSEG = kStK * DK / 4, VSEG = kStK * kDV / 4, QSEG = kStQ * DK / 4;  // 16-byte segments
+  static constexpr int NKS = (KSEG + 255) / 256, NVS = VSEG / 256, NQS = (QSEG + 255) / 256;
+  static_assert(VSEG % 256 == 0, "V segments per thread");
+};
+
+__device__ inline size_t stf_frag_off(int j, int ct, int l) {
+  return (size_t)(16 * j + (l >> 2)) * kDV + 16 * ct + 4 * (l & 3);
+}
+
+// Exclusive scan over spans (in place) into fragments, and the final states;
+// one workgroup per (head, 16-row block), wave = column tile, wave 0's lanes
+// 0-15 also take the block's normaliser rows (in place, natural layout).
+template <int DK, int NT>
+__global__ __launch_bounds__(256) void stream_scan_f32_kernel(float* ws, int nspan, int WP, int BH,
+                                                              const float* init, float* states) {
+  using C = StF<DK, NT>;
+  constexpr int W = C::W;
+  const int bh = blockIdx.x / C::NKB, j = blockIdx.x % C::NKB;
+  const int lane = threadIdx.x & 63, ct = threadIdx.x >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const bool den_lane = ct == 0 && lane < 16;
+  const size_t per = (size_t)WP * (kDV + 1);
+  float* base = ws + (size_t)bh * nspan * per;
+  const int col = 16 * ct + li;
+  const int rd = 16 * j + lane;
+  float run[4], rund = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 16 * j + 4 * lg + u;
+    run[u] = (init != nullptr && r < W) ? init[((size_t)bh * W + r) * kDV + col] : 0.f;
+  }
+  if (init != nullptr && den_lane && rd < W) rund = init[(size_t)BH * W * kDV + (size_t)bh * W + rd];
+  constexpr int G = 4;
+  for (int s0 = 0; s0 < nspan; s0 += G) {
+    float t[G][4], td[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (s0 + g < nspan) {
+        const float* p = base + (size_t)(s0 + g) * per;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) t[g][u] = p[(size_t)(16 * j + 4 * lg + u) * kDV + col];
+        if (den_lane) td[g] = p[(size_t)WP * kDV + rd];
+      }
+    }
+    // every read of these spans has returned before any fragment is written
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (s0 + g < nspan) {
+        float* p = base + (size_t)(s0 + g) * per;
+        *reinterpret_cast<f32x4*>(p + stf_frag_off(j, ct, lane)) = f32x4{run[0], run[1], run[2], run[3]};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) run[u] += t[g][u];
+        if (den_lane) {
+          p[(size_t)WP * kDV + rd] = rund;
+          rund += td[g];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 16 * j + 4 * lg + u;
+    if (r < W) states[((size_t)bh * W + r) * kDV + col] = run[u];
+  }
+  if (den_lane && rd < W) states[(size_t)BH * W * kDV + (size_t)bh * W + rd] = rund;
+}
+
+// Output pass for fp32 inputs: one workgroup of 4 waves per 128 queries of a
+// span; phase A (the span's causal block) and phase B (readout of the prefix
+// state) as in stream_out_kernel, on fp32 MFMA.  Lane layouts of f32
+// 16x16x4: A[i][g], B[g][i]; D: lane holds D[4g + s][i].
+template <int DK, int NT, bool UNN>
+__global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __restrict__ Qg,
+                                                                const float* __restrict__ Kg,
+                                                                const float* __restrict__ Vg, int BH, int N,
+                                                                int nspan, int WP, const float* __restrict__ ws,
+                                                                bool has_init, float* __restrict__ Og,
+                                                                float* __restrict__ Dg) {
+  using C = StF<DK, NT>;
+  constexpr int W = C::W;
+  constexpr int KT = DK / 4;  // K-steps of the scores
+  __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+
+  const int b = blockIdx.x;
+  const int sg = (b / (8 * kStT)) * 8 + (b & 7);
+  const int tile = kStT - 1 - (b >> 3) % kStT;
+  if (sg >= BH * nspan) return;
+  const int bh = sg / nspan, s = sg % nspan;
+  const int q0 = s * kStL + tile * kStQ;
+  if (q0 >= N) return;
+  const float* Qh = Qg + (size_t)bh * N * DK;
+  const float* Kh = Kg + (size_t)bh * N * DK;
+  const float* Vh = Vg + (size_t)bh * N * kDV;
+
+  // ---------------- phase A: the span's causal block ----------------
+  const int qw0 = q0 + 32 * w;
+  float qf[2][KT];  // B operand of S^T = K Q^T: q[query][4t + g]
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int t = 0; t < KT; ++t) qf[qt][t] = Qh[(size_t)min(qw0 + 16 * qt + li, N - 1) * DK + 4 * t + lg];
+  f32x4 oA[2][4], dA[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    dA[qt] = zero4();
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) oA[qt][ct] = zero4();
+  }
+  {
+    auto sK = [&](int buf) { return reinterpret_cast<float*>(lds + buf * (C::B_K + C::B_V)); };
+    auto sV = [&](int buf) { return reinterpret_cast<float*>(lds + buf * (C::B_K + C::B_V) + C::B_K); };
+    const int kbeg = s * kStL;
+    const int kend = min(q0 + kStQ, N);
+    const int nkb = (kend - kbeg + kStK - 1) / kStK;
+    f32x4 rk[C::NKS], rv[C::NVS];
+    auto issue = [&](int kb) {
+      const int k0 = kbeg + kb * kStK;
+#pragma unroll
+      for (int i = 0; i < C::NKS; ++i) {
+        const int seg = tid + 256 * i;
+        if (seg < C::KSEG) {
+          const int tok = seg / (DK / 4), part = seg % (DK / 4);
+          rk[i] = *reinterpret_cast<const f32x4*>(Kh + (size_t)min(k0 + tok, N - 1) * DK + part * 4);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < C::NVS; ++i) {
+        const int seg = tid + 256 * i, tok = seg >> 4, part = seg & 15;
+        rv[i] = *reinterpret_cast<const f32x4*>(Vh + (size_t)min(k0 + tok, N - 1) * kDV + part * 4);
+      }
+    };
+    auto commit = [&](int buf) {
+      float* K = sK(buf);
+      float* V = sV(buf);
+#pragma unroll
+      for (int i = 0; i < C::NKS; ++i) {
+        const int seg = tid + 256 * i;
+        if (seg < C::KSEG) {
+          const int tok = seg / (DK / 4), part = seg % (DK / 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) K[tok * C::XS + part * 4 + e] = rk[i][e];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < C::NVS; ++i) {
+        const int seg = tid + 256 * i, tok = seg >> 4, part = seg & 15;
+        *reinterpret_cast<f32x4*>(V + tok * C::VS + part * 4) = rv[i];
+      }
+    };
+    issue(0);
+    commit(0);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int buf = kb & 1;
+      if (kb + 1 < nkb) issue(kb + 1);
+      const int k0 = kbeg + kb * kStK;
+      const float* K = sK(buf);
+      const float* V = sV(buf);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int kt0 = k0 + 16 * kt;
+        if (kt0 > qw0 + 31) continue;             // every key of the tile is after this wave's queries
+        const bool diag = kt0 + 15 > qw0;         // keys after the wave's first query: mask
+        float p[2][4];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          f32x4 x = zero4();
+#pragma unroll
+          for (int t = 0; t < KT; ++t) x = mfma_f32(K[(16 * kt + li) * C::XS + 4 * t + lg], qf[qt][t], x);
+          const int query = qw0 + 16 * qt + li;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = taylor_poly<NT>(x[e]);
+            p[qt][e] = (diag && kt0 + 4 * lg + e > query) ? 0.f : v;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dA[qt] = mfma_f32(1.0f, p[qt][e], dA[qt]);
+        }
+        // O^T += V^T P^T: K-slot g of step e is key kt0 + 4g + e
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float a = V[(16 * kt + 4 * lg + e) * C::VS + 16 * ct + li];
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) oA[qt][ct] = mfma_f32(a, p[qt][e], oA[qt][ct]);
+          }
+      }
+      if (kb + 1 < nkb) {
+        commit(buf ^ 1);
+        __syncthreads();
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---------------- phase B: readout of the prefix state ----------------
+  f32x4 nB[8], dB[2];
+#pragma unroll
+  for (int qt = 0; qt < 8; ++qt) nB[qt] = zero4();
+  dB[0] = dB[1] = zero4();
+  if (s > 0 || has_init) {
+    float* sQ = reinterpret_cast<float*>(lds);
+    auto sPhi = [&](int buf) { return reinterpret_cast<float*>(lds + C::B_Q + buf * C::B_PHI); };
+#pragma unroll
+    for (int i = 0; i < C::NQS; ++i) {
+      const int seg = tid + 256 * i;
+      if (seg < C::QSEG) {
+        const int tok = seg / (DK / 4), part = seg % (DK / 4);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(Qh + (size_t)min(q0 + tok, N - 1) * DK + part * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sQ[tok * C::XS + part * 4 + e] = v[e];
+      }
+    }
+    // phi rows 16j + 4w .. +3 of the 128 tokens (lane = token, two passes);
+    // the row codes are wave-uniform
+    const auto& tab = RowsOf<DK>::get();
+    auto gen = [&](int j, float* P) {
+      uint32_t code[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 16 * j + 4 * w + u;
+        code[u] = r < W ? tab.code[r] : kPadRow;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int tok = 64 * h + lane;
+        const float* x = sQ + tok * C::XS;
+        f32x4 ph;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int m = row_order(code[u]);
+          float v = 0.f;
+          if (m < 7) {
+            v = row_weight(code[u]);
+            for (int l = 0; l < m; ++l) v *= x[row_index<DK>(code[u], l)];
+          }
+          ph[u] = v;
+        }
+        *reinterpret_cast<f32x4*>(P + tok * C::PHS + 4 * w) = ph;
+      }
+    };
+    const float* S = ws + ((size_t)bh * nspan + s) * (size_t)WP * (kDV + 1);
+    auto load_s = [&](int j, f32x4& sa, f32x4& da) {
+      sa = *reinterpret_cast<const f32x4*>(S + stf_frag_off(j, w, lane));
+      da = *reinterpret_cast<const f32x4*>(S + (size_t)WP * kDV + 16 * j + 4 * lg);
+    };
+    f32x4 sa, da;
+    load_s(0, sa, da);
+    __syncthreads();  // Q tile staged
+    gen(0, sPhi(0));
+    __syncthreads();
+    for (int j = 0; j < C::NKB; ++j) {
+      const float* P = sPhi(j & 1);
+      if (j + 1 < C::NKB) gen(j + 1, sPhi((j + 1) & 1));
+      f32x4 na, nd;
+      if (j + 1 < C::NKB) load_s(j + 1, na, nd);
+      f32x4 af[8];
+#pragma unroll
+      for (int qt = 0; qt < 8; ++qt) af[qt] = *reinterpret_cast<const f32x4*>(P + (qt * 16 + li) * C::PHS + 4 * lg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int qt = 0; qt < 8; ++qt) nB[qt] = mfma_f32(sa[e], af[qt][e], nB[qt]);
+      switch (w) {
+        case 0:
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[e], af[0][e], dB[0]); dB[1] = mfma_f32(da[e], af[1][e], dB[1]); }
+          break;
+        case 1:
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[e], af[2][e], dB[0]); dB[1] = mfma_f32(da[e], af[3][e], dB[1]); }
+          break;
+        case 2:
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[e], af[4][e], dB[0]); dB[1] = mfma_f32(da[e], af[5][e], dB[1]); }
+          break;
+        default:
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[e], af[6][e], dB[0]); dB[1] = mfma_f32(da[e], af[7][e], dB[1]); }
+          break;
+      }
+      if (j + 1 < C::NKB) {
+        sa = na;
+        da = nd;
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---------------- combine ----------------
+  float* sX = reinterpret_cast<float*>(lds);
+  float* sXd = sX + kStQ * C::OXS;
+#pragma unroll
+  for (int qt = 0; qt < 8; ++qt)
+    *reinterpret_cast<f32x4*>(sX + (qt * 16 + li) * C::OXS + 16 * w + 4 * lg) = nB[qt];
+  if (lg == 0) {
+    sXd[(2 * w) * 16 + li] = dB[0].x;
+    sXd[(2 * w + 1) * 16 + li] = dB[1].x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int ql = 32 * w + 16 * qt + li;
+    const int q = q0 + ql;
+    if (q >= N) continue;
+    const float den = dA[qt].x + sXd[ql];
+    const float r = UNN ? 1.0f : 1.0f / den;
+    float* orow = Og + ((size_t)bh * N + q) * kDV;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const f32x4 num = oA[qt][ct] + *reinterpret_cast<const f32x4*>(sX + ql * C::OXS + 16 * ct + 4 * lg);
+      store_nt(orow + 16 * ct + 4 * lg, num * r);
+    }
+    if (UNN && lg == 0) Dg[(size_t)bh * N + q] = den;
+  }
+}
+
+template <int DK, int NT>
+constexpr bool use_stream_f32() { return StF<DK, NT>::W > 256; }
+
+template <int DK, int NT>
+hipError_t stream_launch_f32(const void* Q, const void* K, const void* V, int BH, int N, const PrefillPlan& p,
+                             const float* states_in, float* O, float* den_out, float* states, float* ws,
+                             hipStream_t s) {
+  using S = Shape<float, DK, NT, 64>;
+  using T = typename S::Tot;
+  static_assert(StF<DK, NT>::NKB * 16 <= T::WP, "the readout's row blocks lie inside the span state");
+  static_assert(!T::OCT && S::NVT == 4, "feature-order rows, one column group");
+  const unsigned nblk = (unsigned)((size_t)BH * p.nspan * p.ngroups * S::NRG);
+  hipLaunchKernelGGL((sweep_kernel<T>), dim3(nblk), dim3(T::NTHR), 0, s, (const float*)Q, (const float*)K,
+                     (const float*)V, N, p.span, p.nspan, ws, (float*)nullptr, O, den_out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((stream_scan_f32_kernel<DK, NT>), dim3((unsigned)(BH * StF<DK, NT>::NKB)), dim3(256), 0, s, ws,
+                     p.nspan, (int)T::WP, BH, states_in, states);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned sgs = (unsigned)((BH * p.nspan + 7) / 8 * 8);
+  const dim3 grid(sgs * kStT);
+  if (den_out)
+    hipLaunchKernelGGL((stream_out_f32_kernel<DK, NT, true>), grid, dim3(256), 0, s, (const float*)Q,
+                       (const float*)K, (const float*)V, BH, N, p.nspan, (int)T::WP, (const float*)ws,
+                       states_in != nullptr, O, den_out);
+  else
+    hipLaunchKernelGGL((stream_out_f32_kernel<DK, NT, false>), grid, dim3(256), 0, s, (const float*)Q,
+                       (const float*)K, (const float*)V, BH, N, p.nspan, (int)T::WP, (const float*)ws,
+                       states_in != nullptr, O, den_out);
+  return hipGetLastError();
+}
+
 // The shapes of this path: bf16 inputs with n = 3 and dk = 32 or 64, in
 // 64-token chunks (the totals pass).
 template <int DK, int NT>

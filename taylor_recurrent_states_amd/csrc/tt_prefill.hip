@@ -40,10 +40,9 @@ int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype
       }
       if constexpr (use_stream_f32<DK, NT>()) {
         if (dt == TT_F32) {  // large fp32 feature sets: the same, on fp32 MFMA
-          using S = Shape<float, DK, NT, 64>;
-          wp = S::Tot::WP;
-          ngroups = kDV / S::Tot::GC;
-          nrg = S::NRG;
+          wp = StFT<DK, NT>::WP;
+          ngroups = 1;
+          nrg = StFT<DK, NT>::NRB;
           stream = true;
           return hipSuccess;
         }

@@ -654,8 +654,8 @@ __global__ __launch_bounds__(256, 3) void stream_out_kernel(const uint16_t* __re
 // ---------------------------------------------------------------------------
 // fp32 inputs with more than 256 feature rows: the same three launches on
 // fp32 MFMA (16x16x4), rows in feature order, no hi/lo splits (fp32
-// operands are exact).  The span totals come from the sweep kernel's totals
-// pass over spans of kStL tokens.  The prefix state is rewritten per
+// operands are exact).  The span totals come from stream_totals_f32_kernel
+// over spans of kStL tokens.  The prefix state is rewritten per
 // 16-row block and 16-column tile as the readout's A operand (lane (i, g)
 // holds rows 16j + 4g .. 4g+3 of column 16ct + i: one 16-byte load); the
 // normaliser rows are read in place.
@@ -664,12 +664,14 @@ template <int DK, int NT>
 struct StF {
   static constexpr int W = rows_for(DK, NT);
   static constexpr int NKB = (W + 15) / 16;  // 16-row blocks of the readout
-  static constexpr int XS = DK + 1;          // K and Q tile row stride (floats; odd: column reads hit distinct banks)
+  static constexpr int NKP = (NKB + 1) / 2; // pairs of 16-row blocks: one phi tile and one barrier each
+  static constexpr int XS = DK + 1;          // K tile row stride (floats; odd: column reads hit distinct banks)
+  static constexpr int QS = DK + 4;          // Q tile row stride (16-byte rows: a token's row in vector reads)
   static constexpr int VS = kDV + 4;         // V tile row stride
-  static constexpr int PHS = 16 + 4;         // phi tile row stride: one 16-row block
+  static constexpr int PHS = 32 + 4;         // phi tile row stride: two 16-row blocks
   static constexpr int B_K = kStK * XS * 4, B_V = kStK * VS * 4;
   static constexpr int LDS_A = 2 * (B_K + B_V);
-  static constexpr int B_Q = kStQ * XS * 4, B_PHI = kStQ * PHS * 4;
+  static constexpr int B_Q = kStQ * QS * 4, B_PHI = kStQ * PHS * 4;
   static constexpr int LDS_B = B_Q + 2 * B_PHI;
   static constexpr int OXS = kDV + 4;
   static constexpr int LDS_X = (kStQ * OXS + kStQ) * 4;
@@ -747,7 +749,7 @@ __global__ __launch_bounds__(256) void stream_scan_f32_kernel(float* ws, int nsp
 // state) as in stream_out_kernel, on fp32 MFMA.  Lane layouts of f32
 // 16x16x4: A[i][g], B[g][i]; D: lane holds D[4g + s][i].
 template <int DK, int NT, bool UNN>
-__global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __restrict__ Qg,
+__global__ __launch_bounds__(256, 2) void stream_out_f32_kernel(const float* __restrict__ Qg,
                                                                 const float* __restrict__ Kg,
                                                                 const float* __restrict__ Vg, int BH, int N,
                                                                 int nspan, int WP, const float* __restrict__ ws,
@@ -888,37 +890,64 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
       const int seg = tid + 256 * i;
       if (seg < C::QSEG) {
         const int tok = seg / (DK / 4), part = seg % (DK / 4);
-        const f32x4 v = *reinterpret_cast<const f32x4*>(Qh + (size_t)min(q0 + tok, N - 1) * DK + part * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sQ[tok * C::XS + part * 4 + e] = v[e];
+        *reinterpret_cast<f32x4*>(sQ + tok * C::QS + part * 4) =
+            *reinterpret_cast<const f32x4*>(Qh + (size_t)min(q0 + tok, N - 1) * DK + part * 4);
       }
     }
-    // phi rows 16j + 4w .. +3 of the 128 tokens (lane = token, two passes);
-    // the row codes are wave-uniform
+    // phi rows 32J + 8w .. +7 (a pair of 16-row blocks) of the 128 tokens
+    // (lane = token, two passes); row codes and weights are wave-uniform.
+    // Narrow keys hold the token's coordinates in registers (indexed by a
+    // uniform row index); wider ones read them from the tile.
     const auto& tab = RowsOf<DK>::get();
-    auto gen = [&](int j, float* P) {
-      uint32_t code[4];
+    auto gen = [&](int J, float* P) {
+      uint32_t code[8];
+      float wt[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = 16 * j + 4 * w + u;
+      for (int u = 0; u < 8; ++u) {
+        const int r = 32 * J + 8 * w + u;
         code[u] = r < W ? tab.code[r] : kPadRow;
+        wt[u] = r < W ? tab.weight[r] : 0.f;
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int tok = 64 * h + lane;
-        const float* x = sQ + tok * C::XS;
-        f32x4 ph;
+        const float* xr = sQ + tok * C::QS;
+        if constexpr (DK <= 16) {
+          float x[DK];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int m = row_order(code[u]);
-          float v = 0.f;
-          if (m < 7) {
-            v = row_weight(code[u]);
-            for (int l = 0; l < m; ++l) v *= x[row_index<DK>(code[u], l)];
+          for (int i = 0; i < DK / 4; ++i) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(xr + 4 * i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[4 * i + e] = v[e];
           }
-          ph[u] = v;
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            f32x4 ph;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int u = 4 * g + e;
+              const int m = row_order(code[u]);
+              float v = wt[u];
+              for (int l = 0; l < m && m < 7; ++l) v *= x[row_index<DK>(code[u], l)];
+              ph[e] = v;
+            }
+            *reinterpret_cast<f32x4*>(P + tok * C::PHS + 8 * w + 4 * g) = ph;
+          }
+        } else {
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            f32x4 ph;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int u = 4 * g + e;
+              const int m = row_order(code[u]);
+              float v = wt[u];
+              for (int l = 0; l < m && m < 7; ++l) v *= xr[row_index<DK>(code[u], l)];
+              ph[e] = v;
+            }
+            *reinterpret_cast<f32x4*>(P + tok * C::PHS + 8 * w + 4 * g) = ph;
+          }
         }
-        *reinterpret_cast<f32x4*>(P + tok * C::PHS + 4 * w) = ph;
       }
     };
     const float* S = ws + ((size_t)bh * nspan + s) * (size_t)WP * (kDV + 1);
@@ -926,44 +955,54 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
       sa = *reinterpret_cast<const f32x4*>(S + stf_frag_off(j, w, lane));
       da = *reinterpret_cast<const f32x4*>(S + (size_t)WP * kDV + 16 * j + 4 * lg);
     };
-    f32x4 sa, da;
-    load_s(0, sa, da);
+    // block j = 2J + half of the pair; blocks past NKB hold zero phi rows and
+    // read the zero-padded state rows of the same span (j < WP / 16)
+    f32x4 sa[2], da[2];
+    load_s(0, sa[0], da[0]);
+    load_s(1, sa[1], da[1]);
     __syncthreads();  // Q tile staged
     gen(0, sPhi(0));
     __syncthreads();
-    for (int j = 0; j < C::NKB; ++j) {
-      const float* P = sPhi(j & 1);
-      if (j + 1 < C::NKB) gen(j + 1, sPhi((j + 1) & 1));
-      f32x4 na, nd;
-      if (j + 1 < C::NKB) load_s(j + 1, na, nd);
-      f32x4 af[8];
-#pragma unroll
-      for (int qt = 0; qt < 8; ++qt) af[qt] = *reinterpret_cast<const f32x4*>(P + (qt * 16 + li) * C::PHS + 4 * lg);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int qt = 0; qt < 8; ++qt) nB[qt] = mfma_f32(sa[e], af[qt][e], nB[qt]);
-      switch (w) {
-        case 0:
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[e], af[0][e], dB[0]); dB[1] = mfma_f32(da[e], af[1][e], dB[1]); }
-          break;
-        case 1:
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[e], af[2][e], dB[0]); dB[1] = mfma_f32(da[e], af[3][e], dB[1]); }
-          break;
-        case 2:
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[e], af[4][e], dB[0]); dB[1] = mfma_f32(da[e], af[5][e], dB[1]); }
-          break;
-        default:
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[e], af[6][e], dB[0]); dB[1] = mfma_f32(da[e], af[7][e], dB[1]); }
-          break;
+    for (int J = 0; J < C::NKP; ++J) {
+      const float* P = sPhi(J & 1);
+      if (J + 1 < C::NKP) gen(J + 1, sPhi((J + 1) & 1));
+      f32x4 na[2], nd[2];
+      if (J + 1 < C::NKP) {
+        load_s(2 * J + 2, na[0], nd[0]);
+        load_s(2 * J + 3, na[1], nd[1]);
       }
-      if (j + 1 < C::NKB) {
-        sa = na;
-        da = nd;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        f32x4 af[8];
+#pragma unroll
+        for (int qt = 0; qt < 8; ++qt)
+          af[qt] = *reinterpret_cast<const f32x4*>(P + (qt * 16 + li) * C::PHS + 16 * hf + 4 * lg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int qt = 0; qt < 8; ++qt) nB[qt] = mfma_f32(sa[hf][e], af[qt][e], nB[qt]);
+        switch (w) {
+          case 0:
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[hf][e], af[0][e], dB[0]); dB[1] = mfma_f32(da[hf][e], af[1][e], dB[1]); }
+            break;
+          case 1:
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[hf][e], af[2][e], dB[0]); dB[1] = mfma_f32(da[hf][e], af[3][e], dB[1]); }
+            break;
+          case 2:
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[hf][e], af[4][e], dB[0]); dB[1] = mfma_f32(da[hf][e], af[5][e], dB[1]); }
+            break;
+          default:
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[hf][e], af[6][e], dB[0]); dB[1] = mfma_f32(da[hf][e], af[7][e], dB[1]); }
+            break;
+        }
+      }
+      if (J + 1 < C::NKP) {
+        sa[0] = na[0]; sa[1] = na[1];
+        da[0] = nd[0]; da[1] = nd[1];
       }
       __syncthreads();
     }
@@ -997,6 +1036,176 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
   }
 }
 
+// Span totals for fp32 inputs: one workgroup of 4 waves per (head, span, 128
+// feature rows); wave w owns rows 128*rb + 32w .. +31 (two 16-row tiles) for
+// all 64 value columns.  Per 64-token block each lane (= token) builds the
+// wave's 32 mu rows into a wave-private tile and adds them to its own
+// partial normalisers (summed over the lanes once at the end); the values
+// are contracted with V on fp32 MFMA (A = mu^T, B = V, 4 tokens per step).
+template <int DK, int NT>
+struct StFT {
+  static constexpr int W = rows_for(DK, NT);
+  static constexpr int NRB = (W + 127) / 128;   // 128-row groups
+  static constexpr int WP = NRB * 128;          // padded rows of a span state
+  static constexpr int KS = DK + 4;             // K tile row stride (16-byte rows)
+  static constexpr int VS = kDV + 16;           // V tile row stride: rows 4 apart hit distinct bank groups
+  static constexpr int MS = 32 + 16;            // mu tile row stride (the same for the A reads)
+  static constexpr int B_K = kStK * KS * 4, B_V = kStK * VS * 4, B_MU = kStK * MS * 4;
+  static constexpr int LDS = B_K + B_V + 4 * B_MU;
+  static constexpr int KSEG = kStK * DK / 4, VSEG = kStK * kDV / 4;
+  static constexpr int NKS = (KSEG + 255) / 256, NVS = VSEG / 256;
+};
+
+template <int DK, int NT>
+__global__ __launch_bounds__(256, 2) void stream_totals_f32_kernel(const float* __restrict__ Kg,
+                                                                   const float* __restrict__ Vg, int BH, int N,
+                                                                   int nspan, float* __restrict__ ws) {
+  using C = StFT<DK, NT>;
+  constexpr int W = C::W;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int b = blockIdx.x;
+  const int rb = (b >> 3) % C::NRB;
+  const int hs = (b / (8 * C::NRB)) * 8 + (b & 7);
+  if (hs >= BH * nspan) return;
+  const int bh = hs / nspan, s = hs % nspan;
+  const int t_begin = s * kStL, t_end = min(N, t_begin + kStL);
+  const int ntb = (t_end - t_begin + kStK - 1) / kStK;
+  const int R0 = 128 * rb + 32 * w;  // this wave's first row
+  const bool active = R0 < W;        // wave-uniform
+  const float* Kh = Kg + (size_t)bh * N * DK;
+  const float* Vh = Vg + (size_t)bh * N * kDV;
+  float* sK = reinterpret_cast<float*>(lds);
+  float* sV = reinterpret_cast<float*>(lds + C::B_K);
+  float* sMu = reinterpret_cast<float*>(lds + C::B_K + C::B_V + w * C::B_MU);
+
+  f32x4 rk[C::NKS], rv[C::NVS];
+  auto issue = [&](int tb) {
+    const int k0 = t_begin + tb * kStK;
+#pragma unroll
+    for (int i = 0; i < C::NKS; ++i) {
+      const int seg = tid + 256 * i;
+      if (seg < C::KSEG) {
+        const int tok = seg / (DK / 4), part = seg % (DK / 4);
+        rk[i] = *reinterpret_cast<const f32x4*>(Kh + (size_t)min(k0 + tok, t_end - 1) * DK + part * 4);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::NVS; ++i) {
+      const int seg = tid + 256 * i, tok = seg >> 4, part = seg & 15;
+      rv[i] = *reinterpret_cast<const f32x4*>(Vh + (size_t)min(k0 + tok, t_end - 1) * kDV + part * 4);
+    }
+  };
+  // K rows of tokens past the span end are stored as zeros (their mu rows of
+  // order >= 1 vanish; the order-0 row is masked where it is built)
+  auto commit = [&](int tb) {
+    const int k0 = t_begin + tb * kStK;
+#pragma unroll
+    for (int i = 0; i < C::NKS; ++i) {
+      const int seg = tid + 256 * i;
+      if (seg < C::KSEG) {
+        const int tok = seg / (DK / 4), part = seg % (DK / 4);
+        *reinterpret_cast<f32x4*>(sK + tok * C::KS + part * 4) = k0 + tok < t_end ? rk[i] : zero4();
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::NVS; ++i) {
+      const int seg = tid + 256 * i, tok = seg >> 4, part = seg & 15;
+      *reinterpret_cast<f32x4*>(sV + tok * C::VS + part * 4) = rv[i];
+    }
+  };
+
+  const auto& tab = RowsOf<DK>::get();
+  uint32_t code[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) code[i] = R0 + i < W ? tab.code[R0 + i] : kPadRow;
+  f32x4 st[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) st[rt][ct] = zero4();
+  float dpart[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) dpart[i] = 0.f;
+
+  issue(0);
+  for (int tb = 0; tb < ntb; ++tb) {
+    commit(tb);
+    __syncthreads();
+    if (tb + 1 < ntb) issue(tb + 1);
+    if (active) {
+      const bool kvalid = t_begin + tb * kStK + lane < t_end;
+      const float* xr = sK + lane * C::KS;
+      float mu[32];
+      if constexpr (DK <= 16) {
+        float x[DK];
+#pragma unroll
+        for (int i = 0; i < DK / 4; ++i) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(xr + 4 * i);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * i + e] = v[e];
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int m = row_order(code[i]);
+          float v = (m == 0 && !kvalid) || m == 7 ? 0.f : 1.f;
+          for (int l = 0; l < m && m < 7; ++l) v *= x[row_index<DK>(code[i], l)];
+          mu[i] = v;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int m = row_order(code[i]);
+          float v = (m == 0 && !kvalid) || m == 7 ? 0.f : 1.f;
+          for (int l = 0; l < m && m < 7; ++l) v *= xr[row_index<DK>(code[i], l)];
+          mu[i] = v;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) dpart[i] += mu[i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<f32x4*>(sMu + lane * C::MS + 4 * i) = f32x4{mu[4 * i], mu[4 * i + 1], mu[4 * i + 2], mu[4 * i + 3]};
+      // the tile is wave-private: this wave's LDS writes done, then its reads
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int t = 0; t < kStK / 4; ++t) {
+        float bv[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) bv[ct] = sV[(4 * t + lg) * C::VS + 16 * ct + li];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const float a = sMu[(4 * t + lg) * C::MS + 16 * rt + li];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) st[rt][ct] = mfma_f32(a, bv[ct], st[rt][ct]);
+        }
+      }
+    }
+    __syncthreads();  // the K and V tiles are overwritten next
+  }
+  if (!active) return;
+  float* S = ws + (size_t)hs * C::WP * (kDV + 1);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = R0 + 16 * rt + 4 * lg + e;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) S[(size_t)row * kDV + 16 * ct + li] = st[rt][ct][e];
+    }
+  // normalisers: the sum of the lanes' partial sums
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    float d = dpart[i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) d += __shfl_xor(d, off);
+    if (lane == i) S[(size_t)C::WP * kDV + R0 + i] = d;
+  }
+}
+
 template <int DK, int NT>
 constexpr bool use_stream_f32() { return StF<DK, NT>::W > 256; }
 
@@ -1004,20 +1213,17 @@ template <int DK, int NT>
 hipError_t stream_launch_f32(const void* Q, const void* K, const void* V, int BH, int N, const PrefillPlan& p,
                              const float* states_in, float* O, float* den_out, float* states, float* ws,
                              hipStream_t s) {
-  using S = Shape<float, DK, NT, 64>;
-  using T = typename S::Tot;
-  static_assert(StF<DK, NT>::NKB * 16 <= T::WP, "the readout's row blocks lie inside the span state");
-  static_assert(!T::OCT && S::NVT == 4, "feature-order rows, one column group");
-  const unsigned nblk = (unsigned)((size_t)BH * p.nspan * p.ngroups * S::NRG);
-  hipLaunchKernelGGL((sweep_kernel<T>), dim3(nblk), dim3(T::NTHR), 0, s, (const float*)Q, (const float*)K,
-                     (const float*)V, N, p.span, p.nspan, ws, (float*)nullptr, O, den_out);
+  using T = StFT<DK, NT>;
+  static_assert(StF<DK, NT>::NKP * 32 <= T::WP, "the readout's row blocks (pairs) lie inside the span state");
+  const unsigned sgs = (unsigned)((BH * p.nspan + 7) / 8 * 8);  // (head, span) pairs, padded to the 8 XCDs
+  hipLaunchKernelGGL((stream_totals_f32_kernel<DK, NT>), dim3(sgs * T::NRB), dim3(256), 0, s, (const float*)K,
+                     (const float*)V, BH, N, p.nspan, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((stream_scan_f32_kernel<DK, NT>), dim3((unsigned)(BH * StF<DK, NT>::NKB)), dim3(256), 0, s, ws,
                      p.nspan, (int)T::WP, BH, states_in, states);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned sgs = (unsigned)((BH * p.nspan + 7) / 8 * 8);
   const dim3 grid(sgs * kStT);
   if (den_out)
     hipLaunchKernelGGL((stream_out_f32_kernel<DK, NT, true>), grid, dim3(256), 0, s, (const float*)Q,

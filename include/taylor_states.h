@@ -88,6 +88,14 @@ size_t tt_state_floats(int dk, int dv, int n);
 int tt_prefill_workspace_bytes(int B, int H, int N, int dk, int dv, int n,
                                int chunk, size_t *bytes);
 
+/* The same for one input dtype: the exact workspace tt_prefill,
+ * tt_prefill_from and tt_prefill_from_unnormalized need with in_dtype (at
+ * most what tt_prefill_workspace_bytes reports; the two dtypes can run
+ * different kernels with different workspaces).  Returns TT_OK or an error
+ * code as tt_prefill would. */
+int tt_prefill_workspace_bytes_dtype(int B, int H, int N, int dk, int dv, int n,
+                                     int chunk, tt_dtype in_dtype, size_t *bytes);
+
 /* Chunked causal prefill ("Expanding Attention", abstract: the states add
  * across chunks, so prefill is a parallel scan; comment thread item
  * 46888355, reply on (Q'K)V = Q'(KV)).

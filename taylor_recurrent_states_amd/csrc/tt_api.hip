@@ -233,6 +233,21 @@ int tt_prefill_workspace_bytes(int B, int H, int N, int dk, int dv, int n, int c
   return ok();
 }
 
+int tt_prefill_workspace_bytes_dtype(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype in_dtype,
+                                     size_t* bytes) {
+  if (!bytes) return fail(TT_ERR_INVALID_ARG, "bytes is NULL");
+  if (B < 1 || H < 1 || N < 1) return fail(TT_ERR_INVALID_ARG, "B=%d H=%d N=%d must be >= 1", B, H, N);
+  int rc = check_dtype(in_dtype);
+  if (rc) return rc;
+  rc = check_shape(dk, dv, n);
+  if (rc) return rc;
+  PrefillPlan p;
+  rc = plan_prefill(B, H, N, dk, dv, n, chunk, in_dtype, &p);
+  if (rc) return rc;
+  *bytes = p.ws_floats * sizeof(float);
+  return ok();
+}
+
 int tt_prefill(const void* Q, const void* K, const void* V, tt_dtype in_dtype, int B, int H, int N, int dk,
                int dv, int n, int chunk, float* O, float* states, void* workspace, size_t workspace_bytes,
                void* stream) {
@@ -244,7 +259,7 @@ int tt_prefill_noalloc(const void* Q, const void* K, const void* V, tt_dtype in_
                        int dv, int n, int chunk, float* O, float* states, void* stream) {
   if (B < 1 || H < 1 || N < 1) return fail(TT_ERR_INVALID_ARG, "B=%d H=%d N=%d must be >= 1", B, H, N);
   size_t need = 0;
-  int rc = tt_prefill_workspace_bytes(B, H, N, dk, dv, n, chunk, &need);
+  int rc = tt_prefill_workspace_bytes_dtype(B, H, N, dk, dv, n, chunk, in_dtype, &need);
   if (rc) return rc;
   if (need > (size_t)TT_NOALLOC_SCRATCH_BYTES)
     return fail(TT_ERR_WORKSPACE,

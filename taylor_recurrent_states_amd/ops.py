@@ -4,7 +4,7 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels of the library.  PyTorch supplies device memory and the stream.
 The calls keep the C names:
 
-    tt_state_rows, tt_state_floats, tt_prefill_workspace_bytes,
+    tt_state_rows, tt_state_floats, tt_prefill_workspace_bytes, tt_prefill_workspace_bytes_dtype,
     tt_prefill, tt_prefill_from, tt_decode_step, tt_state_merge,
     tt_feature_map, tt_last_error, tt_normalize_rows,
     tt_prefill_normed_workspace_bytes, tt_prefill_normed, tt_decode_step_normed,
@@ -27,8 +27,9 @@ LIB_PATH = os.path.join(_PKG, "libtaylor_states.so")
 TT_F32, TT_BF16 = 0, 1
 TT_OK, TT_ERR_INVALID_ARG, TT_ERR_UNSUPPORTED, TT_ERR_WORKSPACE, TT_ERR_HIP = 0, -1, -2, -3, -4
 
-EXPORTED = ("tt_state_rows", "tt_state_floats", "tt_prefill_workspace_bytes", "tt_prefill",
-            "tt_prefill_from", "tt_prefill_from_unnormalized", "tt_decode_step", "tt_state_merge", "tt_feature_map", "tt_last_error",
+EXPORTED = ("tt_state_rows", "tt_state_floats", "tt_prefill_workspace_bytes", "tt_prefill_workspace_bytes_dtype",
+            "tt_prefill", "tt_prefill_from", "tt_prefill_from_unnormalized", "tt_decode_step", "tt_state_merge",
+            "tt_feature_map", "tt_last_error",
             "tt_normalize_rows", "tt_prefill_normed_workspace_bytes", "tt_prefill_normed",
             "tt_decode_step_normed", "tt_softmax_prefill", "tt_softmax_decode_workspace_bytes",
             "tt_softmax_decode_step", "tt_prefill_noalloc")
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.tt_state_floats.restype = c_size
     L.tt_prefill_workspace_bytes.argtypes = [c_int] * 7 + [ctypes.POINTER(c_size)]
     L.tt_prefill_workspace_bytes.restype = c_int
+    L.tt_prefill_workspace_bytes_dtype.argtypes = [c_int] * 8 + [ctypes.POINTER(c_size)]
+    L.tt_prefill_workspace_bytes_dtype.restype = c_int
     L.tt_prefill.argtypes = [c_void, c_void, c_void, c_int] + [c_int] * 7 + [c_float_p, c_float_p, c_void,
                                                                               c_size, c_void]
     L.tt_prefill.restype = c_int
@@ -239,6 +242,18 @@ def tt_prefill_workspace_bytes(B: int, H: int, N: int, dk: int, dv: int, n: int,
     return int(out.value)
 
 
+def tt_prefill_workspace_bytes_dtype(B: int, H: int, N: int, dk: int, dv: int, n: int, chunk: int = 64,
+                                     dtype: str = "bf16") -> int:
+    """The exact workspace of tt_prefill / tt_prefill_from for one input
+    dtype ("f32" or "bf16")."""
+    codes = {"f32": 0, "bf16": 1}
+    if dtype not in codes:
+        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    out = ctypes.c_size_t(0)
+    _check(lib().tt_prefill_workspace_bytes_dtype(B, H, N, dk, dv, n, chunk, codes[dtype], ctypes.byref(out)))
+    return int(out.value)
+
+
 def tt_prefill_normed_workspace_bytes(B: int, H: int, N: int, dk: int, dv: int, n: int, chunk: int = 64) -> int:
     out = ctypes.c_size_t(0)
     _check(lib().tt_prefill_normed_workspace_bytes(B, H, N, dk, dv, n, chunk, ctypes.byref(out)))
@@ -255,7 +270,10 @@ def _prefill_args(Q, K, V, n, chunk, O, states, workspace, launch, normed=False,
         _f32(states, "states", nstate)
     if workspace is not None:
         _contig(workspace, "workspace")
-    need = (tt_prefill_normed_workspace_bytes if normed else tt_prefill_workspace_bytes)(B, H, N, dk, dv, n, chunk)
+    if normed:
+        need = tt_prefill_normed_workspace_bytes(B, H, N, dk, dv, n, chunk)
+    else:
+        need = tt_prefill_workspace_bytes_dtype(B, H, N, dk, dv, n, chunk, "bf16" if _dtype_code(Q) == 1 else "f32")
     _on_gpu(Q, (K, "K"), (V, "V"), (O, "O"), (states, "states"), (workspace, "workspace"), *extra)
     if O is None:
         O = launch.alloc((B, H, N, dv), torch.float32, Q.device)

@@ -201,3 +201,28 @@ def test_chunk_lengths_are_validated_before_launch():
     assert rc(ops.TT_F32, 8, 6, 16) == ops.TT_ERR_INVALID_ARG
     for chunk in (16, 32, 64, 128):
         assert ops.tt_prefill_workspace_bytes(2, 4, 1000, 16, 64, 3, chunk) > 0
+
+
+def test_workspace_query_per_dtype():
+    """tt_prefill_workspace_bytes_dtype: the exact workspace of one input
+    dtype, never more than the dtype-free query; the shapes whose two dtypes
+    run different kernels differ."""
+    for args in [(4, 8, 8192, 16, 64, 3, 64), (1, 16, 65536, 64, 64, 3, 64), (1, 16, 16384, 16, 64, 5, 64),
+                 (2, 3, 1000, 32, 64, 3, 32), (1, 2, 100, 8, 64, 6, 64)]:
+        both = ops.tt_prefill_workspace_bytes(*args)
+        per = {}
+        for dt in ("f32", "bf16"):
+            try:
+                per[dt] = ops.tt_prefill_workspace_bytes_dtype(*args, dtype=dt)
+            except ops.TTError as e:
+                assert e.code == ops.TT_ERR_UNSUPPORTED  # dk = 8 prefill is fp32 only
+        assert per and max(per.values()) == both, (args, per, both)
+    # order 5 at dk 16: fp32 runs the streamed path, bf16 the sweep with row-group partials
+    f = ops.tt_prefill_workspace_bytes_dtype(1, 16, 16384, 16, 64, 5, 64, "f32")
+    b = ops.tt_prefill_workspace_bytes_dtype(1, 16, 16384, 16, 64, 5, 64, "bf16")
+    assert f < b
+    with pytest.raises(ValueError):
+        ops.tt_prefill_workspace_bytes_dtype(1, 1, 10, 16, 64, 3, 64, "f16")
+    L = ops.lib()
+    out = ctypes.c_size_t(0)
+    assert L.tt_prefill_workspace_bytes_dtype(1, 1, 10, 16, 64, 3, 64, 7, ctypes.byref(out)) == ops.TT_ERR_INVALID_ARG

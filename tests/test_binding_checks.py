@@ -8,7 +8,7 @@ import torch
 
 from taylor_recurrent_states_amd import ops
 
-SIZE_QUERIES = {"tt_state_rows", "tt_state_floats", "tt_prefill_workspace_bytes",
+SIZE_QUERIES = {"tt_state_rows", "tt_state_floats", "tt_prefill_workspace_bytes", "tt_prefill_workspace_bytes_dtype",
                 "tt_prefill_normed_workspace_bytes", "tt_softmax_decode_workspace_bytes", "tt_last_error"}
 
 

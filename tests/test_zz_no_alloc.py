@@ -39,8 +39,8 @@ def test_noalloc_matches_prefill_twice_then_smaller():
 
 def test_noalloc_refuses_shapes_beyond_the_scratch():
     import torch
-    B, H, N, dk, n = 1, 16, 8192, 64, 3  # row-group partials alone exceed the array
-    need = ops.tt_prefill_workspace_bytes(B, H, N, dk, 64, n)
+    B, H, N, dk, n = 1, 16, 8192, 64, 3  # the span states alone exceed the array
+    need = ops.tt_prefill_workspace_bytes_dtype(B, H, N, dk, 64, n, 64, "bf16")
     assert need > ops.TT_NOALLOC_SCRATCH_BYTES
     Q = torch.zeros((B, H, N, dk), dtype=torch.bfloat16, device="cuda")
     V = torch.zeros((B, H, N, 64), dtype=torch.bfloat16, device="cuda")

@@ -90,8 +90,8 @@ def bench_prefill(args, torch, ops, wl):
     Q, K, V = to_dev(q), to_dev(k), to_dev(v)
     O = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.float32, device=dev)
     S = torch.empty(w.B * w.H * ops.tt_state_floats(w.dk, w.dv, w.n), dtype=torch.float32, device=dev)
-    ws = torch.empty(ops.tt_prefill_workspace_bytes(w.B, w.H, w.N, w.dk, w.dv, w.n, w.chunk), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(ops.tt_prefill_workspace_bytes_dtype(w.B, w.H, w.N, w.dk, w.dv, w.n, w.chunk, "bf16"),
+                     dtype=torch.uint8, device=dev)
 
     def step():
         ops.tt_prefill(Q, K, V, w.n, w.chunk, O=O, states=S, workspace=ws)
@@ -192,8 +192,8 @@ def bench_prefill_other(name, args, torch, ops, wl):
     V = torch.randn((w.B, w.H, w.N, w.dv), generator=tg, device=dev).to(dt)
     O = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.float32, device=dev)
     S = torch.empty(w.B * w.H * ops.tt_state_floats(w.dk, w.dv, w.n), dtype=torch.float32, device=dev)
-    ws = torch.empty(ops.tt_prefill_workspace_bytes(w.B, w.H, w.N, w.dk, w.dv, w.n, w.chunk), dtype=torch.uint8,
-                     device=dev)
+    ws_bytes = ops.tt_prefill_workspace_bytes_dtype(w.B, w.H, w.N, w.dk, w.dv, w.n, w.chunk, w.dtype)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     def step():
         ops.tt_prefill(Q, K, V, w.n, w.chunk, O=O, states=S, workspace=ws)
@@ -220,7 +220,7 @@ def bench_prefill_other(name, args, torch, ops, wl):
     alg_bytes = w.B * w.H * w.N * (2 * w.dk + w.dv) * (4 if w.dtype == "f32" else 2) + w.B * w.H * w.N * w.dv * 4 \
         + w.B * w.H * ops.tt_state_floats(w.dk, w.dv, w.n) * 4
     return {"workload": w.name, "ms_per_call": round(t * 1e3, 4), "tokens_per_s": round(w.B * w.N / t, 1),
-            "ms_per_call_normed": round(t_n * 1e3, 4),
+            "ms_per_call_normed": round(t_n * 1e3, 4), "workspace_bytes": ws_bytes,
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                          "frac": round(achieved / peak, 4), "alg_flops_per_launch": flops,
                          "alg_bytes_per_launch": alg_bytes, "traffic": _traffic(name, src), "source_hash": src}}
@@ -254,8 +254,8 @@ def bench_orders(args, torch, ops, wl):
         for n in range(1, nmax + 1):
             O = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.float32, device=dev)
             S = torch.empty(w.B * w.H * ops.tt_state_floats(dk, w.dv, n), dtype=torch.float32, device=dev)
-            ws = torch.empty(ops.tt_prefill_workspace_bytes(w.B, w.H, w.N, dk, w.dv, n, w.chunk), dtype=torch.uint8,
-                             device=dev)
+            ws = torch.empty(ops.tt_prefill_workspace_bytes_dtype(w.B, w.H, w.N, dk, w.dv, n, w.chunk, dtype),
+                             dtype=torch.uint8, device=dev)
 
             def step():
                 ops.tt_prefill(Q, K, V, n, w.chunk, O=O, states=S, workspace=ws)
@@ -316,8 +316,8 @@ def bench_compare(args, torch, ops, wl):
         V = torch.randn((w.B, w.H, N, w.dv), generator=g, device=dev).to(torch.bfloat16)
         O = torch.empty((w.B, w.H, N, w.dv), dtype=torch.float32, device=dev)
         S = torch.empty(w.B * w.H * ops.tt_state_floats(w.dk, w.dv, w.n), dtype=torch.float32, device=dev)
-        ws = torch.empty(ops.tt_prefill_workspace_bytes(w.B, w.H, N, w.dk, w.dv, w.n, w.chunk), dtype=torch.uint8,
-                         device=dev)
+        ws = torch.empty(ops.tt_prefill_workspace_bytes_dtype(w.B, w.H, N, w.dk, w.dv, w.n, w.chunk, "bf16"),
+                         dtype=torch.uint8, device=dev)
         f_t = lambda: ops.tt_prefill(Q, K, V, w.n, w.chunk, O=O, states=S, workspace=ws)
         f_s = lambda: ops.tt_softmax_prefill(Q, K, V, O=O)
         row = {"N": N}

@@ -1338,7 +1338,10 @@ struct PCfg {
   static constexpr int O_DEN = O_P + 2 * B_P;             // bf16 normaliser rows [2][hi, lo][WP]
   static constexpr int O_DEN0 = O_DEN + al(4 * WP * 2);    // fp32 normaliser of row 0 [2]
   static constexpr int O_RDEN = O_DEN0 + 16;               // 1/den per query [2][64]
-  static constexpr int LDS = O_RDEN + (OUT ? al(2 * kCH * 4) : 0);
+  // output pass, per query: phi . Zh over rows >= 1 (the normaliser readout
+  // from the hi plane), the factor of the state shift's add-back [2][64]
+  static constexpr int O_G = O_RDEN + (OUT ? al(2 * kCH * 4) : 0);
+  static constexpr int LDS = O_G + (OUT ? al(2 * kCH * 4) : 0);
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static constexpr int QV = DK / 8;  // 16-byte pieces of a q or k row
 };
@@ -1359,6 +1362,7 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
   uint16_t* sDenB = reinterpret_cast<uint16_t*>(lds + C::O_DEN);  // [2][hi, lo][WP] bf16 normaliser rows
   float* sDen0 = reinterpret_cast<float*>(lds + C::O_DEN0);         // [2] row-0 normaliser (token count)
   float* sRden = reinterpret_cast<float*>(lds + C::O_RDEN);         // [2][query%16][query/16]
+  float* sG = reinterpret_cast<float*>(lds + C::O_G);               // [2][query%16][query/16]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1498,6 +1502,7 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
   f32x4 nprev[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) nprev[q] = zero4();
+  f32x4 mprev = zero4();  // column means of the previous chunk's readout shift
   const int ct = pw;
   const u32x4 ones_bf = (li == 0) ? u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}
                                   : u32x4{0u, 0u, 0u, 0u};
@@ -1533,7 +1538,8 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
     f32x4 dstate[NJD][2];
 #pragma unroll
     for (int jd = 0; jd < NJD; ++jd) dstate[jd][0] = dstate[jd][1] = zero4();
-    auto publish_den = [&](int buf) {  // hi + lo bf16 readout fragments and the fp32 row 0
+    // hi + lo bf16 readout fragments and the fp32 row 0
+    auto publish_den = [&](int buf) {
       if (li == 0) {
 #pragma unroll
         for (int jd = 0; jd < NJD; ++jd) {
@@ -1642,10 +1648,22 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
             for (int pl = 0; pl < NPL; ++pl) dst[tau][tb][pl] = load_mu(Mu, pl, j, tau, tb);
       };
       if constexpr (OUT) {
+        // previous chunk: normalise (adding back a (phi . Z_hi), below) and
+        // store, 16 bytes per lane and query tile; done first so that its
+        // registers are free during the K-block loop
+        if (ci > 0) {
+          const f32x4 rd = *reinterpret_cast<const f32x4*>(sRden + (b ^ 1) * kCH + li * 4);
+          const f32x4 gq = *reinterpret_cast<const f32x4*>(sG + (b ^ 1) * kCH + li * 4);
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt) {
+            float* ob = Og + ((size_t)bh * N + c0 - kCH + qt * 16 + li) * kDV + ct * 16 + 4 * lg;
+            store_nt(ob, (nprev[qt] + mprev * gq[qt]) * rd[qt]);
+          }
+        }
         const unsigned char* Phi = (const unsigned char*)sPhi(b);
         const unsigned char* P = (const unsigned char*)sP(b);
         // num[qt] is the O^T tile (columns ct*16 + 4*lg + s, query qt*16 + li)
-        f32x4 num[4], den = zero4();
+        f32x4 num[4], den = zero4(), denh = zero4();
 #pragma unroll
         for (int q = 0; q < 4; ++q) num[q] = zero4();
         // normaliser fragment of K-block j: the same normaliser rows in every
@@ -1661,6 +1679,28 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
         f32x4 m0;
 #pragma unroll
         for (int s = 0; s < 4; ++s) m0[s] = __shfl(st[0][0].x, 4 * lg + s);
+        // Readout of rows >= 1 from a shifted state.  With a_c the running
+        // mean of value column c (S[0][c] over the token count Z[0], rounded
+        // to bf16) and Zh the hi bf16 plane of the normaliser rows,
+        //   sum_r phi_r S[r][c] = sum_r phi_r (S[r][c] - a_c Zh[r]) + a_c (phi . Zh),
+        // an identity for any a_c.  The shifted state goes to the MFMA rounded
+        // to bf16 (a_c Zh[r] is exact in fp32, so one bf16 dot product per
+        // row forms the difference); phi . Zh over rows >= 1 is the hi half of
+        // the normaliser readout (the same bf16 phi), and a_c (phi . Zh) is
+        // added in fp32 when the chunk is normalised.  Rounding the state then
+        // moves an output by about 2^-9 |v - a| instead of 2^-9 |v|: values
+        // offset from zero keep the accuracy of zero-mean ones.  A non-finite
+        // mean (non-finite inputs) falls back to no shift.
+        const float rz0 = den0 > 0.f ? rcp_fast(den0) : 0.f;
+        auto col_mean = [&](float s0) {  // bf16 bits of a_c (0 when not finite in bf16)
+          const uint32_t bits = pack_bf16x2(s0 * rz0, 0.f) & 0xFFFFu;
+          return (bits & 0x7F80u) != 0x7F80u ? bits : 0u;
+        };
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        const uint32_t abits = col_mean(__shfl(st[0][0].x, li));  // column ct*16 + li
+        const uint32_t nab = abits ^ 0x8000u;                      // -a_c
+        const bf16x2_t na_lo = __builtin_bit_cast(bf16x2_t, nab);        // {-a_c, 0}
+        const bf16x2_t na_hi = __builtin_bit_cast(bf16x2_t, nab << 16);  // {0, -a_c}
         // readout of K-block j, then its update (the readout has taken st[j]
         // into bs first); phi and mu fragments one K-block ahead
         u32x4 af[2][4];
@@ -1685,27 +1725,38 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
             fetch_mu(j + 1, mf[(j + 1) & 1]);
             bdn[(j + 1) & 1] = load_bdn(j + 1, 0);
           }
-          // S[rows 8lg..8lg+7 of K-block j][column ct*16 + li] as the A
-          // operand (S^T), split into hi + lo bf16 (16 significant bits), so
-          // the readout does not round the state to 8 bits: the values and
-          // their normaliser would round independently, which can move an
-          // output by about 2^-9 |o|
-          u32x4 bs, bsl;
-          split_bf16x8(st[j][0], st[j][1], bs, bsl);
+          // S[rows 8lg..8lg+7 of K-block j][column ct*16 + li] - a Zh[rows]
+          // as the A operand (S^T), rounded to bf16; bdn holds Zh of the same
+          // rows as bf16 pairs (row 8lg + 2e in the low half of dword e)
+          float sh[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w = bdn[j & 1][e];  // through a scalar (see prod8)
+            const bf16x2_t z = __builtin_bit_cast(bf16x2_t, w);
+            const f32x4 sv = st[j][e >> 1];
+            sh[2 * e] = __builtin_amdgcn_fdot2_f32_bf16(na_lo, z, sv[(2 * e) & 3], false);
+            sh[2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(na_hi, z, sv[(2 * e + 1) & 3], false);
+          }
+          const u32x4 bs = {pack_bf16x2(sh[0], sh[1]), pack_bf16x2(sh[2], sh[3]), pack_bf16x2(sh[4], sh[5]),
+                            pack_bf16x2(sh[6], sh[7])};
 #pragma unroll
           for (int qt = 0; qt < 4; ++qt) num[qt] = mfma_bf16(bs, af[j & 1][qt], num[qt]);
-#pragma unroll
-          for (int qt = 0; qt < 4; ++qt) num[qt] = mfma_bf16(bsl, af[j & 1][qt], num[qt]);
-          // normaliser readout of this wave's query tile (hi, then lo plane):
-          // ct is wave-uniform, so this is a scalar branch to one of four
-          // MFMA pairs (no operand select)
+          // normaliser readout of this wave's query tile (hi plane into denh,
+          // lo plane into den): ct is wave-uniform, so this is a scalar branch
+          // to one of four MFMA pairs (no operand select)
           switch (ct) {
-            case 0: den = mfma_bf16(af[j & 1][0], bdn[j & 1], den); den = mfma_bf16(af[j & 1][0], bdl, den); break;
-            case 1: den = mfma_bf16(af[j & 1][1], bdn[j & 1], den); den = mfma_bf16(af[j & 1][1], bdl, den); break;
-            case 2: den = mfma_bf16(af[j & 1][2], bdn[j & 1], den); den = mfma_bf16(af[j & 1][2], bdl, den); break;
-            default: den = mfma_bf16(af[j & 1][3], bdn[j & 1], den); den = mfma_bf16(af[j & 1][3], bdl, den); break;
+            case 0: denh = mfma_bf16(af[j & 1][0], bdn[j & 1], denh); den = mfma_bf16(af[j & 1][0], bdl, den); break;
+            case 1: denh = mfma_bf16(af[j & 1][1], bdn[j & 1], denh); den = mfma_bf16(af[j & 1][1], bdl, den); break;
+            case 2: denh = mfma_bf16(af[j & 1][2], bdn[j & 1], denh); den = mfma_bf16(af[j & 1][2], bdl, den); break;
+            default: denh = mfma_bf16(af[j & 1][3], bdn[j & 1], denh); den = mfma_bf16(af[j & 1][3], bdl, den); break;
           }
           update_block(j, mf[j & 1]);
+        }
+        // phi . Zh over rows >= 1 for queries ct*16 + 4*lg + s (every lane
+        // holds it): the add-back factor, read when the chunk is normalised
+        if (li == 0) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) sG[b * kCH + (4 * lg + s) * 4 + ct] = denh[s];
         }
         // intra-chunk block: O^T += V^T P^T, normaliser P.1 for query tile ct
         u32x4 ph[4][2], pl[4][2];  // (query tile, key block) on or below the diagonal
@@ -1738,7 +1789,7 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
           // normalisers go to Dg
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            const float dq = den[s] + den0;
+            const float dq = denh[s] + den[s] + den0;
             if constexpr (C::UNN) {
               sRden[b * kCH + (4 * lg + s) * 4 + ct] = 1.0f;
               const int t = c0 + ct * 16 + 4 * lg + s;
@@ -1748,17 +1799,11 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
             }
           }
         }
-        // previous chunk: normalise and store (16 bytes per lane and query tile)
-        if (ci > 0) {
-          const f32x4 rd = *reinterpret_cast<const f32x4*>(sRden + (b ^ 1) * kCH + li * 4);
-#pragma unroll
-          for (int qt = 0; qt < 4; ++qt) {
-            float* ob = Og + ((size_t)bh * N + c0 - kCH + qt * 16 + li) * kDV + ct * 16 + 4 * lg;
-            store_nt(ob, nprev[qt] * rd[qt]);
-          }
-        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) nprev[q] = num[q];
+        // a_c of this lane's four output columns, as the shift took them
+#pragma unroll
+        for (int s = 0; s < 4; ++s) mprev[s] = __uint_as_float(col_mean(m0[s]) << 16);
       }
       if constexpr (!OUT) {
         // totals pass (hi + lo planes), state split by rows: consumer ct owns
@@ -1828,11 +1873,12 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
       const int lc0 = t_begin + (nch - 1) * kCH;
       const int nvalid = t_end - lc0;
       const f32x4 rd = *reinterpret_cast<const f32x4*>(sRden + ((nch - 1) & 1) * kCH + li * 4);
+      const f32x4 gq = *reinterpret_cast<const f32x4*>(sG + ((nch - 1) & 1) * kCH + li * 4);
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
         if (qt * 16 + li < nvalid) {
           float* ob = Og + ((size_t)bh * N + lc0 + qt * 16 + li) * kDV + ct * 16 + 4 * lg;
-          store_nt(ob, nprev[qt] * rd[qt]);
+          store_nt(ob, (nprev[qt] + mprev * gq[qt]) * rd[qt]);
         }
       }
     } else {

@@ -15,8 +15,9 @@
 //   1. stream_totals_kernel: the state of each span of kStL tokens (hi + lo
 //      bf16 mu, exact products, fp32 accumulation);
 //   2. stream_scan_kernel: exclusive prefix over spans, in place, rewritten
-//      as MFMA operand fragments (hi + lo bf16, 16 significant bits); the sum
-//      over all spans is the final state, written in feature order;
+//      as MFMA operand fragments (the prefix shifted by its column means,
+//      bf16; normaliser rows hi + lo bf16); the sum over all spans is the
+//      final state, written in feature order;
 //   3. stream_out_kernel: one workgroup per 128 queries.  Phase A is the
 //      in-span causal block, flash-style (S^T = K Q^T and O^T += V^T P^T on
 //      MFMA, P = K_n(S) in registers, hi + lo bf16 on the diagonal block);
@@ -61,7 +62,8 @@ struct StCfg {
   static constexpr int B_Q = kStQ * KS * 2, B_PHI = kStQ * PHS * 2;
   static constexpr int LDS_B = B_Q + 2 * B_PHI;             // phase B: Q tile, phi double-buffered
   static constexpr int OXS = kDV + 4;                       // exchange row stride (floats)
-  static constexpr int LDS_X = (kStQ * OXS + kStQ) * 4;     // exchange: numerators, normalisers
+  // exchange: numerators, normalisers, and the hi half of the normaliser readout
+  static constexpr int LDS_X = (kStQ * OXS + 2 * kStQ) * 4;
   static constexpr int LDS = LDS_A > LDS_B ? (LDS_A > LDS_X ? LDS_A : LDS_X) : (LDS_B > LDS_X ? LDS_B : LDS_X);
   static constexpr int KSEG = kStK * DK / 8, VSEG = kStK * kDV / 8, QSEG = kStQ * DK / 8;
   static constexpr int NKS = KSEG / 256, NVS = VSEG / 256, NQS = QSEG / 256;
@@ -74,10 +76,11 @@ struct StCfg {
 // totals pass writes it so).  The scan rewrites the 32 x 16 region of rows
 // 32j .. 32j+31 and columns 16ct .. 16ct+15 as the A operand of the readout
 // MFMA (S^T: lane (i, g) holds rows 32j + 8g .. 8g+7 of column 16ct + i),
-// hi plane then lo plane, 16 bytes per lane each: lane l's piece h sits in
-// row 32j + 16h + l/4 at columns 16ct + 4(l%4) .. +3.  Normaliser rows
-// 32j .. 32j+31 become eight hi bf16 then eight lo bf16 per group g of 8
-// rows (the same for every lane of the group).
+// 16 bytes per lane: lane l's piece sits in row 32j + l/4 at columns
+// 16ct + 4(l%4) .. +3 (piece h = 1, rows 32j + 16 .. 31, is unused; row 16
+// of block 0 holds the column means of the readout shift, in fp32).
+// Normaliser rows 32j .. 32j+31 become eight hi bf16 then eight lo bf16 per
+// group g of 8 rows (the same for every lane of the group).
 // ---------------------------------------------------------------------------
 __device__ inline size_t st_frag_off(int j, int ct, int l, int h) {
   return (size_t)(32 * j + 16 * h + (l >> 2)) * kDV + 16 * ct + 4 * (l & 3);
@@ -109,6 +112,10 @@ struct StTot {
   static constexpr int NKS = (KSEG + NW * 64 - 1) / (NW * 64), NVS = VSEG / (NW * 64);
   static constexpr int NRB = (StCfg<DK>::NKB + NW - 1) / NW;  // 256-row groups
   static constexpr int WP = NRB * NW * 32;                     // padded rows of a span state
+  // first row past the readout's blocks: a copy of row 0 and of its
+  // normaliser, which the scan rewrites nowhere (every scan workgroup reads it)
+  static constexpr int R0COPY = StCfg<DK>::NKB * 32;
+  static_assert(R0COPY < WP, "a spare row for the copy of row 0");
   static_assert(VSEG % (NW * 64) == 0, "V segments per thread");
 };
 
@@ -294,15 +301,36 @@ __global__ __launch_bounds__(256, 2) void stream_totals_kernel(const uint16_t* _
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) S[(size_t)row * kDV + 16 * ct + li] = st[tau][ct][e];
       if (li == 0) S[(size_t)C::WP * kDV + row] = dn[tau][e];
+      if (row == 0) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) S[(size_t)C::R0COPY * kDV + 16 * ct + li] = st[tau][ct][e];
+        if (li == 0) S[(size_t)C::WP * kDV + C::R0COPY] = dn[tau][e];
+      }
     }
 }
 
 // Exclusive scan over spans, in place, into fragments; final states (feature
 // order, plane layout), starting from `init` (plane layout, or null).  One
-// workgroup per (head, 32-row block), wave = column tile; wave 0's lanes 0-3
-// also take the block's normaliser rows.  Each lane reads the elements whose
-// fragment it writes, but at other addresses of the same region; every read
-// of a span completes before the wave's first write to it.
+// workgroup per (head, 32-row block), wave = column tile; lanes li == 0 of
+// wave 0 also write the block's normaliser fragments (group lg).
+//
+// The value fragment of each prefix is the state shifted by the running mean
+// of its column: with Z the normaliser rows, Zh their hi bf16 plane and a_c
+// the bf16 rounding of S[0][c] / Z[0] (0 when that is not finite), the
+// fragment holds S[r][c] - a_c Zh[r] rounded to bf16.  The readout adds
+// a_c (phi . Zh) back (the hi half of its normaliser readout), so
+//   phi . S = phi . (S - a Zh) + a (phi . Zh)
+// holds for any a_c, and rounding the fragment to bf16 moves an output by
+// about 2^-9 |v - a| rather than 2^-9 |v|.  a_c Zh[r] is exact in fp32 (two
+// bf16 factors), so the difference is one fp32 rounding of the exact value.
+// Every workgroup scans row 0 and Z[0] itself, from the copy the totals pass
+// leaves in row StTot::R0COPY (the same additions in the same order, so the
+// same a_c); block 0's writes a_c into row 16 of the span's region, which
+// the hi-only fragments leave free.
+// The workgroup reads the elements whose fragments it writes, at other
+// addresses of the same region (the normaliser rows by every wave); a
+// barrier after the reads of a group of spans orders them before the
+// group's writes.
 template <int DK>
 __global__ __launch_bounds__(256) void stream_scan_kernel(float* ws, int nspan, int WP, int BH, int W,
                                                           const float* init, float* states) {
@@ -310,63 +338,82 @@ __global__ __launch_bounds__(256) void stream_scan_kernel(float* ws, int nspan, 
   const int bh = blockIdx.x / C::NKB, j = blockIdx.x % C::NKB;
   const int lane = threadIdx.x & 63, ct = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const bool den_lane = ct == 0 && lane < 4;
+  const bool den_lane = ct == 0 && li == 0;
   const size_t per = (size_t)WP * (kDV + 1);
   float* base = ws + (size_t)bh * nspan * per;
   const int col = 16 * ct + li;
-  int ra[8], rd[8];
+  int ra[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    ra[u] = abi_row<DK>(32 * j + 8 * lg + u);
-    rd[u] = abi_row<DK>(32 * j + 8 * lane + u);
-  }
-  float run[8], rund[8];
+  for (int u = 0; u < 8; ++u) ra[u] = abi_row<DK>(32 * j + 8 * lg + u);
+  const int r0 = abi_row<DK>(0);
+  float run[8], runz[8], run0 = 0.f, runz0 = 0.f;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     run[u] = (init != nullptr && ra[u] >= 0) ? init[((size_t)bh * W + ra[u]) * kDV + col] : 0.f;
-    rund[u] = (init != nullptr && den_lane && rd[u] >= 0) ? init[(size_t)BH * W * kDV + (size_t)bh * W + rd[u]] : 0.f;
+    runz[u] = (init != nullptr && ra[u] >= 0) ? init[(size_t)BH * W * kDV + (size_t)bh * W + ra[u]] : 0.f;
+  }
+  if (init != nullptr) {
+    run0 = init[((size_t)bh * W + r0) * kDV + col];
+    runz0 = init[(size_t)BH * W * kDV + (size_t)bh * W + r0];
   }
   constexpr int G = 4;  // spans whose loads are in flight together
   for (int s0 = 0; s0 < nspan; s0 += G) {
-    float t[G][8], td[G][8];
+    float t[G][8], tz[G][8], t0[G], tz0[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       if (s0 + g < nspan) {
         const float* p = base + (size_t)(s0 + g) * per;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) t[g][u] = p[(size_t)(32 * j + 8 * lg + u) * kDV + col];
-        if (den_lane) {
-#pragma unroll
-          for (int u = 0; u < 8; ++u) td[g][u] = p[(size_t)WP * kDV + 32 * j + 8 * lane + u];
+        for (int u = 0; u < 8; ++u) {
+          t[g][u] = p[(size_t)(32 * j + 8 * lg + u) * kDV + col];
+          tz[g][u] = p[(size_t)WP * kDV + 32 * j + 8 * lg + u];
         }
+        t0[g] = p[(size_t)StTot<DK>::R0COPY * kDV + col];
+        tz0[g] = p[(size_t)WP * kDV + StTot<DK>::R0COPY];
       }
     }
-    // every read of these spans has returned before any fragment is written
+    // every read of these spans, by every wave, has returned before any
+    // fragment is written
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       if (s0 + g < nspan) {
         float* p = base + (size_t)(s0 + g) * per;
-        u32x4 hi, lo;
-        split_bf16x8(f32x4{run[0], run[1], run[2], run[3]}, f32x4{run[4], run[5], run[6], run[7]}, hi, lo);
-        *reinterpret_cast<u32x4*>(p + st_frag_off(j, ct, lane, 0)) = hi;
-        *reinterpret_cast<u32x4*>(p + st_frag_off(j, ct, lane, 1)) = lo;
+        u32x4 zhi, zlo;
+        split_bf16x8(f32x4{runz[0], runz[1], runz[2], runz[3]}, f32x4{runz[4], runz[5], runz[6], runz[7]}, zhi, zlo);
+        const float rz0 = runz0 > 0.f ? 1.0f / runz0 : 0.f;
+        uint32_t abits = pack_bf16x2(run0 * rz0, 0.f) & 0xFFFFu;
+        if ((abits & 0x7F80u) == 0x7F80u) abits = 0u;
+        const float a = __uint_as_float(abits << 16);
+        float sh[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) run[u] += t[g][u];
-        if (den_lane) {
-          split_bf16x8(f32x4{rund[0], rund[1], rund[2], rund[3]}, f32x4{rund[4], rund[5], rund[6], rund[7]}, hi, lo);
-          *reinterpret_cast<u32x4*>(p + st_den_off(WP, j, lane, 0)) = hi;
-          *reinterpret_cast<u32x4*>(p + st_den_off(WP, j, lane, 1)) = lo;
-#pragma unroll
-          for (int u = 0; u < 8; ++u) rund[u] += td[g][u];
+        for (int e = 0; e < 4; ++e) {
+          sh[2 * e] = __builtin_fmaf(-a, __uint_as_float(zhi[e] << 16), run[2 * e]);
+          sh[2 * e + 1] = __builtin_fmaf(-a, __uint_as_float(zhi[e] & 0xFFFF0000u), run[2 * e + 1]);
         }
+        *reinterpret_cast<u32x4*>(p + st_frag_off(j, ct, lane, 0)) =
+            u32x4{pack_bf16x2(sh[0], sh[1]), pack_bf16x2(sh[2], sh[3]), pack_bf16x2(sh[4], sh[5]),
+                  pack_bf16x2(sh[6], sh[7])};
+        if (j == 0 && lg == 0) p[16 * kDV + col] = a;
+        if (den_lane) {
+          *reinterpret_cast<u32x4*>(p + st_den_off(WP, j, lg, 0)) = zhi;
+          *reinterpret_cast<u32x4*>(p + st_den_off(WP, j, lg, 1)) = zlo;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          run[u] += t[g][u];
+          runz[u] += tz[g][u];
+        }
+        run0 += t0[g];
+        runz0 += tz0[g];
       }
     }
   }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     if (ra[u] >= 0) states[((size_t)bh * W + ra[u]) * kDV + col] = run[u];
-    if (den_lane && rd[u] >= 0) states[(size_t)BH * W * kDV + (size_t)bh * W + rd[u]] = rund[u];
+    if (den_lane && ra[u] >= 0) states[(size_t)BH * W * kDV + (size_t)bh * W + ra[u]] = runz[u];
   }
 }
 
@@ -529,12 +576,16 @@ __global__ __launch_bounds__(256, 3) void stream_out_kernel(const uint16_t* __re
 
   // ---------------- phase B: readout of the prefix state ----------------
   // wave w owns value columns 16w .. 16w+15 of all 128 queries (eight O^T
-  // tiles) and the normalisers of query tiles 2w, 2w+1
-  f32x4 nB[8], dB[2];
+  // tiles) and the normalisers of query tiles 2w, 2w+1, from the hi (dBh)
+  // and lo (dBl) planes of the normaliser rows.  The value fragments are the
+  // state shifted by a_c Zh (see stream_scan_kernel); a_c (phi . Zh) = a_c dBh
+  // is added back in the combine.
+  f32x4 nB[8], dBh[2], dBl[2];
 #pragma unroll
   for (int qt = 0; qt < 8; ++qt) nB[qt] = zero4();
-  dB[0] = dB[1] = zero4();
-  if (s > 0 || has_init) {
+  dBh[0] = dBh[1] = dBl[0] = dBl[1] = zero4();
+  const bool has_prefix = s > 0 || has_init;
+  if (has_prefix) {
     uint16_t* sQ = reinterpret_cast<uint16_t*>(lds);
     auto sPhi = [&](int buf) { return reinterpret_cast<uint16_t*>(lds + C::B_Q + buf * C::B_PHI); };
 #pragma unroll
@@ -581,43 +632,40 @@ __global__ __launch_bounds__(256, 3) void stream_out_kernel(const uint16_t* __re
       }
     };
     const float* S = ws + ((size_t)bh * nspan + s) * (size_t)WP * (kDV + 1);
-    auto load_s = [&](int j, u32x4& hi, u32x4& lo, u32x4& dhi, u32x4& dlo) {
-      hi = *reinterpret_cast<const u32x4*>(S + st_frag_off(j, w, lane, 0));
-      lo = *reinterpret_cast<const u32x4*>(S + st_frag_off(j, w, lane, 1));
+    auto load_s = [&](int j, u32x4& sf, u32x4& dhi, u32x4& dlo) {
+      sf = *reinterpret_cast<const u32x4*>(S + st_frag_off(j, w, lane, 0));
       dhi = *reinterpret_cast<const u32x4*>(S + st_den_off(WP, j, lg, 0));
       dlo = *reinterpret_cast<const u32x4*>(S + st_den_off(WP, j, lg, 1));
     };
-    u32x4 shi, slo, dhi, dlo;
-    load_s(0, shi, slo, dhi, dlo);
+    u32x4 sf, dhi, dlo;
+    load_s(0, sf, dhi, dlo);
     __syncthreads();  // Q tile staged
     gen(0, sPhi(0));
     __syncthreads();
     for (int j = 0; j < C::NKB; ++j) {
       const uint16_t* P = sPhi(j & 1);
       if (j + 1 < C::NKB) gen(j + 1, sPhi((j + 1) & 1));
-      u32x4 nhi, nlo, ndhi, ndlo;
-      if (j + 1 < C::NKB) load_s(j + 1, nhi, nlo, ndhi, ndlo);
+      u32x4 nsf, ndhi, ndlo;
+      if (j + 1 < C::NKB) load_s(j + 1, nsf, ndhi, ndlo);
       u32x4 af[8];
 #pragma unroll
       for (int qt = 0; qt < 8; ++qt)
         af[qt] = *reinterpret_cast<const u32x4*>(P + (qt * 16 + li) * C::PHS + 8 * lg);
 #pragma unroll
-      for (int qt = 0; qt < 8; ++qt) nB[qt] = mfma_bf16(shi, af[qt], nB[qt]);
-#pragma unroll
-      for (int qt = 0; qt < 8; ++qt) nB[qt] = mfma_bf16(slo, af[qt], nB[qt]);
+      for (int qt = 0; qt < 8; ++qt) nB[qt] = mfma_bf16(sf, af[qt], nB[qt]);
       // normalisers of query tiles 2w, 2w+1 (w is wave-uniform: a scalar branch)
       switch (w) {
-        case 0: dB[0] = mfma_bf16(dhi, af[0], dB[0]); dB[0] = mfma_bf16(dlo, af[0], dB[0]);
-                dB[1] = mfma_bf16(dhi, af[1], dB[1]); dB[1] = mfma_bf16(dlo, af[1], dB[1]); break;
-        case 1: dB[0] = mfma_bf16(dhi, af[2], dB[0]); dB[0] = mfma_bf16(dlo, af[2], dB[0]);
-                dB[1] = mfma_bf16(dhi, af[3], dB[1]); dB[1] = mfma_bf16(dlo, af[3], dB[1]); break;
-        case 2: dB[0] = mfma_bf16(dhi, af[4], dB[0]); dB[0] = mfma_bf16(dlo, af[4], dB[0]);
-                dB[1] = mfma_bf16(dhi, af[5], dB[1]); dB[1] = mfma_bf16(dlo, af[5], dB[1]); break;
-        default: dB[0] = mfma_bf16(dhi, af[6], dB[0]); dB[0] = mfma_bf16(dlo, af[6], dB[0]);
-                 dB[1] = mfma_bf16(dhi, af[7], dB[1]); dB[1] = mfma_bf16(dlo, af[7], dB[1]); break;
+        case 0: dBh[0] = mfma_bf16(dhi, af[0], dBh[0]); dBl[0] = mfma_bf16(dlo, af[0], dBl[0]);
+                dBh[1] = mfma_bf16(dhi, af[1], dBh[1]); dBl[1] = mfma_bf16(dlo, af[1], dBl[1]); break;
+        case 1: dBh[0] = mfma_bf16(dhi, af[2], dBh[0]); dBl[0] = mfma_bf16(dlo, af[2], dBl[0]);
+                dBh[1] = mfma_bf16(dhi, af[3], dBh[1]); dBl[1] = mfma_bf16(dlo, af[3], dBl[1]); break;
+        case 2: dBh[0] = mfma_bf16(dhi, af[4], dBh[0]); dBl[0] = mfma_bf16(dlo, af[4], dBl[0]);
+                dBh[1] = mfma_bf16(dhi, af[5], dBh[1]); dBl[1] = mfma_bf16(dlo, af[5], dBl[1]); break;
+        default: dBh[0] = mfma_bf16(dhi, af[6], dBh[0]); dBl[0] = mfma_bf16(dlo, af[6], dBl[0]);
+                 dBh[1] = mfma_bf16(dhi, af[7], dBh[1]); dBl[1] = mfma_bf16(dlo, af[7], dBl[1]); break;
       }
       if (j + 1 < C::NKB) {
-        shi = nhi; slo = nlo; dhi = ndhi; dlo = ndlo;
+        sf = nsf; dhi = ndhi; dlo = ndlo;
       }
       __syncthreads();
     }
@@ -626,13 +674,22 @@ __global__ __launch_bounds__(256, 3) void stream_out_kernel(const uint16_t* __re
   // ---------------- combine: phase B's tiles to the row split of phase A ----------------
   float* sX = reinterpret_cast<float*>(lds);
   float* sXd = sX + kStQ * C::OXS;
+  float* sXh = sXd + kStQ;
 #pragma unroll
   for (int qt = 0; qt < 8; ++qt)
     *reinterpret_cast<f32x4*>(sX + (qt * 16 + li) * C::OXS + 16 * w + 4 * lg) = nB[qt];
   if (lg == 0) {
-    sXd[(2 * w) * 16 + li] = dB[0].x;
-    sXd[(2 * w + 1) * 16 + li] = dB[1].x;
+    sXd[(2 * w) * 16 + li] = dBh[0].x + dBl[0].x;
+    sXd[(2 * w + 1) * 16 + li] = dBh[1].x + dBl[1].x;
+    sXh[(2 * w) * 16 + li] = dBh[0].x;
+    sXh[(2 * w + 1) * 16 + li] = dBh[1].x;
   }
+  // column means of the readout shift (0 without a prefix state)
+  f32x4 acol[4];
+  const float* Sa = ws + ((size_t)bh * nspan + s) * (size_t)WP * (kDV + 1) + 16 * kDV;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+    acol[ct] = has_prefix ? *reinterpret_cast<const f32x4*>(Sa + 16 * ct + 4 * lg) : zero4();
   __syncthreads();
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
@@ -641,10 +698,12 @@ __global__ __launch_bounds__(256, 3) void stream_out_kernel(const uint16_t* __re
     if (q >= N) continue;
     const float den = dA[qt].x + sXd[ql];
     const float r = UNN ? 1.0f : 1.0f / den;
+    const float dh = sXh[ql];
     float* orow = Og + ((size_t)bh * N + q) * kDV;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      const f32x4 num = oA[qt][ct] + *reinterpret_cast<const f32x4*>(sX + ql * C::OXS + 16 * ct + 4 * lg);
+      const f32x4 num =
+          oA[qt][ct] + *reinterpret_cast<const f32x4*>(sX + ql * C::OXS + 16 * ct + 4 * lg) + acol[ct] * dh;
       store_nt(orow + 16 * ct + 4 * lg, num * r);
     }
     if (UNN && lg == 0) Dg[(size_t)bh * N + q] = den;

@@ -644,9 +644,11 @@ __global__ __launch_bounds__(256, 3) void stream_out_kernel(const uint16_t* __re
     __syncthreads();
     for (int j = 0; j < C::NKB; ++j) {
       const uint16_t* P = sPhi(j & 1);
-      if (j + 1 < C::NKB) gen(j + 1, sPhi((j + 1) & 1));
+      // the next block's state fragments first: their latency runs under
+      // the generation of its phi rows and this block's MFMAs
       u32x4 nsf, ndhi, ndlo;
       if (j + 1 < C::NKB) load_s(j + 1, nsf, ndhi, ndlo);
+      if (j + 1 < C::NKB) gen(j + 1, sPhi((j + 1) & 1));
       u32x4 af[8];
 #pragma unroll
       for (int qt = 0; qt < 8; ++qt)

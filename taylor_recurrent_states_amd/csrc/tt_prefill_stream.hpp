@@ -1108,17 +1108,30 @@ struct StFT {
   static constexpr int W = rows_for(DK, NT);
   static constexpr int NRB = (W + 127) / 128;   // 128-row groups
   static constexpr int WP = NRB * 128;          // padded rows of a span state
-  static constexpr int KS = DK + 4;             // K tile row stride (16-byte rows)
+  static constexpr int KS = DK + 4;             // K tile row stride: coordinates, a ones and a zero column, pad
+  static constexpr int ONE = DK, ZERO = DK + 1; // the constant columns of the K tile
+  static constexpr int MAXM = NT - 1 > 1 ? NT - 1 : 1;  // factors per row (orders 0 .. NT-1)
   static constexpr int VS = kDV + 16;           // V tile row stride: rows 4 apart hit distinct bank groups
-  static constexpr int MS = 32 + 16;            // mu tile row stride (the same for the A reads)
-  static constexpr int B_K = kStK * KS * 4, B_V = kStK * VS * 4, B_MU = kStK * MS * 4;
-  static constexpr int LDS = B_K + B_V + 4 * B_MU;
+  static constexpr int B_K = kStK * KS * 4, B_V = kStK * VS * 4;
+  static constexpr int LDS = B_K + B_V;
   static constexpr int KSEG = kStK * DK / 4, VSEG = kStK * kDV / 4;
   static constexpr int NKS = (KSEG + 255) / 256, NVS = VSEG / 256;
 };
 
+// Span totals, fp32: one workgroup of 4 waves per (head, span, 128 feature
+// rows); wave w owns rows R0 = 128 rb + 32 w .. +31 as two 16-row tiles for
+// all 64 value columns.  The A operand of the 16x16x4 MFMA is built in place:
+// lane (i, g) holds row R0 + 16 rt + i of token 4t + g, the product of the
+// row's factors read from the staged K tile.  Each row has MAXM factor
+// columns: its coordinates, then the ones column (1 for tokens inside the
+// span, 0 past its end) for factors past its order; the order-0 row is all
+// ones columns and a padding row starts with the zero column.  So every row
+// costs MAXM LDS reads and MAXM - 1 multiplies, with no branch, in the same
+// left-to-right order as one factor at a time from 1.  The normaliser rows
+// are per-lane sums over the lane's tokens, added over the four token
+// residues at the end.
 template <int DK, int NT>
-__global__ __launch_bounds__(256, 2) void stream_totals_f32_kernel(const float* __restrict__ Kg,
+__global__ __launch_bounds__(256, 4) void stream_totals_f32_kernel(const float* __restrict__ Kg,
                                                                    const float* __restrict__ Vg, int BH, int N,
                                                                    int nspan, float* __restrict__ ws) {
   using C = StFT<DK, NT>;
@@ -1141,7 +1154,6 @@ __global__ __launch_bounds__(256, 2) void stream_totals_f32_kernel(const float* 
   const float* Vh = Vg + (size_t)bh * N * kDV;
   float* sK = reinterpret_cast<float*>(lds);
   float* sV = reinterpret_cast<float*>(lds + C::B_K);
-  float* sMu = reinterpret_cast<float*>(lds + C::B_K + C::B_V + w * C::B_MU);
 
   f32x4 rk[C::NKS], rv[C::NVS];
   auto issue = [&](int tb) {
@@ -1160,8 +1172,8 @@ __global__ __launch_bounds__(256, 2) void stream_totals_f32_kernel(const float* 
       rv[i] = *reinterpret_cast<const f32x4*>(Vh + (size_t)min(k0 + tok, t_end - 1) * kDV + part * 4);
     }
   };
-  // K rows of tokens past the span end are stored as zeros (their mu rows of
-  // order >= 1 vanish; the order-0 row is masked where it is built)
+  // K rows of tokens past the span end are stored as zeros, and their ones
+  // column as 0 (so every row of such a token is 0)
   auto commit = [&](int tb) {
     const int k0 = t_begin + tb * kStK;
 #pragma unroll
@@ -1172,6 +1184,10 @@ __global__ __launch_bounds__(256, 2) void stream_totals_f32_kernel(const float* 
         *reinterpret_cast<f32x4*>(sK + tok * C::KS + part * 4) = k0 + tok < t_end ? rk[i] : zero4();
       }
     }
+    if (tid < kStK) {
+      sK[tid * C::KS + C::ONE] = k0 + tid < t_end ? 1.f : 0.f;
+      sK[tid * C::KS + C::ZERO] = 0.f;
+    }
 #pragma unroll
     for (int i = 0; i < C::NVS; ++i) {
       const int seg = tid + 256 * i, tok = seg >> 4, part = seg & 15;
@@ -1179,18 +1195,27 @@ __global__ __launch_bounds__(256, 2) void stream_totals_f32_kernel(const float* 
     }
   };
 
+  // byte offsets in the K tile of this lane's factor columns, for token g
+  // (token 4t + g adds 16 t KS bytes, a compile-time offset)
   const auto& tab = RowsOf<DK>::get();
-  uint32_t code[32];
+  uint32_t foff[2][C::MAXM];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) code[i] = R0 + i < W ? tab.code[R0 + i] : kPadRow;
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = R0 + 16 * rt + li;
+    const uint32_t code = r < W ? tab.code[r] : kPadRow;
+    const int m = row_order(code);
+#pragma unroll
+    for (int l = 0; l < C::MAXM; ++l) {
+      const int col = m == 7 ? (l == 0 ? C::ZERO : C::ONE) : (l < m ? row_index<DK>(code, l) : C::ONE);
+      foff[rt][l] = (uint32_t)((lg * C::KS + col) * 4);
+    }
+  }
   f32x4 st[2][4];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) st[rt][ct] = zero4();
-  float dpart[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) dpart[i] = 0.f;
+  float zacc[2] = {0.f, 0.f};
 
   issue(0);
   for (int tb = 0; tb < ntb; ++tb) {
@@ -1198,40 +1223,7 @@ __global__ __launch_bounds__(256, 2) void stream_totals_f32_kernel(const float* 
     __syncthreads();
     if (tb + 1 < ntb) issue(tb + 1);
     if (active) {
-      const bool kvalid = t_begin + tb * kStK + lane < t_end;
-      const float* xr = sK + lane * C::KS;
-      float mu[32];
-      if constexpr (DK <= 16) {
-        float x[DK];
-#pragma unroll
-        for (int i = 0; i < DK / 4; ++i) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(xr + 4 * i);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * i + e] = v[e];
-        }
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const int m = row_order(code[i]);
-          float v = (m == 0 && !kvalid) || m == 7 ? 0.f : 1.f;
-          for (int l = 0; l < m && m < 7; ++l) v *= x[row_index<DK>(code[i], l)];
-          mu[i] = v;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const int m = row_order(code[i]);
-          float v = (m == 0 && !kvalid) || m == 7 ? 0.f : 1.f;
-          for (int l = 0; l < m && m < 7; ++l) v *= xr[row_index<DK>(code[i], l)];
-          mu[i] = v;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 32; ++i) dpart[i] += mu[i];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<f32x4*>(sMu + lane * C::MS + 4 * i) = f32x4{mu[4 * i], mu[4 * i + 1], mu[4 * i + 2], mu[4 * i + 3]};
-      // the tile is wave-private: this wave's LDS writes done, then its reads
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const unsigned char* Kb = reinterpret_cast<const unsigned char*>(sK);
 #pragma unroll
       for (int t = 0; t < kStK / 4; ++t) {
         float bv[4];
@@ -1239,7 +1231,10 @@ __global__ __launch_bounds__(256, 2) void stream_totals_f32_kernel(const float* 
         for (int ct = 0; ct < 4; ++ct) bv[ct] = sV[(4 * t + lg) * C::VS + 16 * ct + li];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          const float a = sMu[(4 * t + lg) * C::MS + 16 * rt + li];
+          float a = *reinterpret_cast<const float*>(Kb + foff[rt][0] + t * 16 * C::KS);
+#pragma unroll
+          for (int l = 1; l < C::MAXM; ++l) a *= *reinterpret_cast<const float*>(Kb + foff[rt][l] + t * 16 * C::KS);
+          zacc[rt] += a;
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct) st[rt][ct] = mfma_f32(a, bv[ct], st[rt][ct]);
         }
@@ -1257,13 +1252,13 @@ __global__ __launch_bounds__(256, 2) void stream_totals_f32_kernel(const float* 
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) S[(size_t)row * kDV + 16 * ct + li] = st[rt][ct][e];
     }
-  // normalisers: the sum of the lanes' partial sums
+  // normalisers: the lanes' partial sums over the four token residues
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float d = dpart[i];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) d += __shfl_xor(d, off);
-    if (lane == i) S[(size_t)C::WP * kDV + R0 + i] = d;
+  for (int rt = 0; rt < 2; ++rt) {
+    float z = zacc[rt];
+    z += __shfl_xor(z, 16);
+    z += __shfl_xor(z, 32);
+    if (lg == 0) S[(size_t)C::WP * kDV + R0 + 16 * rt + li] = z;
   }
 }
 

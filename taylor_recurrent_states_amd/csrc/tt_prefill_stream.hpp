@@ -806,11 +806,11 @@ __global__ __launch_bounds__(256) void stream_scan_f32_kernel(float* ws, int nsp
 }
 
 // Output pass for fp32 inputs: one workgroup of 4 waves per 128 queries of a
-// span; phase A (the span's causal block) and phase B (readout of the prefix
-// state) as in stream_out_kernel, on fp32 MFMA.  Lane layouts of f32
+// span, 3 workgroups per CU; phase A (the span's causal block) and phase B
+// (readout of the prefix state) as in stream_out_kernel, on fp32 MFMA.  Lane layouts of f32
 // 16x16x4: A[i][g], B[g][i]; D: lane holds D[4g + s][i].
 template <int DK, int NT, bool UNN>
-__global__ __launch_bounds__(256, 2) void stream_out_f32_kernel(const float* __restrict__ Qg,
+__global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __restrict__ Qg,
                                                                 const float* __restrict__ Kg,
                                                                 const float* __restrict__ Vg, int BH, int N,
                                                                 int nspan, int WP, const float* __restrict__ ws,
@@ -836,108 +836,9 @@ __global__ __launch_bounds__(256, 2) void stream_out_f32_kernel(const float* __r
   const float* Kh = Kg + (size_t)bh * N * DK;
   const float* Vh = Vg + (size_t)bh * N * kDV;
 
-  // ---------------- phase A: the span's causal block ----------------
-  const int qw0 = q0 + 32 * w;
-  float qf[2][KT];  // B operand of S^T = K Q^T: q[query][4t + g]
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-    for (int t = 0; t < KT; ++t) qf[qt][t] = Qh[(size_t)min(qw0 + 16 * qt + li, N - 1) * DK + 4 * t + lg];
-  f32x4 oA[2][4], dA[2];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    dA[qt] = zero4();
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) oA[qt][ct] = zero4();
-  }
-  {
-    auto sK = [&](int buf) { return reinterpret_cast<float*>(lds + buf * (C::B_K + C::B_V)); };
-    auto sV = [&](int buf) { return reinterpret_cast<float*>(lds + buf * (C::B_K + C::B_V) + C::B_K); };
-    const int kbeg = s * kStL;
-    const int kend = min(q0 + kStQ, N);
-    const int nkb = (kend - kbeg + kStK - 1) / kStK;
-    f32x4 rk[C::NKS], rv[C::NVS];
-    auto issue = [&](int kb) {
-      const int k0 = kbeg + kb * kStK;
-#pragma unroll
-      for (int i = 0; i < C::NKS; ++i) {
-        const int seg = tid + 256 * i;
-        if (seg < C::KSEG) {
-          const int tok = seg / (DK / 4), part = seg % (DK / 4);
-          rk[i] = *reinterpret_cast<const f32x4*>(Kh + (size_t)min(k0 + tok, N - 1) * DK + part * 4);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < C::NVS; ++i) {
-        const int seg = tid + 256 * i, tok = seg >> 4, part = seg & 15;
-        rv[i] = *reinterpret_cast<const f32x4*>(Vh + (size_t)min(k0 + tok, N - 1) * kDV + part * 4);
-      }
-    };
-    auto commit = [&](int buf) {
-      float* K = sK(buf);
-      float* V = sV(buf);
-#pragma unroll
-      for (int i = 0; i < C::NKS; ++i) {
-        const int seg = tid + 256 * i;
-        if (seg < C::KSEG) {
-          const int tok = seg / (DK / 4), part = seg % (DK / 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) K[tok * C::XS + part * 4 + e] = rk[i][e];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < C::NVS; ++i) {
-        const int seg = tid + 256 * i, tok = seg >> 4, part = seg & 15;
-        *reinterpret_cast<f32x4*>(V + tok * C::VS + part * 4) = rv[i];
-      }
-    };
-    issue(0);
-    commit(0);
-    __syncthreads();
-    for (int kb = 0; kb < nkb; ++kb) {
-      const int buf = kb & 1;
-      if (kb + 1 < nkb) issue(kb + 1);
-      const int k0 = kbeg + kb * kStK;
-      const float* K = sK(buf);
-      const float* V = sV(buf);
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int kt0 = k0 + 16 * kt;
-        if (kt0 > qw0 + 31) continue;             // every key of the tile is after this wave's queries
-        const bool diag = kt0 + 15 > qw0;         // keys after the wave's first query: mask
-        float p[2][4];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          f32x4 x = zero4();
-#pragma unroll
-          for (int t = 0; t < KT; ++t) x = mfma_f32(K[(16 * kt + li) * C::XS + 4 * t + lg], qf[qt][t], x);
-          const int query = qw0 + 16 * qt + li;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float v = taylor_poly<NT>(x[e]);
-            p[qt][e] = (diag && kt0 + 4 * lg + e > query) ? 0.f : v;
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dA[qt] = mfma_f32(1.0f, p[qt][e], dA[qt]);
-        }
-        // O^T += V^T P^T: K-slot g of step e is key kt0 + 4g + e
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float a = V[(16 * kt + 4 * lg + e) * C::VS + 16 * ct + li];
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) oA[qt][ct] = mfma_f32(a, p[qt][e], oA[qt][ct]);
-          }
-      }
-      if (kb + 1 < nkb) {
-        commit(buf ^ 1);
-        __syncthreads();
-      }
-    }
-  }
-  __syncthreads();
-
+  // Phase B (the prefix readout) runs first: phase A's accumulators are then
+  // not live across it, which keeps the kernel within 3 waves per SIMD.
+  // Phase B's last barrier orders its LDS reads before phase A's tiles.
   // ---------------- phase B: readout of the prefix state ----------------
   f32x4 nB[8], dB[2];
 #pragma unroll
@@ -1068,6 +969,108 @@ __global__ __launch_bounds__(256, 2) void stream_out_f32_kernel(const float* __r
       __syncthreads();
     }
   }
+
+  // ---------------- phase A: the span's causal block ----------------
+  const int qw0 = q0 + 32 * w;
+  float qf[2][KT];  // B operand of S^T = K Q^T: q[query][4t + g]
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int t = 0; t < KT; ++t) qf[qt][t] = Qh[(size_t)min(qw0 + 16 * qt + li, N - 1) * DK + 4 * t + lg];
+  f32x4 oA[2][4], dA[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    dA[qt] = zero4();
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) oA[qt][ct] = zero4();
+  }
+  {
+    auto sK = [&](int buf) { return reinterpret_cast<float*>(lds + buf * (C::B_K + C::B_V)); };
+    auto sV = [&](int buf) { return reinterpret_cast<float*>(lds + buf * (C::B_K + C::B_V) + C::B_K); };
+    const int kbeg = s * kStL;
+    const int kend = min(q0 + kStQ, N);
+    const int nkb = (kend - kbeg + kStK - 1) / kStK;
+    f32x4 rk[C::NKS], rv[C::NVS];
+    auto issue = [&](int kb) {
+      const int k0 = kbeg + kb * kStK;
+#pragma unroll
+      for (int i = 0; i < C::NKS; ++i) {
+        const int seg = tid + 256 * i;
+        if (seg < C::KSEG) {
+          const int tok = seg / (DK / 4), part = seg % (DK / 4);
+          rk[i] = *reinterpret_cast<const f32x4*>(Kh + (size_t)min(k0 + tok, N - 1) * DK + part * 4);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < C::NVS; ++i) {
+        const int seg = tid + 256 * i, tok = seg >> 4, part = seg & 15;
+        rv[i] = *reinterpret_cast<const f32x4*>(Vh + (size_t)min(k0 + tok, N - 1) * kDV + part * 4);
+      }
+    };
+    auto commit = [&](int buf) {
+      float* K = sK(buf);
+      float* V = sV(buf);
+#pragma unroll
+      for (int i = 0; i < C::NKS; ++i) {
+        const int seg = tid + 256 * i;
+        if (seg < C::KSEG) {
+          const int tok = seg / (DK / 4), part = seg % (DK / 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) K[tok * C::XS + part * 4 + e] = rk[i][e];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < C::NVS; ++i) {
+        const int seg = tid + 256 * i, tok = seg >> 4, part = seg & 15;
+        *reinterpret_cast<f32x4*>(V + tok * C::VS + part * 4) = rv[i];
+      }
+    };
+    issue(0);
+    commit(0);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int buf = kb & 1;
+      if (kb + 1 < nkb) issue(kb + 1);
+      const int k0 = kbeg + kb * kStK;
+      const float* K = sK(buf);
+      const float* V = sV(buf);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int kt0 = k0 + 16 * kt;
+        if (kt0 > qw0 + 31) continue;             // every key of the tile is after this wave's queries
+        const bool diag = kt0 + 15 > qw0;         // keys after the wave's first query: mask
+        float p[2][4];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          f32x4 x = zero4();
+#pragma unroll
+          for (int t = 0; t < KT; ++t) x = mfma_f32(K[(16 * kt + li) * C::XS + 4 * t + lg], qf[qt][t], x);
+          const int query = qw0 + 16 * qt + li;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = taylor_poly<NT>(x[e]);
+            p[qt][e] = (diag && kt0 + 4 * lg + e > query) ? 0.f : v;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dA[qt] = mfma_f32(1.0f, p[qt][e], dA[qt]);
+        }
+        // O^T += V^T P^T: K-slot g of step e is key kt0 + 4g + e
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float a = V[(16 * kt + 4 * lg + e) * C::VS + 16 * ct + li];
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) oA[qt][ct] = mfma_f32(a, p[qt][e], oA[qt][ct]);
+          }
+      }
+      if (kb + 1 < nkb) {
+        commit(buf ^ 1);
+        __syncthreads();
+      }
+    }
+  }
+  __syncthreads();
 
   // ---------------- combine ----------------
   float* sX = reinterpret_cast<float*>(lds);

@@ -63,7 +63,15 @@
 extern "C" {
 #endif
 
+/* Input dtype codes.  C++ sees the same enumeration with int as its fixed
+ * underlying type, so that any int a caller passes is a value of the type and
+ * a code other than these two is rejected (TT_ERR_INVALID_ARG) rather than
+ * undefined; the size and values are those of the C declaration. */
+#ifdef __cplusplus
+typedef enum tt_dtype_code : int { TT_F32 = 0, TT_BF16 = 1 } tt_dtype;
+#else
 typedef enum { TT_F32 = 0, TT_BF16 = 1 } tt_dtype;
+#endif
 
 enum {
   TT_OK = 0,

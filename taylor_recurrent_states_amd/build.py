@@ -1,12 +1,15 @@
 """Builds libtaylor_states.so in-tree with hipcc for gfx950.
 
     python -m taylor_recurrent_states_amd.build [-v] [--resource-usage]
+    python -m taylor_recurrent_states_amd.build --sanitize
 
 Every source is compiled on each call (this is the "does it build" check);
 objects go to ``_build/`` next to this file, the library next to this file.
 ``--resource-usage`` also prints, per kernel, the registers, scratch
 (spill) bytes, occupancy and LDS the compiler assigned (its
-kernel-resource-usage remarks).
+kernel-resource-usage remarks).  ``--sanitize`` builds the same library with
+its host code under AddressSanitizer and UndefinedBehaviorSanitizer (device
+code unchanged) into ``_build/sanitize/``; the ABI tests run against it.
 """
 
 from __future__ import annotations
@@ -79,6 +82,48 @@ def resource_usage():
     return out
 
 
+SAN_BUILD = os.path.join(BUILD, "sanitize")
+SAN_LIB = os.path.join(SAN_BUILD, "libtaylor_states_san.so")
+# sanitizers for the host side of each translation unit only (GPU code is not
+# built with them)
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The library with host-side ASan and UBSan, rebuilt only when a source
+    or header is newer than it.  Loading it needs the sanitizer runtime first
+    in the process (LD_PRELOAD of clang's libclang_rt.asan)."""
+    os.makedirs(SAN_BUILD, exist_ok=True)
+    deps = [os.path.join(CSRC, f) for f in os.listdir(CSRC)]
+    deps.append(os.path.join(os.path.dirname(PKG), "include", "taylor_states.h"))
+    if os.path.exists(SAN_LIB) and os.path.getmtime(SAN_LIB) > max(os.path.getmtime(d) for d in deps):
+        return SAN_LIB
+
+    def compile_one(src: str) -> str:
+        obj = os.path.join(SAN_BUILD, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *FLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    tmp = SAN_LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 def build(verbose: bool = False, resource: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)))
@@ -96,6 +141,9 @@ def build(verbose: bool = False, resource: bool = False) -> str:
 
 
 if __name__ == "__main__":
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+        sys.exit(0)
     lib = build(verbose="-v" in sys.argv, resource="--resource-usage" in sys.argv)
     if "--resource-usage" in sys.argv:
         print(f"{'source':15} {'vgpr':>4} {'agpr':>4} {'sgpr':>4} {'scratch':>7} {'occ':>3} {'lds':>6}  kernel")

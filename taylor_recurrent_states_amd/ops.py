@@ -22,7 +22,9 @@ import os
 from typing import Optional, Tuple
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libtaylor_states.so")
+# The in-tree library; TT_LIBRARY names another build of the same library
+# (the host-sanitizer build that the ABI tests also run against).
+LIB_PATH = os.environ.get("TT_LIBRARY") or os.path.join(_PKG, "libtaylor_states.so")
 
 TT_F32, TT_BF16 = 0, 1
 TT_OK, TT_ERR_INVALID_ARG, TT_ERR_UNSUPPORTED, TT_ERR_WORKSPACE, TT_ERR_HIP = 0, -1, -2, -3, -4

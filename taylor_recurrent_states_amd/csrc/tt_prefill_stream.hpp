@@ -856,59 +856,44 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
             *reinterpret_cast<const f32x4*>(Qh + (size_t)min(q0 + tok, N - 1) * DK + part * 4);
       }
     }
+    if (tid < kStQ) sQ[tid * C::QS + DK] = 1.f;  // the ones column
     // phi rows 32J + 8w .. +7 (a pair of 16-row blocks) of the 128 tokens
     // (lane = token, two passes); row codes and weights are wave-uniform.
-    // Narrow keys hold the token's coordinates in registers (indexed by a
-    // uniform row index); wider ones read them from the tile.
+    // Every row takes MAXM factors from the token's row of the Q tile: its
+    // coordinates, then the ones column past its order (all of them for the
+    // order-0 row and for padding rows, whose weight is 0), so there is no
+    // branch or loop per row; the products run left to right from the
+    // weight, as one factor at a time would.
+    constexpr int MAXM = NT - 1 > 1 ? NT - 1 : 1;
     const auto& tab = RowsOf<DK>::get();
     auto gen = [&](int J, float* P) {
-      uint32_t code[8];
+      int col[8][MAXM];
       float wt[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int r = 32 * J + 8 * w + u;
-        code[u] = r < W ? tab.code[r] : kPadRow;
+        const uint32_t code = r < W ? tab.code[r] : kPadRow;
+        const int m = row_order(code);
         wt[u] = r < W ? tab.weight[r] : 0.f;
+#pragma unroll
+        for (int l = 0; l < MAXM; ++l) col[u][l] = (m == 7 || l >= m) ? DK : row_index<DK>(code, l);
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int tok = 64 * h + lane;
         const float* xr = sQ + tok * C::QS;
-        if constexpr (DK <= 16) {
-          float x[DK];
 #pragma unroll
-          for (int i = 0; i < DK / 4; ++i) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(xr + 4 * i);
+        for (int g = 0; g < 2; ++g) {
+          f32x4 ph;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[4 * i + e] = v[e];
+          for (int e = 0; e < 4; ++e) {
+            const int u = 4 * g + e;
+            float v = wt[u];
+#pragma unroll
+            for (int l = 0; l < MAXM; ++l) v *= xr[col[u][l]];
+            ph[e] = v;
           }
-#pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            f32x4 ph;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int u = 4 * g + e;
-              const int m = row_order(code[u]);
-              float v = wt[u];
-              for (int l = 0; l < m && m < 7; ++l) v *= x[row_index<DK>(code[u], l)];
-              ph[e] = v;
-            }
-            *reinterpret_cast<f32x4*>(P + tok * C::PHS + 8 * w + 4 * g) = ph;
-          }
-        } else {
-#pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            f32x4 ph;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int u = 4 * g + e;
-              const int m = row_order(code[u]);
-              float v = wt[u];
-              for (int l = 0; l < m && m < 7; ++l) v *= xr[row_index<DK>(code[u], l)];
-              ph[e] = v;
-            }
-            *reinterpret_cast<f32x4*>(P + tok * C::PHS + 8 * w + 4 * g) = ph;
-          }
+          *reinterpret_cast<f32x4*>(P + tok * C::PHS + 8 * w + 4 * g) = ph;
         }
       }
     };

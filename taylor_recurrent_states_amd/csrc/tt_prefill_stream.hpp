@@ -727,7 +727,9 @@ struct StF {
   static constexpr int NKB = (W + 15) / 16;  // 16-row blocks of the readout
   static constexpr int NKP = (NKB + 1) / 2; // pairs of 16-row blocks: one phi tile and one barrier each
   static constexpr int XS = DK + 1;          // K tile row stride (floats; odd: column reads hit distinct banks)
-  static constexpr int QS = DK + 4;          // Q tile row stride (16-byte rows: a token's row in vector reads)
+  // Q tile row stride: the coordinates, then the ones column; odd, so that the
+  // 64 lanes (tokens) reading one column of their rows hit distinct banks
+  static constexpr int QS = DK + 1;
   static constexpr int VS = kDV + 4;         // V tile row stride
   static constexpr int PHS = 32 + 4;         // phi tile row stride: two 16-row blocks
   static constexpr int B_K = kStK * XS * 4, B_V = kStK * VS * 4;
@@ -852,8 +854,9 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
       const int seg = tid + 256 * i;
       if (seg < C::QSEG) {
         const int tok = seg / (DK / 4), part = seg % (DK / 4);
-        *reinterpret_cast<f32x4*>(sQ + tok * C::QS + part * 4) =
-            *reinterpret_cast<const f32x4*>(Qh + (size_t)min(q0 + tok, N - 1) * DK + part * 4);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(Qh + (size_t)min(q0 + tok, N - 1) * DK + part * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sQ[tok * C::QS + part * 4 + e] = x[e];  // odd stride: 4-byte stores
       }
     }
     if (tid < kStQ) sQ[tid * C::QS + DK] = 1.f;  // the ones column

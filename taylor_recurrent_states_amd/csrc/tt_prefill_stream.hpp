@@ -842,10 +842,10 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
   // not live across it, which keeps the kernel within 3 waves per SIMD.
   // Phase B's last barrier orders its LDS reads before phase A's tiles.
   // ---------------- phase B: readout of the prefix state ----------------
-  f32x4 nB[8], dB[2];
+  f32x4 nB[8];
+  float dp[2] = {0.f, 0.f};  // partial normaliser readouts (rows of this lane's group)
 #pragma unroll
   for (int qt = 0; qt < 8; ++qt) nB[qt] = zero4();
-  dB[0] = dB[1] = zero4();
   if (s > 0 || has_init) {
     float* sQ = reinterpret_cast<float*>(lds);
     auto sPhi = [&](int buf) { return reinterpret_cast<float*>(lds + C::B_Q + buf * C::B_PHI); };
@@ -931,22 +931,25 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
         for (int e = 0; e < 4; ++e)
 #pragma unroll
           for (int qt = 0; qt < 8; ++qt) nB[qt] = mfma_f32(sa[hf][e], af[qt][e], nB[qt]);
+        // normalisers of query tiles 2w, 2w+1: this lane's share (rows
+        // 4lg .. 4lg+3 of the block, query li) of phi . Z, on the VALU (an
+        // fp32 MFMA against broadcast rows would use one column in 16)
         switch (w) {
           case 0:
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[hf][e], af[0][e], dB[0]); dB[1] = mfma_f32(da[hf][e], af[1][e], dB[1]); }
+            for (int e = 0; e < 4; ++e) { dp[0] = __builtin_fmaf(da[hf][e], af[0][e], dp[0]); dp[1] = __builtin_fmaf(da[hf][e], af[1][e], dp[1]); }
             break;
           case 1:
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[hf][e], af[2][e], dB[0]); dB[1] = mfma_f32(da[hf][e], af[3][e], dB[1]); }
+            for (int e = 0; e < 4; ++e) { dp[0] = __builtin_fmaf(da[hf][e], af[2][e], dp[0]); dp[1] = __builtin_fmaf(da[hf][e], af[3][e], dp[1]); }
             break;
           case 2:
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[hf][e], af[4][e], dB[0]); dB[1] = mfma_f32(da[hf][e], af[5][e], dB[1]); }
+            for (int e = 0; e < 4; ++e) { dp[0] = __builtin_fmaf(da[hf][e], af[4][e], dp[0]); dp[1] = __builtin_fmaf(da[hf][e], af[5][e], dp[1]); }
             break;
           default:
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { dB[0] = mfma_f32(da[hf][e], af[6][e], dB[0]); dB[1] = mfma_f32(da[hf][e], af[7][e], dB[1]); }
+            for (int e = 0; e < 4; ++e) { dp[0] = __builtin_fmaf(da[hf][e], af[6][e], dp[0]); dp[1] = __builtin_fmaf(da[hf][e], af[7][e], dp[1]); }
             break;
         }
       }
@@ -1066,9 +1069,14 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
 #pragma unroll
   for (int qt = 0; qt < 8; ++qt)
     *reinterpret_cast<f32x4*>(sX + (qt * 16 + li) * C::OXS + 16 * w + 4 * lg) = nB[qt];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {  // add the four row groups' shares
+    dp[k] += __shfl_xor(dp[k], 16);
+    dp[k] += __shfl_xor(dp[k], 32);
+  }
   if (lg == 0) {
-    sXd[(2 * w) * 16 + li] = dB[0].x;
-    sXd[(2 * w + 1) * 16 + li] = dB[1].x;
+    sXd[(2 * w) * 16 + li] = dp[0];
+    sXd[(2 * w + 1) * 16 + li] = dp[1];
   }
   __syncthreads();
 #pragma unroll

@@ -968,10 +968,11 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
     for (int t = 0; t < KT; ++t) qf[qt][t] = Qh[(size_t)min(qw0 + 16 * qt + li, N - 1) * DK + 4 * t + lg];
-  f32x4 oA[2][4], dA[2];
+  f32x4 oA[2][4];
+  float da0[2];  // this lane's share (keys 4lg .. 4lg+3 of each tile) of P.1 for query li
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    dA[qt] = zero4();
+    da0[qt] = 0.f;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) oA[qt][ct] = zero4();
   }
@@ -1042,8 +1043,8 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
             const float v = taylor_poly<NT>(x[e]);
             p[qt][e] = (diag && kt0 + 4 * lg + e > query) ? 0.f : v;
           }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dA[qt] = mfma_f32(1.0f, p[qt][e], dA[qt]);
+          // normaliser on the VALU (an fp32 MFMA against ones would use one column in 16)
+          da0[qt] += (p[qt][0] + p[qt][1]) + (p[qt][2] + p[qt][3]);
         }
         // O^T += V^T P^T: K-slot g of step e is key kt0 + 4g + e
 #pragma unroll
@@ -1063,6 +1064,11 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
   }
   __syncthreads();
 
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {  // add the four key groups' shares
+    da0[qt] += __shfl_xor(da0[qt], 16);
+    da0[qt] += __shfl_xor(da0[qt], 32);
+  }
   // ---------------- combine ----------------
   float* sX = reinterpret_cast<float*>(lds);
   float* sXd = sX + kStQ * C::OXS;
@@ -1084,7 +1090,7 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
     const int ql = 32 * w + 16 * qt + li;
     const int q = q0 + ql;
     if (q >= N) continue;
-    const float den = dA[qt].x + sXd[ql];
+    const float den = da0[qt] + sXd[ql];
     const float r = UNN ? 1.0f : 1.0f / den;
     float* orow = Og + ((size_t)bh * N + q) * kDV;
 #pragma unroll

@@ -39,7 +39,9 @@ int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype
         }
       }
       if constexpr (use_stream_f32<DK, NT>()) {
-        if (dt == TT_F32) {  // large fp32 feature sets: the same, on fp32 MFMA
+        // large fp32 feature sets: the same, on fp32 MFMA; bf16 with dk = 16
+        // and n >= 4 too (inputs widened to fp32 as they are staged)
+        if (dt == TT_F32 || (dt == TT_BF16 && bf16_uses_stream_f32<DK, NT>())) {
           wp = StFT<DK, NT>::WP;
           ngroups = 1;
           nrg = StFT<DK, NT>::NRB;
@@ -111,7 +113,12 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype 
       if (dt == TT_BF16) return stream_launch<DK>(Q, K, V, BH, N, p, states_in, O, den_out, states, ws, s);
     }
     if constexpr (use_stream_f32<DK, NT>()) {
-      if (dt == TT_F32) return stream_launch_f32<DK, NT>(Q, K, V, BH, N, p, states_in, O, den_out, states, ws, s);
+      if (dt == TT_F32)
+        return stream_launch_f32<DK, NT, float>(Q, K, V, BH, N, p, states_in, O, den_out, states, ws, s);
+      if constexpr (bf16_uses_stream_f32<DK, NT>()) {
+        if (dt == TT_BF16)
+          return stream_launch_f32<DK, NT, uint16_t>(Q, K, V, BH, N, p, states_in, O, den_out, states, ws, s);
+      }
     }
     if constexpr (use_pipe<DK, NT>()) {
       if (dt == TT_BF16) {

@@ -721,6 +721,17 @@ __global__ __launch_bounds__(256, 3) void stream_out_kernel(const uint16_t* __re
 // holds rows 16j + 4g .. 4g+3 of column 16ct + i: one 16-byte load); the
 // normaliser rows are read in place.
 // ---------------------------------------------------------------------------
+// Four consecutive inputs, and one, as fp32: fp32 as stored, bf16 widened
+// (exact), so the fp32 kernels also take bf16 inputs.
+__device__ inline f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ inline f32x4 ld4f(const uint16_t* p) {
+  const uint2 r = *reinterpret_cast<const uint2*>(p);
+  return f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u), __uint_as_float(r.y << 16),
+               __uint_as_float(r.y & 0xFFFF0000u)};
+}
+__device__ inline float ld1f(const float* p) { return *p; }
+__device__ inline float ld1f(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+
 template <int DK, int NT>
 struct StF {
   static constexpr int W = rows_for(DK, NT);
@@ -811,10 +822,10 @@ __global__ __launch_bounds__(256) void stream_scan_f32_kernel(float* ws, int nsp
 // span, 3 workgroups per CU; phase A (the span's causal block) and phase B
 // (readout of the prefix state) as in stream_out_kernel, on fp32 MFMA.  Lane layouts of f32
 // 16x16x4: A[i][g], B[g][i]; D: lane holds D[4g + s][i].
-template <int DK, int NT, bool UNN>
-__global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __restrict__ Qg,
-                                                                const float* __restrict__ Kg,
-                                                                const float* __restrict__ Vg, int BH, int N,
+template <int DK, int NT, bool UNN, class TIn>
+__global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const TIn* __restrict__ Qg,
+                                                                const TIn* __restrict__ Kg,
+                                                                const TIn* __restrict__ Vg, int BH, int N,
                                                                 int nspan, int WP, const float* __restrict__ ws,
                                                                 bool has_init, float* __restrict__ Og,
                                                                 float* __restrict__ Dg) {
@@ -834,9 +845,9 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
   const int bh = sg / nspan, s = sg % nspan;
   const int q0 = s * kStL + tile * kStQ;
   if (q0 >= N) return;
-  const float* Qh = Qg + (size_t)bh * N * DK;
-  const float* Kh = Kg + (size_t)bh * N * DK;
-  const float* Vh = Vg + (size_t)bh * N * kDV;
+  const TIn* Qh = Qg + (size_t)bh * N * DK;
+  const TIn* Kh = Kg + (size_t)bh * N * DK;
+  const TIn* Vh = Vg + (size_t)bh * N * kDV;
 
   // Phase B (the prefix readout) runs first: phase A's accumulators are then
   // not live across it, which keeps the kernel within 3 waves per SIMD.
@@ -854,7 +865,7 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
       const int seg = tid + 256 * i;
       if (seg < C::QSEG) {
         const int tok = seg / (DK / 4), part = seg % (DK / 4);
-        const f32x4 x = *reinterpret_cast<const f32x4*>(Qh + (size_t)min(q0 + tok, N - 1) * DK + part * 4);
+        const f32x4 x = ld4f(Qh + (size_t)min(q0 + tok, N - 1) * DK + part * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sQ[tok * C::QS + part * 4 + e] = x[e];  // odd stride: 4-byte stores
       }
@@ -967,7 +978,7 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-    for (int t = 0; t < KT; ++t) qf[qt][t] = Qh[(size_t)min(qw0 + 16 * qt + li, N - 1) * DK + 4 * t + lg];
+    for (int t = 0; t < KT; ++t) qf[qt][t] = ld1f(Qh + (size_t)min(qw0 + 16 * qt + li, N - 1) * DK + 4 * t + lg);
   f32x4 oA[2][4];
   float da0[2];  // this lane's share (keys 4lg .. 4lg+3 of each tile) of P.1 for query li
 #pragma unroll
@@ -990,13 +1001,13 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const float* __r
         const int seg = tid + 256 * i;
         if (seg < C::KSEG) {
           const int tok = seg / (DK / 4), part = seg % (DK / 4);
-          rk[i] = *reinterpret_cast<const f32x4*>(Kh + (size_t)min(k0 + tok, N - 1) * DK + part * 4);
+          rk[i] = ld4f(Kh + (size_t)min(k0 + tok, N - 1) * DK + part * 4);
         }
       }
 #pragma unroll
       for (int i = 0; i < C::NVS; ++i) {
         const int seg = tid + 256 * i, tok = seg >> 4, part = seg & 15;
-        rv[i] = *reinterpret_cast<const f32x4*>(Vh + (size_t)min(k0 + tok, N - 1) * kDV + part * 4);
+        rv[i] = ld4f(Vh + (size_t)min(k0 + tok, N - 1) * kDV + part * 4);
       }
     };
     auto commit = [&](int buf) {
@@ -1135,9 +1146,9 @@ struct StFT {
 // left-to-right order as one factor at a time from 1.  The normaliser rows
 // are per-lane sums over the lane's tokens, added over the four token
 // residues at the end.
-template <int DK, int NT>
-__global__ __launch_bounds__(256, 4) void stream_totals_f32_kernel(const float* __restrict__ Kg,
-                                                                   const float* __restrict__ Vg, int BH, int N,
+template <int DK, int NT, class TIn>
+__global__ __launch_bounds__(256, 4) void stream_totals_f32_kernel(const TIn* __restrict__ Kg,
+                                                                   const TIn* __restrict__ Vg, int BH, int N,
                                                                    int nspan, float* __restrict__ ws) {
   using C = StFT<DK, NT>;
   constexpr int W = C::W;
@@ -1155,8 +1166,8 @@ __global__ __launch_bounds__(256, 4) void stream_totals_f32_kernel(const float* 
   const int ntb = (t_end - t_begin + kStK - 1) / kStK;
   const int R0 = 128 * rb + 32 * w;  // this wave's first row
   const bool active = R0 < W;        // wave-uniform
-  const float* Kh = Kg + (size_t)bh * N * DK;
-  const float* Vh = Vg + (size_t)bh * N * kDV;
+  const TIn* Kh = Kg + (size_t)bh * N * DK;
+  const TIn* Vh = Vg + (size_t)bh * N * kDV;
   float* sK = reinterpret_cast<float*>(lds);
   float* sV = reinterpret_cast<float*>(lds + C::B_K);
 
@@ -1168,13 +1179,13 @@ __global__ __launch_bounds__(256, 4) void stream_totals_f32_kernel(const float* 
       const int seg = tid + 256 * i;
       if (seg < C::KSEG) {
         const int tok = seg / (DK / 4), part = seg % (DK / 4);
-        rk[i] = *reinterpret_cast<const f32x4*>(Kh + (size_t)min(k0 + tok, t_end - 1) * DK + part * 4);
+        rk[i] = ld4f(Kh + (size_t)min(k0 + tok, t_end - 1) * DK + part * 4);
       }
     }
 #pragma unroll
     for (int i = 0; i < C::NVS; ++i) {
       const int seg = tid + 256 * i, tok = seg >> 4, part = seg & 15;
-      rv[i] = *reinterpret_cast<const f32x4*>(Vh + (size_t)min(k0 + tok, t_end - 1) * kDV + part * 4);
+      rv[i] = ld4f(Vh + (size_t)min(k0 + tok, t_end - 1) * kDV + part * 4);
     }
   };
   // K rows of tokens past the span end are stored as zeros, and their ones
@@ -1270,15 +1281,20 @@ __global__ __launch_bounds__(256, 4) void stream_totals_f32_kernel(const float* 
 template <int DK, int NT>
 constexpr bool use_stream_f32() { return StF<DK, NT>::W > 256; }
 
+// bf16 inputs with dk = 16 and 969 or 4,845 rows (n = 4, 5) run the same
+// kernels, widening their inputs to fp32 as they stage them
 template <int DK, int NT>
+constexpr bool bf16_uses_stream_f32() { return DK == 16 && NT >= 4; }
+
+template <int DK, int NT, class TIn>
 hipError_t stream_launch_f32(const void* Q, const void* K, const void* V, int BH, int N, const PrefillPlan& p,
                              const float* states_in, float* O, float* den_out, float* states, float* ws,
                              hipStream_t s) {
   using T = StFT<DK, NT>;
   static_assert(StF<DK, NT>::NKP * 32 <= T::WP, "the readout's row blocks (pairs) lie inside the span state");
   const unsigned sgs = (unsigned)((BH * p.nspan + 7) / 8 * 8);  // (head, span) pairs, padded to the 8 XCDs
-  hipLaunchKernelGGL((stream_totals_f32_kernel<DK, NT>), dim3(sgs * T::NRB), dim3(256), 0, s, (const float*)K,
-                     (const float*)V, BH, N, p.nspan, ws);
+  hipLaunchKernelGGL((stream_totals_f32_kernel<DK, NT, TIn>), dim3(sgs * T::NRB), dim3(256), 0, s, (const TIn*)K,
+                     (const TIn*)V, BH, N, p.nspan, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((stream_scan_f32_kernel<DK, NT>), dim3((unsigned)(BH * StF<DK, NT>::NKB)), dim3(256), 0, s, ws,
@@ -1287,12 +1303,12 @@ hipError_t stream_launch_f32(const void* Q, const void* K, const void* V, int BH
   if (e != hipSuccess) return e;
   const dim3 grid(sgs * kStT);
   if (den_out)
-    hipLaunchKernelGGL((stream_out_f32_kernel<DK, NT, true>), grid, dim3(256), 0, s, (const float*)Q,
-                       (const float*)K, (const float*)V, BH, N, p.nspan, (int)T::WP, (const float*)ws,
+    hipLaunchKernelGGL((stream_out_f32_kernel<DK, NT, true, TIn>), grid, dim3(256), 0, s, (const TIn*)Q,
+                       (const TIn*)K, (const TIn*)V, BH, N, p.nspan, (int)T::WP, (const float*)ws,
                        states_in != nullptr, O, den_out);
   else
-    hipLaunchKernelGGL((stream_out_f32_kernel<DK, NT, false>), grid, dim3(256), 0, s, (const float*)Q,
-                       (const float*)K, (const float*)V, BH, N, p.nspan, (int)T::WP, (const float*)ws,
+    hipLaunchKernelGGL((stream_out_f32_kernel<DK, NT, false, TIn>), grid, dim3(256), 0, s, (const TIn*)Q,
+                       (const TIn*)K, (const TIn*)V, BH, N, p.nspan, (int)T::WP, (const float*)ws,
                        states_in != nullptr, O, den_out);
   return hipGetLastError();
 }

@@ -217,10 +217,14 @@ def test_workspace_query_per_dtype():
             except ops.TTError as e:
                 assert e.code == ops.TT_ERR_UNSUPPORTED  # dk = 8 prefill is fp32 only
         assert per and max(per.values()) == both, (args, per, both)
-    # order 5 at dk 16: fp32 runs the streamed path, bf16 the sweep with row-group partials
+    # wide keys: bf16 keeps octet rows (more padded rows than fp32's feature order)
+    f = ops.tt_prefill_workspace_bytes_dtype(1, 16, 65536, 64, 64, 3, 64, "f32")
+    b = ops.tt_prefill_workspace_bytes_dtype(1, 16, 65536, 64, 64, 3, 64, "bf16")
+    assert f < b
+    # order 5 at dk 16: both dtypes run the fp32 streamed kernels, one workspace
     f = ops.tt_prefill_workspace_bytes_dtype(1, 16, 16384, 16, 64, 5, 64, "f32")
     b = ops.tt_prefill_workspace_bytes_dtype(1, 16, 16384, 16, 64, 5, 64, "bf16")
-    assert f < b
+    assert f == b
     with pytest.raises(ValueError):
         ops.tt_prefill_workspace_bytes_dtype(1, 1, 10, 16, 64, 3, 64, "f16")
     L = ops.lib()

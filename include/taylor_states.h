@@ -50,9 +50,15 @@
  *   - Outputs must not alias inputs unless stated.
  *   - Supported shapes: dv = 64; (dk, n) with dk in {8, 16, 32, 64}:
  *     dk=8: n in 1..6 (W up to 1287), dk=16: n in 1..5 (W up to 4845),
- *     dk=32 and dk=64: n in 1..3.  The dk = 8 prefill takes fp32 inputs
- *     (bf16 returns TT_ERR_UNSUPPORTED); its decode takes both.  Other
- *     shapes return TT_ERR_UNSUPPORTED.
+ *     dk=32 and dk=64: n in 1..5 (W up to 58905 and 814385; one head's
+ *     state at dk=64, n=5 is 212 MB).  The dk = 8 prefill takes fp32
+ *     inputs (bf16 returns TT_ERR_UNSUPPORTED); its decode takes both.
+ *     Other shapes return TT_ERR_UNSUPPORTED.
+ *   - dk = 32 and 64 with n = 4 or 5: the row codes of these shapes live in
+ *     a table that the library builds on a device the first time such a
+ *     shape runs there (a synchronous host-to-device copy of up to 3.3 MB,
+ *     kept until the process ends); a first call inside HIP graph capture
+ *     therefore fails, later ones do not copy.
  */
 #ifndef TAYLOR_STATES_H
 #define TAYLOR_STATES_H
@@ -121,9 +127,10 @@ int tt_prefill_workspace_bytes_dtype(int B, int H, int N, int dk, int dv, int n,
  *           bf16 inputs take 32, 64 or 128.  128 runs the shapes whose
  *           tiles fit the 160 KB of LDS of a CU: fp32 dk=8 n<=4, dk=16
  *           n<=3, dk=32 n=1; bf16 dk=16 n<=3, dk=32 n<=2, dk=64 n=1.
- *           Other values and combinations return TT_ERR_UNSUPPORTED.  64
- *           is the tuned default (bf16 with W <= 256 then runs the
- *           warp-specialised kernel).
+ *           dk=32 and dk=64 with n=4 or 5 take 64 only.  Other values
+ *           and combinations return TT_ERR_UNSUPPORTED.  64 is the tuned
+ *           default (bf16 with W <= 256 then runs the warp-specialised
+ *           kernel).
  * Q, K, V, O and workspace must be 16-byte aligned (TT_ERR_INVALID_ARG).
  * Any N >= 1 is accepted (the tail chunk is masked).  Results do not
  * depend on how the work is split beyond fp32 rounding. */

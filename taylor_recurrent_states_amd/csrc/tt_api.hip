@@ -36,7 +36,7 @@ static bool shape_supported(int dk, int dv, int n) {
   if (dv != 64 || n < 1) return false;
   if (dk == 8) return n <= 6;
   if (dk == 16) return n <= 5;
-  if (dk == 32 || dk == 64) return n <= 3;
+  if (dk == 32 || dk == 64) return n <= 5;
   return false;
 }
 
@@ -44,8 +44,7 @@ static int check_shape(int dk, int dv, int n) {
   if (dk < 1 || dv < 1 || n < 1) return fail(TT_ERR_INVALID_ARG, "dk=%d dv=%d n=%d must be >= 1", dk, dv, n);
   if (!shape_supported(dk, dv, n))
     return fail(TT_ERR_UNSUPPORTED,
-                "(dk=%d, dv=%d, n=%d) not compiled: dv must be 64; dk=8 with n<=6, dk=16 with n<=5, dk=32/64 "
-                "with n<=3",
+                "(dk=%d, dv=%d, n=%d) not compiled: dv must be 64; dk=8 with n<=6, dk=16, 32 or 64 with n<=5",
                 dk, dv, n);
   return TT_OK;
 }
@@ -186,6 +185,47 @@ static void* scratch_for_current_device(int* rc) {
   }
   *rc = TT_OK;
   return g_scratch_ptr[dev];
+}
+
+// Row codes of the widest shapes (dk = 32 and 64 with four or five terms:
+// up to 58,905 and 814,385 rows, too many for a compile-time table in every
+// kernel's code object): one table per key width and GPU, enumerated on the
+// host in feature order (enumerate_rows, the generator of the compile-time
+// tables), copied once per device on first use (a synchronous copy) and held
+// until the process ends.  Kernels get its device address as an argument.
+static __device__ uint32_t big_rows32[rows_for(32, 5)];
+static __device__ uint32_t big_rows64[rows_for(64, 5)];
+
+namespace {
+std::once_flag g_rows_once[2][kMaxDevices];
+const uint32_t* g_rows_ptr[2][kMaxDevices];
+hipError_t g_rows_err[2][kMaxDevices];
+}  // namespace
+
+hipError_t big_row_codes(int dk, int n, const uint32_t** out) {
+  *out = nullptr;
+  if (n <= max_terms(dk)) return hipSuccess;  // the compile-time tables serve
+  if ((dk != 32 && dk != 64) || n > 5) return hipErrorInvalidValue;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  const int w = dk == 32 ? 0 : 1;
+  std::call_once(g_rows_once[w][dev], [dk, w, dev] {
+    const int W = rows_for(dk, 5);
+    uint32_t* codes = new uint32_t[(size_t)W];
+    enumerate_rows(dk, 5, index_bits(dk), codes, nullptr);
+    void* p = nullptr;
+    hipError_t r = dk == 32 ? hipGetSymbolAddress(&p, HIP_SYMBOL(big_rows32))
+                            : hipGetSymbolAddress(&p, HIP_SYMBOL(big_rows64));
+    if (r == hipSuccess) r = hipMemcpy(p, codes, (size_t)W * sizeof(uint32_t), hipMemcpyHostToDevice);
+    delete[] codes;
+    g_rows_err[w][dev] = r;
+    g_rows_ptr[w][dev] = r == hipSuccess ? static_cast<const uint32_t*>(p) : nullptr;
+  });
+  if (g_rows_err[w][dev] != hipSuccess) return g_rows_err[w][dev];
+  *out = g_rows_ptr[w][dev];
+  return *out ? hipSuccess : hipErrorInvalidSymbol;
 }
 
 }  // namespace tt

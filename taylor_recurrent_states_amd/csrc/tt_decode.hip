@@ -34,18 +34,29 @@ constexpr int kDecodeThreads = 256;
 // stream their rows eight at a time.  Partial sums are reduced with wave
 // shuffles and one workgroup barrier; the order is fixed, so results are
 // bitwise reproducible.
+//
+// States of more than kDecodeLdsRows rows (dk = 32 and 64 with four or five
+// terms) do not fit mu and phi in LDS: the step then walks the rows in
+// chunks of kDecodeChunkRows, forming the chunk's features in LDS and
+// updating and reading out its rows before the next chunk.
+constexpr int kDecodeLdsRows = 8192;
+constexpr int kDecodeChunkRows = 4096;
+
 template <int DK, int N, typename TIn, bool NORM>
 __global__ __launch_bounds__(kDecodeThreads, 8) void decode_kernel(const TIn* __restrict__ q,
                                                                 const TIn* __restrict__ k,
                                                                 const TIn* __restrict__ v,
                                                                 float* __restrict__ num_plane,
                                                                 float* __restrict__ den_plane,
-                                                                float* __restrict__ o, float qscale) {
+                                                                float* __restrict__ o, float qscale,
+                                                                const uint32_t* __restrict__ big_rows) {
   constexpr int W = rows_for(DK, N);
+  constexpr bool CHUNKED = W > kDecodeLdsRows;
+  constexpr int LW = CHUNKED ? kDecodeChunkRows : W;  // feature rows held in LDS at a time
   constexpr int per = (W + 3) / 4;       // rows of the value plane per wave
   constexpr bool RES = per <= 48;        // all of a wave's rows held in registers
   __shared__ float s_q[DK], s_k[DK];
-  __shared__ float s_mu[W], s_phi[W];
+  __shared__ float s_mu[LW], s_phi[LW];
   __shared__ float s_red[4][kDV];
   __shared__ float s_den[4];
 
@@ -53,7 +64,7 @@ __global__ __launch_bounds__(kDecodeThreads, 8) void decode_kernel(const TIn* __
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const auto& tab = RowsOf<DK>::get();
+  const RowSrc<DK, N> tab{big_rows};
   float* __restrict__ S = num_plane + (size_t)bh * W * kDV;
   float* __restrict__ D = den_plane + (size_t)bh * W;
   const int r0 = wave * per;
@@ -97,16 +108,59 @@ __global__ __launch_bounds__(kDecodeThreads, 8) void decode_kernel(const TIn* __
     }
     load_state();
   }
+  float acc = 0.f, accd = 0.f;
+  if constexpr (CHUNKED) {
+    // chunk c covers rows [c0, c0 + cn); wave w updates its quarter of the
+    // chunk's value rows, thread tid the normaliser rows tid (mod 256)
+    for (int c0 = 0; c0 < W; c0 += LW) {
+      const int cn = min(LW, W - c0);
+      __syncthreads();  // q and k ready; the previous chunk's features read
+      for (int r = tid; r < cn; r += kDecodeThreads) {
+        const uint32_t code = tab.code(c0 + r);
+        s_mu[r] = monomial<DK>(code, [&](int i) { return s_k[i]; });
+        s_phi[r] = row_weight(code) * monomial<DK>(code, [&](int i) { return s_q[i]; });
+      }
+      __syncthreads();
+      // the readout of a chunk is summed on its own and then added, so that
+      // no fp32 accumulation chain runs over all rows
+      const int a0 = wave * (LW / 4), a1 = min(cn, a0 + LW / 4);
+      float accc = 0.f, accdc = 0.f;
+      int r = a0;
+      for (; r + 8 <= a1; r += 8) {
+        float sv8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sv8[u] = S[(size_t)(c0 + r + u) * kDV + lane];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          sv8[u] = fmaf(s_mu[r + u], vc, sv8[u]);
+          store_nt(&S[(size_t)(c0 + r + u) * kDV + lane], sv8[u]);
+          accc = fmaf(s_phi[r + u], sv8[u], accc);
+        }
+      }
+      for (; r < a1; ++r) {
+        float x = S[(size_t)(c0 + r) * kDV + lane];
+        x = fmaf(s_mu[r], vc, x);
+        store_nt(&S[(size_t)(c0 + r) * kDV + lane], x);
+        accc = fmaf(s_phi[r], x, accc);
+      }
+      for (int rr = tid; rr < cn; rr += kDecodeThreads) {
+        const float d = D[c0 + rr] + s_mu[rr];
+        store_nt(&D[c0 + rr], d);
+        accdc = fmaf(s_phi[rr], d, accdc);
+      }
+      acc += accc;
+      accd += accdc;
+    }
+  } else {
   __syncthreads();
   for (int r = tid; r < W; r += kDecodeThreads) {
-    const uint32_t code = tab.code[r];
+    const uint32_t code = tab.code(r);
     s_mu[r] = monomial<DK>(code, [&](int i) { return s_k[i]; });
-    s_phi[r] = tab.weight[r] * monomial<DK>(code, [&](int i) { return s_q[i]; });
+    s_phi[r] = tab.weight(r) * monomial<DK>(code, [&](int i) { return s_q[i]; });
   }
   __syncthreads();
 
   // value plane: wave w updates rows [r0, r1) and reads them out
-  float acc = 0.f;
   if constexpr (RES) {
 #pragma unroll
     for (int u = 0; u < per; ++u)
@@ -137,7 +191,6 @@ __global__ __launch_bounds__(kDecodeThreads, 8) void decode_kernel(const TIn* __
   }
 
   // normaliser plane
-  float accd = 0.f;
   if constexpr (RES) {
     if (tid < W) {
       const float d = dv + s_mu[tid];
@@ -151,6 +204,7 @@ __global__ __launch_bounds__(kDecodeThreads, 8) void decode_kernel(const TIn* __
       accd = fmaf(s_phi[rr], d, accd);
     }
   }
+  }  // CHUNKED
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) accd += __shfl_xor(accd, off);
   s_red[wave][lane] = acc;
@@ -163,18 +217,20 @@ __global__ __launch_bounds__(kDecodeThreads, 8) void decode_kernel(const TIn* __
   }
 }
 
-template <int DK, typename TIn>
+// NT: the number of terms of the row table (the compile-time table of DK,
+// or the run-time table `big_rows` for more terms than it holds).
+template <int DK, int NT, typename TIn>
 __global__ void feature_map_kernel(const TIn* __restrict__ x, size_t rows, int W, int weighted,
-                                   float* __restrict__ out) {
-  const auto& tab = RowsOf<DK>::get();
+                                   float* __restrict__ out, const uint32_t* __restrict__ big_rows) {
+  const RowSrc<DK, NT> tab{big_rows};
   const size_t total = rows * (size_t)W;
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
        e += (size_t)gridDim.x * blockDim.x) {
     const size_t row = e / W;
     const int t = (int)(e - row * W);
-    const uint32_t code = tab.code[t];
+    const uint32_t code = tab.code(t);
     float val = monomial<DK>(code, [&](int i) { return load_f32(x, row * DK + i); });
-    if (weighted) val *= tab.weight[t];
+    if (weighted) val *= tab.weight(t);
     out[e] = val;
   }
 }
@@ -270,12 +326,15 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, tt_dtype d
   const int W = rows_for(dk, n);
   float* num = states;
   float* den = states + (size_t)BH * W * kDV;
+  const uint32_t* big = nullptr;
+  const hipError_t eb = big_row_codes(dk, n, &big);
+  if (eb != hipSuccess) return eb;
   return with_dkn(dk, n, [&](auto DKc, auto Nc) {
     constexpr int DK = decltype(DKc)::value, N = decltype(Nc)::value;
     auto go = [&](auto Tc, auto NORMc) {
       using T = decltype(Tc);
       hipLaunchKernelGGL((decode_kernel<DK, N, T, decltype(NORMc)::value>), dim3(BH), dim3(kDecodeThreads), 0, s,
-                         (const T*)q, (const T*)k, (const T*)v, num, den, o, qscale);
+                         (const T*)q, (const T*)k, (const T*)v, num, den, o, qscale, big);
     };
     using yes = std::integral_constant<bool, true>;
     using no = std::integral_constant<bool, false>;
@@ -315,18 +374,25 @@ hipError_t launch_feature_map(const void* x, tt_dtype dt, size_t rows, int dk, i
   const int W = rows_for(dk, n);
   const unsigned block = 256;
   const unsigned grid = grid_for(rows * (size_t)W, block);
-#define TT_FEAT(DK, T) \
-  hipLaunchKernelGGL((feature_map_kernel<DK, T>), dim3(grid), dim3(block), 0, s, (const T*)x, rows, W, weighted, out)
+  const uint32_t* big = nullptr;
+  const hipError_t eb = big_row_codes(dk, n, &big);
+  if (eb != hipSuccess) return eb;
+#define TT_FEAT(DK, NT, T)                                                                                   \
+  hipLaunchKernelGGL((feature_map_kernel<DK, NT, T>), dim3(grid), dim3(block), 0, s, (const T*)x, rows, W, \
+                     weighted, out, big)
+  // the compile-time table of a key width serves every n up to its terms;
+  // dk = 32 and 64 with more terms read the run-time table
+  const bool rt = big != nullptr;
   if (dt == TT_F32) {
-    if (dk == 8) TT_FEAT(8, float);
-    else if (dk == 16) TT_FEAT(16, float);
-    else if (dk == 32) TT_FEAT(32, float);
-    else TT_FEAT(64, float);
+    if (dk == 8) TT_FEAT(8, 6, float);
+    else if (dk == 16) TT_FEAT(16, 5, float);
+    else if (dk == 32) { if (rt) TT_FEAT(32, 5, float); else TT_FEAT(32, 3, float); }
+    else { if (rt) TT_FEAT(64, 5, float); else TT_FEAT(64, 3, float); }
   } else {
-    if (dk == 8) TT_FEAT(8, uint16_t);
-    else if (dk == 16) TT_FEAT(16, uint16_t);
-    else if (dk == 32) TT_FEAT(32, uint16_t);
-    else TT_FEAT(64, uint16_t);
+    if (dk == 8) TT_FEAT(8, 6, uint16_t);
+    else if (dk == 16) TT_FEAT(16, 5, uint16_t);
+    else if (dk == 32) { if (rt) TT_FEAT(32, 5, uint16_t); else TT_FEAT(32, 3, uint16_t); }
+    else { if (rt) TT_FEAT(64, 5, uint16_t); else TT_FEAT(64, 3, uint16_t); }
   }
 #undef TT_FEAT
   return hipGetLastError();

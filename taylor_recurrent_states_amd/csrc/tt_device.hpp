@@ -41,10 +41,58 @@ constexpr int rows_for(int dk, int n) { return binom(dk + n - 1, n - 1); }
 // each key width (the largest order is max_terms - 1)
 constexpr int index_bits(int dk) { return dk <= 8 ? 3 : dk <= 16 ? 4 : dk <= 32 ? 5 : 6; }
 constexpr int max_terms(int dk) { return dk <= 8 ? 6 : dk <= 16 ? 5 : 3; }
-static_assert(index_bits(8) * 5 <= 24 && index_bits(16) * 4 <= 24 && index_bits(64) * 2 <= 24, "code fields");
+// Terms compiled for each key width, counting the widest shapes (dk = 32 and
+// 64 with four or five terms: 6,545 to 814,385 rows), whose row codes live in
+// a table built once per device at run time instead of a compile-time table.
+constexpr int max_terms_all(int dk) { return dk <= 8 ? 6 : 5; }
+template <int DK, int NT>
+constexpr bool runtime_rows() { return NT > max_terms(DK); }
+static_assert(index_bits(8) * 5 <= 24 && index_bits(16) * 4 <= 24 && index_bits(64) * 4 <= 24, "code fields");
 
 constexpr uint32_t weight_index(int denom) {
   return denom == 1 ? 0u : denom == 2 ? 1u : denom == 4 ? 2u : denom == 6 ? 3u : denom == 12 ? 4u : denom == 24 ? 5u : 6u;
+}
+
+// Row codes of all feature rows of orders 0 .. nmax-1 for key width dk, in
+// feature order: m-blocks ascending, inside a block the non-decreasing index
+// tuples in lexicographic order.  A code holds the order m (bits 24-26), the
+// m indices (ib bits each from bit 0) and the weight index of 1/alpha(t)!
+// (bits 27-29); `weight` (may be null) receives 1/alpha(t)!.  Used at compile
+// time for the tables below and on the host for the run-time tables of the
+// widest shapes.  Returns the number of rows written.
+constexpr int enumerate_rows(int dk, int nmax, int ib, uint32_t* code, float* weight) {
+  int r = 0;
+  for (int m = 0; m < nmax; ++m) {
+    int t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    bool more = true;
+    while (more) {
+      uint32_t c = (uint32_t)m << 24;
+      for (int l = 0; l < m; ++l) c |= (uint32_t)t[l] << (ib * l);
+      // 1 / prod over runs of equal indices of (run length)!
+      int denom = 1, run = 1;
+      for (int l = 1; l <= m; ++l) {
+        if (l < m && t[l] == t[l - 1]) {
+          ++run;
+        } else {
+          for (int f = 2; f <= run; ++f) denom *= f;
+          run = 1;
+        }
+      }
+      code[r] = c | (weight_index(denom) << 27);
+      if (weight != nullptr) weight[r] = 1.0f / (float)denom;
+      ++r;
+      // next non-decreasing tuple in lexicographic order
+      int i = m - 1;
+      while (i >= 0 && t[i] == dk - 1) --i;
+      if (i < 0) {
+        more = false;
+      } else {
+        ++t[i];
+        for (int j = i + 1; j < m; ++j) t[j] = t[i];
+      }
+    }
+  }
+  return r;
 }
 
 template <int DK, int NMAX>
@@ -53,39 +101,7 @@ struct RowTable {
   static constexpr int IB = index_bits(DK);
   uint32_t code[W];
   float weight[W];
-  constexpr RowTable() : code(), weight() {
-    int r = 0;
-    for (int m = 0; m < NMAX; ++m) {
-      int t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      bool more = true;
-      while (more) {
-        uint32_t c = (uint32_t)m << 24;
-        for (int l = 0; l < m; ++l) c |= (uint32_t)t[l] << (IB * l);
-        // 1 / prod over runs of equal indices of (run length)!
-        int denom = 1, run = 1;
-        for (int l = 1; l <= m; ++l) {
-          if (l < m && t[l] == t[l - 1]) {
-            ++run;
-          } else {
-            for (int f = 2; f <= run; ++f) denom *= f;
-            run = 1;
-          }
-        }
-        code[r] = c | (weight_index(denom) << 27);
-        weight[r] = 1.0f / (float)denom;
-        ++r;
-        // next non-decreasing tuple in lexicographic order
-        int i = m - 1;
-        while (i >= 0 && t[i] == DK - 1) --i;
-        if (i < 0) {
-          more = false;
-        } else {
-          ++t[i];
-          for (int j = i + 1; j < m; ++j) t[j] = t[i];
-        }
-      }
-    }
-  }
+  constexpr RowTable() : code(), weight() { enumerate_rows(DK, NMAX, IB, code, weight); }
 };
 
 static_assert(rows_for(16, 3) == 153, "W(16,3)");
@@ -105,6 +121,18 @@ template <> struct RowsOf<16> { static __device__ const RowTable<16, 5>& get() {
 template <> struct RowsOf<32> { static __device__ const RowTable<32, 3>& get() { return kRows32; } };
 template <> struct RowsOf<64> { static __device__ const RowTable<64, 3>& get() { return kRows64; } };
 
+// Row codes and weights of a (DK, NT) shape: the compile-time table, or for
+// the widest shapes the run-time table `big` (weights from the codes).
+template <int DK, int NT>
+struct RowSrc {
+  const uint32_t* big;
+  __device__ uint32_t code(int r) const {
+    if constexpr (runtime_rows<DK, NT>()) return big[r];
+    else return RowsOf<DK>::get().code[r];
+  }
+  __device__ float weight(int r) const;
+};
+
 __host__ __device__ constexpr int row_order(uint32_t code) { return (int)((code >> 24) & 7u); }
 // index l of a row code of key width DK
 template <int DK>
@@ -121,6 +149,12 @@ __host__ __device__ constexpr float row_weight(uint32_t code) {
 constexpr uint32_t kPadRow = 7u << 24;
 template <int DK>
 __device__ inline int row_index(uint32_t code, int l) { return row_index_c<DK>(code, l); }
+
+template <int DK, int NT>
+__device__ inline float RowSrc<DK, NT>::weight(int r) const {
+  if constexpr (runtime_rows<DK, NT>()) return row_weight(big[r]);
+  else return RowsOf<DK>::get().weight[r];
+}
 
 // mu_t(x) for a row code of key width DK, reading coordinates through `get(i)`.
 template <int DK, typename Get>
@@ -314,8 +348,8 @@ inline hipError_t with_dkn(int dk, int n, Fn&& fn) {
   if (dk == D && n == NN) return fn(integral_constant<int, D>{}, integral_constant<int, NN>{});
   TT_CASE(8, 1) TT_CASE(8, 2) TT_CASE(8, 3) TT_CASE(8, 4) TT_CASE(8, 5) TT_CASE(8, 6)
   TT_CASE(16, 1) TT_CASE(16, 2) TT_CASE(16, 3) TT_CASE(16, 4) TT_CASE(16, 5)
-  TT_CASE(32, 1) TT_CASE(32, 2) TT_CASE(32, 3)
-  TT_CASE(64, 1) TT_CASE(64, 2) TT_CASE(64, 3)
+  TT_CASE(32, 1) TT_CASE(32, 2) TT_CASE(32, 3) TT_CASE(32, 4) TT_CASE(32, 5)
+  TT_CASE(64, 1) TT_CASE(64, 2) TT_CASE(64, 3) TT_CASE(64, 4) TT_CASE(64, 5)
 #undef TT_CASE
   return hipErrorInvalidValue;
 }

@@ -12,6 +12,12 @@ namespace tt {
 // Records a message for tt_last_error() and returns `code`.
 int fail(int code, const char* fmt, ...);
 
+// Device address of the run-time row-code table of (dk, n) when n exceeds the
+// compile-time tables of dk (dk = 32 or 64 with n = 4 or 5; built on the
+// current device on first use), else null.  Every launcher of such a shape
+// passes it to its kernels.
+hipError_t big_row_codes(int dk, int n, const uint32_t** out);
+
 // Launchers (argument checking is done by the C entry points).
 hipError_t launch_feature_map(const void* x, tt_dtype dt, size_t rows, int dk, int n, int weighted,
                               float* out, hipStream_t s);

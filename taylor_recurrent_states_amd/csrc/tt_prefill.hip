@@ -23,6 +23,9 @@ int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype
   if (dt == TT_BF16 && dk < 16) return fail(TT_ERR_UNSUPPORTED, "dk=%d prefill takes fp32 inputs only", dk);
   if (dt == TT_BF16 && chunk < 32)
     return fail(TT_ERR_UNSUPPORTED, "chunk=%d with bf16 inputs (32, 64 or 128: token blocks of 32)", chunk);
+  if (dk >= 32 && n >= 4 && chunk != 64)
+    return fail(TT_ERR_UNSUPPORTED, "chunk=%d with dk=%d, n=%d (these shapes run the streamed path: chunk 64)",
+                chunk, dk, n);
   int wp = 0, ngroups = 0, nrg = 1, wg_per_cu = 2;
   bool stream = false;
   hipError_t e = hipSuccess;

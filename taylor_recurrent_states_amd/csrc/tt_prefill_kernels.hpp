@@ -2077,14 +2077,18 @@ hipError_t sweep_shape(int dk, int n, tt_dtype dt, int* wp, int* ngroups, int* n
         return hipSuccess;
       }
     };
-    if (dt == TT_BF16) {
-      if constexpr (DK < 16 || CH < 32 || (CH == 64 && use_pipe<DK, NT>())) {
-        return hipErrorInvalidValue;
-      } else {
-        return fill(uint16_t{});
+    if constexpr (runtime_rows<DK, NT>()) {
+      return hipErrorInvalidValue;  // the widest shapes take the streamed path only
+    } else {
+      if (dt == TT_BF16) {
+        if constexpr (DK < 16 || CH < 32 || (CH == 64 && use_pipe<DK, NT>())) {
+          return hipErrorInvalidValue;
+        } else {
+          return fill(uint16_t{});
+        }
       }
+      return fill(float{});
     }
-    return fill(float{});
   });
 }
 
@@ -2119,14 +2123,18 @@ hipError_t sweep_launch(const void* Q, const void* K, const void* V, tt_dtype dt
         return hipGetLastError();
       }
     };
-    if (dt == TT_BF16) {
-      if constexpr (DK < 16 || CH < 32 || (CH == 64 && use_pipe<DK, NT>())) {
-        return hipErrorInvalidValue;
-      } else {
-        return go(uint16_t{});
+    if constexpr (runtime_rows<DK, NT>()) {
+      return hipErrorInvalidValue;  // the widest shapes take the streamed path only
+    } else {
+      if (dt == TT_BF16) {
+        if constexpr (DK < 16 || CH < 32 || (CH == 64 && use_pipe<DK, NT>())) {
+          return hipErrorInvalidValue;
+        } else {
+          return go(uint16_t{});
+        }
       }
+      return go(float{});
     }
-    return go(float{});
   });
 }
 

@@ -828,7 +828,8 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const TIn* __res
                                                                 const TIn* __restrict__ Vg, int BH, int N,
                                                                 int nspan, int WP, const float* __restrict__ ws,
                                                                 bool has_init, float* __restrict__ Og,
-                                                                float* __restrict__ Dg) {
+                                                                float* __restrict__ Dg,
+                                                                const uint32_t* __restrict__ big_rows) {
   using C = StF<DK, NT>;
   constexpr int W = C::W;
   constexpr int KT = DK / 4;  // K-steps of the scores
@@ -879,16 +880,16 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const TIn* __res
     // branch or loop per row; the products run left to right from the
     // weight, as one factor at a time would.
     constexpr int MAXM = NT - 1 > 1 ? NT - 1 : 1;
-    const auto& tab = RowsOf<DK>::get();
+    const RowSrc<DK, NT> tab{big_rows};
     auto gen = [&](int J, float* P) {
       int col[8][MAXM];
       float wt[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int r = 32 * J + 8 * w + u;
-        const uint32_t code = r < W ? tab.code[r] : kPadRow;
+        const uint32_t code = r < W ? tab.code(r) : kPadRow;
         const int m = row_order(code);
-        wt[u] = r < W ? tab.weight[r] : 0.f;
+        wt[u] = r < W ? tab.weight(r) : 0.f;
 #pragma unroll
         for (int l = 0; l < MAXM; ++l) col[u][l] = (m == 7 || l >= m) ? DK : row_index<DK>(code, l);
       }
@@ -918,6 +919,15 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const TIn* __res
     };
     // block j = 2J + half of the pair; blocks past NKB hold zero phi rows and
     // read the zero-padded state rows of the same span (j < WP / 16)
+    // The widest shapes (tens of thousands of rows) sum the readout in
+    // segments of kSeg pairs, added into nT and dT, so that no fp32
+    // accumulation chain is longer than a segment plus the segment count.
+    constexpr bool SEG = runtime_rows<DK, NT>();
+    constexpr int kSeg = 128;
+    f32x4 nT[SEG ? 8 : 1];
+    float dT[2] = {0.f, 0.f};
+#pragma unroll
+    for (int qt = 0; qt < (SEG ? 8 : 1); ++qt) nT[qt] = zero4();
     f32x4 sa[2], da[2];
     load_s(0, sa[0], da[0]);
     load_s(1, sa[1], da[1]);
@@ -968,7 +978,25 @@ __global__ __launch_bounds__(256, 3) void stream_out_f32_kernel(const TIn* __res
         sa[0] = na[0]; sa[1] = na[1];
         da[0] = nd[0]; da[1] = nd[1];
       }
+      if constexpr (SEG) {
+        if ((J + 1) % kSeg == 0 || J + 1 == C::NKP) {
+#pragma unroll
+          for (int qt = 0; qt < 8; ++qt) {
+            nT[qt] += nB[qt];
+            nB[qt] = zero4();
+          }
+          dT[0] += dp[0];
+          dT[1] += dp[1];
+          dp[0] = dp[1] = 0.f;
+        }
+      }
       __syncthreads();
+    }
+    if constexpr (SEG) {
+#pragma unroll
+      for (int qt = 0; qt < 8; ++qt) nB[qt] = nT[qt];
+      dp[0] = dT[0];
+      dp[1] = dT[1];
     }
   }
 
@@ -1149,7 +1177,8 @@ struct StFT {
 template <int DK, int NT, class TIn>
 __global__ __launch_bounds__(256, 4) void stream_totals_f32_kernel(const TIn* __restrict__ Kg,
                                                                    const TIn* __restrict__ Vg, int BH, int N,
-                                                                   int nspan, float* __restrict__ ws) {
+                                                                   int nspan, float* __restrict__ ws,
+                                                                   const uint32_t* __restrict__ big_rows) {
   using C = StFT<DK, NT>;
   constexpr int W = C::W;
   __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS];
@@ -1213,12 +1242,12 @@ __global__ __launch_bounds__(256, 4) void stream_totals_f32_kernel(const TIn* __
 
   // byte offsets in the K tile of this lane's factor columns, for token g
   // (token 4t + g adds 16 t KS bytes, a compile-time offset)
-  const auto& tab = RowsOf<DK>::get();
+  const RowSrc<DK, NT> tab{big_rows};
   uint32_t foff[2][C::MAXM];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const int r = R0 + 16 * rt + li;
-    const uint32_t code = r < W ? tab.code[r] : kPadRow;
+    const uint32_t code = r < W ? tab.code(r) : kPadRow;
     const int m = row_order(code);
 #pragma unroll
     for (int l = 0; l < C::MAXM; ++l) {
@@ -1281,20 +1310,26 @@ __global__ __launch_bounds__(256, 4) void stream_totals_f32_kernel(const TIn* __
 template <int DK, int NT>
 constexpr bool use_stream_f32() { return StF<DK, NT>::W > 256; }
 
-// bf16 inputs with dk = 16 and 969 or 4,845 rows (n = 4, 5) run the same
-// kernels, widening their inputs to fp32 as they stage them
+// bf16 inputs with four or more terms (dk = 16: 969 or 4,845 rows; dk = 32
+// and 64: 6,545 to 814,385 rows) run the same kernels, widening their inputs
+// to fp32 as they stage them
 template <int DK, int NT>
-constexpr bool bf16_uses_stream_f32() { return DK == 16 && NT >= 4; }
+constexpr bool bf16_uses_stream_f32() { return DK >= 16 && NT >= 4; }
 
 template <int DK, int NT, class TIn>
 hipError_t stream_launch_f32(const void* Q, const void* K, const void* V, int BH, int N, const PrefillPlan& p,
                              const float* states_in, float* O, float* den_out, float* states, float* ws,
                              hipStream_t s) {
   using T = StFT<DK, NT>;
+  const uint32_t* big = nullptr;
+  if constexpr (runtime_rows<DK, NT>()) {
+    const hipError_t eb = big_row_codes(DK, NT, &big);
+    if (eb != hipSuccess) return eb;
+  }
   static_assert(StF<DK, NT>::NKP * 32 <= T::WP, "the readout's row blocks (pairs) lie inside the span state");
   const unsigned sgs = (unsigned)((BH * p.nspan + 7) / 8 * 8);  // (head, span) pairs, padded to the 8 XCDs
   hipLaunchKernelGGL((stream_totals_f32_kernel<DK, NT, TIn>), dim3(sgs * T::NRB), dim3(256), 0, s, (const TIn*)K,
-                     (const TIn*)V, BH, N, p.nspan, ws);
+                     (const TIn*)V, BH, N, p.nspan, ws, big);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((stream_scan_f32_kernel<DK, NT>), dim3((unsigned)(BH * StF<DK, NT>::NKB)), dim3(256), 0, s, ws,
@@ -1305,11 +1340,11 @@ hipError_t stream_launch_f32(const void* Q, const void* K, const void* V, int BH
   if (den_out)
     hipLaunchKernelGGL((stream_out_f32_kernel<DK, NT, true, TIn>), grid, dim3(256), 0, s, (const TIn*)Q,
                        (const TIn*)K, (const TIn*)V, BH, N, p.nspan, (int)T::WP, (const float*)ws,
-                       states_in != nullptr, O, den_out);
+                       states_in != nullptr, O, den_out, big);
   else
     hipLaunchKernelGGL((stream_out_f32_kernel<DK, NT, false, TIn>), grid, dim3(256), 0, s, (const TIn*)Q,
                        (const TIn*)K, (const TIn*)V, BH, N, p.nspan, (int)T::WP, (const float*)ws,
-                       states_in != nullptr, O, den_out);
+                       states_in != nullptr, O, den_out, big);
   return hipGetLastError();
 }
 

@@ -48,8 +48,23 @@ def test_workspace_query_and_errors():
         ops.tt_prefill_workspace_bytes(1, 1, 16, 16, 48, 3, 64)
     assert e.value.code == ops.TT_ERR_UNSUPPORTED
     with pytest.raises(ops.TTError) as e:
-        ops.tt_prefill_workspace_bytes(1, 1, 16, 64, 64, 4, 64)
+        ops.tt_prefill_workspace_bytes(1, 1, 16, 64, 64, 6, 64)
     assert e.value.code == ops.TT_ERR_UNSUPPORTED
+
+
+def test_widest_shapes_plan_the_streamed_path():
+    """dk = 32 and 64 with four and five terms: one span state of the padded
+    rows (128-row groups) per (head, span of 1,024 tokens), for both dtypes
+    (both run the fp32 streamed kernels); other chunk lengths are refused."""
+    for dk, n, W in ((32, 4, 6545), (32, 5, 58905), (64, 4, 47905), (64, 5, 814385)):
+        assert ops.tt_state_rows(dk, n) == W
+        wp = (W + 127) // 128 * 128
+        for dt in ("f32", "bf16"):
+            assert ops.tt_prefill_workspace_bytes_dtype(2, 3, 1100, dk, 64, n, 64, dt) == 2 * 3 * 2 * wp * 65 * 4
+        for chunk in (16, 32, 128):
+            with pytest.raises(ops.TTError) as e:
+                ops.tt_prefill_workspace_bytes(1, 1, 100, dk, 64, n, chunk)
+            assert e.value.code == ops.TT_ERR_UNSUPPORTED
 
 
 def test_entry_points_reject_bad_arguments_without_launching():

@@ -215,13 +215,70 @@ __global__ __launch_bounds__(256, 2) void stream_totals_kernel(const uint16_t* _
     return u32x4{a.x, a.y, c.x, c.y};
   };
 
+  // the wave's four octet descriptors, decoded once (wave-uniform): when all
+  // four are order-2 octets (every wave but the first two), the block loop
+  // issues the LDS reads of all four together and builds them without
+  // per-octet table loads or branches on the order
+  int om[4], oa[4], ob[4];
+  uint32_t omask[4][4];  // diagonal octets: the pairs of x[b0 ..] with b < a cleared
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int o = 4 * j + c;
+    const uint32_t d = (active && o < NO) ? tab[o] : 0xFFu;
+    om[c] = __builtin_amdgcn_readfirstlane((int)(d & 0xFF));
+    oa[c] = __builtin_amdgcn_readfirstlane((int)((d >> 8) & 0xFF));
+    ob[c] = __builtin_amdgcn_readfirstlane((int)(d >> 16));
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      omask[c][e] = (ob[c] + 2 * e >= oa[c] ? 0x0000FFFFu : 0u) | (ob[c] + 2 * e + 1 >= oa[c] ? 0xFFFF0000u : 0u);
+  }
+  const bool all2 = om[0] == 2 && om[1] == 2 && om[2] == 2 && om[3] == 2;
+  // hi and lo planes of one octet's eight products, to this lane's token row
+  auto put_octet = [&](int c, const float* mu) {
+    uint32_t hb[8], lb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      hb[u] = __float_as_uint(mu[u]) & 0xFFFF0000u;
+      lb[u] = __float_as_uint(mu[u] - __uint_as_float(hb[u]));
+    }
+    uint16_t* dst = muRow + 8 * (c ^ mswz);
+    reinterpret_cast<uint2*>(dst)[0] = uint2{__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
+                                             __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)};
+    reinterpret_cast<uint2*>(dst)[1] = uint2{__builtin_amdgcn_perm(hb[5], hb[4], 0x07060302u),
+                                             __builtin_amdgcn_perm(hb[7], hb[6], 0x07060302u)};
+    reinterpret_cast<uint2*>(dst + C::MUPL)[0] = uint2{__builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u),
+                                                       __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u)};
+    reinterpret_cast<uint2*>(dst + C::MUPL)[1] = uint2{__builtin_amdgcn_perm(lb[5], lb[4], 0x07060302u),
+                                                       __builtin_amdgcn_perm(lb[7], lb[6], 0x07060302u)};
+  };
+
   issue(0);
   commit(0, 0);
   __syncthreads();
   for (int tb = 0; tb < ntb; ++tb) {
     const int buf = tb & 1;
     if (tb + 1 < ntb) issue(tb + 1);
-    if (active) {
+    if (active && all2) {
+      const uint16_t* x = reinterpret_cast<const uint16_t*>(sK(buf)) + lane * C::KS;
+      uint32_t xa[4];
+      u32x4 xb[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        xa[c] = x[oa[c]];
+        xb[c] = *reinterpret_cast<const u32x4*>(x + ob[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (ob[c] <= oa[c]) {  // the octet holding (a, a): rows b < a are zero
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xb[c][e] &= omask[c][e];
+        }
+        float mu[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) prod_pair(xa[c], xa[c] << 16, xb[c][e], mu[2 * e], mu[2 * e + 1]);
+        put_octet(c, mu);
+      }
+    } else if (active) {
       const uint16_t* x = reinterpret_cast<const uint16_t*>(sK(buf)) + lane * C::KS;
       const bool kvalid = t_begin + tb * kStK + lane < t_end;  // tokens past the span end: zero rows
       // mu rows of octets 4j .. 4j+3 for this lane's token, hi and lo planes
@@ -251,22 +308,10 @@ __global__ __launch_bounds__(256, 2) void stream_totals_kernel(const uint16_t* _
 #pragma unroll
           for (int u = 0; u < 8; ++u) mu[u] = (m == 0 && u == 0 && kvalid) ? 1.f : 0.f;
         }
-        uint32_t hb[8], lb[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          hb[u] = __float_as_uint(mu[u]) & 0xFFFF0000u;
-          lb[u] = __float_as_uint(mu[u] - __uint_as_float(hb[u]));
-        }
-        uint16_t* dst = muRow + 8 * (c ^ mswz);
-        reinterpret_cast<uint2*>(dst)[0] = uint2{__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u),
-                                                 __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u)};
-        reinterpret_cast<uint2*>(dst)[1] = uint2{__builtin_amdgcn_perm(hb[5], hb[4], 0x07060302u),
-                                                 __builtin_amdgcn_perm(hb[7], hb[6], 0x07060302u)};
-        reinterpret_cast<uint2*>(dst + C::MUPL)[0] = uint2{__builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u),
-                                                           __builtin_amdgcn_perm(lb[3], lb[2], 0x07060302u)};
-        reinterpret_cast<uint2*>(dst + C::MUPL)[1] = uint2{__builtin_amdgcn_perm(lb[5], lb[4], 0x07060302u),
-                                                           __builtin_amdgcn_perm(lb[7], lb[6], 0x07060302u)};
+        put_octet(c, mu);
       }
+    }
+    if (active) {
       // the tile is wave-private: this wave's LDS writes done, then its reads
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       const unsigned char* V = sV(buf);

@@ -1468,11 +1468,19 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
           pr[s] = (key <= query && key < nvalid) ? taylor_poly<C::NT>(x[s]) : 0.f;
         }
         const int kbase = kb * 32 + 8 * lg + 4 * tau;
-        uint2 hi, lo;
-        split_bf16x2(pr[0], pr[1], hi.x, lo.x);
-        split_bf16x2(pr[2], pr[3], hi.y, lo.y);
-        *reinterpret_cast<uint2*>(&P[query * C::PS + kbase]) = hi;
-        *reinterpret_cast<uint2*>(&P[C::PPL + query * C::PS + kbase]) = lo;
+        // the first chunk of a span also gets the lo plane of P (its queries
+        // may have few keys in all); later chunks have at least one chunk of
+        // keys in the state part of their normaliser and take P as bf16
+        if (ci == 0) {
+          uint2 hi, lo;
+          split_bf16x2(pr[0], pr[1], hi.x, lo.x);
+          split_bf16x2(pr[2], pr[3], hi.y, lo.y);
+          *reinterpret_cast<uint2*>(&P[query * C::PS + kbase]) = hi;
+          *reinterpret_cast<uint2*>(&P[C::PPL + query * C::PS + kbase]) = lo;
+        } else {
+          *reinterpret_cast<uint2*>(&P[query * C::PS + kbase]) = uint2{pack_bf16x2(pr[0], pr[1]),
+                                                                        pack_bf16x2(pr[2], pr[3])};
+        }
       }
     }
     // features: lane = token, this producer takes 8-row groups g == pw (mod 4).
@@ -1758,32 +1766,40 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
 #pragma unroll
           for (int s = 0; s < 4; ++s) sG[b * kCH + (4 * lg + s) * 4 + ct] = denh[s];
         }
-        // intra-chunk block: O^T += V^T P^T, normaliser P.1 for query tile ct
-        u32x4 ph[4][2], pl[4][2];  // (query tile, key block) on or below the diagonal
+        // intra-chunk block: O^T += V^T P^T, normaliser P.1 for query tile ct;
+        // the lo plane of P only in the first chunk of the span (see p_build)
+        auto intra = [&](auto loc) {
+          constexpr bool LO = decltype(loc)::value;
+          u32x4 ph[4][2], pl[4][2];  // (query tile, key block) on or below the diagonal
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt)
+          for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            if (kb * 32 <= qt * 16 + 15) {
-              ph[qt][kb] = lds_u32x4(P, ((qt * 16 + li) * C::PS + kb * 32 + 8 * lg) * 2);
-              pl[qt][kb] = lds_u32x4(P, (C::PPL + (qt * 16 + li) * C::PS + kb * 32 + 8 * lg) * 2);
-            }
+            for (int kb = 0; kb < 2; ++kb)
+              if (kb * 32 <= qt * 16 + 15) {
+                ph[qt][kb] = lds_u32x4(P, ((qt * 16 + li) * C::PS + kb * 32 + 8 * lg) * 2);
+                if constexpr (LO) pl[qt][kb] = lds_u32x4(P, (C::PPL + (qt * 16 + li) * C::PS + kb * 32 + 8 * lg) * 2);
+              }
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
+          for (int qt = 0; qt < 4; ++qt) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            if (kb * 32 <= qt * 16 + 15) {
-              num[qt] = mfma_bf16(bvk[kb], ph[qt][kb], num[qt]);
-              num[qt] = mfma_bf16(bvk[kb], pl[qt][kb], num[qt]);
-              if (qt == ct) {
-                // column 0 of the product holds P.1 (only lanes li == 0 read den)
-                den = mfma_bf16(ph[qt][kb], ones_bf, den);
-                den = mfma_bf16(pl[qt][kb], ones_bf, den);
+            for (int kb = 0; kb < 2; ++kb) {
+              if (kb * 32 <= qt * 16 + 15) {
+                num[qt] = mfma_bf16(bvk[kb], ph[qt][kb], num[qt]);
+                if constexpr (LO) num[qt] = mfma_bf16(bvk[kb], pl[qt][kb], num[qt]);
+                if (qt == ct) {
+                  // column 0 of the product holds P.1 (only lanes li == 0 read den)
+                  den = mfma_bf16(ph[qt][kb], ones_bf, den);
+                  if constexpr (LO) den = mfma_bf16(pl[qt][kb], ones_bf, den);
+                }
               }
             }
+            num[qt] += m0;
           }
-          num[qt] += m0;
-        }
+        };
+        if (ci == 0)
+          intra(std::true_type{});
+        else
+          intra(std::false_type{});
         if (li == 0) {
           // unnormalised mode: outputs keep their numerators and the
           // normalisers go to Dg

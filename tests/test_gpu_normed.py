@@ -27,7 +27,8 @@ from taylor_recurrent_states_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(16, 1), (16, 2), (16, 3), (16, 4), (16, 5), (32, 1), (32, 2), (32, 3), (64, 1), (64, 2), (64, 3)]
+SHAPES = [(16, 1), (16, 2), (16, 3), (16, 4), (16, 5), (32, 1), (32, 2), (32, 3), (32, 4), (64, 1), (64, 2), (64, 3),
+          (64, 4)]
 
 
 def _tol(dtype):

@@ -229,7 +229,8 @@ def bench_prefill_other(name, args, torch, ops, wl):
 def bench_orders(args, torch, ops, wl):
     """The variant axis: time per call of the prefill workload's shape
     (B=4, H=8, N=8192, dv=64) for n = 1 .. 5 Taylor terms at dk=16 (bf16)
-    and n = 1 .. 6 at dk=8 (fp32), and the largest deviation from exact
+    and n = 1 .. 6 at dk=8 (fp32), of B=1, H=8, N=8192 for n = 1 .. 5 at
+    dk=32 and 64 (bf16), and the largest deviation from exact
     softmax attention of the GPU outputs on a small seeded case (B=1, H=4,
     N=512).  The softmax reference is torch's causal attention with scale 1
     in fp64 on the CPU."""
@@ -244,17 +245,20 @@ def bench_orders(args, torch, ops, wl):
         return torch.from_numpy(np.ascontiguousarray(r.device).view(np.int16)).view(torch.bfloat16).to(dev)
 
     rows = []
-    for dk, dtype, nmax in ((16, "bf16", 5), (8, "f32", 6)):
-        q, k, v = wl.draw_qkv(w.seed, w.B, w.H, w.N, dk, w.dv, dtype)
+    # dk = 32 and 64 up to five terms (814,385 rows at dk = 64) on 8 heads
+    # (B=1): the span states of all 32 heads at n = 5 would take 54 GB
+    for dk, dtype, nmax, B, H in ((16, "bf16", 5, w.B, w.H), (8, "f32", 6, w.B, w.H), (32, "bf16", 5, 1, 8),
+                                  (64, "bf16", 5, 1, 8)):
+        q, k, v = wl.draw_qkv(w.seed, B, H, w.N, dk, w.dv, dtype)
         Q, K, V = to_dev(q), to_dev(k), to_dev(v)
         qs, ks, vs = wl.draw_qkv(4000, 1, 4, 512, dk, w.dv, dtype)
         tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a.exact, dtype=np.float64)) for a in (qs, ks, vs))
         o_soft = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=1.0).numpy()
         Qs, Ks, Vs = to_dev(qs), to_dev(ks), to_dev(vs)
         for n in range(1, nmax + 1):
-            O = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.float32, device=dev)
-            S = torch.empty(w.B * w.H * ops.tt_state_floats(dk, w.dv, n), dtype=torch.float32, device=dev)
-            ws = torch.empty(ops.tt_prefill_workspace_bytes_dtype(w.B, w.H, w.N, dk, w.dv, n, w.chunk, dtype),
+            O = torch.empty((B, H, w.N, w.dv), dtype=torch.float32, device=dev)
+            S = torch.empty(B * H * ops.tt_state_floats(dk, w.dv, n), dtype=torch.float32, device=dev)
+            ws = torch.empty(ops.tt_prefill_workspace_bytes_dtype(B, H, w.N, dk, w.dv, n, w.chunk, dtype),
                              dtype=torch.uint8, device=dev)
 
             def step():
@@ -266,15 +270,16 @@ def bench_orders(args, torch, ops, wl):
             o_small, _ = ops.tt_prefill(Qs, Ks, Vs, n)
             err = float(np.max(np.abs(o_small.cpu().numpy().astype(np.float64) - o_soft)))
             W = ops.tt_state_rows(dk, n)
-            flops = 4.0 * W * (w.dv + 1) * w.B * w.H * w.N
-            rows.append({"dk": dk, "dtype": dtype, "n": n, "state_rows": W, "ms_per_call": round(t * 1e3, 4),
-                         "tokens_per_s": round(w.B * w.N / t, 1),
+            flops = 4.0 * W * (w.dv + 1) * B * H * w.N
+            rows.append({"dk": dk, "dtype": dtype, "n": n, "B": B, "H": H, "state_rows": W,
+                         "ms_per_call": round(t * 1e3, 4), "tokens_per_s": round(B * w.N / t, 1),
                          "alg_TFLOPs": round(flops / t / 1e12, 2),
                          "max_abs_err_vs_softmax": err, "taylor_eps": math.e / math.factorial(n)})
             print(f"# dk={dk} {dtype} n={n}: {t * 1e6:.1f} us/call, max|o - softmax| = {err:.2e}", file=sys.stderr,
                   flush=True)
             del O, S, ws
-    return {"workload": "prefill B4 H8 N8192 dv64: dk16 bf16 n=1..5, dk8 fp32 n=1..6",
+    return {"workload": "prefill N8192 dv64: B4 H8 dk16 bf16 n=1..5, B4 H8 dk8 fp32 n=1..6, B1 H8 dk32 and dk64 "
+                        "bf16 n=1..5",
             "softmax_check": "B1 H4 N512 (same dk and dtype), seed 4000", "orders": rows}
 
 

@@ -210,6 +210,16 @@ __device__ inline void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo
 __device__ inline void store_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }
 __device__ inline void store_nt(float* p, f32x4_t v) { __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p)); }
 
+// a.lo * b.lo + a.hi * b.hi + c for packed bf16 pairs a and b (products
+// exact, one fp32 rounding), in the three-operand encoding: the builtin is
+// compiled to the two-operand form, which accumulates in place and so costs a
+// register copy whenever c must survive.
+__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  float d;
+  asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 // 1/x by the hardware reciprocal (v_rcp_f32: within 1 ulp for normal x).
 __device__ inline float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
 

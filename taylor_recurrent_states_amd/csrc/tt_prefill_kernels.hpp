@@ -1704,11 +1704,8 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
           const uint32_t bits = pack_bf16x2(s0 * rz0, 0.f) & 0xFFFFu;
           return (bits & 0x7F80u) != 0x7F80u ? bits : 0u;
         };
-        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
         const uint32_t abits = col_mean(__shfl(st[0][0].x, li));  // column ct*16 + li
-        const uint32_t nab = abits ^ 0x8000u;                      // -a_c
-        const bf16x2_t na_lo = __builtin_bit_cast(bf16x2_t, nab);        // {-a_c, 0}
-        const bf16x2_t na_hi = __builtin_bit_cast(bf16x2_t, nab << 16);  // {0, -a_c}
+        const uint32_t nab = abits ^ 0x8000u;  // {-a_c, 0} as a bf16 pair; nab << 16 is {0, -a_c}
         // readout of K-block j, then its update (the readout has taken st[j]
         // into bs first); phi and mu fragments one K-block ahead
         u32x4 af[2][4];
@@ -1740,10 +1737,9 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t w = bdn[j & 1][e];  // through a scalar (see prod8)
-            const bf16x2_t z = __builtin_bit_cast(bf16x2_t, w);
             const f32x4 sv = st[j][e >> 1];
-            sh[2 * e] = __builtin_amdgcn_fdot2_f32_bf16(na_lo, z, sv[(2 * e) & 3], false);
-            sh[2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(na_hi, z, sv[(2 * e + 1) & 3], false);
+            sh[2 * e] = dot2_bf16(nab, w, sv[(2 * e) & 3]);
+            sh[2 * e + 1] = dot2_bf16(nab << 16, w, sv[(2 * e + 1) & 3]);
           }
           const u32x4 bs = {pack_bf16x2(sh[0], sh[1]), pack_bf16x2(sh[2], sh[3]), pack_bf16x2(sh[4], sh[5]),
                             pack_bf16x2(sh[6], sh[7])};

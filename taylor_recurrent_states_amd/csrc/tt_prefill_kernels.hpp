@@ -1512,8 +1512,8 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
   for (int q = 0; q < 4; ++q) nprev[q] = zero4();
   f32x4 mprev = zero4();  // column means of the previous chunk's readout shift
   const int ct = pw;
-  const u32x4 ones_bf = (li == 0) ? u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}
-                                  : u32x4{0u, 0u, 0u, 0u};
+  // all ones: every column of a product with it holds the row sums
+  const u32x4 ones_bf = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
   // Producer and consumer waves run separate loops with the same number of
   // workgroup barriers (one per chunk, plus one after the prologue), so their
@@ -1546,22 +1546,32 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
     f32x4 dstate[NJD][2];
 #pragma unroll
     for (int jd = 0; jd < NJD; ++jd) dstate[jd][0] = dstate[jd][1] = zero4();
-    // hi + lo bf16 readout fragments and the fp32 row 0
+    // hi + lo bf16 readout fragments and the fp32 row 0.  The ones operand
+    // fills every column, so every lane of group lg holds the group's rows
+    // 8lg .. 8lg+7 (dstate[jd][row / 4 % 2][row % 4]); lane li < 8 splits
+    // row 8lg + li, one value per lane instead of eight in lane li == 0.
     auto publish_den = [&](int buf) {
-      if (li == 0) {
+      // a select tree on the bits of li (a per-lane index into the
+      // registers would go through scratch memory)
+      const bool b0 = (li & 1) != 0, b1 = (li & 2) != 0, b2 = (li & 4) != 0;
 #pragma unroll
-        for (int jd = 0; jd < NJD; ++jd) {
-          const int j = 4 * jd + ct;
-          if (j < C::NKB) {
-            const f32x4 d0 = dstate[jd][0], d1 = dstate[jd][1];
-            u32x4 hi, lo;
-            split_bf16x8(d0, d1, hi, lo);
-            *reinterpret_cast<u32x4*>(sDenB + 2 * buf * C::WP + j * 32 + 8 * lg) = hi;
-            *reinterpret_cast<u32x4*>(sDenB + (2 * buf + 1) * C::WP + j * 32 + 8 * lg) = lo;
+      for (int jd = 0; jd < NJD; ++jd) {
+        const int j = 4 * jd + ct;
+        if (j < C::NKB) {
+          const f32x4 d0 = dstate[jd][0], d1 = dstate[jd][1];
+          const float p0 = b0 ? d0.y : d0.x, p1 = b0 ? d0.w : d0.z;
+          const float p2 = b0 ? d1.y : d1.x, p3 = b0 ? d1.w : d1.z;
+          const float q0 = b1 ? p1 : p0, q1 = b1 ? p3 : p2;
+          const float v = b2 ? q1 : q0;
+          uint16_t h, l;
+          split_bf16(v, h, l);
+          if (li < 8) {
+            sDenB[2 * buf * C::WP + j * 32 + 8 * lg + li] = h;
+            sDenB[(2 * buf + 1) * C::WP + j * 32 + 8 * lg + li] = l;
           }
         }
-        if (ct == 0 && lg == 0) sDen0[buf] = dstate[0][0].x;
       }
+      if (ct == 0 && lg == 0 && li == 0) sDen0[buf] = dstate[0][0].x;
     };
     if constexpr (OUT) {
 #pragma unroll
@@ -1783,7 +1793,7 @@ __global__ __launch_bounds__(C::NTHR) void pipe_kernel(const uint16_t* __restric
                 num[qt] = mfma_bf16(bvk[kb], ph[qt][kb], num[qt]);
                 if constexpr (LO) num[qt] = mfma_bf16(bvk[kb], pl[qt][kb], num[qt]);
                 if (qt == ct) {
-                  // column 0 of the product holds P.1 (only lanes li == 0 read den)
+                  // every column of the product holds P.1 (lanes li == 0 read den)
                   den = mfma_bf16(ph[qt][kb], ones_bf, den);
                   if constexpr (LO) den = mfma_bf16(pl[qt][kb], ones_bf, den);
                 }

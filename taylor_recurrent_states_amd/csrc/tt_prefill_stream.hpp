@@ -107,7 +107,9 @@ struct StTot {
   static constexpr int MUPL = kStK * MUS + 32;         // elements per mu plane (with the shift's slack)
   static constexpr int B_K = kStK * KS * 2, B_V = kStK * VS * 2;
   static constexpr int B_MU = 2 * MUPL * 2;            // hi and lo planes of one wave
-  static constexpr int LDS = 2 * (B_K + B_V) + NW * B_MU;
+  // one K/V buffer (51.6 KB at dk = 64): three workgroups fit a CU's 160 KB,
+  // whose other waves cover the second barrier per token block
+  static constexpr int LDS = (B_K + B_V) + NW * B_MU;
   static constexpr int KSEG = kStK * DK / 8, VSEG = kStK * kDV / 8;
   static constexpr int NKS = (KSEG + NW * 64 - 1) / (NW * 64), NVS = VSEG / (NW * 64);
   static constexpr int NRB = (StCfg<DK>::NKB + NW - 1) / NW;  // 256-row groups
@@ -120,7 +122,7 @@ struct StTot {
 };
 
 template <int DK>
-__global__ __launch_bounds__(256, 2) void stream_totals_kernel(const uint16_t* __restrict__ Kg,
+__global__ __launch_bounds__(256, 3) void stream_totals_kernel(const uint16_t* __restrict__ Kg,
                                                             const uint16_t* __restrict__ Vg, int BH, int N,
                                                             int nspan, float* __restrict__ ws) {
   using C = StTot<DK>;
@@ -143,9 +145,9 @@ __global__ __launch_bounds__(256, 2) void stream_totals_kernel(const uint16_t* _
   const bool active = j < NKB;        // wave-uniform; blocks past the last octet hold zero rows
   const uint16_t* Kh = Kg + (size_t)bh * N * DK;
   const uint16_t* Vh = Vg + (size_t)bh * N * kDV;
-  auto sK = [&](int buf) { return lds + buf * (C::B_K + C::B_V); };
-  auto sV = [&](int buf) { return lds + buf * (C::B_K + C::B_V) + C::B_K; };
-  uint16_t* sMu = reinterpret_cast<uint16_t*>(lds + 2 * (C::B_K + C::B_V) + w * C::B_MU);
+  auto sK = [&](int) { return lds; };
+  auto sV = [&](int) { return lds + C::B_K; };
+  uint16_t* sMu = reinterpret_cast<uint16_t*>(lds + (C::B_K + C::B_V) + w * C::B_MU);
 
   u32x4 rk[C::NKS], rv[C::NVS];
   auto issue = [&](int tb) {  // rows past the span end are clamped to its last token (their mu is zero)
@@ -332,6 +334,7 @@ __global__ __launch_bounds__(256, 2) void stream_totals_kernel(const uint16_t* _
       }
     }
     if (tb + 1 < ntb) {
+      __syncthreads();  // every wave's reads of the K and V tiles done
       commit(buf ^ 1, tb + 1);
       __syncthreads();
     }

@@ -624,14 +624,18 @@ __global__ __launch_bounds__(256, 3) void stream_out_kernel(const uint16_t* __re
 
   // ---------------- phase B: readout of the prefix state ----------------
   // wave w owns value columns 16w .. 16w+15 of all 128 queries (eight O^T
-  // tiles) and the normalisers of query tiles 2w, 2w+1, from the hi (dBh)
-  // and lo (dBl) planes of the normaliser rows.  The value fragments are the
-  // state shifted by a_c Zh (see stream_scan_kernel); a_c (phi . Zh) = a_c dBh
-  // is added back in the combine.
-  f32x4 nB[8], dBh[2], dBl[2];
+  // tiles) and the normalisers of query tiles 2w, 2w+1, from the hi and lo
+  // planes of the normaliser rows (dC).  The value fragments are the state
+  // shifted by a_c Zh (see stream_scan_kernel); a_c (phi . Zh), with phi . Zh
+  // the hi half of dC, is added back in the combine.
+  // dC[k]: the normaliser readout of query tile 2w + k, hi plane in rows 0-7
+  // of the product (lanes lg < 2) and lo plane in rows 8-15 (lanes lg >= 2):
+  // the A operand's rows all repeat the normaliser rows, so rows 8-15 carry
+  // the lo plane and one MFMA reads out both planes
+  f32x4 nB[8], dC[2];
 #pragma unroll
   for (int qt = 0; qt < 8; ++qt) nB[qt] = zero4();
-  dBh[0] = dBh[1] = dBl[0] = dBl[1] = zero4();
+  dC[0] = dC[1] = zero4();
   const bool has_prefix = s > 0 || has_init;
   if (has_prefix) {
     uint16_t* sQ = reinterpret_cast<uint16_t*>(lds);
@@ -680,13 +684,13 @@ __global__ __launch_bounds__(256, 3) void stream_out_kernel(const uint16_t* __re
       }
     };
     const float* S = ws + ((size_t)bh * nspan + s) * (size_t)WP * (kDV + 1);
-    auto load_s = [&](int j, u32x4& sf, u32x4& dhi, u32x4& dlo) {
+    const int dpl = li >= 8 ? 1 : 0;  // A-operand rows 8-15: the lo plane
+    auto load_s = [&](int j, u32x4& sf, u32x4& dcb) {
       sf = *reinterpret_cast<const u32x4*>(S + st_frag_off(j, w, lane, 0));
-      dhi = *reinterpret_cast<const u32x4*>(S + st_den_off(WP, j, lg, 0));
-      dlo = *reinterpret_cast<const u32x4*>(S + st_den_off(WP, j, lg, 1));
+      dcb = *reinterpret_cast<const u32x4*>(S + st_den_off(WP, j, lg, dpl));
     };
-    u32x4 sf, dhi, dlo;
-    load_s(0, sf, dhi, dlo);
+    u32x4 sf, dcb;
+    load_s(0, sf, dcb);
     __syncthreads();  // Q tile staged
     gen(0, sPhi(0));
     __syncthreads();
@@ -694,8 +698,8 @@ __global__ __launch_bounds__(256, 3) void stream_out_kernel(const uint16_t* __re
       const uint16_t* P = sPhi(j & 1);
       // the next block's state fragments first: their latency runs under
       // the generation of its phi rows and this block's MFMAs
-      u32x4 nsf, ndhi, ndlo;
-      if (j + 1 < C::NKB) load_s(j + 1, nsf, ndhi, ndlo);
+      u32x4 nsf, ndcb;
+      if (j + 1 < C::NKB) load_s(j + 1, nsf, ndcb);
       if (j + 1 < C::NKB) gen(j + 1, sPhi((j + 1) & 1));
       u32x4 af[8];
 #pragma unroll
@@ -705,17 +709,13 @@ __global__ __launch_bounds__(256, 3) void stream_out_kernel(const uint16_t* __re
       for (int qt = 0; qt < 8; ++qt) nB[qt] = mfma_bf16(sf, af[qt], nB[qt]);
       // normalisers of query tiles 2w, 2w+1 (w is wave-uniform: a scalar branch)
       switch (w) {
-        case 0: dBh[0] = mfma_bf16(dhi, af[0], dBh[0]); dBl[0] = mfma_bf16(dlo, af[0], dBl[0]);
-                dBh[1] = mfma_bf16(dhi, af[1], dBh[1]); dBl[1] = mfma_bf16(dlo, af[1], dBl[1]); break;
-        case 1: dBh[0] = mfma_bf16(dhi, af[2], dBh[0]); dBl[0] = mfma_bf16(dlo, af[2], dBl[0]);
-                dBh[1] = mfma_bf16(dhi, af[3], dBh[1]); dBl[1] = mfma_bf16(dlo, af[3], dBl[1]); break;
-        case 2: dBh[0] = mfma_bf16(dhi, af[4], dBh[0]); dBl[0] = mfma_bf16(dlo, af[4], dBl[0]);
-                dBh[1] = mfma_bf16(dhi, af[5], dBh[1]); dBl[1] = mfma_bf16(dlo, af[5], dBl[1]); break;
-        default: dBh[0] = mfma_bf16(dhi, af[6], dBh[0]); dBl[0] = mfma_bf16(dlo, af[6], dBl[0]);
-                 dBh[1] = mfma_bf16(dhi, af[7], dBh[1]); dBl[1] = mfma_bf16(dlo, af[7], dBl[1]); break;
+        case 0: dC[0] = mfma_bf16(dcb, af[0], dC[0]); dC[1] = mfma_bf16(dcb, af[1], dC[1]); break;
+        case 1: dC[0] = mfma_bf16(dcb, af[2], dC[0]); dC[1] = mfma_bf16(dcb, af[3], dC[1]); break;
+        case 2: dC[0] = mfma_bf16(dcb, af[4], dC[0]); dC[1] = mfma_bf16(dcb, af[5], dC[1]); break;
+        default: dC[0] = mfma_bf16(dcb, af[6], dC[0]); dC[1] = mfma_bf16(dcb, af[7], dC[1]); break;
       }
       if (j + 1 < C::NKB) {
-        sf = nsf; dhi = ndhi; dlo = ndlo;
+        sf = nsf; dcb = ndcb;
       }
       __syncthreads();
     }
@@ -728,11 +728,13 @@ __global__ __launch_bounds__(256, 3) void stream_out_kernel(const uint16_t* __re
 #pragma unroll
   for (int qt = 0; qt < 8; ++qt)
     *reinterpret_cast<f32x4*>(sX + (qt * 16 + li) * C::OXS + 16 * w + 4 * lg) = nB[qt];
+  // lane (lg = 0, li) holds the hi readout of query li, lane (lg = 2, li) the lo one
+  const float dlo0 = __shfl_xor(dC[0].x, 32), dlo1 = __shfl_xor(dC[1].x, 32);
   if (lg == 0) {
-    sXd[(2 * w) * 16 + li] = dBh[0].x + dBl[0].x;
-    sXd[(2 * w + 1) * 16 + li] = dBh[1].x + dBl[1].x;
-    sXh[(2 * w) * 16 + li] = dBh[0].x;
-    sXh[(2 * w + 1) * 16 + li] = dBh[1].x;
+    sXd[(2 * w) * 16 + li] = dC[0].x + dlo0;
+    sXd[(2 * w + 1) * 16 + li] = dC[1].x + dlo1;
+    sXh[(2 * w) * 16 + li] = dC[0].x;
+    sXh[(2 * w + 1) * 16 + li] = dC[1].x;
   }
   // column means of the readout shift (0 without a prefix state)
   f32x4 acol[4];

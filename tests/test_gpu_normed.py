@@ -144,14 +144,16 @@ def test_prefill_normed_from_states_then_decode(dtype):
     assert_states(S.cpu().numpy(), S_log, dk, n, _tol(dtype), "after decode_normed")
 
 
+@pytest.mark.parametrize("dk,n", [(32, 3), (32, 4), (64, 4)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_decode_normed_continues_prefill_normed(dtype):
+def test_decode_normed_continues_prefill_normed(dk, n, dtype):
     """Prefill of N tokens then one decode step equals the prefill of N+1
     tokens on the last output and the states (both normalise with the same
-    device function)."""
+    device function).  dk 64 n 4 (47,905 rows) runs the decode over row
+    chunks."""
     import torch
-    B, H, N, dk, n, tau = 1, 4, 129, 32, 3, 1.0
-    q, k, v = _raw(4500, B, H, N + 1, dk, 64, dtype)
+    B, H, N, tau = 1, 4, 129, 1.0
+    q, k, v = _raw(4500 + dk * 10 + n, B, H, N + 1, dk, 64, dtype)
     Qd, Kd, Vd = to_device(q), to_device(k), to_device(v)
     O_all, S_all = ops.tt_prefill_normed(Qd, Kd, Vd, n, tau)
     _, S = ops.tt_prefill_normed(Qd[:, :, :N].contiguous(), Kd[:, :, :N].contiguous(), Vd[:, :, :N].contiguous(),

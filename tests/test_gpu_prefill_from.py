@@ -112,7 +112,7 @@ def _rel_to_max(x, ref):
     return float(np.max(np.abs(x - ref)) / max(1e-300, np.max(np.abs(ref))))
 
 
-@pytest.mark.parametrize("dk,n", [(16, 2), (16, 3), (32, 2), (64, 2), (64, 3), (16, 5)])
+@pytest.mark.parametrize("dk,n", [(16, 2), (16, 3), (32, 2), (64, 2), (64, 3), (16, 5), (32, 4), (64, 4)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("carried", [True, False])
 def test_prefill_from_unnormalized(dk, n, dtype, carried):
@@ -121,7 +121,8 @@ def test_prefill_from_unnormalized(dk, n, dtype, carried):
     5e-3 for bf16), num / den at the output bar, the same states as the
     normalised call, and the normalised call's O equal to num * (1/den)
     within the hardware reciprocal's rounding.  The shapes cover the pipe
-    kernel, the sweep kernel and the row-group combine (dk 64 n 3, dk 16 n 5)."""
+    kernel, the sweep kernel and both streamed paths (dk 64 n 3 in bf16;
+    dk 16 n 5 and the run-time row tables of dk 32 and 64 with n 4)."""
     import torch
     B, H, P, N = 1, 2, 150, 200
     S0, S0d = _prefix_states(3400 + dk * 10 + n, B, H, P, dk, 64, n, dtype) if carried else (None, None)

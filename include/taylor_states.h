@@ -120,7 +120,18 @@ int tt_prefill_workspace_bytes_dtype(int B, int H, int N, int dk, int dv, int n,
  *   states : B*H*W*(dv+1) fp32 in the plane layout above, written with the
  *            states of all N tokens (prefill starts from zero states)
  *   workspace : device scratch of at least tt_prefill_workspace_bytes();
- *            contents undefined on return
+ *            contents undefined on return.  Plans with spans of a fixed
+ *            length (at chunk 64: fp32 with more than 256 state rows W,
+ *            bf16 with n=3 at dk=32 and 64, bf16 with n>=4 at dk>=16)
+ *            also take a smaller
+ *            workspace: at least one head's share, the size for B*H heads
+ *            divided by B*H.  The heads (b, h in flattened order) then
+ *            run in groups of as many heads as the workspace holds, one
+ *            group after another on `stream`, with bit-identical results;
+ *            each group re-reads nothing of the others, so the cost is
+ *            fewer workgroups per launch.  Less than one head's share,
+ *            or a smaller workspace for the other plans, is
+ *            TT_ERR_WORKSPACE.
  *   chunk : tokens per chunk of the intra-chunk quadratic block: 16, 32,
  *           64 or 128.  Results do not depend on it beyond fp32 rounding
  *           (it moves work between the quadratic block and the state).
@@ -149,9 +160,11 @@ int tt_prefill(const void *Q, const void *K, const void *V, tt_dtype in_dtype,
  * workspace taken from a fixed array of TT_NOALLOC_SCRATCH_BYTES in device
  * memory that the library holds on each GPU it runs on until the process
  * ends.  The call allocates nothing: the caller passes Q, K, V, O and
- * states as for tt_prefill (same layouts, alignment and errors).  A shape
- * whose tt_prefill_workspace_bytes() exceeds TT_NOALLOC_SCRATCH_BYTES
- * returns TT_ERR_WORKSPACE before anything is launched.  The first call on
+ * states as for tt_prefill (same layouts, alignment and errors).  Plans
+ * that run heads in groups (see tt_prefill's workspace) use groups that
+ * fit the array; a shape whose workspace for one head (those plans) or for
+ * the whole call (the others) exceeds TT_NOALLOC_SCRATCH_BYTES returns
+ * TT_ERR_WORKSPACE before anything is launched.  The first call on
  * a device looks the array up on the current device, which `stream` must
  * belong to.  Every call on one GPU shares that GPU's array, and each call
  * overwrites what it needs of it (nothing has to start at zero): calls
@@ -174,7 +187,7 @@ int tt_prefill_noalloc(const void *Q, const void *K, const void *V, tt_dtype in_
  *               same buffer as `states` (the call then continues in place)
  *               but must not otherwise overlap `states`, O or the
  *               workspace (TT_ERR_INVALID_ARG); NULL is TT_ERR_INVALID_ARG.
- * Uses the same workspace size as tt_prefill. */
+ * Uses the same workspace as tt_prefill (head groups included). */
 int tt_prefill_from(const void *Q, const void *K, const void *V, tt_dtype in_dtype,
                     int B, int H, int N, int dk, int dv, int n, int chunk,
                     const float *states_in, float *O, float *states,
@@ -195,7 +208,7 @@ int tt_prefill_from(const void *Q, const void *K, const void *V, tt_dtype in_dty
  *               states_in or the workspace (TT_ERR_INVALID_ARG).
  * The numerators and normalisers are those the normalised call divides
  * (its O is num * (1/den) with the hardware reciprocal); the states are the
- * same.  Uses the same workspace size as tt_prefill. */
+ * same.  Uses the same workspace as tt_prefill (head groups included). */
 int tt_prefill_from_unnormalized(const void *Q, const void *K, const void *V, tt_dtype in_dtype,
                                  int B, int H, int N, int dk, int dv, int n, int chunk,
                                  const float *states_in, float *num, float *den, float *states,

@@ -91,9 +91,27 @@ static int prefill_impl(const void* Q, const void* K, const void* V, tt_dtype in
   const size_t need = normed ? align256(base) + 2 * copy : base;
   if (normed && !valid_scale(qscale))
     return fail(TT_ERR_INVALID_ARG, "temperature %g must be finite and positive", (double)qscale);
-  if (need > 0 && (!workspace || workspace_bytes < need))
+  // Streamed plans (spans of a fixed length) run the heads in groups when the
+  // workspace holds the span states of fewer than all heads but at least one
+  // (not with the normalisation, whose copies of Q and K need the full size).
+  const int BH = B * H;
+  int group = BH;
+  size_t used = need;
+  if (!normed && p.streamed && workspace && need > 0 && workspace_bytes < need) {
+    const size_t per_head = base / (size_t)BH;
+    const size_t g = workspace_bytes / per_head;
+    if (g >= 1) {
+      group = (int)g;
+      used = per_head * g;
+    }
+  }
+  if (need > 0 && (!workspace || workspace_bytes < used)) {
+    if (!normed && p.streamed)
+      return fail(TT_ERR_WORKSPACE, "workspace of %zu bytes needed (or %zu per head, heads in groups), %zu given",
+                  need, base / (size_t)BH, workspace ? workspace_bytes : (size_t)0);
     return fail(TT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
+  }
   if ((((uintptr_t)Q) | ((uintptr_t)K) | ((uintptr_t)V) | ((uintptr_t)O) | ((uintptr_t)workspace)) & 15u)
     return fail(TT_ERR_INVALID_ARG, "Q, K, V, O and workspace must be 16-byte aligned");
   if (den) {
@@ -101,7 +119,7 @@ static int prefill_impl(const void* Q, const void* K, const void* V, tt_dtype in
     const size_t sb = (size_t)B * H * tt_state_floats(dk, dv, n) * sizeof(float);
     if (((uintptr_t)den) & 3u) return fail(TT_ERR_INVALID_ARG, "den must be 4-byte aligned");
     if (overlap(den, db, O, (size_t)B * H * N * dv * sizeof(float)) || overlap(den, db, states, sb) ||
-        (states_in && overlap(den, db, states_in, sb)) || (workspace && overlap(den, db, workspace, need)))
+        (states_in && overlap(den, db, states_in, sb)) || (workspace && overlap(den, db, workspace, used)))
       return fail(TT_ERR_INVALID_ARG, "den overlaps O, the states or the workspace");
   }
   if (states_in) {
@@ -109,7 +127,7 @@ static int prefill_impl(const void* Q, const void* K, const void* V, tt_dtype in
     if (states_in != states && overlap(states_in, sb, states, sb))
       return fail(TT_ERR_INVALID_ARG, "states_in and states overlap without being the same buffer");
     if (overlap(states_in, sb, O, (size_t)B * H * N * dv * sizeof(float)) ||
-        (workspace && overlap(states_in, sb, workspace, need)))
+        (workspace && overlap(states_in, sb, workspace, used)))
       return fail(TT_ERR_INVALID_ARG, "states_in overlaps O or the workspace");
   }
   char what[64];
@@ -123,9 +141,24 @@ static int prefill_impl(const void* Q, const void* K, const void* V, tt_dtype in
     Q = qn;
     K = kn;
   }
-  return hip_status(launch_prefill(Q, K, V, in_dtype, B * H, N, dk, n, p, states_in, O, den, states,
-                                   (float*)workspace, (hipStream_t)stream),
-                    what);
+  if (group == BH)
+    return hip_status(launch_prefill(Q, K, V, in_dtype, BH, N, dk, n, p, states_in, O, den, states,
+                                     (float*)workspace, (hipStream_t)stream, 0, BH),
+                      what);
+  // head groups, one after another on the stream, each with the workspace
+  const size_t esz = in_dtype == TT_BF16 ? 2 : 4;
+  PrefillPlan pg = p;
+  for (int g0 = 0; g0 < BH; g0 += group) {
+    const int gs = group < BH - g0 ? group : BH - g0;
+    pg.ws_floats = p.ws_floats / (size_t)BH * (size_t)gs;
+    const hipError_t e = launch_prefill((const char*)Q + (size_t)g0 * N * dk * esz,
+                                        (const char*)K + (size_t)g0 * N * dk * esz,
+                                        (const char*)V + (size_t)g0 * N * dv * esz, in_dtype, gs, N, dk, n, pg,
+                                        states_in, O + (size_t)g0 * N * dv, den ? den + (size_t)g0 * N : nullptr,
+                                        states, (float*)workspace, (hipStream_t)stream, g0, BH);
+    if (e != hipSuccess) return hip_status(e, what);
+  }
+  return ok();
 }
 
 static int decode_impl(const void* q, const void* k, const void* v, tt_dtype in_dtype, int B, int H, int dk,
@@ -301,6 +334,10 @@ int tt_prefill_noalloc(const void* Q, const void* K, const void* V, tt_dtype in_
   size_t need = 0;
   int rc = tt_prefill_workspace_bytes_dtype(B, H, N, dk, dv, n, chunk, in_dtype, &need);
   if (rc) return rc;
+  // a streamed plan runs its heads in groups that fit the scratch
+  PrefillPlan p;
+  if (plan_prefill(B, H, N, dk, dv, n, chunk, in_dtype, &p) == TT_OK && p.streamed)
+    need = p.ws_floats / ((size_t)B * H) * sizeof(float);
   if (need > (size_t)TT_NOALLOC_SCRATCH_BYTES)
     return fail(TT_ERR_WORKSPACE,
                 "this shape needs %zu bytes of scratch; tt_prefill_noalloc holds %zu (use tt_prefill with a "

@@ -51,15 +51,20 @@ struct PrefillPlan {
   int nrg;        // row groups (workgroups per head-span and column group)
   size_t part_floats;  // row-group partial outputs, floats (0 with one row group)
   size_t ws_floats;    // workspace: span states, then the partial outputs, floats
+  bool streamed;       // the streamed-state path: spans of a fixed length, whatever the head count, so the
+                       // heads can run in groups with one group's workspace (ws_floats is per head x BH)
 };
 
 int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype dt, PrefillPlan* p);
 // states_in: carried-in states in the plane layout, or null for zero states.
 // den_out: null for normalised outputs; otherwise O receives the numerators
-// and den_out [BH][N] the normalisers.
+// and den_out [BH][N] the normalisers.  Q, K, V, O and den_out hold the BH
+// heads of this launch; states_in and states hold BHtot heads (plane layout)
+// of which this launch's are bh0 .. bh0 + BH - 1 (bh0 = 0, BHtot = BH except
+// for head groups of a streamed plan).
 hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype dt, int BH, int N, int dk,
                           int n, const PrefillPlan& p, const float* states_in, float* O, float* den_out,
-                          float* states, float* ws, hipStream_t s);
+                          float* states, float* ws, hipStream_t s, int bh0, int BHtot);
 
 // The sweep-kernel prefill path for chunks of 16, 32 and 128 tokens (one
 // compilation unit each): plan figures and launches, as for 64 tokens.

@@ -81,6 +81,7 @@ int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype
     p->nrg = nrg;
     p->part_floats = 0;
     p->ws_floats = (size_t)BH * p->nspan * (size_t)wp * (kDV + 1);
+    p->streamed = true;
     return TT_OK;
   }
   const int nchunk = (N + chunk - 1) / chunk;
@@ -100,12 +101,15 @@ int plan_prefill(int B, int H, int N, int dk, int dv, int n, int chunk, tt_dtype
   p->nrg = nrg;
   p->part_floats = nrg > 1 ? (size_t)BH * nrg * (size_t)N * (kDV + 1) : 0;
   p->ws_floats = (size_t)BH * nspan * (size_t)wp * (kDV + 1) + p->part_floats;
+  p->streamed = false;
   return TT_OK;
 }
 
 hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype dt, int BH, int N, int dk, int n,
                           const PrefillPlan& p, const float* states_in, float* O, float* den_out, float* states,
-                          float* ws, hipStream_t s) {
+                          float* ws, hipStream_t s, int bh0, int BHtot) {
+  // head groups (bh0 > 0 or BHtot > BH) exist for the streamed paths only
+  if (!p.streamed && (bh0 != 0 || BHtot != BH)) return hipErrorInvalidValue;
   if (p.chunk == 16) return sweep_launch_chunk16(Q, K, V, dt, BH, N, dk, n, p, states_in, O, den_out, states, ws, s);
   if (p.chunk == 32) return sweep_launch_chunk32(Q, K, V, dt, BH, N, dk, n, p, states_in, O, den_out, states, ws, s);
   if (p.chunk == 128)
@@ -113,14 +117,17 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, tt_dtype 
   return with_dkn(dk, n, [&](auto DKc, auto Nc) -> hipError_t {
     constexpr int DK = decltype(DKc)::value, NT = decltype(Nc)::value;
     if constexpr (use_stream<DK, NT>()) {
-      if (dt == TT_BF16) return stream_launch<DK>(Q, K, V, BH, N, p, states_in, O, den_out, states, ws, s);
+      if (dt == TT_BF16)
+        return stream_launch<DK>(Q, K, V, BH, N, p, states_in, O, den_out, states, ws, s, bh0, BHtot);
     }
     if constexpr (use_stream_f32<DK, NT>()) {
       if (dt == TT_F32)
-        return stream_launch_f32<DK, NT, float>(Q, K, V, BH, N, p, states_in, O, den_out, states, ws, s);
+        return stream_launch_f32<DK, NT, float>(Q, K, V, BH, N, p, states_in, O, den_out, states, ws, s, bh0,
+                                                BHtot);
       if constexpr (bf16_uses_stream_f32<DK, NT>()) {
         if (dt == TT_BF16)
-          return stream_launch_f32<DK, NT, uint16_t>(Q, K, V, BH, N, p, states_in, O, den_out, states, ws, s);
+          return stream_launch_f32<DK, NT, uint16_t>(Q, K, V, BH, N, p, states_in, O, den_out, states, ws, s,
+                                                     bh0, BHtot);
       }
     }
     if constexpr (use_pipe<DK, NT>()) {

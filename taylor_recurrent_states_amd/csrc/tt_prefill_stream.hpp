@@ -381,9 +381,12 @@ __global__ __launch_bounds__(256, 3) void stream_totals_kernel(const uint16_t* _
 // group's writes.
 template <int DK>
 __global__ __launch_bounds__(256) void stream_scan_kernel(float* ws, int nspan, int WP, int BH, int W,
-                                                          const float* init, float* states) {
+                                                          const float* init, float* states, int bh0, int BHtot) {
   using C = StCfg<DK>;
   const int bh = blockIdx.x / C::NKB, j = blockIdx.x % C::NKB;
+  // init and states hold BHtot heads (plane layout); this launch scans heads
+  // bh0 .. bh0 + BH - 1 of them, whose span states the workspace holds
+  const size_t gh = (size_t)bh0 + bh;
   const int lane = threadIdx.x & 63, ct = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const bool den_lane = ct == 0 && li == 0;
@@ -397,12 +400,12 @@ __global__ __launch_bounds__(256) void stream_scan_kernel(float* ws, int nspan, 
   float run[8], runz[8], run0 = 0.f, runz0 = 0.f;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    run[u] = (init != nullptr && ra[u] >= 0) ? init[((size_t)bh * W + ra[u]) * kDV + col] : 0.f;
-    runz[u] = (init != nullptr && ra[u] >= 0) ? init[(size_t)BH * W * kDV + (size_t)bh * W + ra[u]] : 0.f;
+    run[u] = (init != nullptr && ra[u] >= 0) ? init[(gh * W + ra[u]) * kDV + col] : 0.f;
+    runz[u] = (init != nullptr && ra[u] >= 0) ? init[(size_t)BHtot * W * kDV + gh * W + ra[u]] : 0.f;
   }
   if (init != nullptr) {
-    run0 = init[((size_t)bh * W + r0) * kDV + col];
-    runz0 = init[(size_t)BH * W * kDV + (size_t)bh * W + r0];
+    run0 = init[(gh * W + r0) * kDV + col];
+    runz0 = init[(size_t)BHtot * W * kDV + gh * W + r0];
   }
   constexpr int G = 4;  // spans whose loads are in flight together
   for (int s0 = 0; s0 < nspan; s0 += G) {
@@ -460,8 +463,8 @@ __global__ __launch_bounds__(256) void stream_scan_kernel(float* ws, int nspan, 
   }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    if (ra[u] >= 0) states[((size_t)bh * W + ra[u]) * kDV + col] = run[u];
-    if (den_lane && ra[u] >= 0) states[(size_t)BH * W * kDV + (size_t)bh * W + ra[u]] = runz[u];
+    if (ra[u] >= 0) states[(gh * W + ra[u]) * kDV + col] = run[u];
+    if (den_lane && ra[u] >= 0) states[(size_t)BHtot * W * kDV + gh * W + ra[u]] = runz[u];
   }
 }
 
@@ -814,10 +817,11 @@ __device__ inline size_t stf_frag_off(int j, int ct, int l) {
 // 0-15 also take the block's normaliser rows (in place, natural layout).
 template <int DK, int NT>
 __global__ __launch_bounds__(256) void stream_scan_f32_kernel(float* ws, int nspan, int WP, int BH,
-                                                              const float* init, float* states) {
+                                                              const float* init, float* states, int bh0, int BHtot) {
   using C = StF<DK, NT>;
   constexpr int W = C::W;
   const int bh = blockIdx.x / C::NKB, j = blockIdx.x % C::NKB;
+  const size_t gh = (size_t)bh0 + bh;  // head in init and states (BHtot heads)
   const int lane = threadIdx.x & 63, ct = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const bool den_lane = ct == 0 && lane < 16;
@@ -829,9 +833,9 @@ __global__ __launch_bounds__(256) void stream_scan_f32_kernel(float* ws, int nsp
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int r = 16 * j + 4 * lg + u;
-    run[u] = (init != nullptr && r < W) ? init[((size_t)bh * W + r) * kDV + col] : 0.f;
+    run[u] = (init != nullptr && r < W) ? init[(gh * W + r) * kDV + col] : 0.f;
   }
-  if (init != nullptr && den_lane && rd < W) rund = init[(size_t)BH * W * kDV + (size_t)bh * W + rd];
+  if (init != nullptr && den_lane && rd < W) rund = init[(size_t)BHtot * W * kDV + gh * W + rd];
   constexpr int G = 4;
   for (int s0 = 0; s0 < nspan; s0 += G) {
     float t[G][4], td[G];
@@ -863,9 +867,9 @@ __global__ __launch_bounds__(256) void stream_scan_f32_kernel(float* ws, int nsp
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int r = 16 * j + 4 * lg + u;
-    if (r < W) states[((size_t)bh * W + r) * kDV + col] = run[u];
+    if (r < W) states[(gh * W + r) * kDV + col] = run[u];
   }
-  if (den_lane && rd < W) states[(size_t)BH * W * kDV + (size_t)bh * W + rd] = rund;
+  if (den_lane && rd < W) states[(size_t)BHtot * W * kDV + gh * W + rd] = rund;
 }
 
 // Output pass for fp32 inputs: one workgroup of 4 waves per 128 queries of a
@@ -1369,7 +1373,7 @@ constexpr bool bf16_uses_stream_f32() { return DK >= 16 && NT >= 4; }
 template <int DK, int NT, class TIn>
 hipError_t stream_launch_f32(const void* Q, const void* K, const void* V, int BH, int N, const PrefillPlan& p,
                              const float* states_in, float* O, float* den_out, float* states, float* ws,
-                             hipStream_t s) {
+                             hipStream_t s, int bh0, int BHtot) {
   using T = StFT<DK, NT>;
   const uint32_t* big = nullptr;
   if constexpr (runtime_rows<DK, NT>()) {
@@ -1383,7 +1387,7 @@ hipError_t stream_launch_f32(const void* Q, const void* K, const void* V, int BH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((stream_scan_f32_kernel<DK, NT>), dim3((unsigned)(BH * StF<DK, NT>::NKB)), dim3(256), 0, s, ws,
-                     p.nspan, (int)T::WP, BH, states_in, states);
+                     p.nspan, (int)T::WP, BH, states_in, states, bh0, BHtot);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(sgs * kStT);
@@ -1405,7 +1409,8 @@ constexpr bool use_stream() { return NT == 3 && (DK == 32 || DK == 64); }
 
 template <int DK>
 hipError_t stream_launch(const void* Q, const void* K, const void* V, int BH, int N, const PrefillPlan& p,
-                         const float* states_in, float* O, float* den_out, float* states, float* ws, hipStream_t s) {
+                         const float* states_in, float* O, float* den_out, float* states, float* ws, hipStream_t s,
+                         int bh0, int BHtot) {
   using T = StTot<DK>;
   static_assert(StCfg<DK>::NKB * 32 <= T::WP, "the readout's row blocks lie inside the span state");
   const unsigned hsg = (unsigned)((BH * p.nspan + 7) / 8 * 8);  // (head, span) pairs, padded to the 8 XCDs
@@ -1414,7 +1419,7 @@ hipError_t stream_launch(const void* Q, const void* K, const void* V, int BH, in
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((stream_scan_kernel<DK>), dim3((unsigned)(BH * StCfg<DK>::NKB)), dim3(256), 0, s, ws, p.nspan,
-                     (int)T::WP, BH, p.W, states_in, states);
+                     (int)T::WP, BH, p.W, states_in, states, bh0, BHtot);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(hsg * kStT);

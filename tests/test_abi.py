@@ -67,6 +67,41 @@ def test_widest_shapes_plan_the_streamed_path():
             assert e.value.code == ops.TT_ERR_UNSUPPORTED
 
 
+def test_head_groups_need_one_heads_share_of_the_workspace():
+    """A streamed plan takes a workspace of at least one head's share of the
+    span states (it then runs the heads in groups); the other plans, and the
+    normalised prefill, take the whole workspace.  Both are refused before
+    anything is launched."""
+    L = ops.lib()
+    fake = ctypes.c_void_p(0x1000)
+    ws = ctypes.c_void_p(0x100000)
+    need = ops.tt_prefill_workspace_bytes_dtype(1, 3, 1100, 64, 64, 3, 64, "bf16")
+    per_head = need // 3
+    assert per_head * 3 == need
+    rc = L.tt_prefill(fake, fake, fake, 1, 1, 3, 1100, 64, 64, 3, 64, fake, fake, ws, per_head - 256, None)
+    assert rc == ops.TT_ERR_WORKSPACE and "per head" in ops.tt_last_error()
+    need = ops.tt_prefill_workspace_bytes_dtype(1, 3, 1100, 16, 64, 3, 32, "f32")  # the chunk-32 sweep
+    rc = L.tt_prefill(fake, fake, fake, 0, 1, 3, 1100, 16, 64, 3, 32, fake, fake, ws, need - 256, None)
+    assert rc == ops.TT_ERR_WORKSPACE and "per head" not in ops.tt_last_error()
+    wn = ops.tt_prefill_normed_workspace_bytes(1, 3, 1100, 64, 64, 3)
+    rc = L.tt_prefill_normed(fake, fake, fake, 1, 1, 3, 1100, 64, 64, 3, 64, ctypes.c_float(1.0), None, fake, fake,
+                             ws, wn // 2, None)
+    assert rc == ops.TT_ERR_WORKSPACE
+    # one head's share passes the workspace check (a misaligned Q then stops the call)
+    odd = ctypes.c_void_p(0x1002)
+    for B, H, N, dk, n, dt in ((1, 5, 2100, 64, 3, "bf16"), (2, 2, 1500, 16, 5, "f32"), (1, 3, 1100, 32, 4, "bf16"),
+                               (1, 3, 1100, 64, 5, "bf16"), (1, 3, 1100, 32, 3, "bf16")):
+        need = ops.tt_prefill_workspace_bytes_dtype(B, H, N, dk, 64, n, 64, dt)
+        assert need % (B * H) == 0
+        code = 1 if dt == "bf16" else 0
+        rc = L.tt_prefill(odd, fake, fake, code, B, H, N, dk, 64, n, 64, fake, fake, ws, need // (B * H), None)
+        assert rc == ops.TT_ERR_INVALID_ARG and "aligned" in ops.tt_last_error(), (B, H, N, dk, n, dt)
+    # tt_prefill_noalloc: one head's share must fit its array
+    assert ops.tt_prefill_workspace_bytes_dtype(1, 16, 8192, 16, 64, 5, 32, "f32") > ops.TT_NOALLOC_SCRATCH_BYTES
+    rc = L.tt_prefill_noalloc(fake, fake, fake, 0, 1, 16, 8192, 16, 64, 5, 32, fake, fake, None)
+    assert rc == ops.TT_ERR_WORKSPACE and "noalloc" in ops.tt_last_error()
+
+
 def test_entry_points_reject_bad_arguments_without_launching():
     L = ops.lib()
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first

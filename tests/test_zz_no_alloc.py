@@ -3,8 +3,10 @@ memory, with its workspace in the library's fixed device scratch array.
 Checked through the C ABI against tt_prefill (the entry point it varies),
 bit for bit: the same kernels and plans run, only the workspace differs.
 Two calls in a row, the second smaller, so the second runs on scratch left
-over from the first; a shape whose workspace exceeds the array is refused
-before anything is launched."""
+over from the first.  A streamed plan whose whole workspace exceeds the
+array runs its heads in groups that fit it (same results); a shape whose
+workspace exceeds the array otherwise is refused before anything is
+launched."""
 import numpy as np
 import pytest
 
@@ -15,14 +17,14 @@ from taylor_recurrent_states_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 
-def _run_both(B, H, N, dk, n, dtype, seed):
+def _run_both(B, H, N, dk, n, dtype, seed, chunk=64):
     import torch
     q, k, v = wl.draw_qkv(seed, B, H, N, dk, 64, dtype)
     Q, K, V = to_device(q), to_device(k), to_device(v)
-    O_ref, S_ref = ops.tt_prefill(Q, K, V, n)
+    O_ref, S_ref = ops.tt_prefill(Q, K, V, n, chunk)
     O = torch.full_like(O_ref, float("nan"))
     S = torch.full_like(S_ref, float("nan"))
-    ops.tt_prefill_noalloc(Q, K, V, n, 64, O, S)
+    ops.tt_prefill_noalloc(Q, K, V, n, chunk, O, S)
     torch.cuda.synchronize()
     assert torch.equal(O, O_ref), f"B{B} H{H} N{N} dk{dk} n{n} {dtype}: outputs differ"
     assert torch.equal(S, S_ref), f"B{B} H{H} N{N} dk{dk} n{n} {dtype}: states differ"
@@ -37,17 +39,26 @@ def test_noalloc_matches_prefill_twice_then_smaller():
     _run_both(1, 3, 777, 32, 3, "bf16", 33)
 
 
+def test_noalloc_runs_streamed_heads_in_groups():
+    """dk 64, n 3, bf16 on 16 heads: 81 MB of span states, 5 MB per head"""
+    need = ops.tt_prefill_workspace_bytes_dtype(1, 16, 8192, 64, 64, 3, 64, "bf16")
+    assert need > ops.TT_NOALLOC_SCRATCH_BYTES
+    print("\n[noalloc] streamed plan in head groups", flush=True)
+    _run_both(1, 16, 8192, 64, 3, "bf16", 34)
+
+
 def test_noalloc_refuses_shapes_beyond_the_scratch():
     import torch
-    B, H, N, dk, n = 1, 16, 8192, 64, 3  # the span states alone exceed the array
-    need = ops.tt_prefill_workspace_bytes_dtype(B, H, N, dk, 64, n, 64, "bf16")
+    # the chunk-32 sweep with row-group partial outputs: 337 MiB, no head groups
+    B, H, N, dk, n, chunk = 1, 16, 8192, 16, 5, 32
+    need = ops.tt_prefill_workspace_bytes_dtype(B, H, N, dk, 64, n, chunk, "f32")
     assert need > ops.TT_NOALLOC_SCRATCH_BYTES
-    Q = torch.zeros((B, H, N, dk), dtype=torch.bfloat16, device="cuda")
-    V = torch.zeros((B, H, N, 64), dtype=torch.bfloat16, device="cuda")
+    Q = torch.zeros((B, H, N, dk), device="cuda")
+    V = torch.zeros((B, H, N, 64), device="cuda")
     O = torch.zeros((B, H, N, 64), device="cuda")
     S = torch.zeros(B * H * ops.tt_state_floats(dk, 64, n), device="cuda")
     with pytest.raises(ops.TTError) as e:
-        ops.tt_prefill_noalloc(Q, Q, V, n, 64, O, S)
+        ops.tt_prefill_noalloc(Q, Q, V, n, chunk, O, S)
     assert e.value.code == ops.TT_ERR_WORKSPACE and "scratch" in str(e.value)
     torch.cuda.synchronize()
     assert not O.abs().max().item()  # nothing ran

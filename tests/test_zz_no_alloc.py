@@ -47,6 +47,47 @@ def test_noalloc_runs_streamed_heads_in_groups():
     _run_both(1, 16, 8192, 64, 3, "bf16", 34)
 
 
+def test_noalloc_replays_in_a_captured_graph():
+    """Code under graph capture is what the entry point is for: a captured
+    tt_prefill_noalloc (a streamed plan in two head groups, and the pipe
+    kernel's plan) is replayed three times, with an eager tt_prefill_noalloc
+    on other inputs (which reuses the same scratch) between the replays;
+    every replay equals the eager tt_prefill bit for bit."""
+    import torch
+    for B, H, N, dk, n, seed in ((1, 16, 8192, 64, 3, 35), (2, 4, 3000, 16, 3, 36)):
+        print(f"\n[noalloc graph] B{B} H{H} N{N} dk{dk} n{n} bf16", flush=True)
+        q, k, v = wl.draw_qkv(seed, B, H, N, dk, 64, "bf16")
+        Q, K, V = to_device(q), to_device(k), to_device(v)
+        O_ref, S_ref = ops.tt_prefill(Q, K, V, n)
+        q2, k2, v2 = wl.draw_qkv(seed + 100, 1, 2, 1500, dk, 64, "bf16")
+        Q2, K2, V2 = to_device(q2), to_device(k2), to_device(v2)
+        O2 = torch.empty((1, 2, 1500, 64), device="cuda")
+        S2 = torch.empty(2 * ops.tt_state_floats(dk, 64, n), device="cuda")
+        O = torch.empty_like(O_ref)
+        S = torch.empty_like(S_ref)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm-up outside the capture
+            ops.tt_prefill_noalloc(Q, K, V, n, 64, O, S)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            ops.tt_prefill_noalloc(Q, K, V, n, 64, O, S)
+        torch.cuda.synchronize()
+        for r in range(3):
+            O.fill_(float("nan"))
+            S.fill_(float("nan"))
+            torch.cuda.synchronize()
+            gr.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(O, O_ref), f"replay {r}: outputs"
+            assert torch.equal(S, S_ref), f"replay {r}: states"
+            ops.tt_prefill_noalloc(Q2, K2, V2, n, 64, O2, S2)  # eager, same scratch
+            torch.cuda.synchronize()
+        del gr
+
+
 def test_noalloc_refuses_shapes_beyond_the_scratch():
     import torch
     # the chunk-32 sweep with row-group partial outputs: 337 MiB, no head groups

@@ -125,7 +125,8 @@ int tt_prefill_workspace_bytes_dtype(int B, int H, int N, int dk, int dv, int n,
  *            bf16 with n=3 at dk=32 and 64, bf16 with n>=4 at dk>=16)
  *            also take a smaller
  *            workspace: at least one head's share, the size for B*H heads
- *            divided by B*H.  The heads (b, h in flattened order) then
+ *            divided by B*H (the query's result for B = H = 1).  The
+ *            heads (b, h in flattened order) then
  *            run in groups of as many heads as the workspace holds, one
  *            group after another on `stream`, with bit-identical results;
  *            each group re-reads nothing of the others, so the cost is
@@ -247,7 +248,10 @@ int tt_prefill_normed_workspace_bytes(int B, int H, int N, int dk, int dv, int n
  * i.e. tt_prefill (states_in == NULL) or tt_prefill_from (states_in given)
  * on q_hat = r(temperature * q/||q||), k_hat = r(k/||k||) as produced by
  * tt_normalize_rows.  The normalised copies live in the workspace, which
- * must hold tt_prefill_normed_workspace_bytes().  temperature must be
+ * must hold tt_prefill_normed_workspace_bytes(); the plans that run heads in
+ * groups (see tt_prefill) also take as little as one head's share, the size
+ * that query reports for B = H = 1, and then normalise each group's rows
+ * into the workspace before its prefill (same results).  temperature must be
  * finite and > 0; the other arguments, layouts and errors are those of
  * tt_prefill_from.  Q and K are read-only. */
 int tt_prefill_normed(const void *Q, const void *K, const void *V, tt_dtype in_dtype,

@@ -92,23 +92,29 @@ static int prefill_impl(const void* Q, const void* K, const void* V, tt_dtype in
   if (normed && !valid_scale(qscale))
     return fail(TT_ERR_INVALID_ARG, "temperature %g must be finite and positive", (double)qscale);
   // Streamed plans (spans of a fixed length) run the heads in groups when the
-  // workspace holds the span states of fewer than all heads but at least one
-  // (not with the normalisation, whose copies of Q and K need the full size).
+  // workspace holds the span states (and, normalised, the copies of Q and K)
+  // of fewer than all heads but at least one.
   const int BH = B * H;
+  const size_t per_head = base / (size_t)BH;
+  auto need_for = [&](size_t g) {
+    return normed ? align256(per_head * g) + 2 * normed_copy_bytes(1, (int)g, N, dk) : per_head * g;
+  };
   int group = BH;
   size_t used = need;
-  if (!normed && p.streamed && workspace && need > 0 && workspace_bytes < need) {
-    const size_t per_head = base / (size_t)BH;
-    const size_t g = workspace_bytes / per_head;
+  if (p.streamed && workspace && need > 0 && workspace_bytes < need) {
+    const size_t per_total = need_for(1);
+    size_t g = workspace_bytes / per_total;  // within one of the largest fit
+    while (g > 0 && need_for(g) > workspace_bytes) --g;
+    while (g + 1 < (size_t)BH && need_for(g + 1) <= workspace_bytes) ++g;
     if (g >= 1) {
       group = (int)g;
-      used = per_head * g;
+      used = need_for(g);
     }
   }
   if (need > 0 && (!workspace || workspace_bytes < used)) {
-    if (!normed && p.streamed)
+    if (p.streamed)
       return fail(TT_ERR_WORKSPACE, "workspace of %zu bytes needed (or %zu per head, heads in groups), %zu given",
-                  need, base / (size_t)BH, workspace ? workspace_bytes : (size_t)0);
+                  need, need_for(1), workspace ? workspace_bytes : (size_t)0);
     return fail(TT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
   }
@@ -132,29 +138,27 @@ static int prefill_impl(const void* Q, const void* K, const void* V, tt_dtype in
   }
   char what[64];
   snprintf(what, sizeof(what), "%s launch", name);
-  if (normed) {
-    unsigned char* qn = (unsigned char*)workspace + align256(base);
-    unsigned char* kn = qn + copy;
-    const size_t rows = (size_t)B * H * N;
-    hipError_t e = launch_normalize(in_dtype, dk, Q, qn, qscale, rows, K, kn, 1.0f, rows, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_status(e, what);
-    Q = qn;
-    K = kn;
-  }
-  if (group == BH)
-    return hip_status(launch_prefill(Q, K, V, in_dtype, BH, N, dk, n, p, states_in, O, den, states,
-                                     (float*)workspace, (hipStream_t)stream, 0, BH),
-                      what);
-  // head groups, one after another on the stream, each with the workspace
+  // head groups (one group of all heads when the workspace holds them), one
+  // after another on the stream, each with the workspace from its start
   const size_t esz = in_dtype == TT_BF16 ? 2 : 4;
   PrefillPlan pg = p;
   for (int g0 = 0; g0 < BH; g0 += group) {
     const int gs = group < BH - g0 ? group : BH - g0;
     pg.ws_floats = p.ws_floats / (size_t)BH * (size_t)gs;
-    const hipError_t e = launch_prefill((const char*)Q + (size_t)g0 * N * dk * esz,
-                                        (const char*)K + (size_t)g0 * N * dk * esz,
-                                        (const char*)V + (size_t)g0 * N * dv * esz, in_dtype, gs, N, dk, n, pg,
-                                        states_in, O + (size_t)g0 * N * dv, den ? den + (size_t)g0 * N : nullptr,
+    const void* Qg = (const char*)Q + (size_t)g0 * N * dk * esz;
+    const void* Kg = (const char*)K + (size_t)g0 * N * dk * esz;
+    if (normed) {  // normalised copies of this group's rows after its span states
+      unsigned char* qn = (unsigned char*)workspace + align256(pg.ws_floats * sizeof(float));
+      unsigned char* kn = qn + normed_copy_bytes(1, gs, N, dk);
+      const size_t rows = (size_t)gs * N;
+      const hipError_t e =
+          launch_normalize(in_dtype, dk, Qg, qn, qscale, rows, Kg, kn, 1.0f, rows, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_status(e, what);
+      Qg = qn;
+      Kg = kn;
+    }
+    const hipError_t e = launch_prefill(Qg, Kg, (const char*)V + (size_t)g0 * N * dv * esz, in_dtype, gs, N, dk, n,
+                                        pg, states_in, O + (size_t)g0 * N * dv, den ? den + (size_t)g0 * N : nullptr,
                                         states, (float*)workspace, (hipStream_t)stream, g0, BH);
     if (e != hipSuccess) return hip_status(e, what);
   }

@@ -68,9 +68,9 @@ def test_widest_shapes_plan_the_streamed_path():
 
 
 def test_head_groups_need_one_heads_share_of_the_workspace():
-    """A streamed plan takes a workspace of at least one head's share of the
-    span states (it then runs the heads in groups); the other plans, and the
-    normalised prefill, take the whole workspace.  Both are refused before
+    """A streamed plan takes a workspace of at least one head's share (it
+    then runs the heads in groups), with or without the normalisation; the
+    other plans take the whole workspace.  Smaller ones are refused before
     anything is launched."""
     L = ops.lib()
     fake = ctypes.c_void_p(0x1000)
@@ -83,10 +83,18 @@ def test_head_groups_need_one_heads_share_of_the_workspace():
     need = ops.tt_prefill_workspace_bytes_dtype(1, 3, 1100, 16, 64, 3, 32, "f32")  # the chunk-32 sweep
     rc = L.tt_prefill(fake, fake, fake, 0, 1, 3, 1100, 16, 64, 3, 32, fake, fake, ws, need - 256, None)
     assert rc == ops.TT_ERR_WORKSPACE and "per head" not in ops.tt_last_error()
-    wn = ops.tt_prefill_normed_workspace_bytes(1, 3, 1100, 64, 64, 3)
+    # the normalised prefill: one head's share of its workspace (the query at B = H = 1), not less
+    w1 = ops.tt_prefill_normed_workspace_bytes(1, 1, 1100, 64, 64, 3)
     rc = L.tt_prefill_normed(fake, fake, fake, 1, 1, 3, 1100, 64, 64, 3, 64, ctypes.c_float(1.0), None, fake, fake,
-                             ws, wn // 2, None)
-    assert rc == ops.TT_ERR_WORKSPACE
+                             ws, w1 // 2, None)
+    assert rc == ops.TT_ERR_WORKSPACE and "per head" in ops.tt_last_error()
+    rc = L.tt_prefill_normed(ctypes.c_void_p(0x1002), fake, fake, 1, 1, 3, 1100, 64, 64, 3, 64, ctypes.c_float(1.0),
+                             None, fake, fake, ws, w1, None)
+    assert rc == ops.TT_ERR_INVALID_ARG and "aligned" in ops.tt_last_error()
+    # a sweep plan's normalised prefill takes its whole workspace
+    rc = L.tt_prefill_normed(fake, fake, fake, 0, 1, 3, 1100, 16, 64, 3, 32, ctypes.c_float(1.0), None, fake, fake,
+                             ws, 4096, None)
+    assert rc == ops.TT_ERR_WORKSPACE and "per head" not in ops.tt_last_error()
     # one head's share passes the workspace check (a misaligned Q then stops the call)
     odd = ctypes.c_void_p(0x1002)
     for B, H, N, dk, n, dt in ((1, 5, 2100, 64, 3, "bf16"), (2, 2, 1500, 16, 5, "f32"), (1, 3, 1100, 32, 4, "bf16"),

@@ -5,9 +5,9 @@ four or more terms) then run the heads in groups, one after another, each
 group through the same kernels and the same spans, so every output and
 state must be bit-identical to the call with the whole workspace.  Checked
 for tt_prefill, tt_prefill_from (carried-in states of the heads of every
-group) and tt_prefill_from_unnormalized; a workspace below one head's
-share, and the normalised prefill with less than its whole workspace, are
-refused before anything runs."""
+group), tt_prefill_from_unnormalized and tt_prefill_normed (each group's
+rows of Q and K normalised into its share of the workspace); a workspace
+below one head's share is refused before anything runs."""
 import pytest
 
 from gpu_util import to_device
@@ -43,6 +43,16 @@ def test_head_groups_match_the_whole_workspace(B, H, N, dk, n, dtype, group):
     num, den, S3 = ops.tt_prefill_from_unnormalized(Q, K, V, S_ref, n, workspace=small)
     torch.cuda.synchronize()
     assert torch.equal(num, num_ref) and torch.equal(den, den_ref) and torch.equal(S3, S3_ref), "unnormalised"
+    # raw q, k: each group's rows are normalised into its share of the workspace
+    Qr, Kr = Q * 1.5, K * 0.75
+    wn = ops.tt_prefill_normed_workspace_bytes(B, H, N, dk, 64, n)
+    wg = ops.tt_prefill_normed_workspace_bytes(1, group, N, dk, 64, n)
+    assert wg < wn
+    small_n = torch.empty(wg, dtype=torch.uint8, device="cuda")
+    O4_ref, S4_ref = ops.tt_prefill_normed(Qr, Kr, V, n, 0.9, states_in=S_ref)
+    O4, S4 = ops.tt_prefill_normed(Qr, Kr, V, n, 0.9, states_in=S_ref, workspace=small_n)
+    torch.cuda.synchronize()
+    assert torch.equal(O4, O4_ref) and torch.equal(S4, S4_ref), "normalised"
 
 
 def test_head_groups_refuse_less_than_one_head():
@@ -56,9 +66,9 @@ def test_head_groups_refuse_less_than_one_head():
     with pytest.raises(ops.TTError) as e:
         ops.tt_prefill(Q, K, V, n, O=O, workspace=tiny)
     assert e.value.code == ops.TT_ERR_WORKSPACE and "per head" in str(e.value)
-    # the normalised prefill keeps copies of Q and K in its workspace: whole size only
-    wn = ops.tt_prefill_normed_workspace_bytes(B, H, N, dk, 64, n)
-    half = torch.empty(wn // 2, dtype=torch.uint8, device="cuda")
+    # the normalised prefill: less than one head's share of its workspace
+    w1 = ops.tt_prefill_normed_workspace_bytes(1, 1, N, dk, 64, n)
+    half = torch.empty(w1 // 2, dtype=torch.uint8, device="cuda")
     with pytest.raises(ops.TTError) as e:
         ops.tt_prefill_normed(Q, K, V, n, 1.0, O=O, workspace=half)
     assert e.value.code == ops.TT_ERR_WORKSPACE

@@ -74,3 +74,25 @@ def test_head_groups_refuse_less_than_one_head():
     assert e.value.code == ops.TT_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert not O.abs().max().item()  # nothing ran
+
+
+@pytest.mark.parametrize("B,H,N,dk,n,dtype,group", [(1, 16, 65536, 64, 3, "bf16", 2), (1, 16, 16384, 16, 5, "f32", 4)])
+def test_head_groups_at_full_size(B, H, N, dk, n, dtype, group):
+    """The wide-key (dk 64, 65,536 tokens) and order-5 workloads at their
+    full sizes with a workspace of at most 100 MB (2 and 4 heads per group):
+    bit-identical to the whole workspace."""
+    import torch
+    print(f"\n[groups full size] B{B} H{H} N{N} dk{dk} n{n} {dtype}, {group} heads per group", flush=True)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5300 + dk)
+    Q = torch.nn.functional.normalize(torch.randn((B, H, N, dk), generator=g, device="cuda"), dim=-1).to(dt)
+    K = torch.nn.functional.normalize(torch.randn((B, H, N, dk), generator=g, device="cuda"), dim=-1).to(dt)
+    V = torch.randn((B, H, N, 64), generator=g, device="cuda").to(dt)
+    per_head = ops.tt_prefill_workspace_bytes_dtype(1, 1, N, dk, 64, n, 64, dtype)
+    assert per_head * group <= 100_000_000
+    O_ref, S_ref = ops.tt_prefill(Q, K, V, n)
+    ws = torch.empty(per_head * group, dtype=torch.uint8, device="cuda")
+    O, S = ops.tt_prefill(Q, K, V, n, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O_ref) and torch.equal(S, S_ref)

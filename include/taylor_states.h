@@ -123,16 +123,15 @@ int tt_prefill_workspace_bytes_dtype(int B, int H, int N, int dk, int dv, int n,
  *            contents undefined on return.  Plans with spans of a fixed
  *            length (at chunk 64: fp32 with more than 256 state rows W,
  *            bf16 with n=3 at dk=32 and 64, bf16 with n>=4 at dk>=16)
- *            also take a smaller
- *            workspace: at least one head's share, the size for B*H heads
- *            divided by B*H (the query's result for B = H = 1).  The
- *            heads (b, h in flattened order) then
- *            run in groups of as many heads as the workspace holds, one
- *            group after another on `stream`, with bit-identical results;
- *            each group re-reads nothing of the others, so the cost is
- *            fewer workgroups per launch.  Less than one head's share,
- *            or a smaller workspace for the other plans, is
- *            TT_ERR_WORKSPACE.
+ *            also take a smaller workspace of at least one head's share:
+ *            tt_prefill_workspace_bytes_dtype() for B = H = 1, which is the
+ *            size for B*H heads divided by B*H.  The heads (b, h in
+ *            flattened order) then run in groups of as many heads as the
+ *            workspace holds, one group after another on `stream`, with
+ *            bit-identical results.  No group reads another group's
+ *            share, so the only cost is fewer workgroups per launch.  Less
+ *            than one head's share, or less than the whole workspace for
+ *            the other plans, is TT_ERR_WORKSPACE.
  *   chunk : tokens per chunk of the intra-chunk quadratic block: 16, 32,
  *           64 or 128.  Results do not depend on it beyond fp32 rounding
  *           (it moves work between the quadratic block and the state).

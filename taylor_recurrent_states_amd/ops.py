@@ -262,7 +262,7 @@ def tt_prefill_normed_workspace_bytes(B: int, H: int, N: int, dk: int, dv: int, 
     return int(out.value)
 
 
-def _prefill_args(Q, K, V, n, chunk, O, states, workspace, launch, normed=False, extra=()):
+def _prefill_args(Q, K, V, n, chunk, O, states, workspace, launch, normed=False, extra=(), max_ws=None):
     torch = _torch()
     B, H, N, dk, dv = _qkv(Q, K, V)
     nstate = B * H * tt_state_floats(dk, dv, n)
@@ -282,6 +282,12 @@ def _prefill_args(Q, K, V, n, chunk, O, states, workspace, launch, normed=False,
     if states is None:
         states = launch.alloc((nstate,), torch.float32, Q.device)
     if workspace is None and need > 0:
+        # capped: plans that run heads in groups take a smaller workspace, the
+        # library refuses it for the others (TT_ERR_WORKSPACE)
+        if max_ws is not None and int(max_ws) < need:
+            if int(max_ws) < 1:
+                raise ValueError("max_workspace_bytes must be >= 1")
+            need = int(max_ws)
         workspace = launch.alloc((need,), torch.uint8, Q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -291,13 +297,19 @@ def _prefill_args(Q, K, V, n, chunk, O, states, workspace, launch, normed=False,
     return (B, H, N, dk, dv), O, states, workspace, ws_ptr, ws_bytes
 
 
-def tt_prefill(Q, K, V, n: int, chunk: int = 64, O=None, states=None, workspace=None, stream=None):
+def tt_prefill(Q, K, V, n: int, chunk: int = 64, O=None, states=None, workspace=None, stream=None,
+               max_workspace_bytes=None):
     """Causal prefill of Q, K [B, H, N, dk] and V [B, H, N, dv] (float32 or
     bfloat16, same dtype).  Returns (O [B, H, N, dv] float32, states flat
-    float32 in the library's plane layout)."""
+    float32 in the library's plane layout).  Without ``workspace`` one is
+    allocated for the call; ``max_workspace_bytes`` caps it, and plans with
+    spans of a fixed length then run the heads in groups that fit (the
+    other plans refuse a capped workspace with TT_ERR_WORKSPACE).  The same
+    holds for tt_prefill_from, tt_prefill_from_unnormalized and
+    tt_prefill_normed."""
     launch = _Launch(stream)
     (B, H, N, dk, dv), O, states, ws, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace,
-                                                                       launch)
+                                                                       launch, max_ws=max_workspace_bytes)
     _check(lib().tt_prefill(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk, dv, n, chunk,
                             O.data_ptr(), states.data_ptr(), ws_ptr, ws_bytes, launch.handle))
     return O, states
@@ -324,7 +336,7 @@ def tt_prefill_noalloc(Q, K, V, n: int, chunk: int, O, states, stream=None):
 
 
 def tt_prefill_from(Q, K, V, states_in, n: int, chunk: int = 64, O=None, states=None, workspace=None,
-                    stream=None):
+                    stream=None, max_workspace_bytes=None):
     """Prefill continuing from carried-in states (flat float32, plane layout).
     ``states`` may be ``states_in`` itself to continue in place.  Returns
     (O, states)."""
@@ -333,7 +345,8 @@ def tt_prefill_from(Q, K, V, states_in, n: int, chunk: int = 64, O=None, states=
         raise ValueError("states_in is None (use tt_prefill for zero states)")
     _states_in(states_in, Q, K, V, n)
     (B, H, N, dk, dv), O, states, ws, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace,
-                                                                       launch, extra=((states_in, "states_in"),))
+                                                                       launch, extra=((states_in, "states_in"),),
+                                                                       max_ws=max_workspace_bytes)
     _check(lib().tt_prefill_from(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk, dv, n,
                                  chunk, states_in.data_ptr(), O.data_ptr(), states.data_ptr(), ws_ptr, ws_bytes,
                                  launch.handle))
@@ -341,7 +354,7 @@ def tt_prefill_from(Q, K, V, states_in, n: int, chunk: int = 64, O=None, states=
 
 
 def tt_prefill_from_unnormalized(Q, K, V, states_in, n: int, chunk: int = 64, num=None, den=None, states=None,
-                                 workspace=None, stream=None):
+                                 workspace=None, stream=None, max_workspace_bytes=None):
     """tt_prefill_from without the division: returns (num [B, H, N, dv],
     den [B, H, N], states); o = num / den[..., None].  ``states_in`` may be
     None (zero states)."""
@@ -352,7 +365,8 @@ def tt_prefill_from_unnormalized(Q, K, V, states_in, n: int, chunk: int = 64, nu
         B, H, N, _, _ = _qkv(Q, K, V)
         _f32(den, "den", B * H * N)
     (B, H, N, dk, dv), num, states, ws, ws_ptr, ws_bytes = _prefill_args(
-        Q, K, V, n, chunk, num, states, workspace, launch, extra=((states_in, "states_in"), (den, "den")))
+        Q, K, V, n, chunk, num, states, workspace, launch, extra=((states_in, "states_in"), (den, "den")),
+        max_ws=max_workspace_bytes)
     if den is None:
         den = launch.alloc((B, H, N), torch.float32, Q.device)
     sin = states_in.data_ptr() if states_in is not None else 0
@@ -363,7 +377,7 @@ def tt_prefill_from_unnormalized(Q, K, V, states_in, n: int, chunk: int = 64, nu
 
 
 def tt_prefill_normed(Q, K, V, n: int, temperature: float = 1.0, states_in=None, chunk: int = 64, O=None,
-                      states=None, workspace=None, stream=None):
+                      states=None, workspace=None, stream=None, max_workspace_bytes=None):
     """Prefill on raw Q, K: the library normalises them (Q scaled by
     ``temperature``) and runs the prefill, from ``states_in`` (flat float32,
     plane layout) or from zero states when it is None.  Returns (O, states)."""
@@ -371,7 +385,8 @@ def tt_prefill_normed(Q, K, V, n: int, temperature: float = 1.0, states_in=None,
     _states_in(states_in, Q, K, V, n)
     (B, H, N, dk, dv), O, states, ws, ws_ptr, ws_bytes = _prefill_args(Q, K, V, n, chunk, O, states, workspace,
                                                                        launch, normed=True,
-                                                                       extra=((states_in, "states_in"),))
+                                                                       extra=((states_in, "states_in"),),
+                                                                       max_ws=max_workspace_bytes)
     sin = states_in.data_ptr() if states_in is not None else None
     _check(lib().tt_prefill_normed(Q.data_ptr(), K.data_ptr(), V.data_ptr(), _dtype_code(Q), B, H, N, dk, dv, n,
                                    chunk, float(temperature), sin, O.data_ptr(), states.data_ptr(), ws_ptr, ws_bytes,

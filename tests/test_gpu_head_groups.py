@@ -96,3 +96,31 @@ def test_head_groups_at_full_size(B, H, N, dk, n, dtype, group):
     O, S = ops.tt_prefill(Q, K, V, n, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(O, O_ref) and torch.equal(S, S_ref)
+
+
+def test_binding_caps_the_workspace_it_allocates():
+    """max_workspace_bytes: the binding allocates at most that much; a
+    streamed plan then runs in head groups (same results), a sweep plan
+    refuses the capped workspace."""
+    import torch
+    B, H, N, dk, n = 1, 4, 1500, 64, 3
+    print(f"\n[groups via the binding] B{B} H{H} N{N} dk{dk} n{n} bf16", flush=True)
+    q, k, v = wl.draw_qkv(5400, B, H, N, dk, 64, "bf16")
+    Q, K, V = to_device(q), to_device(k), to_device(v)
+    per_head = ops.tt_prefill_workspace_bytes_dtype(1, 1, N, dk, 64, n, 64, "bf16")
+    O_ref, S_ref = ops.tt_prefill(Q, K, V, n)
+    O, S = ops.tt_prefill(Q, K, V, n, max_workspace_bytes=per_head * 3)
+    O2_ref, S2_ref = ops.tt_prefill_from(Q, K, V, S_ref, n)
+    O2, S2 = ops.tt_prefill_from(Q, K, V, S_ref, n, max_workspace_bytes=per_head)
+    w1 = ops.tt_prefill_normed_workspace_bytes(1, 1, N, dk, 64, n)
+    O3_ref, S3_ref = ops.tt_prefill_normed(Q, K, V, n, 1.2)
+    O3, S3 = ops.tt_prefill_normed(Q, K, V, n, 1.2, max_workspace_bytes=w1 * 2)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O_ref) and torch.equal(S, S_ref)
+    assert torch.equal(O2, O2_ref) and torch.equal(S2, S2_ref)
+    assert torch.equal(O3, O3_ref) and torch.equal(S3, S3_ref)
+    with pytest.raises(ops.TTError) as e:  # the chunk-32 sweep: whole workspace only
+        ops.tt_prefill(Q, K, V, n, 32, max_workspace_bytes=per_head)
+    assert e.value.code == ops.TT_ERR_WORKSPACE
+    with pytest.raises(ValueError):
+        ops.tt_prefill(Q, K, V, n, max_workspace_bytes=0)

@@ -107,8 +107,10 @@ static int prefill_impl(const void* Q, const void* K, const void* V, tt_dtype in
     while (g > 0 && need_for(g) > workspace_bytes) --g;
     while (g + 1 < (size_t)BH && need_for(g + 1) <= workspace_bytes) ++g;
     if (g >= 1) {
-      group = (int)g;
-      used = need_for(g);
+      // as many groups as g heads each need, with the heads spread evenly
+      const size_t ngroups = ((size_t)BH + g - 1) / g;
+      group = (int)(((size_t)BH + ngroups - 1) / ngroups);
+      used = need_for((size_t)group);
     }
   }
   if (need > 0 && (!workspace || workspace_bytes < used)) {

@@ -126,9 +126,9 @@ int tt_prefill_workspace_bytes_dtype(int B, int H, int N, int dk, int dv, int n,
  *            also take a smaller workspace of at least one head's share:
  *            tt_prefill_workspace_bytes_dtype() for B = H = 1, which is the
  *            size for B*H heads divided by B*H.  The heads (b, h in
- *            flattened order) then run in groups of as many heads as the
- *            workspace holds, one group after another on `stream`, with
- *            bit-identical results.  No group reads another group's
+ *            flattened order) then run in as few groups as the workspace
+ *            allows, spread evenly over them, one group after another on
+ *            `stream`, with bit-identical results.  No group reads another group's
  *            share, so the only cost is fewer workgroups per launch.  Less
  *            than one head's share, or less than the whole workspace for
  *            the other plans, is TT_ERR_WORKSPACE.
